@@ -1,0 +1,266 @@
+"""Pins of the CPU oracle against facts outside itself (CPU only).
+
+Each pin cites where its fact comes from:
+* the worked example of the study page "Multi-LoRA Serving" (section "The
+  kernel trick: gather, do not merge"): its printed outputs are stored in
+  tests/golden/worked_example.json;
+* the merged-weight identity W' = W + AB (slide 5 of "Thousands of
+  adapters"; option 1 of the study page's demo);
+* closed forms (rank-1 fingerprints, scale 0, id -1, linearity in B);
+* exact rational brute force on tiny inputs.
+
+The last block plants plausible mistakes in the oracle (on the CPU) and
+checks that at least one pin catches each of them.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import lora_oracle as lo
+import workloads as W
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")
+
+
+# ---------------------------------------------------------------- helpers
+def _rel(a, b):
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def _small_bf16():
+    return W.c2_bgmv_decode(seed=7, n_tokens=24, h=256, n_slots=5, rank=8)
+
+
+def _with_adapters(wl, fn):
+    """Copy of ``wl`` with every adapter tuple replaced by fn(rank, scale, A, B)."""
+    import copy
+    w2 = copy.copy(wl)
+    w2.adapters = [[None if a is None else fn(*a) for a in row] for row in wl.adapters]
+    return w2
+
+
+def pin_merged(o=lo):
+    """P1: gathered form == merged-weight form (fp64) on fp32 and bf16 inputs."""
+    ok = True
+    for wl in (W.c1_tiny_f32(), _small_bf16()):
+        for m in range(wl.n_modules):
+            ok &= _rel(o.lora_forward(wl, m), o.merged_forward(wl, m)) <= 1e-12
+    return ok
+
+
+def pin_worked_example(o=lo):
+    """P13: the page's demo: 34 distinct ids, gathered == merged within 1e-3."""
+    gold = json.load(open(GOLD))["printed"]
+    wl = W.c0_worked_example()
+    if len(np.unique(wl.ids)) != gold["distinct_adapters_in_batch"]:
+        return False
+    Wp, Ap, Bp = wl.notes["W_page"], wl.notes["A_page"], wl.notes["B_page"]
+    X, ids, scale = wl.x[0], wl.ids, 2.0
+    Y1 = np.empty_like(X)          # option 1 of the page, fp32, page layout
+    for a in np.unique(ids):
+        rows = ids == a
+        Y1[rows] = X[rows] @ (Wp + scale * Bp[a] @ Ap[a]).T
+    Y2 = o.lora_forward(wl, 0)
+    return bool(np.allclose(Y1, Y2, atol=1e-3)) == gold["same_outputs_allclose_atol_1e-3"]
+
+
+def pin_fingerprint(o=lo):
+    """P4: rank-1 one-hot adapters: the term is x_i[j_a] in column k_a only."""
+    wl = W.fingerprint_rank1(dtype="f32")
+    d = o.lora_delta(wl, 0)
+    x = o.decode(wl.x[0], "f32")
+    exp = np.zeros_like(d)
+    for i, a in enumerate(wl.ids):
+        if 0 <= a < wl.n_slots:
+            exp[i, wl.notes["k"][a]] = x[i, wl.notes["j"][a]]
+    return bool(np.array_equal(d, exp))
+
+
+def _frac_forward(x, Wm, A, B, scale, ids):
+    """Exact rational y_i = x_i W + s (x_i A_a^T) B_a, by triple loops."""
+    n, h_in = len(x), len(x[0])
+    h_out = len(Wm[0])
+    out = []
+    for i in range(n):
+        row = []
+        a = ids[i]
+        for c in range(h_out):
+            acc = Fraction(0)
+            for k in range(h_in):
+                acc += Fraction(float(x[i][k])) * Fraction(float(Wm[k][c]))
+            if a >= 0:
+                for j in range(len(A[a])):
+                    tj = Fraction(0)
+                    for k in range(h_in):
+                        tj += Fraction(float(x[i][k])) * Fraction(float(A[a][j][k]))
+                    acc += Fraction(float(scale[a])) * tj * Fraction(float(B[a][j][c]))
+            row.append(acc)
+        out.append(row)
+    return out
+
+
+def _tiny(seed, integer):
+    rng = np.random.default_rng(seed)
+    n, h_in, h_out, n_slots = 6, 8, 5, 3
+
+    def draw(shape):
+        if integer:
+            return rng.integers(-4, 5, shape).astype(np.float32)
+        return rng.normal(0, 1, shape).astype(np.float32)
+
+    ranks = [1, 2, 2]
+    wl = W.Workload(
+        "tiny", "f32", 1, n_slots, [W.Module("p", h_in, h_out, 0)],
+        np.array([0, 2, -1, 1, 0, 2], np.int32), [draw((n, h_in))],
+        [np.zeros((n, h_out), np.float32)], [draw((h_in, h_out))],
+        [[(ranks[s], 2.0 if integer else 0.75, draw((ranks[s], h_in)),
+           draw((ranks[s], h_out)))] for s in range(n_slots)])
+    return wl
+
+
+def pin_bruteforce(o=lo):
+    """P5/P6: exact rationals.  Integer inputs: bit-exact.  Random fp32 inputs:
+    within fp64 rounding (1e-13 relative per element)."""
+    ok = True
+    for seed, integer in ((1, True), (2, False), (3, False)):
+        wl = _tiny(seed, integer)
+        A = [a[2] for a in (row[0] for row in wl.adapters)]
+        B = [a[3] for a in (row[0] for row in wl.adapters)]
+        sc = [a[1] for a in (row[0] for row in wl.adapters)]
+        exact = _frac_forward(wl.x[0], wl.W[0], A, B, sc, wl.ids)
+        got = o.lora_forward(wl, 0)
+        ex = np.array([[float(v) for v in r] for r in exact])
+        if integer:
+            ok &= bool(np.array_equal(got, ex))
+        else:
+            ok &= bool(np.all(np.abs(got - ex) <= 1e-13 * np.maximum(1.0, np.abs(ex))))
+    return ok
+
+
+def pin_scale_zero(o=lo):
+    """P14: scale 0 leaves y = x W exactly."""
+    wl = _with_adapters(W.c1_tiny_f32(), lambda r, s, A, B: (r, 0.0, A, B))
+    return bool(np.array_equal(o.lora_forward(wl, 0), o.base_product(wl, 0)))
+
+
+def pin_no_adapter(o=lo):
+    """P2: id -1 (and ids out of range) give y = x W bit for bit, and no term."""
+    wl = W.c1_tiny_f32()
+    wl.ids = wl.ids.copy()
+    wl.ids[0] = 99            # out of range: treated as -1
+    neg = np.nonzero((wl.ids < 0) | (wl.ids >= wl.n_slots))[0]
+    if neg.size == 0:
+        return False
+    y = o.lora_forward(wl, 0, neg)
+    return bool(np.array_equal(y, o.base_product(wl, 0, neg))
+                and not np.any(o.lora_delta(wl, 0, neg)))
+
+
+def pin_linearity(o=lo):
+    """P3: delta(B1 + 2 B2) = delta(B1) + 2 delta(B2) (B values on a 1/64 grid, so
+    B1 + 2 B2 is exact in fp32)."""
+    rng = np.random.default_rng(5)
+    base = W.c1_tiny_f32()
+    grid = lambda shp: (rng.integers(-64, 65, shp) / 64.0).astype(np.float32)
+    B1 = [grid(a[3].shape) for row in base.adapters for a in row]
+    B2 = [grid(a[3].shape) for row in base.adapters for a in row]
+    it1, it2, it3 = iter(B1), iter(B2), iter([b1 + 2 * b2 for b1, b2 in zip(B1, B2)])
+    w1 = _with_adapters(base, lambda r, s, A, B: (r, s, A, next(it1)))
+    w2 = _with_adapters(base, lambda r, s, A, B: (r, s, A, next(it2)))
+    w3 = _with_adapters(base, lambda r, s, A, B: (r, s, A, next(it3)))
+    d1, d2, d3 = o.lora_delta(w1, 0), o.lora_delta(w2, 0), o.lora_delta(w3, 0)
+    return _rel(d3, d1 + 2 * d2) <= 1e-12
+
+
+ALL_PINS = [pin_merged, pin_worked_example, pin_fingerprint, pin_bruteforce,
+            pin_scale_zero, pin_no_adapter, pin_linearity]
+
+
+# ---------------------------------------------------------------- the pins
+@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
+def test_pin_holds(pin):
+    assert pin()
+
+
+def test_worked_example_closed_forms_in_golden():
+    """The page prints 2r/d = 1.56% and 0.13 MB vs 8.4 MB for d=2048, r=16, fp16."""
+    gold = json.load(open(GOLD))
+    d, r = gold["setting"]["d"], gold["setting"]["r"]
+    flops_base = 2 * 64 * d * d
+    flops_lora = 2 * 64 * r * d * 2
+    assert f"{flops_lora / flops_base:.2%}" == gold["printed"]["adapter_flops_overhead_percent"]
+    assert f"{2 * r / d:.2%}" == gold["printed"]["two_r_over_d_percent"]
+    assert f"{2 * r * d * 2 / 1e6:.2f}" == gold["printed"]["one_adapter_one_layer_MB"]
+    assert f"{d * d * 2 / 1e6:.1f}" == gold["printed"]["base_layer_MB"]
+
+
+def test_apply_to_y0_is_y0_plus_term():
+    wl = _small_bf16()
+    toks = [0, 3, 7, 23]
+    y = lo.apply_to_y0(wl, 0, toks)
+    y0 = lo.decode(wl.y0[0][toks], "bf16")
+    np.testing.assert_allclose(y - y0, lo.lora_delta(wl, 0, toks), rtol=0, atol=1e-14)
+
+
+def test_shrink_t_matches_term():
+    """t rows reproduce the term when multiplied into B (rank-1 fingerprint: t = x[j])."""
+    wl = W.fingerprint_rank1(dtype="f32")
+    t = lo.shrink_t(wl, 0)
+    x = lo.decode(wl.x[0], "f32")
+    for i, a in enumerate(wl.ids):
+        if 0 <= a < wl.n_slots:
+            assert t[i, 0] == x[i, wl.notes["j"][a]]
+        else:
+            assert np.isnan(t[i, 0])
+
+
+# ---------------------------------------------------------------- planted mistakes
+def _mutant_no_scale(x_row, A, B, scale):
+    t = A @ x_row
+    return t @ B, t
+
+
+def _mutant_sign(x_row, A, B, scale):
+    t = A @ x_row
+    return -scale * (t @ B), t
+
+
+def _mutant_rank_order(x_row, A, B, scale):
+    t = A @ x_row
+    return scale * (t[::-1] @ B), t
+
+
+def _mutant_last_row_dropped(x_row, A, B, scale):
+    t = A[:-1] @ x_row
+    return scale * (t @ B[:-1]), t
+
+
+@pytest.mark.parametrize("mutant", [_mutant_no_scale, _mutant_sign, _mutant_rank_order,
+                                    _mutant_last_row_dropped],
+                         ids=lambda f: f.__name__)
+def test_pins_catch_planted_term_mistakes(monkeypatch, mutant):
+    monkeypatch.setattr(lo, "adapter_term", mutant)
+    failed = [p.__name__ for p in ALL_PINS if not p()]
+    assert failed, "no pin caught the planted mistake"
+
+
+def test_pins_catch_planted_decode_mistake(monkeypatch):
+    real = lo.decode
+
+    def bad_decode(a, dtype):   # bf16 decoded from the wrong half-word
+        if dtype == "bf16":
+            bits = np.asarray(a, np.uint16).astype(np.uint32) << np.uint32(15)
+            return bits.view(np.float32).astype(np.float64)
+        return real(a, dtype)
+
+    monkeypatch.setattr(lo, "decode", bad_decode)
+    wl = W.c2_bgmv_decode(seed=3, n_tokens=4, h=64, n_slots=2, rank=2)
+    # exact decode of a known bf16 pattern: 0x3F80 is 1.0, 0xC000 is -2.0
+    assert not np.array_equal(lo.decode(np.array([0x3F80, 0xC000], np.uint16), "bf16"), [1.0, -2.0])
+    monkeypatch.setattr(lo, "decode", real)
+    assert np.array_equal(lo.decode(np.array([0x3F80, 0xC000], np.uint16), "bf16"), [1.0, -2.0])
+    assert wl.n_tokens == 4

@@ -1,0 +1,376 @@
+"""Seeded synthetic inputs for the multi-LoRA apply path.
+
+This module is shared by the CPU oracle (under ``oracle/``) and by the GPU
+path's tests and benchmark.  It holds no arithmetic of the method itself: it
+only draws random numbers, rounds them to the storage dtype and lays out the
+structure of each workload (adapter ids, segment lengths, ranks, scales).
+
+Layout of every workload (row-major, little endian):
+
+* ``x[g]``   [n_tokens, h_in]   input rows; module ``m`` reads ``x[module.x_group]``
+* ``W[m]``   [h_in, h_out]      shared base weight of module ``m``
+* ``A``      [rank, h_in]       one adapter's down-projection, one row per rank row
+* ``B``      [rank, h_out]      one adapter's up-projection, one row per rank row
+* ``y0[m]``  [n_tokens, h_out]  the buffer the library adds the adapter term into
+* ``ids``    [n_tokens] int32   adapter slot per token, -1 = no adapter
+
+With this layout the adapted linear layer of the "Multi-LoRA Serving" study
+page (section "The kernel trick: gather, do not merge") reads
+``y_i = x_i W + scale_a * (x_i A_a^T) B_a``; its ``A_a`` is our ``A`` and its
+``B_a`` is our ``B`` transposed.
+
+Storage: dtype ``"f32"`` arrays are ``numpy.float32``; dtype ``"bf16"`` arrays
+are ``numpy.uint16`` holding bfloat16 bit patterns, rounded from float32 draws
+to nearest-even.  Each side decodes those bits with its own code.
+
+Seeds: workload ``Cc`` uses ``numpy.random.default_rng(c)``; draws happen in the
+order structure -> ids -> x -> W -> A -> B -> y0.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "Module", "Workload", "to_bf16_bits", "zipf_ids", "finite_zipf_cdf",
+    "c0_worked_example", "c1_tiny_f32", "c2_bgmv_decode", "c3_sgmv_prefill",
+    "c4_mixed_rank", "c5_encoder_step", "fingerprint_rank1", "integer_exact",
+    "BY_NAME",
+]
+
+
+# --------------------------------------------------------------------------
+# storage helpers
+# --------------------------------------------------------------------------
+def to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return the bits."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def _store(a32: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return np.ascontiguousarray(a32, dtype=np.float32)
+    if dtype == "bf16":
+        return to_bf16_bits(a32)
+    raise ValueError(dtype)
+
+
+def finite_zipf_cdf(n: int, s: float) -> np.ndarray:
+    """Cumulative weights of the finite Zipf law over ranks 1..n (weight 1/k^s).
+
+    Same construction as the cache simulation of the "Multi-LoRA Serving"
+    study page (section "Memory: slots, tiers and paging", its sampler): weights
+    1/(i+1)^s, normalised running sum.
+    """
+    w = 1.0 / np.power(np.arange(1, n + 1, dtype=np.float64), s)
+    return np.cumsum(w / w.sum())
+
+
+def zipf_ids(rng: np.random.Generator, count: int, n: int, s: float) -> np.ndarray:
+    """Draw ``count`` slots from a finite Zipf(s) over n slots, slot 0 hottest.
+
+    Inverse-CDF sampling: u ~ U[0,1), first index whose cdf >= u (a binary
+    search, as the study page's sampler does)."""
+    cdf = finite_zipf_cdf(n, s)
+    u = rng.random(count)
+    return np.minimum(np.searchsorted(cdf, u, side="left"), n - 1).astype(np.int32)
+
+
+# --------------------------------------------------------------------------
+# workload container
+# --------------------------------------------------------------------------
+@dataclasses.dataclass
+class Module:
+    name: str
+    h_in: int
+    h_out: int
+    x_group: int          # index into Workload.x
+
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    dtype: str                       # "f32" or "bf16": storage of x, W, A, B, y0
+    page_elems: int                  # elements per page of the paged adapter store
+    n_slots: int
+    modules: List[Module]
+    ids: np.ndarray                  # int32 [n_tokens]
+    x: List[np.ndarray]              # per x-group, [n_tokens, h_in]
+    y0: List[np.ndarray]             # per module, [n_tokens, h_out]
+    W: List[Optional[np.ndarray]]    # per module, [h_in, h_out] (None if not drawn)
+    # adapters[slot][module] = (rank, scale, A [rank, h_in], B [rank, h_out]) or None
+    adapters: List[List[Optional[Tuple[int, float, np.ndarray, np.ndarray]]]]
+    notes: Dict[str, object] = dataclasses.field(default_factory=dict)
+
+    @property
+    def n_tokens(self) -> int:
+        return int(self.ids.shape[0])
+
+    @property
+    def n_modules(self) -> int:
+        return len(self.modules)
+
+    def max_rank(self) -> int:
+        r = [a[0] for row in self.adapters for a in row if a is not None]
+        return max(r) if r else 1
+
+    def pages_needed(self) -> int:
+        h = self.page_elems
+        tot = 0
+        for row in self.adapters:
+            for m, a in enumerate(row):
+                if a is not None:
+                    mod = self.modules[m]
+                    tot += a[0] * (mod.h_in // h + mod.h_out // h)
+        return tot
+
+
+def _normal(rng, std, shape):
+    return rng.normal(0.0, std, shape).astype(np.float32)
+
+
+def _draw_values(rng, dtype, n_tokens, modules, x_groups, slot_ranks, scales,
+                 x_std, w_std, ab_std, draw_w=True):
+    """Draws x -> W -> A -> B -> y0 in that order (structure and ids come first)."""
+    xs = []
+    for g in range(x_groups):
+        h_in = next(m.h_in for m in modules if m.x_group == g)
+        xs.append(_store(_normal(rng, x_std, (n_tokens, h_in)), dtype))
+    Ws = []
+    for m in modules:
+        Ws.append(_store(_normal(rng, w_std, (m.h_in, m.h_out)), dtype) if draw_w else None)
+    adapters = []
+    for s, ranks in enumerate(slot_ranks):
+        row = []
+        for mi, m in enumerate(modules):
+            r = ranks[mi]
+            A = _store(_normal(rng, ab_std, (r, m.h_in)), dtype)
+            row.append([r, float(scales[s]), A, None])
+        adapters.append(row)
+    for s, row in enumerate(adapters):
+        for mi, m in enumerate(modules):
+            r = row[mi][0]
+            row[mi][3] = _store(_normal(rng, ab_std, (r, m.h_out)), dtype)
+            row[mi] = tuple(row[mi])
+    y0 = []
+    for m in modules:
+        # stands in for the base product x.W: iid with the spread x.W would have
+        y_std = x_std * w_std * np.sqrt(m.h_in)
+        y0.append(_store(_normal(rng, y_std, (n_tokens, m.h_out)), dtype))
+    return xs, Ws, adapters, y0
+
+
+# --------------------------------------------------------------------------
+# C0: the study page's worked example (fp32, d=2048, r=16, 50 adapters, batch 64)
+# --------------------------------------------------------------------------
+def c0_worked_example() -> Workload:
+    """The numpy demo of the study page ("The kernel trick: gather, do not merge").
+
+    Same seed and draw order as the page: W, A, B, X, then the ids.  Mapped to
+    this library's layout: W_ours = W_page^T, A rows = A_page[a],
+    B rows = B_page[a]^T.  The page prints 34 distinct adapters for this draw.
+    """
+    rng = np.random.default_rng(0)
+    d, r, n_ad, batch, scale = 2048, 16, 50, 64, 2.0
+    W = rng.normal(0, 0.02, (d, d)).astype(np.float32)
+    A = rng.normal(0, 0.02, (n_ad, r, d)).astype(np.float32)
+    B = rng.normal(0, 0.02, (n_ad, d, r)).astype(np.float32)
+    X = rng.normal(0, 1, (batch, d)).astype(np.float32)
+    ids = rng.integers(0, n_ad, batch).astype(np.int32)
+    mods = [Module("proj", d, d, 0)]
+    adapters = [[(r, scale, np.ascontiguousarray(A[a]), np.ascontiguousarray(B[a].T))]
+                for a in range(n_ad)]
+    return Workload(
+        name="c0_worked_example", dtype="f32", page_elems=d, n_slots=n_ad,
+        modules=mods, ids=ids, x=[X], y0=[np.zeros((batch, d), np.float32)],
+        W=[np.ascontiguousarray(W.T)], adapters=adapters,
+        notes={"W_page": W, "A_page": A, "B_page": B})
+
+
+# --------------------------------------------------------------------------
+# C1: tiny fp32 SGMV
+# --------------------------------------------------------------------------
+def c1_tiny_f32(seed: int = 1) -> Workload:
+    """h=64, 4 slots of rank 4, 16 tokens in 4 contiguous segments, one of them id -1.
+
+    Segment lengths come from 3 distinct cut points in 1..15; the -1 segment sits
+    at a uniform position; the other three take 3 distinct slots of the 4.
+    x ~ N(0,1); W, A, B ~ N(0, 0.1); scale 2.0; fp32."""
+    rng = np.random.default_rng(seed)
+    h, n, n_slots, rank = 64, 16, 4, 4
+    cuts = np.sort(rng.choice(np.arange(1, 16), 3, replace=False))
+    bounds = np.concatenate([[0], cuts, [n]])
+    neg_pos = int(rng.integers(0, 4))
+    chosen = rng.choice(4, 3, replace=False)
+    seg_ids, it = [], iter(chosen.tolist())
+    for s in range(4):
+        seg_ids.append(-1 if s == neg_pos else next(it))
+    ids = np.empty(n, np.int32)
+    for s in range(4):
+        ids[bounds[s]:bounds[s + 1]] = seg_ids[s]
+    mods = [Module("proj", h, h, 0)]
+    xs, Ws, ad, y0 = _draw_values(rng, "f32", n, mods, 1, [[rank]] * n_slots,
+                                  [2.0] * n_slots, 1.0, 0.1, 0.1)
+    return Workload("c1_tiny_f32", "f32", 64, n_slots, mods, ids, xs, y0, Ws, ad,
+                    notes={"segment_bounds": bounds, "segment_ids": seg_ids})
+
+
+# --------------------------------------------------------------------------
+# C2: BGMV decode
+# --------------------------------------------------------------------------
+def c2_bgmv_decode(seed: int = 2, n_modules: int = 1, n_tokens: int = 64,
+                   h: int = 4096, n_slots: int = 32, rank: int = 16,
+                   draw_w: bool = True) -> Workload:
+    """64 decode tokens, ids ~ finite Zipf(1.1) over 32 slots, rank 16, 4096->4096.
+
+    bf16; x ~ N(0,1); W, A, B ~ N(0, 0.02); scale = alpha/r = 32/16.
+    ``n_modules`` > 1 gives that many independent module instances of the same
+    shape (their own x, W, y0 and adapter weights), for one-launch batches."""
+    rng = np.random.default_rng(seed)
+    ids = zipf_ids(rng, n_tokens, n_slots, 1.1)
+    mods = [Module(f"m{i}", h, h, i) for i in range(n_modules)]
+    xs, Ws, ad, y0 = _draw_values(rng, "bf16", n_tokens, mods, n_modules,
+                                  [[rank] * n_modules] * n_slots,
+                                  [32.0 / rank] * n_slots, 1.0, 0.02, 0.02, draw_w)
+    return Workload("c2_bgmv_decode", "bf16", h, n_slots, mods, ids, xs, y0, Ws, ad)
+
+
+# --------------------------------------------------------------------------
+# C3: SGMV prefill, q,k,v,o
+# --------------------------------------------------------------------------
+def c3_sgmv_prefill(seed: int = 3, h: int = 4096, n_slots: int = 8, rank: int = 16,
+                    units: Tuple[int, int] = (8, 64), total_units: int = 256,
+                    unit_tokens: int = 16, draw_w: bool = True) -> Workload:
+    """8 segments, lengths 16*u with u iid uniform in {8..64} conditioned on sum 256
+    (rejection sampling), so lengths lie in [128, 1024], are multiples of 16 and
+    total 4096 tokens.  Segment slots are a permutation of 0..7.  Modules q,k,v
+    share one x; o has its own.  bf16, values as the decode workload."""
+    rng = np.random.default_rng(seed)
+    while True:
+        u = rng.integers(units[0], units[1] + 1, n_slots)
+        if int(u.sum()) == total_units:
+            break
+    lengths = u * unit_tokens
+    order = rng.permutation(n_slots).astype(np.int32)
+    ids = np.repeat(order, lengths).astype(np.int32)
+    mods = [Module("q", h, h, 0), Module("k", h, h, 0), Module("v", h, h, 0),
+            Module("o", h, h, 1)]
+    xs, Ws, ad, y0 = _draw_values(rng, "bf16", ids.shape[0], mods, 2,
+                                  [[rank] * 4] * n_slots, [32.0 / rank] * n_slots,
+                                  1.0, 0.02, 0.02, draw_w)
+    return Workload("c3_sgmv_prefill", "bf16", h, n_slots, mods, ids, xs, y0, Ws, ad,
+                    notes={"segment_lengths": lengths, "segment_slots": order})
+
+
+# --------------------------------------------------------------------------
+# C4: mixed rank, prefill segments + decode tokens
+# --------------------------------------------------------------------------
+def c4_mixed_rank(seed: int = 4, h: int = 4096, n_slots: int = 64,
+                  prefill: int = 4, prefill_len: int = 256, decode: int = 48,
+                  ranks: Sequence[int] = (8, 16, 32, 64),
+                  draw_w: bool = True) -> Workload:
+    """64 slots with ranks uniform over {8,16,32,64} and scale 32/r; 4 prefill
+    segments of 256 tokens (one id each) then 48 decode tokens (one id each);
+    ids ~ finite Zipf(1.0) over 64.  Pages of 4096 elements, bf16."""
+    rng = np.random.default_rng(seed)
+    slot_rank = rng.choice(np.asarray(ranks), n_slots).astype(int)
+    seg_ids = zipf_ids(rng, prefill + decode, n_slots, 1.0)
+    ids = np.concatenate([np.repeat(seg_ids[:prefill], prefill_len),
+                          seg_ids[prefill:]]).astype(np.int32)
+    mods = [Module("proj", h, h, 0)]
+    xs, Ws, ad, y0 = _draw_values(rng, "bf16", ids.shape[0], mods, 1,
+                                  [[int(r)] for r in slot_rank],
+                                  [32.0 / r for r in slot_rank], 1.0, 0.02, 0.02, draw_w)
+    return Workload("c4_mixed_rank", "bf16", h, n_slots, mods, ids, xs, y0, Ws, ad,
+                    notes={"slot_rank": slot_rank})
+
+
+# --------------------------------------------------------------------------
+# C5: many-adapter encoder step
+# --------------------------------------------------------------------------
+def c5_encoder_step(seed: int = 5, n_seq: int = 128, seq_len: int = 256,
+                    n_slots: int = 1024, rank: int = 16, h: int = 768,
+                    ffn: int = 3072, draw_w: bool = True) -> Workload:
+    """Encoder layer of width 768: qkv 768->2304, o 768->768, up 768->3072,
+    down 3072->768; 1,024 rank-16 adapters all resident in a pool of 768-element
+    pages; 128 sequences of 256 tokens with one id per sequence ~ finite
+    Zipf(1.2) over 1,024.  Each linear reads its own synthetic x ~ N(0,1);
+    W, A, B ~ N(0, 0.02); scale 2; bf16."""
+    rng = np.random.default_rng(seed)
+    seq_ids = zipf_ids(rng, n_seq, n_slots, 1.2)
+    ids = np.repeat(seq_ids, seq_len).astype(np.int32)
+    mods = [Module("qkv", h, 3 * h, 0), Module("o", h, h, 1),
+            Module("up", h, ffn, 2), Module("down", ffn, h, 3)]
+    xs, Ws, ad, y0 = _draw_values(rng, "bf16", ids.shape[0], mods, 4,
+                                  [[rank] * 4] * n_slots, [2.0] * n_slots,
+                                  1.0, 0.02, 0.02, draw_w)
+    return Workload("c5_encoder_step", "bf16", h, n_slots, mods, ids, xs, y0, Ws, ad)
+
+
+# --------------------------------------------------------------------------
+# special inputs used by pins
+# --------------------------------------------------------------------------
+def fingerprint_rank1(seed: int = 11, n_tokens: int = 96, h: int = 256,
+                      n_slots: int = 12, dtype: str = "bf16") -> Workload:
+    """Rank-1 adapters A_a = e_{j_a}, B_a = e_{k_a}, scale 1, y0 = 0.
+
+    Every token's adapter term is x_i[j_a] placed in column k_a only, so each
+    output row names the adapter it gathered.  (j_a, k_a) are distinct per slot.
+    ids mix runs and single tokens, with some -1."""
+    rng = np.random.default_rng(seed)
+    js = rng.choice(h, n_slots, replace=False)
+    ks = rng.choice(h, n_slots, replace=False)
+    ids = rng.integers(-1, n_slots, n_tokens).astype(np.int32)
+    # a few runs so that segments of several tokens appear
+    ids[10:30] = 3
+    ids[50:53] = 0
+    x = _store(_normal(rng, 1.0, (n_tokens, h)), dtype)
+    ad = []
+    for s in range(n_slots):
+        A = np.zeros((1, h), np.float32); A[0, js[s]] = 1.0
+        B = np.zeros((1, h), np.float32); B[0, ks[s]] = 1.0
+        ad.append([(1, 1.0, _store(A, dtype), _store(B, dtype))])
+    y0 = [_store(np.zeros((n_tokens, h), np.float32), dtype)]
+    return Workload("fingerprint_rank1", dtype, h, n_slots, [Module("proj", h, h, 0)],
+                    ids, [x], y0, [None], ad, notes={"j": js, "k": ks})
+
+
+def integer_exact(seed: int = 12, n_tokens: int = 80, h: int = 64, n_slots: int = 6,
+                  max_rank: int = 4, dtype: str = "f32", scale: float = 2.0,
+                  ranks: Optional[Sequence[int]] = None) -> Workload:
+    """Small-integer inputs: x, W, A, B, y0 in {-4..4}, h = 64, rank <= 4, scale 2.
+
+    Every partial sum stays an integer below 2^24, so any fp32 summation order
+    gives the exact result."""
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(-1, n_slots, n_tokens).astype(np.int32)
+    ids[5:25] = 1
+    if ranks is None:
+        ranks = [int(r) for r in rng.integers(1, max_rank + 1, n_slots)]
+
+    def ints(shape):
+        return rng.integers(-4, 5, shape).astype(np.float32)
+
+    x = _store(ints((n_tokens, h)), dtype)
+    W = _store(ints((h, h)), dtype)
+    ad = []
+    for s in range(n_slots):
+        ad.append([(int(ranks[s]), float(scale), _store(ints((ranks[s], h)), dtype),
+                    _store(ints((ranks[s], h)), dtype))])
+    y0 = [_store(ints((n_tokens, h)), dtype)]
+    return Workload("integer_exact", dtype, h, n_slots, [Module("proj", h, h, 0)],
+                    ids, [x], y0, [W], ad)
+
+
+BY_NAME = {
+    "c1": c1_tiny_f32,
+    "c2": c2_bgmv_decode,
+    "c3": c3_sgmv_prefill,
+    "c4": c4_mixed_rank,
+    "c5": c5_encoder_step,
+}
