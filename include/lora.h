@@ -1,0 +1,250 @@
+/*
+ * lora.h - C ABI of the MI355X multi-LoRA apply library (gfx950, HIP).
+ *
+ * What the library computes.  For an adapted linear layer, token i with
+ * adapter a(i) needs
+ *
+ *     y_i = x_i W + scale_a * (x_i A_a^T) B_a
+ *
+ * ("Multi-LoRA Serving - S-LoRA/Punica Batching" study page, section "The
+ * kernel trick: gather, do not merge").  The shared base product x W is one
+ * dense GEMM for the whole batch and is NOT computed here: the caller puts it
+ * in y first.  This library adds the adapter term, gathering each token's own
+ * adapter from a device-resident paged store, without merging weights.
+ *
+ * Layouts (row-major; elements of the pool's dtype unless noted):
+ *   x   [n_tokens][ld_x]   input rows (h_in used)
+ *   t   [n_tokens][ld_t]   float32 intermediate x A^T (rank columns used)
+ *   y   [n_tokens][ld_y]   output rows (h_out used), updated in place
+ *   A   [rank][h_in]       one adapter's rank rows, each of length h_in
+ *   B   [rank][h_out]      one adapter's rank rows, each of length h_out
+ * Rows of x, t and y are indexed by the ORIGINAL token index.
+ *
+ * Paged store ("Thousands of adapters", slide 8: a page holds H elements, a
+ * rank-R adapter takes R pages).  The pool is an array of pages of
+ * page_elems elements.  Each rank row of A (B) spans h_in/page_elems
+ * (h_out/page_elems) pages, so one (slot, module) entry uses
+ * rank * (h_in + h_out) / page_elems pages, allocated at the adapter's own
+ * rank (no padding to the maximum rank).  Pages need not be contiguous.
+ *
+ * Adapter ids: -1 means "no adapter" (y untouched).  An id outside
+ * [-1, n_slots) is treated as -1 and counted in the segment meta (word
+ * LORA_META_N_BAD); lora_segments_check reports it as LORA_ERR_DEVICE_IDS.
+ * A slot with no adapter loaded for a module adds nothing.
+ *
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = null stream).
+ * Every compute call is asynchronous on `stream` and returns after enqueueing.
+ * Pointers are device pointers unless marked [host].
+ *
+ * Errors: every call returns a lora_status.  Argument checks run on the host
+ * before anything is enqueued; a call that returns an error has enqueued
+ * nothing and changed nothing.  No call aborts or throws.
+ *
+ * Ownership: the pool owns its pages and slot table.  The caller owns x, t,
+ * y, ids, the segment buffer and workspaces; the library never frees them.
+ */
+#ifndef LORA_MI355X_H
+#define LORA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LORA_ABI_VERSION 1
+
+typedef int32_t lora_status;
+enum {
+    LORA_OK = 0,
+    LORA_ERR_ARG = -1,         /* null pointer, bad enum, negative size, misaligned pointer */
+    LORA_ERR_SHAPE = -2,       /* dims not multiples of page_elems, module shape mismatch   */
+    LORA_ERR_RANK = -3,        /* rank < 1 or rank > the pool's max_rank (the rank cap)      */
+    LORA_ERR_NO_PAGES = -4,    /* not enough free pages for the adapter                      */
+    LORA_ERR_SLOT = -5,        /* slot/module out of range, already loaded, or empty         */
+    LORA_ERR_DTYPE = -6,       /* unsupported dtype combination                              */
+    LORA_ERR_HIP = -7,         /* a HIP runtime call failed                                  */
+    LORA_ERR_DEVICE_IDS = -8,  /* (segments_check) the batch held ids outside [-1, n_slots)  */
+    LORA_ERR_WORKSPACE = -9    /* workspace too small                                        */
+};
+
+typedef enum { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype;
+
+/* Largest rank a pool accepts (the load-time rank cap: study page, "Memory:
+ * slots, tiers and paging", cap ranks because slots reserve the maximum). */
+#define LORA_MAX_RANK 64
+
+/* Returns LORA_ABI_VERSION. */
+int32_t lora_abi_version(void);
+
+/* Static text for a status code. */
+const char *lora_status_str(lora_status s);
+
+/* ------------------------------------------------------------------------ */
+/* Paged adapter store ("GPU slots": study page, "Memory: slots, tiers and  */
+/* paging"; unified paging: "Thousands of adapters", slide 8)               */
+/* ------------------------------------------------------------------------ */
+typedef struct lora_pool lora_pool;   /* opaque, library-owned */
+
+typedef struct {
+    int64_t n_pages;         /* pages in the pool                 */
+    int64_t free_pages;      /* pages not held by any adapter      */
+    int32_t loaded_entries;  /* (slot, module) entries loaded      */
+    int32_t loaded_slots;    /* slots with at least one entry      */
+    int64_t loads;           /* successful lora_pool_load calls    */
+    int64_t evicts;          /* successful lora_pool_evict calls   */
+} lora_pool_stats_t;
+
+/* Creates a pool on HIP device `device`.
+ *   wdtype      element type of pages (LORA_F32 or LORA_BF16); x uses the same type
+ *   page_elems  elements per page; a multiple of 64
+ *   n_pages     pages to allocate (n_pages * page_elems elements of device memory)
+ *   n_slots     adapter slots (ids 0..n_slots-1), 1..8192
+ *   n_modules   adapted linear layers per slot, >= 1
+ *   h_in,h_out  [host] [n_modules] input/output widths; multiples of page_elems
+ *   max_rank    rank cap, 1..LORA_MAX_RANK
+ * On success *out holds the pool.  Synchronous.  Errors: ARG, SHAPE, RANK, HIP. */
+lora_status lora_pool_create(lora_pool **out, int32_t device, lora_dtype wdtype,
+                             int64_t page_elems, int64_t n_pages, int32_t n_slots,
+                             int32_t n_modules, const int64_t *h_in, const int64_t *h_out,
+                             int32_t max_rank);
+
+/* Frees the pool's device memory after synchronizing its device.  NULL is OK. */
+lora_status lora_pool_destroy(lora_pool *p);
+
+/* Copies one adapter into freshly allocated pages and publishes the
+ * (slot, module) entry: "copy a few MB into a GPU slot" (study page,
+ * "Strategies compared").  A and B are [rank][h_in] and [rank][h_out] of the
+ * pool's dtype, in host or device memory.  The upload runs on `stream` and
+ * the call returns once it has completed, so A and B may be reused at once.
+ * Kernels enqueued later on `stream` see the entry.
+ * Errors: ARG (null), SLOT (range / already loaded), RANK, NO_PAGES, HIP. */
+lora_status lora_pool_load(lora_pool *p, int32_t slot, int32_t module, int32_t rank,
+                           const void *A, const void *B, float scale, void *stream);
+
+/* Unloads every module of `slot`: the slot's entries read as empty for work
+ * enqueued on `stream` after this call, and its pages return to the free list.
+ * The pages may be reused by the next load; a load on the same stream is
+ * ordered after earlier kernels, so reuse is safe in stream order.  Callers
+ * that read the pool from other streams order those streams themselves.
+ * Errors: ARG, SLOT (range or nothing loaded), HIP. */
+lora_status lora_pool_evict(lora_pool *p, int32_t slot, void *stream);
+
+/* [host] out: counters.  Synchronous, no device work. */
+lora_status lora_pool_stats(const lora_pool *p, lora_pool_stats_t *out);
+
+/* Debug read-back of one entry into [host] buffers (A: rank*h_in, B:
+ * rank*h_out elements of the pool's dtype, either may be NULL) and its
+ * [host] page list (up to max_pages ids, either may be NULL).  Synchronizes
+ * the device.  Errors: ARG, SLOT (empty), HIP. */
+lora_status lora_pool_read(const lora_pool *p, int32_t slot, int32_t module,
+                           int32_t *rank, float *scale, void *A, void *B,
+                           int32_t *pages, int32_t max_pages);
+
+/* ------------------------------------------------------------------------ */
+/* Segments: tokens grouped by adapter                                      */
+/* ("groups a batch's tokens by adapter": Fastino article; "contiguous      */
+/* segments of tokens sharing an adapter": study page, "The kernel trick")  */
+/* ------------------------------------------------------------------------ */
+#define LORA_META_WORDS 16
+enum {
+    LORA_META_N_SEG = 0,        /* distinct adapters in the batch                       */
+    LORA_META_N_ACTIVE = 1,     /* tokens with a valid id                               */
+    LORA_META_MAX_SEG_LEN = 2,  /* tokens in the longest segment                        */
+    LORA_META_N_BAD = 3,        /* ids outside [-1, n_slots)                            */
+    LORA_META_N_UNITS_SHORT = 4,/* GEMV work units of segments shorter than LONG_MIN    */
+    LORA_META_N_UNITS_ALL = 5,  /* GEMV work units of all segments                      */
+    LORA_META_N_TILES = 6,      /* matrix-core tiles of segments of >= LONG_MIN tokens  */
+    LORA_META_UNIT_TOKENS = 7,  /* tokens per GEMV unit                                 */
+    LORA_META_TILE_TOKENS = 8,  /* tokens per matrix-core tile                          */
+    LORA_META_LONG_MIN = 9,     /* segment length from which tiles are used             */
+    LORA_META_N_TOKENS = 10,
+    LORA_META_N_SLOTS = 11
+};
+
+/* Views into one caller-owned device buffer (see lora_segments_bind). */
+typedef struct {
+    int32_t *perm;       /* [n_tokens] token indices: ascending slot, original order within a slot */
+    int32_t *seg_start;  /* [max_segs + 1] offsets into perm; seg_start[n_seg] = n_active          */
+    int32_t *seg_slot;   /* [max_segs] slot of each segment, ascending                             */
+    int32_t *meta;       /* [LORA_META_WORDS]                                                      */
+    int32_t *units;      /* [2 * max_units] (segment, position in perm) per GEMV work unit         */
+    int32_t *tiles;      /* [2 * max_tiles] (segment, position in perm) per matrix-core tile       */
+    int32_t n_tokens, n_slots, max_segs, max_units, max_tiles;
+} lora_segments;
+
+/* Bytes of device memory lora_segments_bind needs for a batch. */
+size_t lora_segments_bytes(int32_t n_tokens, int32_t n_slots);
+
+/* [host] Lays out the views over `buf` (device, >= lora_segments_bytes bytes,
+ * 256-byte aligned).  No device work.  Errors: ARG, WORKSPACE. */
+lora_status lora_segments_bind(void *buf, size_t bytes, int32_t n_tokens, int32_t n_slots,
+                               lora_segments *out);
+
+/* Builds the segments of the batch `ids` [n_tokens] (int32, device) on the
+ * GPU: a stable sort of token indices by slot that drops ids outside
+ * [0, n_slots), the segment offsets and slots, and the work lists of the
+ * apply kernels.  Built once per batch and reused by every layer and module.
+ * One launch; n_tokens == 0 enqueues nothing.  Errors: ARG, HIP. */
+lora_status lora_build_segments(const int32_t *ids, const lora_segments *seg, void *stream);
+
+/* Debug: waits for `stream`, copies the meta words to [host] meta_out (may be
+ * NULL) and returns LORA_ERR_DEVICE_IDS if the batch held invalid ids. */
+lora_status lora_segments_check(const lora_segments *seg, void *stream, int32_t *meta_out);
+
+/* ------------------------------------------------------------------------ */
+/* Apply                                                                    */
+/* ------------------------------------------------------------------------ */
+/* Shared arguments:
+ *   module0, n_modules   consecutive modules [module0, module0+n_modules), all
+ *                        with the same h_in (and h_out for expand/bgmv)
+ *   module_stride_*      element offset between modules' x / t / y; a stride of
+ *                        0 for x means the modules share one x (q, k, v)
+ *   seg                  segments built for this batch (n_tokens = seg->n_tokens)
+ * x and the pool have the same dtype.  y may be LORA_F32 or LORA_BF16; each y
+ * element is rounded once, to nearest even, after y0 + term is formed in fp32.
+ * Pointers and leading dimensions must keep every row 16-byte aligned. */
+
+/* Workspace bytes for the split-K reduction of lora_shrink's matrix-core
+ * path.  0 is always accepted (no split); more gives more parallelism. */
+size_t lora_shrink_workspace_bytes(const lora_pool *p, int32_t n_tokens, int32_t n_modules);
+
+/* Shrink: t[i][j] = sum_k x_i[k] A_a[j][k] for j < rank_a, i with a valid id
+ * ("shrink" of the study page's demo: the per-row product with the gathered
+ * A).  t rows of tokens without an adapter, and columns past rank_a, are not
+ * written.  Segments of >= LONG_MIN tokens run on bf16 matrix cores.
+ * ws: device workspace, zero-filled before its first use and left zeroed
+ * by every call; calls that share a workspace must not overlap.
+ * Errors: ARG, SHAPE, DTYPE, HIP. */
+lora_status lora_shrink(const lora_pool *p, int32_t module0, int32_t n_modules,
+                        const void *x, int64_t ld_x, int64_t module_stride_x,
+                        const lora_segments *seg,
+                        float *t, int64_t ld_t, int64_t module_stride_t,
+                        void *ws, size_t ws_bytes, void *stream);
+
+/* Expand: y_i[c] = round(y_i[c] + scale_a * sum_{j<rank_a} t[i][j] B_a[j][c])
+ * for tokens with a valid id ("expand" of the study page's demo, fused into
+ * the update of y).  Other rows of y are not touched.
+ * Errors: ARG, SHAPE, DTYPE, HIP. */
+lora_status lora_expand(const lora_pool *p, int32_t module0, int32_t n_modules,
+                        const float *t, int64_t ld_t, int64_t module_stride_t,
+                        const lora_segments *seg,
+                        void *y, int64_t ld_y, int64_t module_stride_y, lora_dtype ydtype,
+                        void *stream);
+
+/* Fused BGMV for decode ("batched gather matrix-vector, one adapter per
+ * decode token": study page, "The kernel trick"): shrink and expand in one
+ * launch with t kept on chip; tokens that share an adapter share each read
+ * of its pages.  Same result as lora_shrink followed by lora_expand.
+ * Errors: ARG, SHAPE, DTYPE, HIP. */
+lora_status lora_apply_bgmv(const lora_pool *p, int32_t module0, int32_t n_modules,
+                            const void *x, int64_t ld_x, int64_t module_stride_x,
+                            const lora_segments *seg,
+                            void *y, int64_t ld_y, int64_t module_stride_y, lora_dtype ydtype,
+                            void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LORA_MI355X_H */

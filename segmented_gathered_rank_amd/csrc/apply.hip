@@ -1,0 +1,256 @@
+// C ABI of the apply path: argument checks, path selection and launches.
+//
+// Dispatch.  Segments shorter than kLongMin tokens (decode tokens, short
+// requests) run on the GEMV path; longer ones run on matrix-core tiles when
+// the pool is bf16 and its page and output widths tile evenly.  Both work
+// lists come from the segment builder and stay on the device; grids are sized
+// by their upper bounds and idle workgroups exit at once.
+#include "gemv_kernels.hpp"
+#include "mfma_kernels.hpp"
+#include "pool.hpp"
+
+using namespace lora;
+
+namespace {
+
+constexpr int kMaxGrid = 4096;   // persistent grids loop over work beyond this
+
+SegView seg_view(const lora_segments* s) {
+  SegView v;
+  v.perm = s->perm;
+  v.seg_start = s->seg_start;
+  v.seg_slot = s->seg_slot;
+  v.meta = s->meta;
+  v.units = s->units;
+  v.tiles = s->tiles;
+  return v;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks shared by the apply calls.  `need_out` also checks equal h_out.
+lora_status check_call(const lora_pool* p, int32_t module0, int32_t n_modules, const lora_segments* seg) {
+  if (!p || !seg) return LORA_ERR_ARG;
+  if (n_modules < 1 || module0 < 0 || module0 + n_modules > p->n_modules) return LORA_ERR_ARG;
+  if (seg->n_tokens < 0 || seg->n_slots < 1 || seg->n_slots > p->n_slots) return LORA_ERR_ARG;
+  if (seg->n_tokens > 0 && (!seg->perm || !seg->seg_start || !seg->seg_slot || !seg->meta || !seg->units ||
+                            !seg->tiles))
+    return LORA_ERR_ARG;
+  if (seg->max_units != max_units_of(seg->n_tokens, seg->n_slots) || seg->max_tiles != max_tiles_of(seg->n_tokens))
+    return LORA_ERR_ARG;
+  for (int32_t m = module0 + 1; m < module0 + n_modules; ++m) {
+    if (p->h_in[m] != p->h_in[module0] || p->h_out[m] != p->h_out[module0]) return LORA_ERR_SHAPE;
+  }
+  return LORA_OK;
+}
+
+// Element rows of a [n_tokens][ld] operand repeated per module.
+lora_status check_operand(const void* ptr, int64_t ld, int64_t mstride, int64_t width, size_t eb,
+                          int32_t n_tokens, int32_t n_modules, bool written, bool vec16) {
+  if (!ptr) return LORA_ERR_ARG;
+  if (ld < width || mstride < 0) return LORA_ERR_ARG;
+  if (vec16 && (!aligned16(ptr) || (ld * static_cast<int64_t>(eb)) % 16 != 0 ||
+                (mstride * static_cast<int64_t>(eb)) % 16 != 0))
+    return LORA_ERR_ARG;
+  if (written && n_modules > 1 && mstride < static_cast<int64_t>(n_tokens) * ld) return LORA_ERR_ARG;
+  return LORA_OK;
+}
+
+bool mfma_ok(const lora_pool* p, int32_t module) {
+  return p->dtype == LORA_BF16 && p->page_elems % kExpandCols == 0 && p->h_out[module] % kExpandCols == 0;
+}
+
+unsigned grid_of(int32_t bound) {
+  if (bound < 1) bound = 1;
+  return static_cast<unsigned>(bound < kMaxGrid ? bound : kMaxGrid);
+}
+
+int32_t ldr_of(const lora_pool* p) { return (p->max_rank + 15) / 16 * 16; }
+
+// Workspace of the split-K shrink for `ks` splits.
+size_t split_ws_bytes(const lora_pool* p, int32_t n_tokens, int32_t n_modules, int32_t ks) {
+  if (ks <= 1) return 0;
+  const size_t tiles = static_cast<size_t>(max_tiles_of(n_tokens));
+  const size_t tickets = (tiles * n_modules * 4 + 255) / 256 * 256;
+  return tickets + tiles * n_modules * ks * kTileTokens * ldr_of(p) * sizeof(float);
+}
+
+constexpr int32_t kMaxSplits = 8;
+
+template <typename TI>
+lora_status launch_shrink(const lora_pool* p, int32_t module0, int32_t n_modules, const void* x, int64_t ld_x,
+                          int64_t msx, const lora_segments* seg, float* t, int64_t ld_t, int64_t mst, void* ws,
+                          size_t ws_bytes, hipStream_t s) {
+  const PoolView pv = p->view();
+  const SegView sv = seg_view(seg);
+  const int32_t h_in = static_cast<int32_t>(p->h_in[module0]);
+  const bool use_mfma = mfma_ok(p, module0);
+  const int32_t units_word = use_mfma ? LORA_META_N_UNITS_SHORT : LORA_META_N_UNITS_ALL;
+  hipLaunchKernelGGL(k_shrink_gemv<TI>, dim3(grid_of(seg->max_units), n_modules), dim3(kGemvThreads), 0, s, pv,
+                     module0, sv, units_word, static_cast<const TI*>(x), ld_x, msx, t, ld_t, mst, h_in);
+  if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
+  if constexpr (sizeof(TI) == 2) {
+    if (use_mfma && seg->max_tiles > 0) {
+      const bool shared = (msx == 0 && n_modules > 1 && n_modules <= kShrinkMaxModules);
+      const int32_t groups = shared ? 1 : n_modules;
+      const int32_t per_wg = shared ? n_modules : 1;
+      // enough workgroups for 256 CUs: split K when tiles alone are too few
+      const int32_t est_tiles = (seg->n_tokens + kTileTokens - 1) / kTileTokens;
+      int32_t ks = 512 / (est_tiles * groups > 0 ? est_tiles * groups : 1);
+      if (ks > kMaxSplits) ks = kMaxSplits;
+      if (ks > h_in / 256) ks = h_in / 256;
+      if (ks < 1) ks = 1;
+      while (ks > 1 && split_ws_bytes(p, seg->n_tokens, n_modules, ks) > ws_bytes) --ks;
+      int32_t kps = (h_in + ks - 1) / ks;
+      kps = (kps + 31) / 32 * 32;
+      ks = (h_in + kps - 1) / kps;
+      ShrinkArgs a;
+      a.pv = pv;
+      a.sv = sv;
+      a.x = static_cast<const __bf16*>(x);
+      a.ld_x = ld_x;
+      a.msx = shared ? 0 : msx;
+      a.t = t;
+      a.ld_t = ld_t;
+      a.mst = mst;
+      a.module0 = module0;
+      a.mods_per_wg = per_wg;
+      a.h_in = h_in;
+      a.ks_count = ks;
+      a.k_per_split = kps;
+      a.ldr = ldr_of(p);
+      const size_t tiles = static_cast<size_t>(seg->max_tiles);
+      const size_t tickets = (tiles * n_modules * 4 + 255) / 256 * 256;
+      a.tickets = static_cast<int32_t*>(ws);
+      a.part = ks > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + tickets) : nullptr;
+      hipLaunchKernelGGL(k_shrink_mfma, dim3(grid_of(seg->max_tiles), ks, groups), dim3(kMfmaThreads), 0, s, a);
+      if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
+    }
+  }
+  return LORA_OK;
+}
+
+template <typename TI, typename TO>
+lora_status launch_expand(const lora_pool* p, int32_t module0, int32_t n_modules, const float* t, int64_t ld_t,
+                          int64_t mst, const lora_segments* seg, void* y, int64_t ld_y, int64_t msy,
+                          hipStream_t s) {
+  const PoolView pv = p->view();
+  const SegView sv = seg_view(seg);
+  const int32_t h_out = static_cast<int32_t>(p->h_out[module0]);
+  const bool use_mfma = mfma_ok(p, module0);
+  const int32_t units_word = use_mfma ? LORA_META_N_UNITS_SHORT : LORA_META_N_UNITS_ALL;
+  hipLaunchKernelGGL((k_expand_gemv<TI, TO>), dim3(grid_of(seg->max_units), n_modules), dim3(kGemvThreads), 0, s,
+                     pv, module0, sv, units_word, t, ld_t, mst, static_cast<TO*>(y), ld_y, msy, h_out);
+  if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
+  if constexpr (sizeof(TI) == 2) {
+    if (use_mfma && seg->max_tiles > 0) {
+      hipLaunchKernelGGL((k_expand_mfma<TO>), dim3(grid_of(seg->max_tiles), h_out / kExpandCols, n_modules),
+                         dim3(kMfmaThreads), 0, s, pv, module0, sv, t, ld_t, mst, static_cast<TO*>(y), ld_y, msy,
+                         h_out);
+      if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
+    }
+  }
+  return LORA_OK;
+}
+
+template <typename TI, typename TO>
+lora_status launch_bgmv(const lora_pool* p, int32_t module0, int32_t n_modules, const void* x, int64_t ld_x,
+                        int64_t msx, const lora_segments* seg, void* y, int64_t ld_y, int64_t msy, hipStream_t s) {
+  hipLaunchKernelGGL((k_bgmv<TI, TO>), dim3(grid_of(seg->max_units), n_modules), dim3(kGemvThreads), 0, s,
+                     p->view(), module0, seg_view(seg), static_cast<const TI*>(x), ld_x, msx, static_cast<TO*>(y),
+                     ld_y, msy, static_cast<int32_t>(p->h_in[module0]), static_cast<int32_t>(p->h_out[module0]));
+  return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lora_shrink_workspace_bytes(const lora_pool* p, int32_t n_tokens, int32_t n_modules) {
+  if (!p || n_tokens < 0 || n_modules < 1) return 0;
+  return split_ws_bytes(p, n_tokens, n_modules, kMaxSplits);
+}
+
+lora_status lora_shrink(const lora_pool* p, int32_t module0, int32_t n_modules, const void* x, int64_t ld_x,
+                        int64_t module_stride_x, const lora_segments* seg, float* t, int64_t ld_t,
+                        int64_t module_stride_t, void* ws, size_t ws_bytes, void* stream) {
+  lora_status st = check_call(p, module0, n_modules, seg);
+  if (st != LORA_OK) return st;
+  const int32_t n = seg->n_tokens;
+  st = check_operand(x, ld_x, module_stride_x, p->h_in[module0], p->elem_bytes(), n, n_modules, false, true);
+  if (st != LORA_OK) return st;
+  st = check_operand(t, ld_t, module_stride_t, p->max_rank, 4, n, n_modules, true, false);
+  if (st != LORA_OK) return st;
+  if (ws_bytes > 0 && (!ws || !aligned16(ws))) return LORA_ERR_ARG;
+  if (n == 0) return LORA_OK;
+  DeviceGuard g(p->device);
+  if (!g.ok) return LORA_ERR_HIP;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p->dtype == LORA_BF16)
+    return launch_shrink<__bf16>(p, module0, n_modules, x, ld_x, module_stride_x, seg, t, ld_t, module_stride_t,
+                                 ws, ws_bytes, s);
+  return launch_shrink<float>(p, module0, n_modules, x, ld_x, module_stride_x, seg, t, ld_t, module_stride_t, ws,
+                              ws_bytes, s);
+}
+
+lora_status lora_expand(const lora_pool* p, int32_t module0, int32_t n_modules, const float* t, int64_t ld_t,
+                        int64_t module_stride_t, const lora_segments* seg, void* y, int64_t ld_y,
+                        int64_t module_stride_y, lora_dtype ydtype, void* stream) {
+  lora_status st = check_call(p, module0, n_modules, seg);
+  if (st != LORA_OK) return st;
+  if (ydtype != LORA_F32 && ydtype != LORA_BF16) return LORA_ERR_DTYPE;
+  const int32_t n = seg->n_tokens;
+  st = check_operand(t, ld_t, module_stride_t, p->max_rank, 4, n, n_modules, false, false);
+  if (st != LORA_OK) return st;
+  st = check_operand(y, ld_y, module_stride_y, p->h_out[module0], ydtype == LORA_BF16 ? 2 : 4, n, n_modules, true,
+                     true);
+  if (st != LORA_OK) return st;
+  if (n == 0) return LORA_OK;
+  DeviceGuard g(p->device);
+  if (!g.ok) return LORA_ERR_HIP;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p->dtype == LORA_BF16) {
+    if (ydtype == LORA_BF16)
+      return launch_expand<__bf16, __bf16>(p, module0, n_modules, t, ld_t, module_stride_t, seg, y, ld_y,
+                                           module_stride_y, s);
+    return launch_expand<__bf16, float>(p, module0, n_modules, t, ld_t, module_stride_t, seg, y, ld_y,
+                                        module_stride_y, s);
+  }
+  if (ydtype == LORA_BF16)
+    return launch_expand<float, __bf16>(p, module0, n_modules, t, ld_t, module_stride_t, seg, y, ld_y,
+                                        module_stride_y, s);
+  return launch_expand<float, float>(p, module0, n_modules, t, ld_t, module_stride_t, seg, y, ld_y,
+                                     module_stride_y, s);
+}
+
+lora_status lora_apply_bgmv(const lora_pool* p, int32_t module0, int32_t n_modules, const void* x, int64_t ld_x,
+                            int64_t module_stride_x, const lora_segments* seg, void* y, int64_t ld_y,
+                            int64_t module_stride_y, lora_dtype ydtype, void* stream) {
+  lora_status st = check_call(p, module0, n_modules, seg);
+  if (st != LORA_OK) return st;
+  if (ydtype != LORA_F32 && ydtype != LORA_BF16) return LORA_ERR_DTYPE;
+  const int32_t n = seg->n_tokens;
+  st = check_operand(x, ld_x, module_stride_x, p->h_in[module0], p->elem_bytes(), n, n_modules, false, true);
+  if (st != LORA_OK) return st;
+  st = check_operand(y, ld_y, module_stride_y, p->h_out[module0], ydtype == LORA_BF16 ? 2 : 4, n, n_modules, true,
+                     true);
+  if (st != LORA_OK) return st;
+  if (n == 0) return LORA_OK;
+  DeviceGuard g(p->device);
+  if (!g.ok) return LORA_ERR_HIP;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p->dtype == LORA_BF16) {
+    if (ydtype == LORA_BF16)
+      return launch_bgmv<__bf16, __bf16>(p, module0, n_modules, x, ld_x, module_stride_x, seg, y, ld_y,
+                                         module_stride_y, s);
+    return launch_bgmv<__bf16, float>(p, module0, n_modules, x, ld_x, module_stride_x, seg, y, ld_y,
+                                      module_stride_y, s);
+  }
+  if (ydtype == LORA_BF16)
+    return launch_bgmv<float, __bf16>(p, module0, n_modules, x, ld_x, module_stride_x, seg, y, ld_y,
+                                      module_stride_y, s);
+  return launch_bgmv<float, float>(p, module0, n_modules, x, ld_x, module_stride_x, seg, y, ld_y, module_stride_y,
+                                   s);
+}
+
+}  // extern "C"

@@ -1,0 +1,294 @@
+// Paged adapter store: pool creation, adapter upload into pages, eviction.
+//
+// "GPU slots" of the study page ("Memory: slots, tiers and paging") hold the
+// hot adapters; S-LoRA's unified paging ("Thousands of adapters", slide 8)
+// stores rank-R adapters in R pages of H elements.  Here a page holds
+// page_elems elements; each rank row of A and of B is cut into whole pages and
+// a (slot, module) entry lists its pages, so adapters of any rank share one
+// pool without padding to the maximum rank.
+#include <cstring>
+#include <new>
+
+#include "pool.hpp"
+
+using namespace lora;
+
+namespace {
+
+// Copies one upload (A rows then B rows, contiguous in `src`) into its pages
+// and publishes the slot-table entry.  One workgroup per page.
+template <typename T>
+__global__ __launch_bounds__(256) void k_upload(T* __restrict__ pages, const T* __restrict__ src,
+                                                const int32_t* __restrict__ plist, int32_t n_plist,
+                                                int64_t page_elems, int32_t* __restrict__ page_ids,
+                                                int32_t ids_off, SlotEntry* __restrict__ entry,
+                                                SlotEntry value) {
+  const int32_t piece = blockIdx.x;
+  if (piece >= n_plist) return;
+  const int32_t page = plist[piece];
+  const T* s = src + static_cast<int64_t>(piece) * page_elems;
+  T* d = pages + static_cast<int64_t>(page) * page_elems;
+  constexpr int kVec = 16 / sizeof(T);
+  for (int64_t e = static_cast<int64_t>(threadIdx.x) * kVec; e < page_elems; e += 256 * kVec) {
+    *reinterpret_cast<u32x4*>(d + e) = *reinterpret_cast<const u32x4*>(s + e);
+  }
+  if (threadIdx.x == 0) {
+    page_ids[ids_off + piece] = page;
+    if (piece == 0) *entry = value;
+  }
+}
+
+__global__ void k_clear_entries(SlotEntry* __restrict__ e, int32_t count) {
+  const int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) e[i] = SlotEntry{0, 0.f, 0, 0};
+}
+
+__global__ void k_fill_zero(uint32_t* __restrict__ p, int64_t words) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < words;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+bool fill_zero(void* p, size_t bytes, hipStream_t s) {
+  const int64_t words = static_cast<int64_t>(bytes / 4);
+  if (words == 0) return true;
+  int64_t blocks = (words + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_fill_zero, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                     static_cast<uint32_t*>(p), words);
+  return hipGetLastError() == hipSuccess;
+}
+
+void free_device(lora_pool* p) {
+  if (p->d_pages) (void)hipFree(p->d_pages);
+  if (p->d_entries) (void)hipFree(p->d_entries);
+  if (p->d_page_ids) (void)hipFree(p->d_page_ids);
+  if (p->d_staging) (void)hipFree(p->d_staging);
+  p->d_pages = nullptr;
+  p->d_entries = nullptr;
+  p->d_page_ids = nullptr;
+  p->d_staging = nullptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t lora_abi_version(void) { return LORA_ABI_VERSION; }
+
+const char* lora_status_str(lora_status s) {
+  switch (s) {
+    case LORA_OK: return "ok";
+    case LORA_ERR_ARG: return "invalid argument";
+    case LORA_ERR_SHAPE: return "shape not supported by the pool";
+    case LORA_ERR_RANK: return "rank outside [1, max_rank]";
+    case LORA_ERR_NO_PAGES: return "not enough free pages";
+    case LORA_ERR_SLOT: return "slot/module out of range, already loaded, or empty";
+    case LORA_ERR_DTYPE: return "unsupported dtype combination";
+    case LORA_ERR_HIP: return "HIP runtime error";
+    case LORA_ERR_DEVICE_IDS: return "batch held adapter ids outside [-1, n_slots)";
+    case LORA_ERR_WORKSPACE: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+lora_status lora_pool_create(lora_pool** out, int32_t device, lora_dtype wdtype, int64_t page_elems,
+                             int64_t n_pages, int32_t n_slots, int32_t n_modules, const int64_t* h_in,
+                             const int64_t* h_out, int32_t max_rank) {
+  if (!out || !h_in || !h_out) return LORA_ERR_ARG;
+  *out = nullptr;
+  if (wdtype != LORA_F32 && wdtype != LORA_BF16) return LORA_ERR_ARG;
+  if (device < 0 || page_elems <= 0 || n_pages <= 0 || n_pages > INT32_MAX) return LORA_ERR_ARG;
+  if (n_slots < 1 || n_slots > kMaxSlots || n_modules < 1 || n_modules > 4096) return LORA_ERR_ARG;
+  if (max_rank < 1 || max_rank > kMaxRank) return LORA_ERR_RANK;
+  if (page_elems % 64 != 0) return LORA_ERR_SHAPE;
+  int64_t max_ppe = 0, max_in = 0, max_out = 0;
+  for (int32_t m = 0; m < n_modules; ++m) {
+    if (h_in[m] <= 0 || h_out[m] <= 0) return LORA_ERR_ARG;
+    if (h_in[m] % page_elems != 0 || h_out[m] % page_elems != 0) return LORA_ERR_SHAPE;
+    if (h_in[m] > (1 << 20) || h_out[m] > (1 << 20)) return LORA_ERR_SHAPE;
+    const int64_t ppe = static_cast<int64_t>(max_rank) * (h_in[m] + h_out[m]) / page_elems;
+    if (ppe > max_ppe) max_ppe = ppe;
+    if (h_in[m] > max_in) max_in = h_in[m];
+    if (h_out[m] > max_out) max_out = h_out[m];
+  }
+  const int64_t table = static_cast<int64_t>(n_slots) * n_modules * max_ppe;
+  if (table > INT32_MAX) return LORA_ERR_ARG;
+
+  lora_pool* p = new (std::nothrow) lora_pool();
+  if (!p) return LORA_ERR_ARG;
+  p->device = device;
+  p->dtype = wdtype;
+  p->page_elems = page_elems;
+  p->n_pages = n_pages;
+  p->n_slots = n_slots;
+  p->n_modules = n_modules;
+  p->max_rank = max_rank;
+  p->max_pages_per_entry = static_cast<int32_t>(max_ppe);
+  p->h_in.assign(h_in, h_in + n_modules);
+  p->h_out.assign(h_out, h_out + n_modules);
+  p->alloc.reset(n_pages);
+  p->entries.resize(static_cast<size_t>(n_slots) * n_modules);
+
+  DeviceGuard g(device);
+  if (!g.ok) { delete p; return LORA_ERR_HIP; }
+  const size_t eb = p->elem_bytes();
+  const size_t ab = ((static_cast<size_t>(max_rank) * (max_in + max_out) * eb) + 255) / 256 * 256;
+  p->staging_bytes = ab + static_cast<size_t>(max_ppe) * 4 + 256;
+  const size_t n_entries = static_cast<size_t>(n_slots) * n_modules;
+  bool ok = hipMalloc(&p->d_pages, static_cast<size_t>(n_pages) * page_elems * eb) == hipSuccess &&
+            hipMalloc(reinterpret_cast<void**>(&p->d_entries), n_entries * sizeof(SlotEntry)) == hipSuccess &&
+            hipMalloc(reinterpret_cast<void**>(&p->d_page_ids),
+                      static_cast<size_t>(table > 0 ? table : 1) * 4) == hipSuccess &&
+            hipMalloc(&p->d_staging, p->staging_bytes) == hipSuccess;
+  ok = ok && fill_zero(p->d_entries, n_entries * sizeof(SlotEntry), nullptr) &&
+       fill_zero(p->d_page_ids, static_cast<size_t>(table) * 4, nullptr) &&
+       hipDeviceSynchronize() == hipSuccess;
+  if (!ok) {
+    free_device(p);
+    delete p;
+    return LORA_ERR_HIP;
+  }
+  *out = p;
+  return LORA_OK;
+}
+
+lora_status lora_pool_destroy(lora_pool* p) {
+  if (!p) return LORA_OK;
+  lora_status st = LORA_OK;
+  {
+    DeviceGuard g(p->device);
+    if (!g.ok || hipDeviceSynchronize() != hipSuccess) st = LORA_ERR_HIP;
+    free_device(p);
+  }
+  delete p;
+  return st;
+}
+
+lora_status lora_pool_load(lora_pool* p, int32_t slot, int32_t module, int32_t rank, const void* A,
+                           const void* B, float scale, void* stream) {
+  if (!p || !A || !B) return LORA_ERR_ARG;
+  if (slot < 0 || slot >= p->n_slots || module < 0 || module >= p->n_modules) return LORA_ERR_SLOT;
+  if (rank < 1 || rank > p->max_rank) return LORA_ERR_RANK;
+  const size_t ei = static_cast<size_t>(slot) * p->n_modules + module;
+  if (p->entries[ei].rank != 0) return LORA_ERR_SLOT;
+  const int64_t h = p->page_elems;
+  const int64_t ppr_a = p->h_in[module] / h, ppr_b = p->h_out[module] / h;
+  const int64_t n_plist = rank * (ppr_a + ppr_b);
+  std::vector<int32_t> pages;
+  if (!p->alloc.allocate(n_plist, pages)) return LORA_ERR_NO_PAGES;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t eb = p->elem_bytes();
+  const size_t a_bytes = static_cast<size_t>(rank) * p->h_in[module] * eb;
+  const size_t b_bytes = static_cast<size_t>(rank) * p->h_out[module] * eb;
+  const size_t ids_at = (a_bytes + b_bytes + 255) / 256 * 256;
+  char* st = static_cast<char*>(p->d_staging);
+  const int32_t ids_off = static_cast<int32_t>(ei * p->max_pages_per_entry);
+  SlotEntry value{rank, scale, ids_off, ids_off + static_cast<int32_t>(rank * ppr_a)};
+
+  DeviceGuard g(p->device);
+  bool ok = g.ok &&
+            hipMemcpyAsync(st, A, a_bytes, hipMemcpyDefault, s) == hipSuccess &&
+            hipMemcpyAsync(st + a_bytes, B, b_bytes, hipMemcpyDefault, s) == hipSuccess &&
+            hipMemcpyAsync(st + ids_at, pages.data(), pages.size() * 4, hipMemcpyHostToDevice, s) ==
+                hipSuccess;
+  if (ok) {
+    if (p->dtype == LORA_BF16) {
+      hipLaunchKernelGGL(k_upload<__bf16>, dim3(static_cast<unsigned>(n_plist)), dim3(256), 0, s,
+                         static_cast<__bf16*>(p->d_pages), reinterpret_cast<const __bf16*>(st),
+                         reinterpret_cast<const int32_t*>(st + ids_at), static_cast<int32_t>(n_plist), h,
+                         p->d_page_ids, ids_off, p->d_entries + ei, value);
+    } else {
+      hipLaunchKernelGGL(k_upload<float>, dim3(static_cast<unsigned>(n_plist)), dim3(256), 0, s,
+                         static_cast<float*>(p->d_pages), reinterpret_cast<const float*>(st),
+                         reinterpret_cast<const int32_t*>(st + ids_at), static_cast<int32_t>(n_plist), h,
+                         p->d_page_ids, ids_off, p->d_entries + ei, value);
+    }
+    ok = hipGetLastError() == hipSuccess && hipStreamSynchronize(s) == hipSuccess;
+  }
+  if (!ok) {
+    p->alloc.release(pages);
+    return LORA_ERR_HIP;
+  }
+  auto& e = p->entries[ei];
+  e.rank = rank;
+  e.scale = scale;
+  e.pages = std::move(pages);
+  ++p->loads;
+  return LORA_OK;
+}
+
+lora_status lora_pool_evict(lora_pool* p, int32_t slot, void* stream) {
+  if (!p) return LORA_ERR_ARG;
+  if (slot < 0 || slot >= p->n_slots) return LORA_ERR_SLOT;
+  const size_t e0 = static_cast<size_t>(slot) * p->n_modules;
+  bool any = false;
+  for (int32_t m = 0; m < p->n_modules; ++m) any |= p->entries[e0 + m].rank != 0;
+  if (!any) return LORA_ERR_SLOT;
+  DeviceGuard g(p->device);
+  if (!g.ok) return LORA_ERR_HIP;
+  hipLaunchKernelGGL(k_clear_entries, dim3((p->n_modules + 255) / 256), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), p->d_entries + e0, p->n_modules);
+  if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
+  for (int32_t m = 0; m < p->n_modules; ++m) {
+    auto& e = p->entries[e0 + m];
+    if (e.rank == 0) continue;
+    p->alloc.release(e.pages);
+    e = lora_pool::Entry();
+  }
+  ++p->evicts;
+  return LORA_OK;
+}
+
+lora_status lora_pool_stats(const lora_pool* p, lora_pool_stats_t* out) {
+  if (!p || !out) return LORA_ERR_ARG;
+  std::memset(out, 0, sizeof(*out));
+  out->n_pages = p->n_pages;
+  out->free_pages = p->alloc.free_count();
+  for (int32_t s = 0; s < p->n_slots; ++s) {
+    bool any = false;
+    for (int32_t m = 0; m < p->n_modules; ++m) {
+      if (p->entries[static_cast<size_t>(s) * p->n_modules + m].rank != 0) {
+        ++out->loaded_entries;
+        any = true;
+      }
+    }
+    out->loaded_slots += any ? 1 : 0;
+  }
+  out->loads = p->loads;
+  out->evicts = p->evicts;
+  return LORA_OK;
+}
+
+lora_status lora_pool_read(const lora_pool* p, int32_t slot, int32_t module, int32_t* rank, float* scale,
+                           void* A, void* B, int32_t* pages, int32_t max_pages) {
+  if (!p) return LORA_ERR_ARG;
+  if (slot < 0 || slot >= p->n_slots || module < 0 || module >= p->n_modules) return LORA_ERR_SLOT;
+  const auto& e = p->entries[static_cast<size_t>(slot) * p->n_modules + module];
+  if (e.rank == 0) return LORA_ERR_SLOT;
+  if (rank) *rank = e.rank;
+  if (scale) *scale = e.scale;
+  if (pages) {
+    for (int32_t i = 0; i < max_pages && i < static_cast<int32_t>(e.pages.size()); ++i) pages[i] = e.pages[i];
+  }
+  DeviceGuard g(p->device);
+  if (!g.ok || hipDeviceSynchronize() != hipSuccess) return LORA_ERR_HIP;
+  const int64_t h = p->page_elems;
+  const size_t eb = p->elem_bytes();
+  const int64_t ppr_a = p->h_in[module] / h, ppr_b = p->h_out[module] / h;
+  const char* base = static_cast<const char*>(p->d_pages);
+  for (int64_t i = 0; i < static_cast<int64_t>(e.pages.size()); ++i) {
+    const bool is_a = i < e.rank * ppr_a;
+    void* dst = is_a ? A : B;
+    if (!dst) continue;
+    const int64_t local = is_a ? i : i - e.rank * ppr_a;
+    char* d = static_cast<char*>(dst) + static_cast<size_t>(local) * h * eb;
+    const char* src = base + static_cast<size_t>(e.pages[static_cast<size_t>(i)]) * h * eb;
+    if (hipMemcpy(d, src, static_cast<size_t>(h) * eb, hipMemcpyDeviceToHost) != hipSuccess) return LORA_ERR_HIP;
+  }
+  (void)ppr_b;
+  return LORA_OK;
+}
+
+}  // extern "C"

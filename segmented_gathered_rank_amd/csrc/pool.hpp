@@ -1,0 +1,64 @@
+// Host-side state of a pool (internal to the library).
+#pragma once
+
+#include <vector>
+
+#include "common.hpp"
+#include "page_alloc.hpp"
+
+struct lora_pool {
+  int32_t device = 0;
+  lora_dtype dtype = LORA_BF16;
+  int64_t page_elems = 0;
+  int64_t n_pages = 0;
+  int32_t n_slots = 0;
+  int32_t n_modules = 0;
+  int32_t max_rank = 0;
+  int32_t max_pages_per_entry = 0;
+  std::vector<int64_t> h_in, h_out;
+
+  void* d_pages = nullptr;
+  lora::SlotEntry* d_entries = nullptr;
+  int32_t* d_page_ids = nullptr;
+  void* d_staging = nullptr;      // A and B rows of one upload, then its page list
+  size_t staging_bytes = 0;
+
+  lora::PageAllocator alloc;
+  struct Entry {
+    int32_t rank = 0;
+    float scale = 0.f;
+    std::vector<int32_t> pages;   // A's rows then B's rows, page by page
+  };
+  std::vector<Entry> entries;     // [n_slots * n_modules]
+  int64_t loads = 0, evicts = 0;
+
+  size_t elem_bytes() const { return dtype == LORA_BF16 ? 2 : 4; }
+  lora::PoolView view() const {
+    lora::PoolView v;
+    v.pages = d_pages;
+    v.entries = d_entries;
+    v.page_ids = d_page_ids;
+    v.page_elems = page_elems;
+    v.n_slots = n_slots;
+    v.n_modules = n_modules;
+    return v;
+  }
+};
+
+namespace lora {
+
+// Makes the pool's device current for the lifetime of the guard.
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = false;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) return;
+    ok = (prev == dev) || (hipSetDevice(dev) == hipSuccess);
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (ok && hipGetDevice(&cur) == hipSuccess && cur != prev && prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+}  // namespace lora

@@ -1,0 +1,203 @@
+"""Host-side driver: uploads a workload and issues the library's calls.
+
+Used by the tests, the benchmark and the smoke check.  It only moves data
+(numpy -> device tensors, adapters -> pool pages) and sequences C-ABI calls;
+every step of the apply path runs in the HIP library.
+
+A workload is any object with the attributes of ``workloads.Workload``:
+dtype, page_elems, n_slots, modules (h_in, h_out, x_group), ids, x, y0 and
+adapters[slot][module] = (rank, scale, A, B) or None.
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Tuple
+
+import numpy as np
+import torch
+
+from . import (LORA_BF16, LORA_F32, lora_apply_bgmv, lora_build_segments, lora_expand,
+               lora_pool_create, lora_pool_destroy, lora_pool_load, lora_segments_bind,
+               lora_segments_bytes, lora_shrink, lora_shrink_workspace_bytes)
+
+__all__ = ["DeviceWorkload", "to_device", "from_device"]
+
+
+def to_device(a: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """Storage array (float32, or uint16 bf16 bits) -> device tensor, bits unchanged."""
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+def from_device(t: torch.Tensor) -> np.ndarray:
+    """Device tensor -> storage array (float32, or uint16 bf16 bits)."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+class DeviceWorkload:
+    """A workload resident on one GPU: pool, x, y (= y0 copies), t, segments."""
+
+    def __init__(self, wl, device: int = 0, n_pages: Optional[int] = None, y_dtype: Optional[str] = None,
+                 extra_pages: int = 0, max_rank: Optional[int] = None, load: bool = True):
+        self.wl = wl
+        self.dev = torch.device("cuda", device)
+        self.dtype = wl.dtype
+        self.y_dtype = y_dtype or wl.dtype
+        n = wl.n_tokens
+        self.n = n
+        mods = wl.modules
+        tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+        ydt = torch.bfloat16 if self.y_dtype == "bf16" else torch.float32
+        self.max_rank = max_rank or wl.max_rank()
+        self.ld_t = max(16, (self.max_rank + 3) // 4 * 4)
+
+        # x: one flat tensor, every x group at a known element offset
+        self.x_off = []
+        sizes = [int(np.prod(a.shape)) for a in wl.x]
+        self.x = torch.empty(max(1, sum(sizes)), dtype=tdt, device=self.dev)
+        off = 0
+        for g, a in enumerate(wl.x):
+            self.x[off:off + sizes[g]] = to_device(a, wl.dtype, self.dev).reshape(-1)
+            self.x_off.append(off)
+            off += sizes[g]
+
+        # shape groups: consecutive modules with equal (h_in, h_out) share one y and one t tensor
+        self.groups: List[Tuple[int, int]] = []
+        m = 0
+        while m < len(mods):
+            e = m + 1
+            while e < len(mods) and (mods[e].h_in, mods[e].h_out) == (mods[m].h_in, mods[m].h_out):
+                e += 1
+            self.groups.append((m, e))
+            m = e
+        self.y, self.t = [], []
+        for (m0, m1) in self.groups:
+            y = torch.empty((m1 - m0, n, mods[m0].h_out), dtype=ydt, device=self.dev)
+            self.y.append(y)
+            self.t.append(torch.zeros((m1 - m0, n, self.ld_t), dtype=torch.float32, device=self.dev))
+        self.reset_y()
+
+        self.pool = None
+        if load:
+            self.pool = lora_pool_create(device, LORA_BF16 if wl.dtype == "bf16" else LORA_F32,
+                                         wl.page_elems, (n_pages or wl.pages_needed()) + extra_pages,
+                                         wl.n_slots, len(mods), [m.h_in for m in mods],
+                                         [m.h_out for m in mods], self.max_rank)
+            self.load_all()
+        self.ids = torch.from_numpy(np.ascontiguousarray(wl.ids, dtype=np.int32)).to(self.dev)
+        nb = lora_segments_bytes(n, wl.n_slots)
+        self.seg_buf = torch.zeros(max(nb, 256), dtype=torch.uint8, device=self.dev)
+        self.seg = lora_segments_bind(self.seg_buf, n, wl.n_slots)
+        self.ws_bytes = max(lora_shrink_workspace_bytes(self.pool, n, len(mods)) if self.pool else 0, 16)
+        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=self.dev)
+
+    # ---------------------------------------------------------------- data
+    def load_all(self):
+        for s, row in enumerate(self.wl.adapters):
+            for m, a in enumerate(row):
+                if a is not None:
+                    rank, scale, A, B = a
+                    lora_pool_load(self.pool, s, m, rank, np.ascontiguousarray(A), np.ascontiguousarray(B),
+                                   scale)
+        torch.cuda.synchronize(self.dev)
+
+    def reset_y(self):
+        """y <- y0 (converted to the output dtype if it differs)."""
+        for gi, (m0, m1) in enumerate(self.groups):
+            for m in range(m0, m1):
+                y0 = to_device(self.wl.y0[m], self.wl.dtype, self.dev)
+                self.y[gi][m - m0].copy_(y0.to(self.y[gi].dtype))
+
+    def zero_y(self):
+        for y in self.y:
+            y.zero_()
+
+    def y_of(self, module: int) -> torch.Tensor:
+        for gi, (m0, m1) in enumerate(self.groups):
+            if m0 <= module < m1:
+                return self.y[gi][module - m0]
+        raise IndexError(module)
+
+    def t_of(self, module: int) -> torch.Tensor:
+        for gi, (m0, m1) in enumerate(self.groups):
+            if m0 <= module < m1:
+                return self.t[gi][module - m0]
+        raise IndexError(module)
+
+    # ---------------------------------------------------------------- calls
+    def _x_runs(self, m0: int, m1: int):
+        """Split modules [m0, m1) into runs whose x offsets step uniformly."""
+        mods = self.wl.modules
+        runs, m = [], m0
+        while m < m1:
+            e = m + 1
+            xo = self.x_off[mods[m].x_group]
+            stride = None
+            while e < m1:
+                d = self.x_off[mods[e].x_group] - self.x_off[mods[e - 1].x_group]
+                if stride is None:
+                    stride = d
+                if d != stride or d < 0:
+                    break
+                e += 1
+            runs.append((m, e, xo, stride or 0))
+            m = e
+        return runs
+
+    def _xp(self, off: int) -> int:
+        return self.x.data_ptr() + off * self.x.element_size()
+
+    def build_segments(self, stream=None):
+        lora_build_segments(self.ids, self.seg, stream)
+
+    def shrink(self, stream=None):
+        mods = self.wl.modules
+        for gi, (m0, m1) in enumerate(self.groups):
+            h_in = mods[m0].h_in
+            t = self.t[gi]
+            for (a, b, xo, msx) in self._x_runs(m0, m1):
+                tp = t.data_ptr() + (a - m0) * t.stride(0) * 4
+                lora_shrink(self.pool, a, b - a, self._xp(xo), h_in, msx, self.seg, tp, self.ld_t, t.stride(0),
+                            self.ws, self.ws_bytes, stream)
+
+    def expand(self, stream=None):
+        ydt = LORA_BF16 if self.y_dtype == "bf16" else LORA_F32
+        mods = self.wl.modules
+        for gi, (m0, m1) in enumerate(self.groups):
+            y, t = self.y[gi], self.t[gi]
+            lora_expand(self.pool, m0, m1 - m0, t, self.ld_t, t.stride(0), self.seg, y, mods[m0].h_out,
+                        y.stride(0), ydt, stream)
+
+    def bgmv(self, stream=None):
+        ydt = LORA_BF16 if self.y_dtype == "bf16" else LORA_F32
+        mods = self.wl.modules
+        for gi, (m0, m1) in enumerate(self.groups):
+            y = self.y[gi]
+            for (a, b, xo, msx) in self._x_runs(m0, m1):
+                yp = y.data_ptr() + (a - m0) * y.stride(0) * y.element_size()
+                lora_apply_bgmv(self.pool, a, b - a, self._xp(xo), mods[m0].h_in, msx, self.seg, yp,
+                                mods[m0].h_out, y.stride(0), ydt, stream)
+
+    def sgmv_step(self, stream=None):
+        self.build_segments(stream)
+        self.shrink(stream)
+        self.expand(stream)
+
+    def bgmv_step(self, stream=None):
+        self.build_segments(stream)
+        self.bgmv(stream)
+
+    def close(self):
+        if self.pool is not None:
+            torch.cuda.synchronize(self.dev)
+            lora_pool_destroy(self.pool)
+            self.pool = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

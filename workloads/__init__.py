@@ -45,11 +45,17 @@ __all__ = [
 # storage helpers
 # --------------------------------------------------------------------------
 def to_bf16_bits(a: np.ndarray) -> np.ndarray:
-    """Round float32 values to bfloat16 (nearest, ties to even); return the bits."""
+    """Round finite float32 values to bfloat16 (nearest, ties to even); return the bits."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return u.astype(np.uint16)
+    out = np.empty(a.shape, dtype=np.uint16)
+    flat_in, flat_out = a.reshape(-1), out.reshape(-1)
+    step = 1 << 24
+    for s in range(0, flat_in.size, step):
+        u = flat_in[s:s + step].view(np.uint32).copy()
+        u += np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+        u >>= np.uint32(16)
+        flat_out[s:s + step] = u
+    return out
 
 
 def _store(a32: np.ndarray, dtype: str) -> np.ndarray:
@@ -131,7 +137,10 @@ class Workload:
 
 
 def _normal(rng, std, shape):
-    return rng.normal(0.0, std, shape).astype(np.float32)
+    """N(0, std) in float32 (std is the standard deviation)."""
+    z = rng.standard_normal(shape, dtype=np.float32)
+    z *= np.float32(std)
+    return z
 
 
 def _draw_values(rng, dtype, n_tokens, modules, x_groups, slot_ranks, scales,
