@@ -40,6 +40,11 @@ STATUS = {
     -8: "LORA_ERR_DEVICE_IDS", -9: "LORA_ERR_WORKSPACE",
 }
 
+try:  # load torch's HIP runtime first so that the library and torch share one runtime
+    import torch  # noqa: F401
+except ImportError:
+    pass
+
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m segmented_gathered_rank_amd.build`")
 _lib = ctypes.CDLL(LIB_PATH)

@@ -60,22 +60,35 @@ bool mfma_ok(const lora_pool* p, int32_t module) {
   return p->dtype == LORA_BF16 && p->page_elems % kExpandCols == 0 && p->h_out[module] % kExpandCols == 0;
 }
 
+// Grid for a persistent loop over `bound` work items: a multiple of 8 (one
+// share per XCD), at most kMaxGrid.
 unsigned grid_of(int32_t bound) {
   if (bound < 1) bound = 1;
-  return static_cast<unsigned>(bound < kMaxGrid ? bound : kMaxGrid);
+  if (bound > kMaxGrid) bound = kMaxGrid;
+  return static_cast<unsigned>((bound + 7) / 8 * 8);
+}
+
+GemvArgs gemv_args(const lora_pool* p, int32_t module0, const SegView& sv, int32_t units_word) {
+  GemvArgs g{};
+  g.pv = p->view();
+  g.sv = sv;
+  g.module0 = module0;
+  g.units_word = units_word;
+  g.h_in = static_cast<int32_t>(p->h_in[module0]);
+  g.h_out = static_cast<int32_t>(p->h_out[module0]);
+  g.magic = static_cast<uint32_t>(((uint64_t(1) << 32) + p->page_elems - 1) / p->page_elems);
+  return g;
 }
 
 int32_t ldr_of(const lora_pool* p) { return (p->max_rank + 15) / 16 * 16; }
 
-// Workspace of the split-K shrink for `ks` splits.
+// Workspace of the split-K shrink for `ks` splits: one partial tile per split.
 size_t split_ws_bytes(const lora_pool* p, int32_t n_tokens, int32_t n_modules, int32_t ks) {
   if (ks <= 1) return 0;
   const size_t tiles = static_cast<size_t>(max_tiles_of(n_tokens));
-  const size_t tickets = (tiles * n_modules * 4 + 255) / 256 * 256;
-  return tickets + tiles * n_modules * ks * kTileTokens * ldr_of(p) * sizeof(float);
+  return tiles * n_modules * ks * kTileTokens * ldr_of(p) * sizeof(float);
 }
 
-constexpr int32_t kMaxSplits = 8;
 
 template <typename TI>
 lora_status launch_shrink(const lora_pool* p, int32_t module0, int32_t n_modules, const void* x, int64_t ld_x,
@@ -86,8 +99,14 @@ lora_status launch_shrink(const lora_pool* p, int32_t module0, int32_t n_modules
   const int32_t h_in = static_cast<int32_t>(p->h_in[module0]);
   const bool use_mfma = mfma_ok(p, module0);
   const int32_t units_word = use_mfma ? LORA_META_N_UNITS_SHORT : LORA_META_N_UNITS_ALL;
-  hipLaunchKernelGGL(k_shrink_gemv<TI>, dim3(grid_of(seg->max_units), n_modules), dim3(kGemvThreads), 0, s, pv,
-                     module0, sv, units_word, static_cast<const TI*>(x), ld_x, msx, t, ld_t, mst, h_in);
+  GemvArgs g = gemv_args(p, module0, sv, units_word);
+  g.x = x;
+  g.ld_x = ld_x;
+  g.msx = msx;
+  g.t = t;
+  g.ld_t = ld_t;
+  g.mst = mst;
+  hipLaunchKernelGGL((k_gemv<1, TI, TI>), dim3(grid_of(seg->max_units), n_modules), dim3(kGemvThreads), 0, s, g);
   if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
   if constexpr (sizeof(TI) == 2) {
     if (use_mfma && seg->max_tiles > 0) {
@@ -119,12 +138,39 @@ lora_status launch_shrink(const lora_pool* p, int32_t module0, int32_t n_modules
       a.ks_count = ks;
       a.k_per_split = kps;
       a.ldr = ldr_of(p);
-      const size_t tiles = static_cast<size_t>(seg->max_tiles);
-      const size_t tickets = (tiles * n_modules * 4 + 255) / 256 * 256;
-      a.tickets = static_cast<int32_t*>(ws);
-      a.part = ks > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + tickets) : nullptr;
-      hipLaunchKernelGGL(k_shrink_mfma, dim3(grid_of(seg->max_tiles), ks, groups), dim3(kMfmaThreads), 0, s, a);
+      a.magic = static_cast<uint32_t>(((uint64_t(1) << 32) + p->page_elems - 1) / p->page_elems);
+      // staged A per sub-chunk: at most kStageBatch 16-byte chunks per thread (32 KiB)
+      int32_t kc = (kMfmaThreads * kStageBatch * 8 / (per_wg * a.ldr)) / 32 * 32;
+      if (kc > 32 * kShrinkSteps) kc = 32 * kShrinkSteps;
+      if (kc > kps) kc = kps;
+      if (kc < 32) kc = 32;
+      a.kc = kc;
+      a.max_pids = p->max_pages_per_entry;
+      const size_t lds = static_cast<size_t>(per_wg) * a.ldr * (kc + 8) * 2 +
+                         static_cast<size_t>(per_wg) * a.max_pids * 4;
+      a.part = ks > 1 ? static_cast<float*>(ws) : nullptr;
+      const dim3 grid(grid_of(seg->max_tiles), ks, groups), block(kMfmaThreads);
+      const int ntiles = a.ldr <= 16 ? 1 : a.ldr <= 32 ? 2 : 4;
+#define LORA_SHRINK_LAUNCH(M, NT) hipLaunchKernelGGL((k_shrink_mfma<M, NT>), grid, block, lds, s, a)
+#define LORA_SHRINK_NT(M)                                 \
+  do {                                                    \
+    if (ntiles == 1) LORA_SHRINK_LAUNCH(M, 1);            \
+    else if (ntiles == 2) LORA_SHRINK_LAUNCH(M, 2);       \
+    else LORA_SHRINK_LAUNCH(M, 4);                        \
+  } while (0)
+      switch (per_wg) {
+        case 1: LORA_SHRINK_NT(1); break;
+        case 2: LORA_SHRINK_NT(2); break;
+        case 3: LORA_SHRINK_NT(3); break;
+        default: LORA_SHRINK_NT(4); break;
+      }
+#undef LORA_SHRINK_NT
+#undef LORA_SHRINK_LAUNCH
       if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
+      if (ks > 1) {
+        hipLaunchKernelGGL(k_shrink_reduce, dim3(grid_of(seg->max_tiles), n_modules), block, 0, s, a);
+        if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
+      }
     }
   }
   return LORA_OK;
@@ -139,14 +185,26 @@ lora_status launch_expand(const lora_pool* p, int32_t module0, int32_t n_modules
   const int32_t h_out = static_cast<int32_t>(p->h_out[module0]);
   const bool use_mfma = mfma_ok(p, module0);
   const int32_t units_word = use_mfma ? LORA_META_N_UNITS_SHORT : LORA_META_N_UNITS_ALL;
-  hipLaunchKernelGGL((k_expand_gemv<TI, TO>), dim3(grid_of(seg->max_units), n_modules), dim3(kGemvThreads), 0, s,
-                     pv, module0, sv, units_word, t, ld_t, mst, static_cast<TO*>(y), ld_y, msy, h_out);
+  GemvArgs g = gemv_args(p, module0, sv, units_word);
+  g.t = const_cast<float*>(t);
+  g.ld_t = ld_t;
+  g.mst = mst;
+  g.y = y;
+  g.ld_y = ld_y;
+  g.msy = msy;
+  hipLaunchKernelGGL((k_gemv<2, TI, TO>), dim3(grid_of(seg->max_units), n_modules), dim3(kGemvThreads), 0, s, g);
   if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
   if constexpr (sizeof(TI) == 2) {
     if (use_mfma && seg->max_tiles > 0) {
-      hipLaunchKernelGGL((k_expand_mfma<TO>), dim3(grid_of(seg->max_tiles), h_out / kExpandCols, n_modules),
-                         dim3(kMfmaThreads), 0, s, pv, module0, sv, t, ld_t, mst, static_cast<TO*>(y), ld_y, msy,
-                         h_out);
+      const int32_t ldr = ldr_of(p);
+      const size_t ysz = sizeof(TO);
+      const size_t lds = (static_cast<size_t>(kTileTokens) * (ldr + 1) * 4 + 15) / 16 * 16 +
+                         (static_cast<size_t>(ldr) * (kExpandCols + 8) * 2 + 15) / 16 * 16 +
+                         static_cast<size_t>(kTileTokens) * (kExpandCols + 16 / ysz) * ysz;
+      const int32_t col_groups = (h_out / kExpandCols + kExpandBlocks - 1) / kExpandBlocks;
+      hipLaunchKernelGGL((k_expand_mfma<TO>), dim3(grid_of(seg->max_tiles), col_groups, n_modules),
+                         dim3(kMfmaThreads), lds, s, pv, module0, sv, t, ld_t, mst, static_cast<TO*>(y), ld_y, msy,
+                         h_out, ldr);
       if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
     }
   }
@@ -156,9 +214,14 @@ lora_status launch_expand(const lora_pool* p, int32_t module0, int32_t n_modules
 template <typename TI, typename TO>
 lora_status launch_bgmv(const lora_pool* p, int32_t module0, int32_t n_modules, const void* x, int64_t ld_x,
                         int64_t msx, const lora_segments* seg, void* y, int64_t ld_y, int64_t msy, hipStream_t s) {
-  hipLaunchKernelGGL((k_bgmv<TI, TO>), dim3(grid_of(seg->max_units), n_modules), dim3(kGemvThreads), 0, s,
-                     p->view(), module0, seg_view(seg), static_cast<const TI*>(x), ld_x, msx, static_cast<TO*>(y),
-                     ld_y, msy, static_cast<int32_t>(p->h_in[module0]), static_cast<int32_t>(p->h_out[module0]));
+  GemvArgs g = gemv_args(p, module0, seg_view(seg), LORA_META_N_UNITS_ALL);
+  g.x = x;
+  g.ld_x = ld_x;
+  g.msx = msx;
+  g.y = y;
+  g.ld_y = ld_y;
+  g.msy = msy;
+  hipLaunchKernelGGL((k_gemv<0, TI, TO>), dim3(grid_of(seg->max_units), n_modules), dim3(kGemvThreads), 0, s, g);
   return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 

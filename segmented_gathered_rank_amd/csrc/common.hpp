@@ -10,11 +10,12 @@
 namespace lora {
 
 // Work decomposition fixed by the library (recorded in the segment meta).
-constexpr int kUnitTokens = 8;     // tokens per GEMV work unit
+constexpr int kUnitTokens = 4;     // tokens per GEMV work unit
 constexpr int kTileTokens = 64;    // tokens per matrix-core tile
 constexpr int kLongMin = 64;       // segments this long or longer use matrix-core tiles
 constexpr int kMaxRank = LORA_MAX_RANK;
 constexpr int kMaxSlots = 8192;   // the segment builder's LDS histogram bound
+constexpr int kMaxEntryPages = 1024;  // pages of one (slot, module) entry (an LDS table in the GEMV kernels)
 
 // One (slot, module) entry of the device slot table.
 struct SlotEntry {
@@ -149,6 +150,30 @@ __device__ __forceinline__ float wave_transpose_reduce(float (&v)[64], int lane)
   if constexpr (V <= 32) s += xor_lane<1>(s);
   return s;
 }
+
+// Work distribution over the 8 XCDs.  Workgroups are dealt to the XCDs
+// round-robin (linear id mod 8) and each XCD has its own L2.  The n work items
+// (known only on the device) are cut into 8 contiguous shares, share x going to
+// the workgroups of XCD x, so consecutive items (the pieces of one segment,
+// which read the same adapter pages) meet in one L2 and every XCD gets work.
+// Usage: for (XcdIter it(n); it.valid(); it.next()) { int u = it.item; ... }
+// gridDim.x must be a multiple of 8.
+struct XcdIter {
+  int item, idx, per, n, step, xcd;
+  __device__ __forceinline__ explicit XcdIter(int n_items) {
+    n = n_items;
+    per = (n_items + 7) >> 3;
+    xcd = static_cast<int>(blockIdx.x & 7);
+    idx = static_cast<int>(blockIdx.x >> 3);
+    step = static_cast<int>(gridDim.x >> 3);
+    item = xcd * per + idx;
+  }
+  __device__ __forceinline__ bool valid() const { return idx < per && item < n; }
+  __device__ __forceinline__ void next() {
+    idx += step;
+    item = xcd * per + idx;
+  }
+};
 
 // Upper bounds of the segment work lists (host and device agree on them).
 __host__ __device__ inline int32_t max_segs_of(int32_t n_tokens, int32_t n_slots) {

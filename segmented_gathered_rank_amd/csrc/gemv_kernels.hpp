@@ -2,257 +2,327 @@
 //
 // A work unit is up to kUnitTokens tokens of one segment, i.e. tokens that
 // share one adapter ("BGMV ... one adapter per decode token" and SGMV's
-// segments, study page "The kernel trick").  One 256-thread workgroup takes a
-// unit and reads each gathered page of its adapter once for all its tokens.
+// segments, study page "The kernel trick").  One 1024-thread workgroup (16
+// wave64s) takes a unit and reads each gathered page of its adapter once for
+// all its tokens.  The work is laid out so that every lane issues all of its
+// loads for a phase back to back: a unit costs about three memory round trips
+// (token ids and page ids; x and A; B and y), which is what bounds a decode
+// step made of many small units.
 //
-// shrink: t[tb][j] = sum_k x[tok_tb][k] * A[j][k].  The 256 threads split k
-//         (16-byte loads, 8 elements each, so a wave reads 1 KiB of a row
-//         per instruction); each lane keeps RG x NT partial sums, which a
-//         wave64 transpose-reduction (DPP row ops and ds_bpermute) folds into
-//         one sum per lane, and four wave partials are added in LDS in a
-//         fixed order (deterministic, no float atomics).
-// expand: y[tok_tb][c] = round(y + scale * sum_j t[tb][j] * B[j][c]).  Each
-//         thread owns 8 consecutive columns, streams the rank rows of B with
-//         16-byte loads (16 rows in flight) and updates y in place, one
-//         rounding per element.
+// shrink: t[tb][j] = sum_k x[tok_tb][k] * A[j][k].  The unit's x rows are
+//         staged in LDS (16-byte coalesced loads).  Wave w owns rank rows
+//         w, w+16, ...; a lane takes eight 16-byte chunks of the row (a wave
+//         reads 1 KiB of the row per instruction) and keeps NT partial sums,
+//         folded across the wave by DPP row operations (lane distance < 16)
+//         and ds_bpermute (16, 32): no LDS reduction, no float atomics, a
+//         fixed summation order.
+// expand: y[tok_tb][c] = round(y + scale * sum_j t[tb][j] * B[j][c]).  A
+//         thread owns 4 consecutive columns (8-byte loads of bf16, 16-byte of
+//         fp32), loads up to 16 rank rows of B and its y rows at once, and
+//         updates y in place with one rounding per element.
 #pragma once
 
 #include "common.hpp"
 
 namespace lora {
 
-constexpr int kGemvThreads = 256;
+#ifndef LORA_GEMV_THREADS
+#define LORA_GEMV_THREADS 256
+#endif
+#ifndef LORA_SHRINK_BATCH
+#define LORA_SHRINK_BATCH 8
+#endif
+#ifndef LORA_EXPAND_BATCH
+#define LORA_EXPAND_BATCH 16
+#endif
+constexpr int kGemvThreads = LORA_GEMV_THREADS;
+constexpr int kGemvWaves = kGemvThreads / 64;
+constexpr int kXSliceBytes = 32768;                 // LDS for the staged x rows of a unit
+constexpr int kShrinkBatch = LORA_SHRINK_BATCH;     // 16-byte chunks of a row in flight per lane
+template <typename TI>
+constexpr int kExpandBatch = sizeof(TI) == 2 ? LORA_EXPAND_BATCH : 8;   // rank rows of B in flight per thread
+
+template <typename TI>
+struct XSlice {
+  static constexpr int kElems = kXSliceBytes / (kUnitTokens * static_cast<int>(sizeof(TI)));
+};
+
+// Page of element k of a row: k / h, with h's reciprocal (exact for k*h < 2^32).
+__device__ __forceinline__ int page_of(int k, uint32_t magic, int ppr) {
+  return ppr == 1 ? 0 : static_cast<int>(__umulhi(static_cast<uint32_t>(k), magic));
+}
+
+// Four consecutive elements as floats / stored with one rounding.
+template <typename T> struct Quad;
+template <> struct Quad<__bf16> {
+  uint32_t lo, hi;
+  __device__ __forceinline__ void load(const __bf16* p) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    lo = v.x;
+    hi = v.y;
+  }
+  __device__ __forceinline__ void zero() { lo = hi = 0u; }
+  __device__ __forceinline__ void unpack(float (&f)[4]) const {
+    f[0] = bf16lo(lo); f[1] = bf16hi(lo); f[2] = bf16lo(hi); f[3] = bf16hi(hi);
+  }
+  static __device__ __forceinline__ void store(__bf16* p, const float (&f)[4]) {
+    __bf16 h[4] = {static_cast<__bf16>(f[0]), static_cast<__bf16>(f[1]), static_cast<__bf16>(f[2]),
+                   static_cast<__bf16>(f[3])};
+    *reinterpret_cast<uint2*>(p) = __builtin_bit_cast(uint2, h);
+  }
+};
+template <> struct Quad<float> {
+  f32x4 v;
+  __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const f32x4*>(p); }
+  __device__ __forceinline__ void zero() { v = f32x4{0.f, 0.f, 0.f, 0.f}; }
+  __device__ __forceinline__ void unpack(float (&f)[4]) const { f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w; }
+  static __device__ __forceinline__ void store(float* p, const float (&f)[4]) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{f[0], f[1], f[2], f[3]};
+  }
+};
+
+struct UnitLds {
+  float t[kUnitTokens * kMaxRank];
+  int32_t pid[kMaxEntryPages];
+  int32_t toks[kUnitTokens];
+};
+
+// Copies x[tok][k0 .. k0+len) of the unit's tokens into xs[tb][0 .. len).
+template <typename TI>
+__device__ __forceinline__ void stage_x(const TI* __restrict__ x, int64_t ld_x, const int32_t* toks, int nt,
+                                        int k0, int len, TI* xs) {
+  constexpr int V = 16 / sizeof(TI);
+  constexpr int S = XSlice<TI>::kElems;
+  const int per_tok = len / V;
+  for (int i = threadIdx.x; i < nt * per_tok; i += kGemvThreads) {
+    const int tb = i / per_tok, c = (i - tb * per_tok) * V;
+    *reinterpret_cast<u32x4*>(xs + tb * S + c) =
+        *reinterpret_cast<const u32x4*>(x + static_cast<int64_t>(toks[tb]) * ld_x + k0 + c);
+  }
+}
 
 template <typename TI, int NT>
-__device__ __forceinline__ void shrink_unit(const TI* __restrict__ x, int64_t ld_x, const int32_t* toks,
-                                            int nt, const TI* __restrict__ pages,
-                                            const int32_t* __restrict__ pids_a, int32_t h, int32_t h_in,
-                                            int32_t rank, float* t_s, float* red_s) {
-  constexpr int RG = (NT >= 8) ? 8 : 16;   // rank rows per pass
-  constexpr int V = RG * NT;               // partial sums per lane
-  constexpr int G = 64 / V;                // lanes holding the same reduced value
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n_chunks = h_in >> 3;
+__device__ __forceinline__ void shrink_unit(const TI* __restrict__ x, int64_t ld_x, UnitLds& L, int nt,
+                                            const TI* __restrict__ pages, int pid0, int32_t h, uint32_t magic,
+                                            int32_t h_in, int32_t rank, TI* xs) {
+  constexpr int S = XSlice<TI>::kElems;
+  constexpr int CE = 16 / sizeof(TI);  // elements per 16-byte chunk
+  constexpr int G = 64 / NT;           // lanes holding the same reduced value
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ppr = h_in / h;
-  int64_t xoff[NT];
-#pragma unroll
-  for (int tb = 0; tb < NT; ++tb) xoff[tb] = static_cast<int64_t>(toks[tb < nt ? tb : 0]) * ld_x;
-
-  for (int g = 0; g < rank; g += RG) {
+  (void)magic;
+  const int n_slices = (h_in + S - 1) / S;
+  if (n_slices == 1) {
+    stage_x(x, ld_x, L.toks, nt, 0, h_in, xs);
+    __syncthreads();
+  }
+  for (int j0 = 0; j0 < rank; j0 += kGemvWaves) {
+    const int j = j0 + wave;             // this wave's row
     float acc[64];
 #pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] = 0.f;
-    for (int c = tid; c < n_chunks; c += kGemvThreads) {
-      const int k = c << 3;
-      const int p = k / h;
-      const int off = k - p * h;
-      float xv[NT][8];
-#pragma unroll
-      for (int tb = 0; tb < NT; ++tb) {
-        if (tb < nt) {
-          load8(x + xoff[tb] + k, xv[tb]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) xv[tb][e] = 0.f;
-        }
+    for (int i = 0; i < NT; ++i) acc[i] = 0.f;
+    for (int sl = 0; sl < n_slices; ++sl) {
+      const int k0 = sl * S;
+      const int len = min(S, h_in - k0);
+      if (n_slices > 1) {
+        __syncthreads();
+        stage_x(x, ld_x, L.toks, nt, k0, len, xs);
+        __syncthreads();
       }
+      if (j >= rank) continue;           // wave-uniform
+      // pages of row j that overlap [k0, k0+len): each has one base address for the whole wave
+      for (int p = k0 / h; p * h < k0 + len; ++p) {
+        const int kp0 = max(k0, p * h), kp1 = min(k0 + len, (p + 1) * h);
+        const int pid = __builtin_amdgcn_readfirstlane(L.pid[pid0 + j * ppr + p]);
+        const TI* base = pages + (static_cast<int64_t>(pid) - p) * h;   // base + k -> element k of row j
+        for (int kb = kp0; kb < kp1; kb += 64 * CE * kShrinkBatch) {
+          Chunk<TI> raw[kShrinkBatch];
 #pragma unroll
-      for (int q = 0; q < RG; ++q) {
-        const int j = g + q;
-        if (j < rank) {
-          float av[8];
-          load8(pages + static_cast<int64_t>(pids_a[j * ppr + p]) * h + off, av);
+          for (int i = 0; i < kShrinkBatch; ++i) {
+            const int k = kb + (lane + 64 * i) * CE;
+            if (k < kp1) raw[i].load(base + static_cast<uint32_t>(k));
+            else raw[i].zero();
+          }
 #pragma unroll
-          for (int tb = 0; tb < NT; ++tb) {
+          for (int i = 0; i < kShrinkBatch; ++i) {
+            const int k = kb + (lane + 64 * i) * CE;
+            if (k < kp1) {
+              float av[CE];
+              raw[i].unpack(av);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[q * NT + tb] = fmaf(av[e], xv[tb][e], acc[q * NT + tb]);
+              for (int tb = 0; tb < NT; ++tb) {
+                if (tb < nt) {
+                  float xv[CE];
+                  Chunk<TI> xc;
+                  xc.load(xs + tb * S + (k - k0));
+                  xc.unpack(xv);
+#pragma unroll
+                  for (int e = 0; e < CE; ++e) acc[tb] = fmaf(av[e], xv[e], acc[tb]);
+                }
+              }
+            }
+            __builtin_amdgcn_sched_barrier(0);   // keep the x reads of later chunks from piling up
           }
         }
       }
     }
-    const float r = wave_transpose_reduce<V>(acc, lane);
-    if ((lane % G) == 0) red_s[wave * 64 + lane / G] = r;
-    __syncthreads();
-    if (tid < V) {
-      const float s = ((red_s[tid] + red_s[64 + tid]) + red_s[128 + tid]) + red_s[192 + tid];
-      const int q = tid / NT, tb = tid % NT;
-      if (g + q < rank && tb < nt) t_s[tb * kMaxRank + g + q] = s;
+    if (j < rank) {
+      const float r = wave_transpose_reduce<NT>(acc, lane);
+      const int tb = lane / G;
+      if ((lane % G) == 0 && tb < nt) L.t[tb * kMaxRank + j] = r;
     }
-    __syncthreads();
   }
+  __syncthreads();
 }
 
 template <typename TI, typename TO, int NT>
-__device__ __forceinline__ void expand_unit(TO* __restrict__ y, int64_t ld_y, const int32_t* toks, int nt,
-                                            const TI* __restrict__ pages, const int32_t* __restrict__ pids_b,
-                                            int32_t h, int32_t h_out, int32_t rank, float scale,
-                                            const float* t_s) {
-  constexpr int JB = (sizeof(TI) == 2) ? 16 : 8;   // rank rows of B in flight
-  const int tid = threadIdx.x;
-  const int n_chunks = h_out >> 3;
+__device__ __forceinline__ void expand_unit(TO* __restrict__ y, int64_t ld_y, const UnitLds& L, int nt,
+                                            const TI* __restrict__ pages, int pid0, int32_t h, uint32_t magic,
+                                            int32_t h_out, int32_t rank, float scale) {
+  const int n_quads = h_out >> 2;
   const int ppr = h_out / h;
   int64_t yoff[NT];
 #pragma unroll
-  for (int tb = 0; tb < NT; ++tb) yoff[tb] = static_cast<int64_t>(toks[tb < nt ? tb : 0]) * ld_y;
+  for (int tb = 0; tb < NT; ++tb) yoff[tb] = static_cast<int64_t>(L.toks[tb < nt ? tb : 0]) * ld_y;
 
-  for (int c = tid; c < n_chunks; c += kGemvThreads) {
-    const int k = c << 3;
-    const int p = k / h;
-    const int off = k - p * h;
-    float acc[NT][8];
+  // A wave covers 256 consecutive columns; when the page size is a multiple
+  // of 256 they lie in one page, so each rank row has one base address for
+  // the wave (scalar registers) and every load needs one 32-bit lane offset.
+  const bool wave_page = (h % 256) == 0;
+  for (int c = threadIdx.x; c < n_quads; c += kGemvThreads) {
+    const int k = c << 2;
+    Quad<TO> yq[NT];
+#pragma unroll
+    for (int tb = 0; tb < NT; ++tb) {
+      if (tb < nt) yq[tb].load(y + yoff[tb] + k);
+    }
+    float acc[NT][4];
 #pragma unroll
     for (int tb = 0; tb < NT; ++tb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[tb][e] = 0.f;
-    for (int j0 = 0; j0 < rank; j0 += JB) {
-      float bv[JB][8];
+      for (int e = 0; e < 4; ++e) acc[tb][e] = 0.f;
+    int p, off;
+    if (wave_page) {
+      p = __builtin_amdgcn_readfirstlane(page_of(k, magic, ppr));
+      off = k - p * h;
+    } else {
+      p = page_of(k, magic, ppr);
+      off = k - p * h;
+    }
+    for (int j0 = 0; j0 < rank; j0 += kExpandBatch<TI>) {
+      Quad<TI> raw[kExpandBatch<TI>];
 #pragma unroll
-      for (int jj = 0; jj < JB; ++jj) {
+      for (int jj = 0; jj < kExpandBatch<TI>; ++jj) {
         if (j0 + jj < rank) {
-          load8(pages + static_cast<int64_t>(pids_b[(j0 + jj) * ppr + p]) * h + off, bv[jj]);
+          int pid = L.pid[pid0 + (j0 + jj) * ppr + p];
+          if (wave_page) pid = __builtin_amdgcn_readfirstlane(pid);
+          raw[jj].load(pages + static_cast<int64_t>(pid) * h + static_cast<uint32_t>(off));
         } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) bv[jj][e] = 0.f;
+          raw[jj].zero();
         }
       }
 #pragma unroll
-      for (int jj = 0; jj < JB; ++jj) {
+      for (int jj = 0; jj < kExpandBatch<TI>; ++jj) {
+        float bv[4];
+        raw[jj].unpack(bv);
 #pragma unroll
         for (int tb = 0; tb < NT; ++tb) {
-          const float tv = t_s[tb * kMaxRank + j0 + jj];
+          // t is the same for the whole workgroup: keep it in a scalar register
+          const float tv = __builtin_bit_cast(
+              float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, L.t[tb * kMaxRank + j0 + jj])));
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[tb][e] = fmaf(tv, bv[jj][e], acc[tb][e]);
+          for (int e = 0; e < 4; ++e) acc[tb][e] = fmaf(tv, bv[e], acc[tb][e]);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 #pragma unroll
     for (int tb = 0; tb < NT; ++tb) {
       if (tb < nt) {
-        TO* yp = y + yoff[tb] + k;
-        float yv[8];
-        load8(yp, yv);
+        float yv[4];
+        yq[tb].unpack(yv);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) yv[e] = fmaf(scale, acc[tb][e], yv[e]);
-        store8(yp, yv);
+        for (int e = 0; e < 4; ++e) yv[e] = fmaf(scale, acc[tb][e], yv[e]);
+        Quad<TO>::store(y + yoff[tb] + k, yv);
       }
     }
   }
 }
 
-// Loads a unit's tokens into LDS and clears its t rows.  Ends with a barrier.
-__device__ __forceinline__ void unit_prologue(const SegView& sv, int pos, int nt, int32_t* toks_s, float* t_s) {
-  __syncthreads();   // the previous unit is done with the LDS buffers
-  if (threadIdx.x < kUnitTokens) toks_s[threadIdx.x] = threadIdx.x < nt ? sv.perm[pos + threadIdx.x] : 0;
-  for (int i = threadIdx.x; i < kUnitTokens * kMaxRank; i += kGemvThreads) t_s[i] = 0.f;
+// Loads a unit's tokens and page ids (A rows from a_off, B rows from b_off)
+// into LDS and clears its t rows.  Ends with a barrier.
+__device__ __forceinline__ void unit_prologue(const SegView& sv, const PoolView& pv, const SlotEntry& e, int pos,
+                                              int nt, int n_a, int n_b, UnitLds& L) {
+  __syncthreads();   // the previous unit is done with LDS
+  const int tid = threadIdx.x;
+  if (tid < kUnitTokens) L.toks[tid] = tid < nt ? sv.perm[pos + tid] : 0;
+  for (int i = tid; i < n_a; i += kGemvThreads) L.pid[i] = pv.page_ids[e.a_off + i];
+  for (int i = tid; i < n_b; i += kGemvThreads) L.pid[n_a + i] = pv.page_ids[e.b_off + i];
+  for (int i = tid; i < kUnitTokens * kMaxRank; i += kGemvThreads) L.t[i] = 0.f;
   __syncthreads();
 }
 
-// Fused BGMV: shrink and expand of each unit, t kept in LDS.
-template <typename TI, typename TO>
-__global__ __launch_bounds__(kGemvThreads) void k_bgmv(PoolView pv, int32_t module0, SegView sv,
-                                                      const TI* __restrict__ x, int64_t ld_x, int64_t msx,
-                                                      TO* __restrict__ y, int64_t ld_y, int64_t msy,
-                                                      int32_t h_in, int32_t h_out) {
-  __shared__ float t_s[kUnitTokens * kMaxRank];
-  __shared__ float red_s[4 * 64];
-  __shared__ int32_t toks_s[kUnitTokens];
-  const int m = blockIdx.y;
-  const int n_units = sv.meta[LORA_META_N_UNITS_ALL];
-  const TI* xm = x + m * msx;
-  TO* ym = y + m * msy;
-  const TI* pages = static_cast<const TI*>(pv.pages);
-  const int32_t h = static_cast<int32_t>(pv.page_elems);
-  for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
-    const int seg = sv.units[2 * u], pos = sv.units[2 * u + 1];
-    const int nt = min(kUnitTokens, sv.seg_start[seg + 1] - pos);
-    const int slot = sv.seg_slot[seg];
-    const SlotEntry e = pv.entries[slot * pv.n_modules + module0 + m];
-    if (e.rank <= 0) continue;
-    unit_prologue(sv, pos, nt, toks_s, t_s);
-    const int32_t* pa = pv.page_ids + e.a_off;
-    const int32_t* pb = pv.page_ids + e.b_off;
-    if (nt == 1) {
-      shrink_unit<TI, 1>(xm, ld_x, toks_s, nt, pages, pa, h, h_in, e.rank, t_s, red_s);
-      expand_unit<TI, TO, 1>(ym, ld_y, toks_s, nt, pages, pb, h, h_out, e.rank, e.scale, t_s);
-    } else if (nt == 2) {
-      shrink_unit<TI, 2>(xm, ld_x, toks_s, nt, pages, pa, h, h_in, e.rank, t_s, red_s);
-      expand_unit<TI, TO, 2>(ym, ld_y, toks_s, nt, pages, pb, h, h_out, e.rank, e.scale, t_s);
-    } else if (nt <= 4) {
-      shrink_unit<TI, 4>(xm, ld_x, toks_s, nt, pages, pa, h, h_in, e.rank, t_s, red_s);
-      expand_unit<TI, TO, 4>(ym, ld_y, toks_s, nt, pages, pb, h, h_out, e.rank, e.scale, t_s);
-    } else {
-      shrink_unit<TI, 8>(xm, ld_x, toks_s, nt, pages, pa, h, h_in, e.rank, t_s, red_s);
-      expand_unit<TI, TO, 8>(ym, ld_y, toks_s, nt, pages, pb, h, h_out, e.rank, e.scale, t_s);
-    }
-  }
-}
+struct GemvArgs {
+  PoolView pv;
+  SegView sv;
+  int32_t module0;
+  int32_t units_word;   // meta word holding the unit count to process
+  int32_t h_in, h_out;
+  uint32_t magic;       // reciprocal of the page size
+  const void* x;
+  int64_t ld_x, msx;
+  float* t;
+  int64_t ld_t, mst;
+  void* y;
+  int64_t ld_y, msy;
+};
 
-// Shrink only: t rows written to global memory (t[tok][j], j < rank).
-// units_word selects the unit list: short segments only, or all segments.
-template <typename TI>
-__global__ __launch_bounds__(kGemvThreads) void k_shrink_gemv(PoolView pv, int32_t module0, SegView sv,
-                                                             int32_t units_word, const TI* __restrict__ x,
-                                                             int64_t ld_x, int64_t msx, float* __restrict__ t,
-                                                             int64_t ld_t, int64_t mst, int32_t h_in) {
-  __shared__ float t_s[kUnitTokens * kMaxRank];
-  __shared__ float red_s[4 * 64];
-  __shared__ int32_t toks_s[kUnitTokens];
+// MODE 0: fused BGMV (t kept in LDS); 1: shrink only (t to memory); 2: expand only.
+template <int MODE, typename TI, typename TO>
+__global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvArgs a) {
+  __shared__ UnitLds L;
+  __shared__ __attribute__((aligned(16))) TI xs[(MODE == 2) ? 8 : kUnitTokens * XSlice<TI>::kElems];
   const int m = blockIdx.y;
-  const int n_units = sv.meta[units_word];
-  const TI* xm = x + m * msx;
-  float* tm = t + m * mst;
-  const TI* pages = static_cast<const TI*>(pv.pages);
-  const int32_t h = static_cast<int32_t>(pv.page_elems);
-  for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
-    const int seg = sv.units[2 * u], pos = sv.units[2 * u + 1];
-    const int nt = min(kUnitTokens, sv.seg_start[seg + 1] - pos);
-    const int slot = sv.seg_slot[seg];
-    const SlotEntry e = pv.entries[slot * pv.n_modules + module0 + m];
+  const int n_units = a.sv.meta[a.units_word];
+  const TI* xm = static_cast<const TI*>(a.x) + m * a.msx;
+  float* tm = a.t + m * a.mst;
+  TO* ym = static_cast<TO*>(a.y) + m * a.msy;
+  const TI* pages = static_cast<const TI*>(a.pv.pages);
+  const int32_t h = static_cast<int32_t>(a.pv.page_elems);
+  const int ppr_a = a.h_in / h, ppr_b = a.h_out / h;
+  for (XcdIter it(n_units); it.valid(); it.next()) {
+    const int u = it.item;
+    const int seg = a.sv.units[2 * u], pos = a.sv.units[2 * u + 1];
+    const int nt = min(kUnitTokens, a.sv.seg_start[seg + 1] - pos);
+    const int slot = a.sv.seg_slot[seg];
+    const SlotEntry e = a.pv.entries[slot * a.pv.n_modules + a.module0 + m];
     if (e.rank <= 0) continue;
-    unit_prologue(sv, pos, nt, toks_s, t_s);
-    const int32_t* pa = pv.page_ids + e.a_off;
-    if (nt == 1) shrink_unit<TI, 1>(xm, ld_x, toks_s, nt, pages, pa, h, h_in, e.rank, t_s, red_s);
-    else if (nt == 2) shrink_unit<TI, 2>(xm, ld_x, toks_s, nt, pages, pa, h, h_in, e.rank, t_s, red_s);
-    else if (nt <= 4) shrink_unit<TI, 4>(xm, ld_x, toks_s, nt, pages, pa, h, h_in, e.rank, t_s, red_s);
-    else shrink_unit<TI, 8>(xm, ld_x, toks_s, nt, pages, pa, h, h_in, e.rank, t_s, red_s);
-    for (int i = threadIdx.x; i < nt * e.rank; i += kGemvThreads) {
-      const int tb = i / e.rank, j = i - tb * e.rank;
-      tm[static_cast<int64_t>(toks_s[tb]) * ld_t + j] = t_s[tb * kMaxRank + j];
+    const int n_a = (MODE == 2) ? 0 : e.rank * ppr_a;
+    const int n_b = (MODE == 1) ? 0 : e.rank * ppr_b;
+    unit_prologue(a.sv, a.pv, e, pos, nt, n_a, n_b, L);
+    if constexpr (MODE != 2) {
+      if (nt == 1) shrink_unit<TI, 1>(xm, a.ld_x, L, nt, pages, 0, h, a.magic, a.h_in, e.rank, xs);
+      else if (nt == 2) shrink_unit<TI, 2>(xm, a.ld_x, L, nt, pages, 0, h, a.magic, a.h_in, e.rank, xs);
+      else shrink_unit<TI, 4>(xm, a.ld_x, L, nt, pages, 0, h, a.magic, a.h_in, e.rank, xs);
     }
-  }
-}
-
-// Expand only: t rows read from global memory.
-template <typename TI, typename TO>
-__global__ __launch_bounds__(kGemvThreads) void k_expand_gemv(PoolView pv, int32_t module0, SegView sv,
-                                                             int32_t units_word, const float* __restrict__ t,
-                                                             int64_t ld_t, int64_t mst, TO* __restrict__ y,
-                                                             int64_t ld_y, int64_t msy, int32_t h_out) {
-  __shared__ float t_s[kUnitTokens * kMaxRank];
-  __shared__ int32_t toks_s[kUnitTokens];
-  const int m = blockIdx.y;
-  const int n_units = sv.meta[units_word];
-  const float* tm = t + m * mst;
-  TO* ym = y + m * msy;
-  const TI* pages = static_cast<const TI*>(pv.pages);
-  const int32_t h = static_cast<int32_t>(pv.page_elems);
-  for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
-    const int seg = sv.units[2 * u], pos = sv.units[2 * u + 1];
-    const int nt = min(kUnitTokens, sv.seg_start[seg + 1] - pos);
-    const int slot = sv.seg_slot[seg];
-    const SlotEntry e = pv.entries[slot * pv.n_modules + module0 + m];
-    if (e.rank <= 0) continue;
-    unit_prologue(sv, pos, nt, toks_s, t_s);
-    for (int i = threadIdx.x; i < nt * e.rank; i += kGemvThreads) {
-      const int tb = i / e.rank, j = i - tb * e.rank;
-      t_s[tb * kMaxRank + j] = tm[static_cast<int64_t>(toks_s[tb]) * ld_t + j];
+    if constexpr (MODE == 1) {
+      for (int i = threadIdx.x; i < nt * e.rank; i += kGemvThreads) {
+        const int tb = i / e.rank, j = i - tb * e.rank;
+        tm[static_cast<int64_t>(L.toks[tb]) * a.ld_t + j] = L.t[tb * kMaxRank + j];
+      }
     }
-    __syncthreads();
-    const int32_t* pb = pv.page_ids + e.b_off;
-    if (nt == 1) expand_unit<TI, TO, 1>(ym, ld_y, toks_s, nt, pages, pb, h, h_out, e.rank, e.scale, t_s);
-    else if (nt == 2) expand_unit<TI, TO, 2>(ym, ld_y, toks_s, nt, pages, pb, h, h_out, e.rank, e.scale, t_s);
-    else if (nt <= 4) expand_unit<TI, TO, 4>(ym, ld_y, toks_s, nt, pages, pb, h, h_out, e.rank, e.scale, t_s);
-    else expand_unit<TI, TO, 8>(ym, ld_y, toks_s, nt, pages, pb, h, h_out, e.rank, e.scale, t_s);
+    if constexpr (MODE == 2) {
+      for (int i = threadIdx.x; i < nt * e.rank; i += kGemvThreads) {
+        const int tb = i / e.rank, j = i - tb * e.rank;
+        L.t[tb * kMaxRank + j] = tm[static_cast<int64_t>(L.toks[tb]) * a.ld_t + j];
+      }
+      __syncthreads();
+    }
+    if constexpr (MODE != 1) {
+      if (nt == 1) expand_unit<TI, TO, 1>(ym, a.ld_y, L, nt, pages, n_a, h, a.magic, a.h_out, e.rank, e.scale);
+      else if (nt == 2) expand_unit<TI, TO, 2>(ym, a.ld_y, L, nt, pages, n_a, h, a.magic, a.h_out, e.rank, e.scale);
+      else expand_unit<TI, TO, 4>(ym, a.ld_y, L, nt, pages, n_a, h, a.magic, a.h_out, e.rank, e.scale);
+    }
   }
 }
 

@@ -9,17 +9,17 @@
 //   token row) and a 32 x 16 slice of A^T (each lane 8 consecutive bf16 of one
 //   rank row), so both operands stream straight from row-major memory.  When
 //   several modules share x (q, k, v), one workgroup computes all of them from
-//   one read of the x slice.  K may be split across workgroups; the partial
-//   tiles then go to a workspace and the last workgroup to finish a tile adds
-//   them in split order (an atomic ticket decides who is last, the sum order
-//   does not depend on it: deterministic).
+//   one read of the x slice.  K may be split across workgroups to fill the
+//   chip; the partial tiles then go to a workspace and a second launch adds
+//   them in split order (deterministic; the launch boundary orders the writes
+//   and reads, so no device-wide fence is needed inside a kernel).
 // expand (fp32 t, bf16 B, y bf16 or fp32): Y[64 x 128] += s * T[64 x r] B[r x 128]
-//   with v_mfma_f32_32x32x2_f32, so t stays in fp32.  T, the B tile and the
-//   y tile are staged in LDS with 16-byte coalesced loads; the epilogue adds
-//   s*acc to y in fp32 and rounds once on the way out.
+//   with v_mfma_f32_32x32x2_f32, so t stays in fp32; formed transposed so that
+//   y moves between HBM and registers directly (see k_expand_mfma).
 #pragma once
 
 #include "common.hpp"
+#include "gemv_kernels.hpp"   // Quad<T>: four-element loads and stores
 
 namespace lora {
 
@@ -28,7 +28,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kMfmaThreads = 256;
 constexpr int kShrinkMaxModules = 4;   // modules sharing one x slice in a workgroup
-constexpr int kExpandCols = 128;       // output columns per expand workgroup
+constexpr int kExpandCols = 128;       // output columns per expand block
+#ifndef LORA_EXPAND_BLOCKS
+#define LORA_EXPAND_BLOCKS 4
+#endif
+constexpr int kExpandBlocks = LORA_EXPAND_BLOCKS;   // column blocks per expand workgroup
 
 __device__ __forceinline__ bf16x8 ld_bf16x8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
@@ -42,16 +46,32 @@ struct ShrinkArgs {
   int32_t module0;
   int32_t mods_per_wg;        // modules computed from one x slice
   int32_t h_in;
+  uint32_t magic;             // reciprocal of the page size
   int32_t ks_count;           // K splits (grid y)
   int32_t k_per_split;        // multiple of 32
-  int32_t ldr;                // rank columns of a partial tile (multiple of 16)
+  int32_t kc;                 // K staged in LDS at a time (multiple of 32, <= 32 * kShrinkSteps)
+  int32_t ldr;                // rank rows per module in LDS and columns of a partial tile (multiple of 16)
+  int32_t max_pids;           // page ids per entry in LDS
   float* part;                // [tiles][groups][mods_per_wg][ks_count][64][ldr]
-  int32_t* tickets;           // [tiles][groups], zero between calls
 };
 
+constexpr int kShrinkSteps = 16;   // 32-wide k steps of x prefetched per lane
+constexpr int kMaxSplits = 8;      // K splits of the shrink at most
+constexpr int kStageBatch = 8;     // 16-byte chunks of A each thread loads at once when staging
+
+// Shrink tile: 64 tokens x one K split, for mods_per_wg modules.  Per K
+// sub-chunk the adapter's A rows (all modules) are staged in LDS once and read
+// by the 4 waves; each wave first issues all its x loads for the sub-chunk
+// (up to kShrinkSteps 16-byte loads per lane), so the x stream overlaps the A
+// staging and the previous sub-chunk's MFMAs.
+template <int MODS, int NTILES>
 __global__ __launch_bounds__(kMfmaThreads) void k_shrink_mfma(ShrinkArgs a) {
+  static_assert(MODS >= 1 && MODS <= kShrinkMaxModules && NTILES >= 1 && NTILES <= 4, "tile shape");
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int ALD = a.kc + 8;                                   // A_s row stride (bf16)
+  __bf16* A_s = reinterpret_cast<__bf16*>(smem);              // [mods][ldr][ALD]
+  int32_t* pid_s = reinterpret_cast<int32_t*>(smem + static_cast<size_t>(MODS) * a.ldr * ALD * 2);
   __shared__ int32_t toks_s[kTileTokens];
-  __shared__ int last_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ks = blockIdx.y;
   const int grp = blockIdx.z;
@@ -62,57 +82,86 @@ __global__ __launch_bounds__(kMfmaThreads) void k_shrink_mfma(ShrinkArgs a) {
   const int k_begin = ks * a.k_per_split;
   const int k_end = min(a.h_in, k_begin + a.k_per_split);
   const int ppr = a.h_in / h;
-  const int kq = (lane >> 4) * 8;        // this lane's k offset inside a 32-wide slice
+  const int kq = (lane >> 4) * 8;        // this lane's k offset inside a 32-wide step
   const int mrow = wave * 16 + (lane & 15);
 
-  for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+  for (XcdIter it(n_tiles); it.valid(); it.next()) {
+    const int tile = it.item;
     const int seg = a.sv.tiles[2 * tile], pos = a.sv.tiles[2 * tile + 1];
     const int len = min(kTileTokens, a.sv.seg_start[seg + 1] - pos);
     const int slot = a.sv.seg_slot[seg];
+    SlotEntry e[MODS];
+#pragma unroll
+    for (int mi = 0; mi < MODS; ++mi) e[mi] = a.pv.entries[slot * a.pv.n_modules + a.module0 + grp * MODS + mi];
     __syncthreads();
     if (tid < kTileTokens) toks_s[tid] = tid < len ? a.sv.perm[pos + tid] : -1;
-    __syncthreads();
-
-    SlotEntry e[kShrinkMaxModules];
 #pragma unroll
-    for (int mi = 0; mi < kShrinkMaxModules; ++mi) {
-      e[mi] = SlotEntry{0, 0.f, 0, 0};
-      if (mi < a.mods_per_wg)
-        e[mi] = a.pv.entries[slot * a.pv.n_modules + a.module0 + grp * a.mods_per_wg + mi];
-    }
+    for (int mi = 0; mi < MODS; ++mi)
+      for (int i = tid; i < e[mi].rank * ppr; i += kMfmaThreads) pid_s[mi * a.max_pids + i] = a.pv.page_ids[e[mi].a_off + i];
+    __syncthreads();
     const int tok = toks_s[mrow];
     const __bf16* xrow = a.x + grp * a.msx + static_cast<int64_t>(tok < 0 ? 0 : tok) * a.ld_x + kq;
 
-    f32x4 acc[kShrinkMaxModules][4];
+    f32x4 acc[MODS][NTILES];
 #pragma unroll
-    for (int mi = 0; mi < kShrinkMaxModules; ++mi)
+    for (int mi = 0; mi < MODS; ++mi)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[mi][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < NTILES; ++nt) acc[mi][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int p = k_begin / h; p * h < k_end; ++p) {
-      const int kb = max(k_begin, p * h), ke = min(k_end, (p + 1) * h);
-      const __bf16* arow[kShrinkMaxModules][4];
+    for (int kc0 = k_begin; kc0 < k_end; kc0 += a.kc) {
+      const int kc1 = min(k_end, kc0 + a.kc);
+      const int nsteps = (kc1 - kc0) >> 5;
+      // 1) this thread's share of the sub-chunk's A rows [mods][ldr][kc1-kc0]
+      //    (at most kStageBatch 16-byte chunks: the host sizes kc for that).
+      //    Rows past a module's rank read its last row: they only feed output
+      //    columns past the rank, which are never stored.
+      const int cpr = (kc1 - kc0) >> 3;                       // 16-byte chunks per row
+      const int n_chunks = MODS * a.ldr * cpr;
+      u32x4 av[kStageBatch];
 #pragma unroll
-      for (int mi = 0; mi < kShrinkMaxModules; ++mi) {
+      for (int q = 0; q < kStageBatch; ++q) {
+        const int idx = min(tid + kMfmaThreads * q, n_chunks - 1);
+        const int row = idx / cpr, c = idx - row * cpr;
+        const int mi = row / a.ldr, j = row - mi * a.ldr;
+        int rank_mi = 0;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const int j = nt * 16 + (lane & 15);
-          arow[mi][nt] = nullptr;
-          if (mi < a.mods_per_wg && j < e[mi].rank)
-            arow[mi][nt] = pages + static_cast<int64_t>(a.pv.page_ids[e[mi].a_off + j * ppr + p]) * h -
-                           static_cast<int64_t>(p) * h + kq;
+        for (int m2 = 0; m2 < MODS; ++m2)
+          if (m2 == mi) rank_mi = e[m2].rank;
+        const int jj = max(0, min(j, rank_mi - 1));
+        const int k = kc0 + c * 8;
+        const int pg = ppr == 1 ? 0 : static_cast<int>(__umulhi(static_cast<uint32_t>(k), a.magic));
+        const int pid = rank_mi > 0 ? pid_s[mi * a.max_pids + jj * ppr + pg] : 0;
+        av[q] = *reinterpret_cast<const u32x4*>(pages + static_cast<int64_t>(pid) * h + (k - pg * h));
+      }
+      // 2) the x fragments of the sub-chunk, unconditional (no branch, so no
+      //    wait between them): steps past the sub-chunk repeat its last step and
+      //    rows without a token read row 0; an output row depends only on its
+      //    own x row, and those rows are never stored.
+      bf16x8 xf[kShrinkSteps];
+#pragma unroll
+      for (int i = 0; i < kShrinkSteps; ++i) xf[i] = ld_bf16x8(xrow + min(kc0 + 32 * i, kc1 - 32));
+      // 3) write A to LDS once the previous sub-chunk's reads are done
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < kStageBatch; ++q) {
+        const int idx = tid + kMfmaThreads * q;
+        if (idx < n_chunks) {
+          const int row = idx / cpr, c = idx - row * cpr;
+          *reinterpret_cast<u32x4*>(A_s + static_cast<size_t>(row) * ALD + c * 8) = av[q];
         }
       }
-      for (int k = kb; k < ke; k += 32) {
-        const bf16x8 xf = tok >= 0 ? ld_bf16x8(xrow + k) : bf16x8{};
+      __syncthreads();
 #pragma unroll
-        for (int mi = 0; mi < kShrinkMaxModules; ++mi) {
-          if (mi >= a.mods_per_wg) break;
+      for (int i = 0; i < kShrinkSteps; ++i) {
+        if (i >= nsteps) continue;             // fixed trip count: xf stays in registers
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) {
-            if (nt * 16 >= e[mi].rank) break;
-            const bf16x8 af = arow[mi][nt] ? ld_bf16x8(arow[mi][nt] + k) : bf16x8{};
-            acc[mi][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf, af, acc[mi][nt], 0, 0, 0);
+        for (int mi = 0; mi < MODS; ++mi) {
+#pragma unroll
+          for (int nt = 0; nt < NTILES; ++nt) {
+            if (nt * 16 >= e[mi].rank) continue;
+            const bf16x8 af = *reinterpret_cast<const bf16x8*>(
+                A_s + static_cast<size_t>(mi * a.ldr + nt * 16 + (lane & 15)) * ALD + 32 * i + kq);
+            acc[mi][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[i], af, acc[mi][nt], 0, 0, 0);
           }
         }
       }
@@ -122,13 +171,12 @@ __global__ __launch_bounds__(kMfmaThreads) void k_shrink_mfma(ShrinkArgs a) {
     const int rbase = wave * 16 + (lane >> 4) * 4;
     if (a.ks_count == 1) {
 #pragma unroll
-      for (int mi = 0; mi < kShrinkMaxModules; ++mi) {
-        if (mi >= a.mods_per_wg) break;
-        float* tm = a.t + (grp * a.mods_per_wg + mi) * a.mst;
+      for (int mi = 0; mi < MODS; ++mi) {
+        float* tm = a.t + (grp * MODS + mi) * a.mst;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
+        for (int nt = 0; nt < NTILES; ++nt) {
           const int j = nt * 16 + (lane & 15);
-          if (nt * 16 >= e[mi].rank) break;
+          if (nt * 16 >= e[mi].rank) continue;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int tk = toks_s[rbase + i];
@@ -139,78 +187,92 @@ __global__ __launch_bounds__(kMfmaThreads) void k_shrink_mfma(ShrinkArgs a) {
       continue;
     }
 
-    // split K: write this split's partial tile, take a ticket, the last one reduces
+    // split K: this split's partial tile goes to the workspace; k_shrink_reduce
+    // (the next launch on the stream) adds the splits in order
     const int64_t tile_block = static_cast<int64_t>(kTileTokens) * a.ldr;
-    const int64_t base_tg = (static_cast<int64_t>(tile) * groups + grp) * a.mods_per_wg;
+    const int64_t base_tg = (static_cast<int64_t>(tile) * groups + grp) * MODS;
 #pragma unroll
-    for (int mi = 0; mi < kShrinkMaxModules; ++mi) {
-      if (mi >= a.mods_per_wg) break;
+    for (int mi = 0; mi < MODS; ++mi) {
       float* pp = a.part + ((base_tg + mi) * a.ks_count + ks) * tile_block;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        if (nt * 16 >= e[mi].rank) break;
+      for (int nt = 0; nt < NTILES; ++nt) {
+        if (nt * 16 >= e[mi].rank) continue;
         const int j = nt * 16 + (lane & 15);
 #pragma unroll
         for (int i = 0; i < 4; ++i) pp[(rbase + i) * a.ldr + j] = acc[mi][nt][i];
       }
     }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      const int prev = atomicAdd(&a.tickets[static_cast<int64_t>(tile) * groups + grp], 1);
-      last_s = (prev == a.ks_count - 1);
-    }
-    __syncthreads();
-    if (!last_s) continue;
-    __threadfence();
-#pragma unroll
-    for (int mi = 0; mi < kShrinkMaxModules; ++mi) {
-      if (mi >= a.mods_per_wg) break;
-      const int rank = e[mi].rank;
-      float* tm = a.t + (grp * a.mods_per_wg + mi) * a.mst;
-      const float* pp = a.part + (base_tg + mi) * a.ks_count * tile_block;
-      for (int idx = tid; idx < kTileTokens * rank; idx += kMfmaThreads) {
-        const int r = idx / rank, j = idx - r * rank;
-        const int tk = toks_s[r];
-        if (tk < 0) continue;
-        float s = 0.f;
-        for (int q = 0; q < a.ks_count; ++q)
-          s += __hip_atomic_load(pp + q * tile_block + r * a.ldr + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        tm[static_cast<int64_t>(tk) * a.ld_t + j] = s;
-      }
-    }
-    if (tid == 0) a.tickets[static_cast<int64_t>(tile) * groups + grp] = 0;
   }
 }
 
+// Sum of the K splits of each tile, in split order: t[tok][j] = sum_q part[q].
+// One workgroup per (tile, module); grid (tiles, groups * mods_per_wg).
+__global__ __launch_bounds__(kMfmaThreads) void k_shrink_reduce(ShrinkArgs a) {
+  const int n_tiles = a.sv.meta[LORA_META_N_TILES];
+  const int gm = blockIdx.y;                        // group * mods_per_wg + module in group
+  const int64_t tile_block = static_cast<int64_t>(kTileTokens) * a.ldr;
+  for (XcdIter it(n_tiles); it.valid(); it.next()) {
+    const int tile = it.item;
+    const int seg = a.sv.tiles[2 * tile], pos = a.sv.tiles[2 * tile + 1];
+    const int len = min(kTileTokens, a.sv.seg_start[seg + 1] - pos);
+    const int slot = a.sv.seg_slot[seg];
+    const int rank = a.pv.entries[slot * a.pv.n_modules + a.module0 + gm].rank;
+    const float* pp = a.part + (static_cast<int64_t>(tile) * gridDim.y + gm) * a.ks_count * tile_block;
+    float* tm = a.t + gm * a.mst;
+    for (int idx = threadIdx.x; idx < len * rank; idx += kMfmaThreads) {
+      const int r = idx / rank, j = idx - r * rank;
+      float part[kMaxSplits];
+#pragma unroll
+      for (int q = 0; q < kMaxSplits; ++q)    // all splits' loads in flight together
+        part[q] = pp[min(q, a.ks_count - 1) * tile_block + r * a.ldr + j];
+      float sum = 0.f;
+#pragma unroll
+      for (int q = 0; q < kMaxSplits; ++q)
+        if (q < a.ks_count) sum += part[q];
+      tm[static_cast<int64_t>(a.sv.perm[pos + r]) * a.ld_t + j] = sum;
+    }
+  }
+}
+
+// Expand tile: 64 tokens x kExpandBlocks blocks of kExpandCols columns of one
+// module.  The product is formed transposed, Y^T[cols x tokens] += B^T[cols x r]
+// T^T[r x tokens] (v_mfma_f32_32x32x2_f32: lane l holds token l%32 and, for
+// i = 0..3, columns 8i + 4(l/32) .. +3 of its wave's 32).  y moves between HBM
+// and an LDS tile with coalesced 16-byte row accesses (a wave covers whole
+// rows), and between LDS and the MFMA layout with 8- or 16-byte accesses.
+// T (fp32) is staged once per tile, the B block (bf16) once per column block.
 template <typename TO>
 __global__ __launch_bounds__(kMfmaThreads) void k_expand_mfma(PoolView pv, int32_t module0, SegView sv,
                                                              const float* __restrict__ t, int64_t ld_t,
                                                              int64_t mst, TO* __restrict__ y, int64_t ld_y,
-                                                             int64_t msy, int32_t h_out) {
+                                                             int64_t msy, int32_t h_out, int32_t ldr) {
   constexpr int TN = kExpandCols;
-  constexpr int TLD = kMaxRank + 1;   // T_s row stride (floats)
-  constexpr int BLD = TN + 16;        // B_s row stride (bf16)
-  constexpr int YLD = TN + 4;         // Y_s row stride (floats)
-  constexpr int CPR = TN / 8;         // 16-byte chunks per B row / per bf16 y row
-  __shared__ float T_s[kTileTokens * TLD];
-  __shared__ __bf16 B_s[kMaxRank * BLD];
-  __shared__ float Y_s[kTileTokens * YLD];
+  constexpr int BLD = TN + 8;                         // B_s row stride (bf16)
+  constexpr int YLD = TN + 16 / sizeof(TO);           // Y_s row stride (elements)
+  constexpr int YCPR = TN * sizeof(TO) / 16;          // 16-byte chunks per y row of the block
+  constexpr int YCH = kTileTokens * YCPR / kMfmaThreads;   // y chunks per thread
+  constexpr int YV = 16 / sizeof(TO);                 // elements per 16-byte chunk
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int TLD = ldr + 1;                            // T_s row stride (floats)
+  float* T_s = reinterpret_cast<float*>(smem);                                              // [64][TLD]
+  size_t o = (static_cast<size_t>(kTileTokens) * TLD * 4 + 15) & ~static_cast<size_t>(15);
+  __bf16* B_s = reinterpret_cast<__bf16*>(smem + o);                                        // [ldr][BLD]
+  o += (static_cast<size_t>(ldr) * BLD * 2 + 15) & ~static_cast<size_t>(15);
+  TO* Y_s = reinterpret_cast<TO*>(smem + o);                                                // [64][YLD]
   __shared__ int32_t toks_s[kTileTokens];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = blockIdx.z;
-  const int c0 = blockIdx.y * TN;
   const int n_tiles = sv.meta[LORA_META_N_TILES];
   const int32_t h = static_cast<int32_t>(pv.page_elems);
   const __bf16* pages = static_cast<const __bf16*>(pv.pages);
   const float* tm = t + m * mst;
   TO* ym = y + m * msy;
   const int ppr = h_out / h;
-  const int p = c0 / h;              // the column tile lies inside page p of each row
-  const int off = c0 - p * h;
+  const int l32 = lane & 31, kh = lane >> 5;
 
-  for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+  for (XcdIter it(n_tiles); it.valid(); it.next()) {
+    const int tile = it.item;
     const int seg = sv.tiles[2 * tile], pos = sv.tiles[2 * tile + 1];
     const int len = min(kTileTokens, sv.seg_start[seg + 1] - pos);
     const int slot = sv.seg_slot[seg];
@@ -218,67 +280,110 @@ __global__ __launch_bounds__(kMfmaThreads) void k_expand_mfma(PoolView pv, int32
     if (e.rank <= 0) continue;
     const int rank = e.rank;
     const int r2 = (rank + 1) & ~1;
-    __syncthreads();
+    __syncthreads();   // the previous tile is done with LDS
     if (tid < kTileTokens) toks_s[tid] = tid < len ? sv.perm[pos + tid] : -1;
     __syncthreads();
-    // T tile [64][r2] (fp32), zero past rank and for rows without a token
-    for (int idx = tid; idx < kTileTokens * r2; idx += kMfmaThreads) {
-      const int r = idx / r2, j = idx - r * r2;
+    const int first = toks_s[0];
+    // T tile [64][r2] (fp32): thread -> row tid/4, columns (tid%4) + 4q; loads issued together
+    {
+      const int r = tid >> 2, jq = tid & 3;
       const int tk = toks_s[r];
-      T_s[r * TLD + j] = (tk >= 0 && j < rank) ? tm[static_cast<int64_t>(tk) * ld_t + j] : 0.f;
-    }
-    // B tile [r2][TN] (bf16), rank row j, columns c0..c0+TN of that row
-    for (int idx = tid; idx < r2 * CPR; idx += kMfmaThreads) {
-      const int j = idx / CPR, c = (idx - j * CPR) * 8;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (j < rank) {
-        const __bf16* src = pages + static_cast<int64_t>(pv.page_ids[e.b_off + j * ppr + p]) * h + off + c;
-        v = *reinterpret_cast<const u32x4*>(src);
-      }
-      *reinterpret_cast<u32x4*>(&B_s[j * BLD + c]) = v;
-    }
-    // y tile [64][TN] as fp32
-    for (int idx = tid; idx < kTileTokens * CPR; idx += kMfmaThreads) {
-      const int r = idx / CPR, c = (idx - r * CPR) * 8;
-      const int tk = toks_s[r];
-      if (tk >= 0) {
-        float f[8];
-        load8(ym + static_cast<int64_t>(tk) * ld_y + c0 + c, f);
-        *reinterpret_cast<f32x4*>(&Y_s[r * YLD + c]) = f32x4{f[0], f[1], f[2], f[3]};
-        *reinterpret_cast<f32x4*>(&Y_s[r * YLD + c + 4]) = f32x4{f[4], f[5], f[6], f[7]};
-      }
-    }
-    __syncthreads();
-
-    // wave w: columns 32w..32w+31, rows 0..31 (acc0) and 32..63 (acc1)
-    f32x16 acc0 = {}, acc1 = {};
-    const int col = wave * 32 + (lane & 31);
-    const int kh = lane >> 5;
-    for (int kk = 0; kk < r2; kk += 2) {
-      const int kr = kk + kh;
-      const float a0 = T_s[(lane & 31) * TLD + kr];
-      const float a1 = T_s[(32 + (lane & 31)) * TLD + kr];
-      const float b = static_cast<float>(B_s[kr * BLD + col]);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b, acc1, 0, 0, 0);
-    }
-    // D layout: lane l, register v -> row 8*(v/4) + 4*(l/32) + v%4, column l%32
-    const float s = e.scale;
+      const float* trow = tm + static_cast<int64_t>(tk >= 0 ? tk : first) * ld_t;
+      float tv[kMaxRank / 4];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = 8 * (v >> 2) + 4 * kh + (v & 3);
-      Y_s[row * YLD + col] = fmaf(s, acc0[v], Y_s[row * YLD + col]);
-      Y_s[(row + 32) * YLD + col] = fmaf(s, acc1[v], Y_s[(row + 32) * YLD + col]);
+      for (int q = 0; q < kMaxRank / 4; ++q) tv[q] = trow[min(jq + 4 * q, rank - 1)];
+#pragma unroll
+      for (int q = 0; q < kMaxRank / 4; ++q) {
+        const int j = jq + 4 * q;
+        if (j < r2) T_s[r * TLD + j] = (tk >= 0 && j < rank) ? tv[q] : 0.f;
+      }
     }
-    __syncthreads();
-    for (int idx = tid; idx < kTileTokens * CPR; idx += kMfmaThreads) {
-      const int r = idx / CPR, c = (idx - r * CPR) * 8;
-      const int tk = toks_s[r];
-      if (tk >= 0) {
-        const f32x4 lo = *reinterpret_cast<const f32x4*>(&Y_s[r * YLD + c]);
-        const f32x4 hi = *reinterpret_cast<const f32x4*>(&Y_s[r * YLD + c + 4]);
-        const float f[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        store8(ym + static_cast<int64_t>(tk) * ld_y + c0 + c, f);
+    for (int cb = 0; cb < kExpandBlocks; ++cb) {
+      const int c0 = (blockIdx.y * kExpandBlocks + cb) * TN;
+      if (c0 >= h_out) break;                  // uniform
+      const int p = c0 / h;                    // the column block lies inside page p of each row
+      const int off = c0 - p * h;
+      // y block [64][TN]: coalesced 16-byte chunks, rows without a token read the first token's
+      u32x4 yv[YCH];
+#pragma unroll
+      for (int q = 0; q < YCH; ++q) {
+        const int idx = tid + kMfmaThreads * q;
+        const int r = idx / YCPR, c = (idx % YCPR) * YV;
+        const int tk = toks_s[r];
+        yv[q] = *reinterpret_cast<const u32x4*>(ym + static_cast<int64_t>(tk >= 0 ? tk : first) * ld_y + c0 + c);
+      }
+      // B block [r2][TN] (bf16): rank row j, columns c0..c0+TN of that row
+      u32x4 bv[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int idx = min(tid + kMfmaThreads * q, r2 * (TN / 8) - 1);
+        const int j = idx / (TN / 8), c = (idx % (TN / 8)) * 8;
+        bv[q] = *reinterpret_cast<const u32x4*>(
+            pages + static_cast<int64_t>(pv.page_ids[e.b_off + min(j, rank - 1) * ppr + p]) * h + off + c);
+      }
+      __syncthreads();                         // the previous block's B_s / Y_s reads are done
+#pragma unroll
+      for (int q = 0; q < YCH; ++q) {
+        const int idx = tid + kMfmaThreads * q;
+        const int r = idx / YCPR, c = (idx % YCPR) * YV;
+        *reinterpret_cast<u32x4*>(Y_s + r * YLD + c) = yv[q];
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int idx = tid + kMfmaThreads * q;
+        if (idx < r2 * (TN / 8)) {
+          const int j = idx / (TN / 8), c = (idx % (TN / 8)) * 8;
+          *reinterpret_cast<u32x4*>(&B_s[j * BLD + c]) = (j < rank) ? bv[q] : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+      for (int base = 2 * kMfmaThreads; base < r2 * (TN / 8); base += kMfmaThreads) {   // ranks above 16
+        const int idx = base + tid;
+        if (idx < r2 * (TN / 8)) {
+          const int j = idx / (TN / 8), c = (idx % (TN / 8)) * 8;
+          u32x4 v = *reinterpret_cast<const u32x4*>(
+              pages + static_cast<int64_t>(pv.page_ids[e.b_off + min(j, rank - 1) * ppr + p]) * h + off + c);
+          *reinterpret_cast<u32x4*>(&B_s[j * BLD + c]) = (j < rank) ? v : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+      __syncthreads();
+
+      f32x16 acc0 = {}, acc1 = {};
+      for (int kk = 0; kk < r2; kk += 2) {
+        const int kr = kk + kh;
+        const float a = static_cast<float>(B_s[kr * BLD + wave * 32 + l32]);   // B^T[col][k]
+        const float b0 = T_s[l32 * TLD + kr];                                  // T^T[k][token]
+        const float b1 = T_s[(32 + l32) * TLD + kr];
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b0, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b1, acc1, 0, 0, 0);
+      }
+      // epilogue in LDS: lane l, register 4i+j: column 32w + 8i + 4(l/32) + j, token l%32 (+32)
+      const float s = e.scale;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int col = wave * 32 + 8 * i + 4 * kh;
+        float v[4];
+        Quad<TO> q0;
+        q0.load(Y_s + l32 * YLD + col);
+        q0.unpack(v);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = fmaf(s, acc0[4 * i + j], v[j]);
+        Quad<TO>::store(Y_s + l32 * YLD + col, v);
+        Quad<TO> q1;
+        q1.load(Y_s + (32 + l32) * YLD + col);
+        q1.unpack(v);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = fmaf(s, acc1[4 * i + j], v[j]);
+        Quad<TO>::store(Y_s + (32 + l32) * YLD + col, v);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < YCH; ++q) {
+        const int idx = tid + kMfmaThreads * q;
+        const int r = idx / YCPR, c = (idx % YCPR) * YV;
+        const int tk = toks_s[r];
+        if (tk >= 0)
+          *reinterpret_cast<u32x4*>(ym + static_cast<int64_t>(tk) * ld_y + c0 + c) =
+              *reinterpret_cast<const u32x4*>(Y_s + r * YLD + c);
       }
     }
   }

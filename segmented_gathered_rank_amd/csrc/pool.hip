@@ -107,7 +107,11 @@ lora_status lora_pool_create(lora_pool** out, int32_t device, lora_dtype wdtype,
     if (h_in[m] <= 0 || h_out[m] <= 0) return LORA_ERR_ARG;
     if (h_in[m] % page_elems != 0 || h_out[m] % page_elems != 0) return LORA_ERR_SHAPE;
     if (h_in[m] > (1 << 20) || h_out[m] > (1 << 20)) return LORA_ERR_SHAPE;
+    // kernels find a page by multiplying with the page size's reciprocal: exact while width * page < 2^32
+    if (h_in[m] * page_elems >= (int64_t(1) << 32) || h_out[m] * page_elems >= (int64_t(1) << 32))
+      return LORA_ERR_SHAPE;
     const int64_t ppe = static_cast<int64_t>(max_rank) * (h_in[m] + h_out[m]) / page_elems;
+    if (ppe > kMaxEntryPages) return LORA_ERR_SHAPE;
     if (ppe > max_ppe) max_ppe = ppe;
     if (h_in[m] > max_in) max_in = h_in[m];
     if (h_out[m] > max_out) max_out = h_out[m];

@@ -29,6 +29,7 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kLdsWords = 16384;   // 64 KiB: V histogram rows + one row of totals
+constexpr int kIdBatch = 16;       // ids each lane loads at once
 
 // Mask of the lanes whose (valid) id equals this lane's id.
 __device__ __forceinline__ uint64_t match_peers(int id, bool valid, int nbits) {
@@ -57,21 +58,30 @@ __global__ __launch_bounds__(kThreads) void k_build_segments(
   for (int i = tid; i < V * n_slots; i += kThreads) hist[i] = 0;
   __syncthreads();
 
-  // ---- count: wave w < V owns tokens [w*span, (w+1)*span)
+  // ---- count: wave w < V owns tokens [w*span, (w+1)*span); each lane loads
+  //      kIdBatch ids at once, then the wave matches them 64 at a time in order
   const int span = ((n_tokens + V - 1) / V + 63) / 64 * 64;
   const int beg = wave * span;
   const int end = min(n_tokens, beg + span);
   int bad = 0;
   if (wave < V) {
     int32_t* row = hist + wave * n_slots;
-    for (int base = beg; base < end; base += 64) {
-      const int i = base + lane;
-      const int id = i < end ? ids[i] : -1;
-      const bool valid = id >= 0 && id < n_slots;
-      if (i < end && (id < -1 || id >= n_slots)) ++bad;
-      const uint64_t peers = match_peers(id, valid, nbits);
-      if (valid && (__ffsll(static_cast<unsigned long long>(peers)) - 1) == lane)
-        row[id] += __popcll(peers);
+    for (int base = beg; base < end; base += 64 * kIdBatch) {
+      int idv[kIdBatch];
+#pragma unroll
+      for (int i = 0; i < kIdBatch; ++i) {
+        const int t = base + i * 64 + lane;
+        idv[i] = t < end ? ids[t] : -1;
+      }
+#pragma unroll
+      for (int i = 0; i < kIdBatch; ++i) {
+        const int t = base + i * 64 + lane;
+        const int id = idv[i];
+        const bool valid = id >= 0 && id < n_slots;
+        if (t < end && (id < -1 || id >= n_slots)) ++bad;
+        const uint64_t peers = match_peers(id, valid, nbits);
+        if (valid && (__ffsll(static_cast<unsigned long long>(peers)) - 1) == lane) row[id] += __popcll(peers);
+      }
     }
   }
   for (int m = 32; m >= 1; m >>= 1) bad += __shfl_xor(bad, m, 64);
@@ -152,40 +162,56 @@ __global__ __launch_bounds__(kThreads) void k_build_segments(
   }
   __syncthreads();
 
-  // ---- segments, work lists and cursors of this thread's slots
+  // ---- segments, work lists and cursors.  Slots are visited in order b of
+  //      each thread's block; a slot's work-list entries are written by all 64
+  //      lanes of its wave (its counters are broadcast from the owning lane).
   int off[5];
 #pragma unroll
   for (int q = 0; q < 5; ++q) off[q] = scan_w[wave][q] + v[q] - own[q];
   const int long_units_at = scan_tot[2];   // long-segment units follow all short ones
-  for (int s = s0; s < s1; ++s) {
-    const int run = total[s];
-    if (run == 0) continue;
-    const int base = off[0], si = off[1];
-    seg_slot[si] = s;
-    seg_start[si] = base;
-    const int nu = (run + kUnitTokens - 1) / kUnitTokens;
-    if (run >= kLongMin) {
-      for (int u = 0; u < nu; ++u) {
-        units[2 * (long_units_at + off[3] + u)] = si;
-        units[2 * (long_units_at + off[3] + u) + 1] = base + u * kUnitTokens;
+  for (int b = 0; b < bpt; ++b) {
+    const int s = s0 + b;
+    const int run = (s < s1) ? total[s] : 0;
+    for (int src = 0; src < 64; ++src) {
+      const int r = __shfl(run, src, 64);
+      if (r == 0) continue;                 // wave-uniform
+      const int sbase = __shfl(off[0], src, 64);
+      const int ssi = __shfl(off[1], src, 64);
+      const int nu = (r + kUnitTokens - 1) / kUnitTokens;
+      if (r >= kLongMin) {
+        const int u0 = long_units_at + __shfl(off[3], src, 64);
+        const int t0 = __shfl(off[4], src, 64);
+        for (int u = lane; u < nu; u += 64) {
+          units[2 * (u0 + u)] = ssi;
+          units[2 * (u0 + u) + 1] = sbase + u * kUnitTokens;
+        }
+        const int ntl = (r + kTileTokens - 1) / kTileTokens;
+        for (int u = lane; u < ntl; u += 64) {
+          tiles[2 * (t0 + u)] = ssi;
+          tiles[2 * (t0 + u) + 1] = sbase + u * kTileTokens;
+        }
+      } else {
+        const int u0 = __shfl(off[2], src, 64);
+        for (int u = lane; u < nu; u += 64) {
+          units[2 * (u0 + u)] = ssi;
+          units[2 * (u0 + u) + 1] = sbase + u * kUnitTokens;
+        }
       }
-      const int nt = (run + kTileTokens - 1) / kTileTokens;
-      for (int u = 0; u < nt; ++u) {
-        tiles[2 * (off[4] + u)] = si;
-        tiles[2 * (off[4] + u) + 1] = base + u * kTileTokens;
-      }
-      off[3] += nu;
-      off[4] += nt;
-    } else {
-      for (int u = 0; u < nu; ++u) {
-        units[2 * (off[2] + u)] = si;
-        units[2 * (off[2] + u) + 1] = base + u * kUnitTokens;
-      }
-      off[2] += nu;
     }
-    for (int w = 0; w < V; ++w) hist[w * n_slots + s] += base;
-    off[0] += run;
-    off[1] += 1;
+    if (run > 0) {
+      seg_slot[off[1]] = s;
+      seg_start[off[1]] = off[0];
+      for (int w = 0; w < V; ++w) hist[w * n_slots + s] += off[0];
+      const int nu = (run + kUnitTokens - 1) / kUnitTokens;
+      if (run >= kLongMin) {
+        off[3] += nu;
+        off[4] += (run + kTileTokens - 1) / kTileTokens;
+      } else {
+        off[2] += nu;
+      }
+      off[0] += run;
+      off[1] += 1;
+    }
   }
   __syncthreads();
 
@@ -193,16 +219,22 @@ __global__ __launch_bounds__(kThreads) void k_build_segments(
   if (wave < V) {
     int32_t* row = hist + wave * n_slots;
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int base = beg; base < end; base += 64) {
-      const int i = base + lane;
-      const int id = i < end ? ids[i] : -1;
-      const bool valid = id >= 0 && id < n_slots;
-      const uint64_t peers = match_peers(id, valid, nbits);
-      int pos = 0;
-      if (valid) pos = row[id] + __popcll(peers & lt);
-      if (valid) perm[pos] = i;
-      if (valid && (__ffsll(static_cast<unsigned long long>(peers)) - 1) == lane)
-        row[id] += __popcll(peers);
+    for (int base = beg; base < end; base += 64 * kIdBatch) {
+      int idv[kIdBatch];
+#pragma unroll
+      for (int i = 0; i < kIdBatch; ++i) {
+        const int t = base + i * 64 + lane;
+        idv[i] = t < end ? ids[t] : -1;
+      }
+#pragma unroll
+      for (int i = 0; i < kIdBatch; ++i) {
+        const int t = base + i * 64 + lane;
+        const int id = idv[i];
+        const bool valid = id >= 0 && id < n_slots;
+        const uint64_t peers = match_peers(id, valid, nbits);
+        if (valid) perm[row[id] + __popcll(peers & lt)] = t;
+        if (valid && (__ffsll(static_cast<unsigned long long>(peers)) - 1) == lane) row[id] += __popcll(peers);
+      }
     }
   }
 }

@@ -89,7 +89,7 @@ def test_segments_layout_and_bounds():
         st = sgr._lib.lora_segments_bind(fake, nb, n, s, ctypes.byref(seg))
         assert st == 0
         assert seg.max_segs == min(n, s)
-        assert seg.max_units == (n + 7) // 8 + min(n, s)
+        assert seg.max_units == (n + 3) // 4 + min(n, s)
         assert seg.max_tiles == (n + 63) // 64 + n // 64
         ptrs = [seg.perm, seg.seg_start, seg.seg_slot, seg.meta, seg.units, seg.tiles]
         assert all(p % 256 == 0 for p in ptrs) and ptrs == sorted(ptrs)
