@@ -39,7 +39,15 @@ def parse():
     ap.add_argument("--workload", default="bgmv_decode_x128",
                     choices=["bgmv_decode_x128", "bgmv_decode", "sgmv_prefill", "mixed_rank", "encoder_step"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--single-module", action="store_true",
+                    help="also time one-module calls of the decode batch (replayed from a captured graph)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="copy a buffer of this size once before timing (reference for HBM counters)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarize two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) instead of benchmarking")
+    ap.add_argument("--pmc-kernel", default="k_gemvILi0E", help="substring of the kernel to summarize")
+    ap.add_argument("--pmc-out", default=None, help="write the traffic summary JSON here")
     return ap.parse_args()
 
 
@@ -65,6 +73,68 @@ def make_workload(name):
         "modules": "qkv 768->2304, o 768->768, up 768->3072, down 3072->768"}
 
 
+KERNEL_SOURCES = ["common.hpp", "gemv_kernels.hpp", "mfma_kernels.hpp", "apply.hip", "segments.hip"]
+
+
+def kernel_source_sha():
+    """sha256 over the HIP sources of the apply kernels (identifies the kernel version)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "segmented_gathered_rank_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+
+
+def load_traffic(workload):
+    """Counter-measured HBM bytes per launch, if taken on the current kernel sources."""
+    try:
+        with open(traffic_file(workload)) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    return t.get("hbm_bytes_per_launch") if t.get("kernel_source_sha") == kernel_source_sha() else None
+
+
+def pmc_summary(args):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the target kernel, each scaled by what the
+    same counter reads for the calibration copy of known size in the same run."""
+    import csv
+    import glob
+
+    def rows(d):
+        out = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            out += list(csv.DictReader(open(f)))
+        return out
+
+    res = {}
+    for name, d in (("FETCH_SIZE", args.pmc_summary[0]), ("WRITE_SIZE", args.pmc_summary[1])):
+        rs = [r for r in rows(d) if r["Counter_Name"] == name]
+        copies = [float(r["Counter_Value"]) for r in rs if "copyBuffer" in r["Kernel_Name"]]
+        match = [r for r in rs if args.pmc_kernel in r["Kernel_Name"]]
+        big = max((int(r["Grid_Size"]) for r in match), default=0)     # the bench's own launch shape
+        target = [float(r["Counter_Value"]) for r in match if int(r["Grid_Size"]) == big]
+        if not copies or not target:
+            raise SystemExit(f"{name}: no copy or no target dispatch found in {d}")
+        ref_kib = args.calibrate_copy_mib * 1024.0
+        res[name] = {"kernel_kib_mean": sum(target) / len(target), "dispatches": len(target),
+                     "grid_size": big, "copy_kib": max(copies), "copy_expected_kib": ref_kib,
+                     "scale": ref_kib / max(copies)}
+    hbm = 1024.0 * (res["FETCH_SIZE"]["kernel_kib_mean"] * res["FETCH_SIZE"]["scale"] +
+                    res["WRITE_SIZE"]["kernel_kib_mean"] * res["WRITE_SIZE"]["scale"])
+    out = {"workload": args.workload, "kernel": args.pmc_kernel, "kernel_source_sha": kernel_source_sha(),
+           "hbm_bytes_per_launch": hbm, "counters": res}
+    if args.pmc_out:
+        with open(args.pmc_out, "w") as fh:
+            json.dump(out, fh, indent=1)
+    print(json.dumps(out))
+
+
 def cpu_baseline(wl, seconds):
     """The oracle, untouched, on one core: whole steps (all modules, all tokens) until `seconds`."""
     from threadpoolctl import threadpool_limits
@@ -85,6 +155,9 @@ def cpu_baseline(wl, seconds):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (see DESIGN.md, 'Sharding').",
               file=sys.stderr)
@@ -111,6 +184,12 @@ def main():
         if ev is not None:
             ev[1].record(stream)
 
+    if args.calibrate_copy_mib > 0:   # a plain device copy of known size, for the HBM counters
+        src = torch.empty(args.calibrate_copy_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -127,7 +206,7 @@ def main():
     extra = {"apply_ms_mean": kern_avg, "apply_ms_min": float(np.min(kern_ms)),
              "algorithmic_bytes_per_step": work["bytes"], "flops_per_step": work["flops"],
              "achieved_tflops": work["flops"] / (kern_avg * 1e-3) / 1e12}
-    if mode == "bgmv" and wl.n_modules > 1:
+    if mode == "bgmv" and wl.n_modules > 1 and args.single_module:
         # one-module calls (the decode batch as the config states it), replayed from a
         # captured graph so that host launch cost is not in the figure
         import segmented_gathered_rank_amd as sgr
@@ -155,7 +234,7 @@ def main():
     bound_bytes = work["bytes"]
     achieved = bound_bytes / (kern_avg * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(args.workload),
                 "kernel": "k_bgmv" if mode == "bgmv" else "shrink+expand",
                 "bytes_per_launch": bound_bytes}
     out = {

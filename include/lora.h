@@ -206,16 +206,19 @@ lora_status lora_segments_check(const lora_segments *seg, void *stream, int32_t 
  * element is rounded once, to nearest even, after y0 + term is formed in fp32.
  * Pointers and leading dimensions must keep every row 16-byte aligned. */
 
-/* Workspace bytes for the split-K reduction of lora_shrink's matrix-core
- * path.  0 is always accepted (no split); more gives more parallelism. */
+/* Workspace bytes that let lora_shrink split its matrix-core contraction over
+ * K as far as it ever does (partial tiles of the splits).  Any smaller size,
+ * including 0, is accepted and limits the split. */
 size_t lora_shrink_workspace_bytes(const lora_pool *p, int32_t n_tokens, int32_t n_modules);
 
 /* Shrink: t[i][j] = sum_k x_i[k] A_a[j][k] for j < rank_a, i with a valid id
  * ("shrink" of the study page's demo: the per-row product with the gathered
  * A).  t rows of tokens without an adapter, and columns past rank_a, are not
  * written.  Segments of >= LONG_MIN tokens run on bf16 matrix cores.
- * ws: device workspace, zero-filled before its first use and left zeroed
- * by every call; calls that share a workspace must not overlap.
+ * ws: optional device workspace (16-byte aligned, no initialization needed)
+ * for splitting the matrix-core contraction over K when there are too few
+ * tiles to fill the GPU; with ws_bytes == 0 no split is made.  Calls that
+ * share a workspace must be ordered on one stream.
  * Errors: ARG, SHAPE, DTYPE, HIP. */
 lora_status lora_shrink(const lora_pool *p, int32_t module0, int32_t n_modules,
                         const void *x, int64_t ld_x, int64_t module_stride_x,
