@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="bgmv_decode_x128",
                     choices=["bgmv_decode_x128", "bgmv_decode", "sgmv_prefill", "mixed_rank", "encoder_step"])
+    ap.add_argument("--path", choices=["auto", "bgmv", "sgmv"], default="auto",
+                    help="force the fused BGMV or the shrink+expand path (default: the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--single-module", action="store_true",
                     help="also time one-module calls of the decode batch (replayed from a captured graph)")
@@ -168,6 +170,9 @@ def main():
     from segmented_gathered_rank_amd.harness import DeviceWorkload
 
     wl, mode, config = make_workload(args.workload)
+    if args.path != "auto":
+        mode = args.path
+        config["path"] = mode
     dw = DeviceWorkload(wl, device=0)
     stream = torch.cuda.current_stream()
     work = accounting.step_work(wl, fused=(mode == "bgmv"))

@@ -45,7 +45,22 @@ struct SegView {
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming (non-temporal) 16-byte loads for data read once per launch; on
+// gfx950 they sustain a higher share of HBM bandwidth than plain loads.
+#ifndef LORA_NT_PAGES
+#define LORA_NT_PAGES 1
+#endif
+#ifndef LORA_NT_ROWS
+#define LORA_NT_ROWS 0
+#endif
+template <bool NT, typename V>
+__device__ __forceinline__ V ld16(const V* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
 
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
@@ -56,6 +71,9 @@ template <> struct Chunk<__bf16> {
   static constexpr int kElems = 8;
   u32x4 v;
   __device__ __forceinline__ void load(const __bf16* p) { v = *reinterpret_cast<const u32x4*>(p); }
+  __device__ __forceinline__ void load_nt(const __bf16* p) {
+    v = ld16<LORA_NT_PAGES != 0>(reinterpret_cast<const u32x4*>(p));
+  }
   __device__ __forceinline__ void zero() { v = u32x4{0u, 0u, 0u, 0u}; }
   __device__ __forceinline__ void unpack(float (&f)[8]) const {
     f[0] = bf16lo(v.x); f[1] = bf16hi(v.x); f[2] = bf16lo(v.y); f[3] = bf16hi(v.y);
@@ -66,6 +84,9 @@ template <> struct Chunk<float> {
   static constexpr int kElems = 4;
   f32x4 v;
   __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const f32x4*>(p); }
+  __device__ __forceinline__ void load_nt(const float* p) {
+    v = ld16<LORA_NT_PAGES != 0>(reinterpret_cast<const f32x4*>(p));
+  }
   __device__ __forceinline__ void zero() { v = f32x4{0.f, 0.f, 0.f, 0.f}; }
   __device__ __forceinline__ void unpack(float (&f)[4]) const { f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w; }
 };

@@ -35,10 +35,18 @@ namespace lora {
 #ifndef LORA_EXPAND_BATCH
 #define LORA_EXPAND_BATCH 16
 #endif
+#ifndef LORA_SHRINK_ROWS
+#define LORA_SHRINK_ROWS 2
+#endif
+#ifndef LORA_EXPAND_PASSES
+#define LORA_EXPAND_PASSES 1
+#endif
 constexpr int kGemvThreads = LORA_GEMV_THREADS;
 constexpr int kGemvWaves = kGemvThreads / 64;
 constexpr int kXSliceBytes = 32768;                 // LDS for the staged x rows of a unit
 constexpr int kShrinkBatch = LORA_SHRINK_BATCH;     // 16-byte chunks of a row in flight per lane
+constexpr int kShrinkRows = LORA_SHRINK_ROWS;       // rank rows a wave streams at once
+constexpr int kExpandPasses = LORA_EXPAND_PASSES;   // column groups a thread updates at once
 template <typename TI>
 constexpr int kExpandBatch = sizeof(TI) == 2 ? LORA_EXPAND_BATCH : 8;   // rank rows of B in flight per thread
 
@@ -61,6 +69,11 @@ template <> struct Quad<__bf16> {
     lo = v.x;
     hi = v.y;
   }
+  __device__ __forceinline__ void load_nt(const __bf16* p) {
+    const u32x2 v = ld16<LORA_NT_PAGES != 0>(reinterpret_cast<const u32x2*>(p));
+    lo = v.x;
+    hi = v.y;
+  }
   __device__ __forceinline__ void zero() { lo = hi = 0u; }
   __device__ __forceinline__ void unpack(float (&f)[4]) const {
     f[0] = bf16lo(lo); f[1] = bf16hi(lo); f[2] = bf16lo(hi); f[3] = bf16hi(hi);
@@ -74,6 +87,7 @@ template <> struct Quad<__bf16> {
 template <> struct Quad<float> {
   f32x4 v;
   __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const f32x4*>(p); }
+  __device__ __forceinline__ void load_nt(const float* p) { v = ld16<LORA_NT_PAGES != 0>(reinterpret_cast<const f32x4*>(p)); }
   __device__ __forceinline__ void zero() { v = f32x4{0.f, 0.f, 0.f, 0.f}; }
   __device__ __forceinline__ void unpack(float (&f)[4]) const { f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w; }
   static __device__ __forceinline__ void store(float* p, const float (&f)[4]) {
@@ -107,7 +121,9 @@ __device__ __forceinline__ void shrink_unit(const TI* __restrict__ x, int64_t ld
                                             int32_t h_in, int32_t rank, TI* xs) {
   constexpr int S = XSlice<TI>::kElems;
   constexpr int CE = 16 / sizeof(TI);  // elements per 16-byte chunk
-  constexpr int G = 64 / NT;           // lanes holding the same reduced value
+  constexpr int SR = kShrinkRows;      // rank rows a wave streams at once
+  constexpr int V = SR * NT;           // partial sums per lane
+  constexpr int G = 64 / V;            // lanes holding the same reduced value
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ppr = h_in / h;
   (void)magic;
@@ -116,11 +132,12 @@ __device__ __forceinline__ void shrink_unit(const TI* __restrict__ x, int64_t ld
     stage_x(x, ld_x, L.toks, nt, 0, h_in, xs);
     __syncthreads();
   }
-  for (int j0 = 0; j0 < rank; j0 += kGemvWaves) {
-    const int j = j0 + wave;             // this wave's row
+  // wave w streams rows j0 + w + kGemvWaves*q for q < SR
+  for (int j0 = 0; j0 < rank; j0 += kGemvWaves * SR) {
+    const int jw = j0 + wave;
     float acc[64];
 #pragma unroll
-    for (int i = 0; i < NT; ++i) acc[i] = 0.f;
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
     for (int sl = 0; sl < n_slices; ++sl) {
       const int k0 = sl * S;
       const int len = min(S, h_in - k0);
@@ -129,26 +146,30 @@ __device__ __forceinline__ void shrink_unit(const TI* __restrict__ x, int64_t ld
         stage_x(x, ld_x, L.toks, nt, k0, len, xs);
         __syncthreads();
       }
-      if (j >= rank) continue;           // wave-uniform
-      // pages of row j that overlap [k0, k0+len): each has one base address for the whole wave
+      if (jw >= rank) continue;          // wave-uniform
+      // pages of the rows that overlap [k0, k0+len): one base address per row for the whole wave
       for (int p = k0 / h; p * h < k0 + len; ++p) {
         const int kp0 = max(k0, p * h), kp1 = min(k0 + len, (p + 1) * h);
-        const int pid = __builtin_amdgcn_readfirstlane(L.pid[pid0 + j * ppr + p]);
-        const TI* base = pages + (static_cast<int64_t>(pid) - p) * h;   // base + k -> element k of row j
-        for (int kb = kp0; kb < kp1; kb += 64 * CE * kShrinkBatch) {
-          Chunk<TI> raw[kShrinkBatch];
+        const TI* base[SR];
 #pragma unroll
-          for (int i = 0; i < kShrinkBatch; ++i) {
-            const int k = kb + (lane + 64 * i) * CE;
-            if (k < kp1) raw[i].load(base + static_cast<uint32_t>(k));
-            else raw[i].zero();
-          }
+        for (int q = 0; q < SR; ++q) {
+          const int j = min(jw + kGemvWaves * q, rank - 1);   // rows past the rank repeat the last
+          const int pid = __builtin_amdgcn_readfirstlane(L.pid[pid0 + j * ppr + p]);
+          base[q] = pages + (static_cast<int64_t>(pid) - p) * h;
+        }
+        for (int kb = kp0; kb < kp1; kb += 64 * CE * kShrinkBatch) {
+          Chunk<TI> raw[SR][kShrinkBatch];
+#pragma unroll
+          for (int q = 0; q < SR; ++q)
+#pragma unroll
+            for (int i = 0; i < kShrinkBatch; ++i) {
+              const int k = kb + (lane + 64 * i) * CE;
+              raw[q][i].load_nt(base[q] + static_cast<uint32_t>(min(k, kp1 - CE)));
+            }
 #pragma unroll
           for (int i = 0; i < kShrinkBatch; ++i) {
             const int k = kb + (lane + 64 * i) * CE;
             if (k < kp1) {
-              float av[CE];
-              raw[i].unpack(av);
 #pragma unroll
               for (int tb = 0; tb < NT; ++tb) {
                 if (tb < nt) {
@@ -157,7 +178,12 @@ __device__ __forceinline__ void shrink_unit(const TI* __restrict__ x, int64_t ld
                   xc.load(xs + tb * S + (k - k0));
                   xc.unpack(xv);
 #pragma unroll
-                  for (int e = 0; e < CE; ++e) acc[tb] = fmaf(av[e], xv[e], acc[tb]);
+                  for (int q = 0; q < SR; ++q) {
+                    float av[CE];
+                    raw[q][i].unpack(av);
+#pragma unroll
+                    for (int e = 0; e < CE; ++e) acc[q * NT + tb] = fmaf(av[e], xv[e], acc[q * NT + tb]);
+                  }
                 }
               }
             }
@@ -166,10 +192,12 @@ __device__ __forceinline__ void shrink_unit(const TI* __restrict__ x, int64_t ld
         }
       }
     }
-    if (j < rank) {
-      const float r = wave_transpose_reduce<NT>(acc, lane);
-      const int tb = lane / G;
-      if ((lane % G) == 0 && tb < nt) L.t[tb * kMaxRank + j] = r;
+    if (jw < rank) {
+      const float r = wave_transpose_reduce<V>(acc, lane);
+      const int idx = lane / G;
+      const int q = idx / NT, tb = idx - q * NT;
+      const int j = jw + kGemvWaves * q;
+      if ((lane % G) == 0 && j < rank && tb < nt) L.t[tb * kMaxRank + j] = r;
     }
   }
   __syncthreads();
@@ -179,6 +207,8 @@ template <typename TI, typename TO, int NT>
 __device__ __forceinline__ void expand_unit(TO* __restrict__ y, int64_t ld_y, const UnitLds& L, int nt,
                                             const TI* __restrict__ pages, int pid0, int32_t h, uint32_t magic,
                                             int32_t h_out, int32_t rank, float scale) {
+  constexpr int EP = kExpandPasses;    // column groups (of 4 columns) a thread updates at once
+  constexpr int EB = kExpandBatch<TI>; // rank rows of B in flight per group
   const int n_quads = h_out >> 2;
   const int ppr = h_out / h;
   int64_t yoff[NT];
@@ -187,63 +217,72 @@ __device__ __forceinline__ void expand_unit(TO* __restrict__ y, int64_t ld_y, co
 
   // A wave covers 256 consecutive columns; when the page size is a multiple
   // of 256 they lie in one page, so each rank row has one base address for
-  // the wave (scalar registers) and every load needs one 32-bit lane offset.
+  // the wave and every load needs one 32-bit lane offset.
   const bool wave_page = (h % 256) == 0;
-  for (int c = threadIdx.x; c < n_quads; c += kGemvThreads) {
-    const int k = c << 2;
-    Quad<TO> yq[NT];
+  for (int c0 = threadIdx.x; c0 < n_quads; c0 += kGemvThreads * EP) {
+    int kq[EP], p[EP], off[EP];
 #pragma unroll
-    for (int tb = 0; tb < NT; ++tb) {
-      if (tb < nt) yq[tb].load(y + yoff[tb] + k);
+    for (int g = 0; g < EP; ++g) {
+      const int c = min(c0 + kGemvThreads * g, n_quads - 1);   // a thread past the end repeats the last group
+      kq[g] = c << 2;
+      p[g] = page_of(kq[g], magic, ppr);
+      if (wave_page) p[g] = __builtin_amdgcn_readfirstlane(p[g]);
+      off[g] = kq[g] - p[g] * h;
     }
-    float acc[NT][4];
+    Quad<TO> yq[EP][NT];
 #pragma unroll
-    for (int tb = 0; tb < NT; ++tb)
+    for (int g = 0; g < EP; ++g)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[tb][e] = 0.f;
-    int p, off;
-    if (wave_page) {
-      p = __builtin_amdgcn_readfirstlane(page_of(k, magic, ppr));
-      off = k - p * h;
-    } else {
-      p = page_of(k, magic, ppr);
-      off = k - p * h;
-    }
-    for (int j0 = 0; j0 < rank; j0 += kExpandBatch<TI>) {
-      Quad<TI> raw[kExpandBatch<TI>];
+      for (int tb = 0; tb < NT; ++tb) yq[g][tb].load(y + yoff[tb] + kq[g]);
+    float acc[EP][NT][4];
 #pragma unroll
-      for (int jj = 0; jj < kExpandBatch<TI>; ++jj) {
-        if (j0 + jj < rank) {
-          int pid = L.pid[pid0 + (j0 + jj) * ppr + p];
+    for (int g = 0; g < EP; ++g)
+#pragma unroll
+      for (int tb = 0; tb < NT; ++tb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[g][tb][e] = 0.f;
+    for (int j0 = 0; j0 < rank; j0 += EB) {
+      Quad<TI> raw[EP][EB];
+#pragma unroll
+      for (int jj = 0; jj < EB; ++jj) {
+        const int j = min(j0 + jj, rank - 1);    // rows past the rank repeat the last (their t is 0)
+#pragma unroll
+        for (int g = 0; g < EP; ++g) {
+          int pid = L.pid[pid0 + j * ppr + p[g]];
           if (wave_page) pid = __builtin_amdgcn_readfirstlane(pid);
-          raw[jj].load(pages + static_cast<int64_t>(pid) * h + static_cast<uint32_t>(off));
-        } else {
-          raw[jj].zero();
+          raw[g][jj].load_nt(pages + static_cast<int64_t>(pid) * h + static_cast<uint32_t>(off[g]));
         }
       }
 #pragma unroll
-      for (int jj = 0; jj < kExpandBatch<TI>; ++jj) {
-        float bv[4];
-        raw[jj].unpack(bv);
+      for (int jj = 0; jj < EB; ++jj) {
 #pragma unroll
         for (int tb = 0; tb < NT; ++tb) {
           // t is the same for the whole workgroup: keep it in a scalar register
           const float tv = __builtin_bit_cast(
               float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, L.t[tb * kMaxRank + j0 + jj])));
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[tb][e] = fmaf(tv, bv[e], acc[tb][e]);
+          for (int g = 0; g < EP; ++g) {
+            float bv[4];
+            raw[g][jj].unpack(bv);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[g][tb][e] = fmaf(tv, bv[e], acc[g][tb][e]);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
 #pragma unroll
-    for (int tb = 0; tb < NT; ++tb) {
-      if (tb < nt) {
-        float yv[4];
-        yq[tb].unpack(yv);
+    for (int g = 0; g < EP; ++g) {
+      if (c0 + kGemvThreads * g >= n_quads) continue;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) yv[e] = fmaf(scale, acc[tb][e], yv[e]);
-        Quad<TO>::store(y + yoff[tb] + k, yv);
+      for (int tb = 0; tb < NT; ++tb) {
+        if (tb < nt) {
+          float yv[4];
+          yq[g][tb].unpack(yv);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) yv[e] = fmaf(scale, acc[g][tb][e], yv[e]);
+          Quad<TO>::store(y + yoff[tb] + kq[g], yv);
+        }
       }
     }
   }

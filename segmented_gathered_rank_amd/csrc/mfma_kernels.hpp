@@ -35,6 +35,9 @@ constexpr int kExpandCols = 128;       // output columns per expand block
 constexpr int kExpandBlocks = LORA_EXPAND_BLOCKS;   // column blocks per expand workgroup
 
 __device__ __forceinline__ bf16x8 ld_bf16x8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ bf16x8 ld_bf16x8_nt(const __bf16* p) {
+  return ld16<LORA_NT_ROWS != 0>(reinterpret_cast<const bf16x8*>(p));
+}
 
 struct ShrinkArgs {
   PoolView pv;
@@ -139,7 +142,7 @@ __global__ __launch_bounds__(kMfmaThreads) void k_shrink_mfma(ShrinkArgs a) {
       //    own x row, and those rows are never stored.
       bf16x8 xf[kShrinkSteps];
 #pragma unroll
-      for (int i = 0; i < kShrinkSteps; ++i) xf[i] = ld_bf16x8(xrow + min(kc0 + 32 * i, kc1 - 32));
+      for (int i = 0; i < kShrinkSteps; ++i) xf[i] = ld_bf16x8_nt(xrow + min(kc0 + 32 * i, kc1 - 32));
       // 3) write A to LDS once the previous sub-chunk's reads are done
       __syncthreads();
 #pragma unroll
@@ -310,7 +313,8 @@ __global__ __launch_bounds__(kMfmaThreads) void k_expand_mfma(PoolView pv, int32
         const int idx = tid + kMfmaThreads * q;
         const int r = idx / YCPR, c = (idx % YCPR) * YV;
         const int tk = toks_s[r];
-        yv[q] = *reinterpret_cast<const u32x4*>(ym + static_cast<int64_t>(tk >= 0 ? tk : first) * ld_y + c0 + c);
+        yv[q] = ld16<LORA_NT_ROWS != 0>(
+            reinterpret_cast<const u32x4*>(ym + static_cast<int64_t>(tk >= 0 ? tk : first) * ld_y + c0 + c));
       }
       // B block [r2][TN] (bf16): rank row j, columns c0..c0+TN of that row
       u32x4 bv[2];
