@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 1
+#define LORA_ABI_VERSION 2
 
 typedef int32_t lora_status;
 enum {
@@ -171,7 +171,9 @@ typedef struct {
     int32_t *meta;       /* [LORA_META_WORDS]                                                      */
     int32_t *units;      /* [2 * max_units] (segment, position in perm) per GEMV work unit         */
     int32_t *tiles;      /* [2 * max_tiles] (segment, position in perm) per matrix-core tile       */
+    int32_t *work;       /* builder scratch of large batches (n_chunks > 0), else NULL             */
     int32_t n_tokens, n_slots, max_segs, max_units, max_tiles;
+    int32_t n_chunks;    /* 0: one-workgroup build; else the large-batch build's token chunks      */
 } lora_segments;
 
 /* Bytes of device memory lora_segments_bind needs for a batch. */

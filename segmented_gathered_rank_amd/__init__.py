@@ -59,8 +59,9 @@ class LoraError(RuntimeError):
 class lora_segments(ctypes.Structure):
     _fields_ = [("perm", ctypes.c_void_p), ("seg_start", ctypes.c_void_p), ("seg_slot", ctypes.c_void_p),
                 ("meta", ctypes.c_void_p), ("units", ctypes.c_void_p), ("tiles", ctypes.c_void_p),
+                ("work", ctypes.c_void_p),
                 ("n_tokens", ctypes.c_int32), ("n_slots", ctypes.c_int32), ("max_segs", ctypes.c_int32),
-                ("max_units", ctypes.c_int32), ("max_tiles", ctypes.c_int32)]
+                ("max_units", ctypes.c_int32), ("max_tiles", ctypes.c_int32), ("n_chunks", ctypes.c_int32)]
 
 
 class lora_pool_stats_t(ctypes.Structure):

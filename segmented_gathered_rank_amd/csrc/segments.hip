@@ -1,24 +1,33 @@
 // Segment builder: groups a batch's tokens by adapter slot on the GPU.
 //
-// The Fastino article describes the kernel as grouping "a batch's tokens by
-// adapter"; the study page's SGMV works on "contiguous segments of tokens
-// sharing an adapter".  This is a stable counting sort of token indices by
-// slot, done by one workgroup of 16 wave64s:
+// The Fastino article's batching kernel and the SGMV of the "Multi-LoRA
+// Serving - S-LoRA/Punica Batching" study page (section "The kernel trick:
+// gather, do not merge") both work on runs of tokens that use one adapter.
+// This file builds those runs: a stable counting sort of token indices by
+// slot, plus the offsets and work lists the apply kernels read.
 //
-//   count   each scanning wave owns a contiguous range of tokens and counts
-//           its ids into its own LDS histogram row.  Lanes holding the same
-//           id find each other with one ballot per id bit (a multi-split
-//           match), so one leader lane updates the row per distinct id.
-//   scan    per slot, an exclusive prefix over the waves' rows (in wave
-//           order) and the slot total; then a block scan over slots of five
-//           counters at once: tokens, segments, GEMV units of short and of
-//           long segments, and matrix-core tiles.  Non-empty slots write
-//           seg_slot/seg_start and their work-list entries.
-//   scatter each wave walks its range again in token order; a token's
-//           position is its wave's cursor for the slot plus its rank among
-//           earlier lanes with the same id.  Ranges are in token order and
-//           cursors in wave order, so the sort is stable.
+// Building blocks (per wave of 64 lanes, one 64-token batch at a time):
+//   match   lanes holding the same id find each other: one ballot when the
+//           batch holds a single id (prefill, encoder), else one ballot per
+//           id bit.  A token's rank among equal ids of its batch is the
+//           count of matching lanes below it.
+//   count   LDS atomics into a histogram row (one add for a single-id batch).
+//   rows    each scanning wave owns a contiguous range of tokens and counts
+//           into its own LDS histogram row; rows in wave order, ranges in
+//           token order and ranks in lane order make the sort stable.
+//   layout  per slot: total, then one block-wide scan of five counters
+//           (tokens, segments, GEMV units of short and of long segments,
+//           matrix-core tiles) in slot order gives every offset.
 //
+// Two schedules, chosen by the host from the tokens per histogram row:
+//   one workgroup   count rows -> layout -> scatter, one launch; the ids of a
+//                   wave's range stay in registers between count and scatter.
+//   chunked         k_seg_count (grid: per-chunk slot counts) -> k_seg_scan
+//                   (one workgroup: per-slot prefix over chunks into chunk
+//                   offsets, layout) ->
+//                   k_seg_scatter (grid: rows and scatter inside each chunk,
+//                   from the chunk's offsets).  Spreads the matching of large
+//                   batches over the whole chip.
 // All counts stay on the device: no host synchronization.
 #include "common.hpp"
 
@@ -28,181 +37,249 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kLdsWords = 16384;   // 64 KiB: V histogram rows + one row of totals
-constexpr int kIdBatch = 16;       // ids each lane loads at once
+constexpr int kLdsWords = 16384;      // 64 KiB: histogram rows (+ one row of totals)
+constexpr int kIdBatch = 16;          // 64-token batches a wave loads at once
+constexpr int kRound = 64 * kIdBatch; // tokens a wave loads at once
+constexpr int kChunkTokens = 1024;    // chunked schedule: tokens per workgroup (minimum)
+constexpr int kChunkWords = 1 << 19;  // chunked schedule: bound on chunks * n_slots
+constexpr int kMaxChunks = 256;       // chunked schedule: bound on chunks (the scan walks them per slot)
+#ifndef LORA_SEG_ONE_PER_ROW
+#define LORA_SEG_ONE_PER_ROW 512
+#endif
+// Batches of up to this many tokens per histogram row use one workgroup.
+constexpr int kOneGroupPerRow = LORA_SEG_ONE_PER_ROW;
 
-// Mask of the lanes whose (valid) id equals this lane's id.
-__device__ __forceinline__ uint64_t match_peers(int id, bool valid, int nbits) {
-  uint64_t peers = __ballot(valid);
+int rows_of(int n_slots) {
+  const int v = kLdsWords / n_slots - 1;
+  return v > kWaves ? kWaves : v;
+}
+
+// Chunked schedule: tokens per chunk (a multiple of 64) and number of chunks;
+// 0 chunks means the one-workgroup schedule.
+int chunk_tokens_of(int n, int n_slots) {
+  if (static_cast<int64_t>(n) <= static_cast<int64_t>(kOneGroupPerRow) * rows_of(n_slots)) return 0;
+  int gmax = kChunkWords / n_slots;
+  if (gmax > kMaxChunks) gmax = kMaxChunks;
+  if (gmax < 1) gmax = 1;
+  int c = (n + gmax - 1) / gmax;
+  if (c < kChunkTokens) c = kChunkTokens;
+  return (c + 63) / 64 * 64;
+}
+int chunks_of(int n, int n_slots) {
+  const int c = chunk_tokens_of(n, n_slots);
+  return c ? (n + c - 1) / c : 0;
+}
+size_t work_words_of(int n, int n_slots) {
+  const size_t g = static_cast<size_t>(chunks_of(n, n_slots));
+  return g ? 2 * g * n_slots + n_slots + g : 0;   // chunk counts, chunk offsets, slot bases, bad ids
+}
+
+// ------------------------------------------------------------ wave helpers
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ int dpp0(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, kCtrl, kRowMask, 0xf, false);
+}
+// Inclusive scan over the 64 lanes with DPP: row shifts by 1, 2, 4, 8 inside
+// each row of 16 lanes, then the row broadcasts of lane 15 and lane 31.
+// Lanes outside a shift's row read 0, the identity of both operations
+// (values are non-negative).
+template <bool kMax>
+__device__ __forceinline__ int wave_scan(int v) {
+  auto op = [](int a, int b) { return kMax ? (a > b ? a : b) : a + b; };
+  v = op(v, dpp0<0x111, 0xf>(v));
+  v = op(v, dpp0<0x112, 0xf>(v));
+  v = op(v, dpp0<0x114, 0xf>(v));
+  v = op(v, dpp0<0x118, 0xf>(v));
+  v = op(v, dpp0<0x142, 0xa>(v));
+  v = op(v, dpp0<0x143, 0xc>(v));
+  return v;
+}
+__device__ __forceinline__ int lane63(int v) { return __builtin_amdgcn_readlane(v, 63); }
+
+__device__ __forceinline__ int lowest_lane(uint64_t m) {
+  return __ffsll(static_cast<unsigned long long>(m)) - 1;
+}
+
+// Mask of the lanes whose (valid) id equals this lane's id; 0 for an invalid lane.
+__device__ __forceinline__ uint64_t peers_of(int id, bool valid, int nbits) {
+  const uint64_t vm = __ballot(valid);
+  const int first = __builtin_amdgcn_readfirstlane(id);
+  if (__ballot(valid && id == first) == vm) return valid ? vm : 0ull;   // one id in the batch
+  uint64_t peers = vm;
   for (int b = 0; b < nbits; ++b) {
     const bool bit = valid && ((id >> b) & 1);
     const uint64_t m = __ballot(bit);
     peers &= bit ? m : ~m;
   }
-  return peers;
+  return valid ? peers : 0ull;
 }
 
-__global__ __launch_bounds__(kThreads) void k_build_segments(
-    const int32_t* __restrict__ ids, int32_t n_tokens, int32_t n_slots, int32_t V, int32_t nbits,
-    int32_t* __restrict__ perm, int32_t* __restrict__ seg_start, int32_t* __restrict__ seg_slot,
-    int32_t* __restrict__ meta, int32_t* __restrict__ units, int32_t* __restrict__ tiles) {
-  extern __shared__ int32_t lds[];
-  int32_t* hist = lds;                      // [V][n_slots]: counts, then cursors
-  int32_t* total = lds + V * n_slots;       // [n_slots]
-  __shared__ int scan_w[kWaves][5];
-  __shared__ int scan_tot[5];
-  __shared__ int max_w[kWaves];
-  __shared__ int bad_w[kWaves];
+// Ids of tokens [base, base + kRound) clamped to end - 1 (base < end): every
+// load is unconditional so all are in flight at once; callers mask t >= end.
+__device__ __forceinline__ void load_ids(const int32_t* __restrict__ ids, int base, int end, int lane,
+                                         int (&idv)[kIdBatch]) {
+#pragma unroll
+  for (int i = 0; i < kIdBatch; ++i) idv[i] = ids[min(base + i * 64 + lane, end - 1)];
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < V * n_slots; i += kThreads) hist[i] = 0;
-  __syncthreads();
-
-  // ---- count: wave w < V owns tokens [w*span, (w+1)*span); each lane loads
-  //      kIdBatch ids at once, then the wave matches them 64 at a time in order
-  const int span = ((n_tokens + V - 1) / V + 63) / 64 * 64;
-  const int beg = wave * span;
-  const int end = min(n_tokens, beg + span);
+// Counts one round of tokens into the LDS histogram `row`: one add when the
+// batch holds a single id, else one LDS atomic per token (counting needs no
+// ranks).  Returns this lane's count of ids outside [-1, n_slots).
+__device__ __forceinline__ int count_round(const int (&idv)[kIdBatch], int base, int end, int lane,
+                                           int n_slots, int32_t* row) {
   int bad = 0;
-  if (wave < V) {
-    int32_t* row = hist + wave * n_slots;
-    for (int base = beg; base < end; base += 64 * kIdBatch) {
-      int idv[kIdBatch];
 #pragma unroll
-      for (int i = 0; i < kIdBatch; ++i) {
-        const int t = base + i * 64 + lane;
-        idv[i] = t < end ? ids[t] : -1;
-      }
-#pragma unroll
-      for (int i = 0; i < kIdBatch; ++i) {
-        const int t = base + i * 64 + lane;
-        const int id = idv[i];
-        const bool valid = id >= 0 && id < n_slots;
-        if (t < end && (id < -1 || id >= n_slots)) ++bad;
-        const uint64_t peers = match_peers(id, valid, nbits);
-        if (valid && (__ffsll(static_cast<unsigned long long>(peers)) - 1) == lane) row[id] += __popcll(peers);
-      }
+  for (int i = 0; i < kIdBatch; ++i) {
+    const int t = base + i * 64 + lane;
+    const int id = idv[i];
+    const bool in = t < end;
+    const bool valid = in && id >= 0 && id < n_slots;
+    bad += (in && (id < -1 || id >= n_slots)) ? 1 : 0;
+    const uint64_t vm = __ballot(valid);
+    const int first = __builtin_amdgcn_readfirstlane(id);
+    if (__ballot(valid && id == first) == vm) {
+      if (valid && lowest_lane(vm) == lane) atomicAdd(&row[id], __popcll(vm));
+    } else if (valid) {
+      atomicAdd(&row[id], 1);
     }
   }
-  for (int m = 32; m >= 1; m >>= 1) bad += __shfl_xor(bad, m, 64);
-  if (lane == 0) bad_w[wave] = bad;
-  __syncthreads();
+  return bad;
+}
 
-  // ---- scan: thread tid owns slots [s0, s1), consecutive, in slot order
-  const int bpt = (n_slots + kThreads - 1) / kThreads;
-  const int s0 = min(n_slots, tid * bpt);
-  const int s1 = min(n_slots, s0 + bpt);
+// Scatters one round: a token goes to its row's cursor for its slot plus its
+// rank among the equal ids below it in the batch.
+__device__ __forceinline__ void scatter_round(const int (&idv)[kIdBatch], int base, int end, int lane,
+                                              int n_slots, int nbits, int32_t* row, int32_t* __restrict__ perm) {
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int i = 0; i < kIdBatch; ++i) {
+    const int t = base + i * 64 + lane;
+    const int id = idv[i];
+    const bool valid = t < end && id >= 0 && id < n_slots;
+    const uint64_t peers = peers_of(id, valid, nbits);
+    if (valid) perm[row[id] + __popcll(peers & below)] = t;
+    if (valid && lowest_lane(peers) == lane) row[id] += __popcll(peers);
+  }
+}
+
+// Block sum of a per-thread count; `cell` is an LDS word zeroed before a
+// barrier that precedes this call.  Result valid after the next barrier.
+__device__ __forceinline__ void block_add(int v, int lane, int* cell) {
+  const int w = lane63(wave_scan<false>(v));
+  if (lane == 0 && w) atomicAdd(cell, w);
+}
+
+struct Out {
+  int32_t *perm, *seg_start, *seg_slot, *meta, *units, *tiles;
+};
+
+struct LayoutLds {
+  int wsum[kWaves][6];   // per wave: inclusive counter totals, max segment length
+  int woff[kWaves][5];   // per wave: exclusive offsets
+  int tot[5];
+};
+
+// Block-wide layout from the per-slot totals `total` (LDS).  Thread tid owns
+// slots [s0, s1) (consecutive, in slot order, the same partition the caller
+// used to fill `total`).  Writes meta, seg_start/seg_slot and both work lists
+// and calls base_of(s, first position in perm) for each slot that has tokens.
+template <class BaseFn>
+__device__ void layout_segments(const int32_t* total, int n_tokens, int n_slots, int s0, int s1, int bpt,
+                                int bad_total, const Out& o, LayoutLds& L, BaseFn base_of) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int own[5] = {0, 0, 0, 0, 0};   // tokens, segments, short units, long units, tiles
   int mx = 0;
   for (int s = s0; s < s1; ++s) {
-    int run = 0;
-    for (int w = 0; w < V; ++w) {
-      const int c = hist[w * n_slots + s];
-      hist[w * n_slots + s] = run;
-      run += c;
-    }
-    total[s] = run;
+    const int run = total[s];
     if (run > 0) {
+      const int nu = (run + kUnitTokens - 1) / kUnitTokens;
       own[0] += run;
       own[1] += 1;
       if (run >= kLongMin) {
-        own[3] += (run + kUnitTokens - 1) / kUnitTokens;
+        own[3] += nu;
         own[4] += (run + kTileTokens - 1) / kTileTokens;
       } else {
-        own[2] += (run + kUnitTokens - 1) / kUnitTokens;
+        own[2] += nu;
       }
       mx = max(mx, run);
     }
   }
-  int v[5];
+  int incl[5];
 #pragma unroll
-  for (int q = 0; q < 5; ++q) {
-    v[q] = own[q];
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(v[q], d, 64);
-      if (lane >= d) v[q] += o;
-    }
-  }
-  for (int m = 32; m >= 1; m >>= 1) mx = max(mx, __shfl_xor(mx, m, 64));
+  for (int q = 0; q < 5; ++q) incl[q] = wave_scan<false>(own[q]);
+  const int wmx = lane63(wave_scan<true>(mx));
   if (lane == 63) {
 #pragma unroll
-    for (int q = 0; q < 5; ++q) scan_w[wave][q] = v[q];
-    max_w[wave] = mx;
+    for (int q = 0; q < 5; ++q) L.wsum[wave][q] = incl[q];
+    L.wsum[wave][5] = wmx;
   }
   __syncthreads();
-  if (tid == 0) {
-    int acc[5] = {0, 0, 0, 0, 0};
-    int m = 0, b = 0;
-    for (int w = 0; w < kWaves; ++w) {
+  if (wave == 0) {
+    int tq[5];
 #pragma unroll
-      for (int q = 0; q < 5; ++q) {
-        const int t = scan_w[w][q];
-        scan_w[w][q] = acc[q];
-        acc[q] += t;
-      }
-      m = max(m, max_w[w]);
-      b += bad_w[w];
+    for (int q = 0; q < 5; ++q) {
+      const int v = lane < kWaves ? L.wsum[lane][q] : 0;
+      const int c = wave_scan<false>(v);
+      if (lane < kWaves) L.woff[lane][q] = c - v;
+      tq[q] = lane63(c);
     }
+    const int m = lane63(wave_scan<true>(lane < kWaves ? L.wsum[lane][5] : 0));
+    if (lane == 0) {
 #pragma unroll
-    for (int q = 0; q < 5; ++q) scan_tot[q] = acc[q];
-    meta[LORA_META_N_SEG] = acc[1];
-    meta[LORA_META_N_ACTIVE] = acc[0];
-    meta[LORA_META_MAX_SEG_LEN] = m;
-    meta[LORA_META_N_BAD] = b;
-    meta[LORA_META_N_UNITS_SHORT] = acc[2];
-    meta[LORA_META_N_UNITS_ALL] = acc[2] + acc[3];
-    meta[LORA_META_N_TILES] = acc[4];
-    meta[LORA_META_UNIT_TOKENS] = kUnitTokens;
-    meta[LORA_META_TILE_TOKENS] = kTileTokens;
-    meta[LORA_META_LONG_MIN] = kLongMin;
-    meta[LORA_META_N_TOKENS] = n_tokens;
-    meta[LORA_META_N_SLOTS] = n_slots;
-    for (int q = 12; q < LORA_META_WORDS; ++q) meta[q] = 0;
-    seg_start[acc[1]] = acc[0];
+      for (int q = 0; q < 5; ++q) L.tot[q] = tq[q];
+      int32_t* meta = o.meta;
+      meta[LORA_META_N_SEG] = tq[1];
+      meta[LORA_META_N_ACTIVE] = tq[0];
+      meta[LORA_META_MAX_SEG_LEN] = m;
+      meta[LORA_META_N_BAD] = bad_total;
+      meta[LORA_META_N_UNITS_SHORT] = tq[2];
+      meta[LORA_META_N_UNITS_ALL] = tq[2] + tq[3];
+      meta[LORA_META_N_TILES] = tq[4];
+      meta[LORA_META_UNIT_TOKENS] = kUnitTokens;
+      meta[LORA_META_TILE_TOKENS] = kTileTokens;
+      meta[LORA_META_LONG_MIN] = kLongMin;
+      meta[LORA_META_N_TOKENS] = n_tokens;
+      meta[LORA_META_N_SLOTS] = n_slots;
+      for (int q = 12; q < LORA_META_WORDS; ++q) meta[q] = 0;
+      o.seg_start[tq[1]] = tq[0];
+    }
   }
   __syncthreads();
 
-  // ---- segments, work lists and cursors.  Slots are visited in order b of
-  //      each thread's block; a slot's work-list entries are written by all 64
-  //      lanes of its wave (its counters are broadcast from the owning lane).
   int off[5];
 #pragma unroll
-  for (int q = 0; q < 5; ++q) off[q] = scan_w[wave][q] + v[q] - own[q];
-  const int long_units_at = scan_tot[2];   // long-segment units follow all short ones
+  for (int q = 0; q < 5; ++q) off[q] = L.woff[wave][q] + incl[q] - own[q];
+  const int long_at = L.tot[2];   // long-segment units follow all short ones
+  int2* units = reinterpret_cast<int2*>(o.units);
+  int2* tiles = reinterpret_cast<int2*>(o.tiles);
   for (int b = 0; b < bpt; ++b) {
     const int s = s0 + b;
     const int run = (s < s1) ? total[s] : 0;
-    for (int src = 0; src < 64; ++src) {
-      const int r = __shfl(run, src, 64);
-      if (r == 0) continue;                 // wave-uniform
-      const int sbase = __shfl(off[0], src, 64);
-      const int ssi = __shfl(off[1], src, 64);
-      const int nu = (r + kUnitTokens - 1) / kUnitTokens;
-      if (r >= kLongMin) {
-        const int u0 = long_units_at + __shfl(off[3], src, 64);
-        const int t0 = __shfl(off[4], src, 64);
-        for (int u = lane; u < nu; u += 64) {
-          units[2 * (u0 + u)] = ssi;
-          units[2 * (u0 + u) + 1] = sbase + u * kUnitTokens;
-        }
-        const int ntl = (r + kTileTokens - 1) / kTileTokens;
-        for (int u = lane; u < ntl; u += 64) {
-          tiles[2 * (t0 + u)] = ssi;
-          tiles[2 * (t0 + u) + 1] = sbase + u * kTileTokens;
-        }
-      } else {
-        const int u0 = __shfl(off[2], src, 64);
-        for (int u = lane; u < nu; u += 64) {
-          units[2 * (u0 + u)] = ssi;
-          units[2 * (u0 + u) + 1] = sbase + u * kUnitTokens;
-        }
+    const int nu = (run + kUnitTokens - 1) / kUnitTokens;
+    if (run > 0) {
+      o.seg_slot[off[1]] = s;
+      o.seg_start[off[1]] = off[0];
+      base_of(s, off[0]);
+      if (run < kLongMin) {   // at most kLongMin / kUnitTokens entries: written by this lane
+        for (int u = 0; u < nu; ++u) units[off[2] + u] = make_int2(off[1], off[0] + u * kUnitTokens);
       }
     }
+    // long segments: the whole wave writes each one's entries, lane by lane
+    uint64_t lm = __ballot(run >= kLongMin);
+    while (lm) {
+      const int src = lowest_lane(lm);
+      lm &= lm - 1;
+      const int r = __builtin_amdgcn_readlane(run, src);
+      const int ssi = __builtin_amdgcn_readlane(off[1], src);
+      const int sb = __builtin_amdgcn_readlane(off[0], src);
+      const int u0 = long_at + __builtin_amdgcn_readlane(off[3], src);
+      const int t0 = __builtin_amdgcn_readlane(off[4], src);
+      const int lnu = (r + kUnitTokens - 1) / kUnitTokens;
+      for (int u = lane; u < lnu; u += 64) units[u0 + u] = make_int2(ssi, sb + u * kUnitTokens);
+      const int ntl = (r + kTileTokens - 1) / kTileTokens;
+      for (int u = lane; u < ntl; u += 64) tiles[t0 + u] = make_int2(ssi, sb + u * kTileTokens);
+    }
     if (run > 0) {
-      seg_slot[off[1]] = s;
-      seg_start[off[1]] = off[0];
-      for (int w = 0; w < V; ++w) hist[w * n_slots + s] += off[0];
-      const int nu = (run + kUnitTokens - 1) / kUnitTokens;
       if (run >= kLongMin) {
         off[3] += nu;
         off[4] += (run + kTileTokens - 1) / kTileTokens;
@@ -213,40 +290,231 @@ __global__ __launch_bounds__(kThreads) void k_build_segments(
       off[1] += 1;
     }
   }
+}
+
+// Per-slot exclusive prefix over V rows plus `base`, written back into the rows.
+__device__ __forceinline__ void rows_to_cursors(int32_t* hist, int n_slots, int V, int s, int base) {
+  int c[kWaves];
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) c[w] = hist[min(w, V - 1) * n_slots + s];
+  int run = base;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    if (w < V) {
+      hist[w * n_slots + s] = run;
+      run += c[w];
+    }
+  }
+}
+__device__ __forceinline__ int rows_total(const int32_t* hist, int n_slots, int V, int s) {
+  int c[kWaves];
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) c[w] = hist[min(w, V - 1) * n_slots + s];
+  int run = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) run += (w < V) ? c[w] : 0;
+  return run;
+}
+
+// ------------------------------------------------------------ one workgroup
+__global__ __launch_bounds__(kThreads) void k_segments_one(const int32_t* __restrict__ ids, int32_t n_tokens,
+                                                           int32_t n_slots, int32_t V, int32_t nbits, Out o) {
+  extern __shared__ int32_t lds[];
+  int32_t* hist = lds;                  // [V][n_slots]: counts, then cursors
+  int32_t* total = lds + V * n_slots;   // [n_slots]
+  __shared__ LayoutLds L;
+  __shared__ int bad_cell;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < V * n_slots; i += kThreads) hist[i] = 0;
+  if (tid == 0) bad_cell = 0;
   __syncthreads();
 
-  // ---- scatter, stable: same ranges, same order as the count
-  if (wave < V) {
-    int32_t* row = hist + wave * n_slots;
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int base = beg; base < end; base += 64 * kIdBatch) {
-      int idv[kIdBatch];
+  // count: wave w < V owns tokens [w*span, (w+1)*span); waves >= V own none
+  const int span = ((n_tokens + V - 1) / V + 63) / 64 * 64;
+  const int beg = min(n_tokens, wave * span);
+  const int end = min(n_tokens, beg + span);
+  int32_t* row = hist + min(wave, V - 1) * n_slots;
+  int idv[kIdBatch];
+  int bad = 0;
+  for (int base = beg; base < end; base += kRound) {
+    load_ids(ids, base, end, lane, idv);
+    bad += count_round(idv, base, end, lane, n_slots, row);
+  }
+  block_add(bad, lane, &bad_cell);
+  const int bpt = (n_slots + kThreads - 1) / kThreads;
+  const int s0 = min(n_slots, tid * bpt);
+  const int s1 = min(n_slots, s0 + bpt);
+  __syncthreads();
+
+  for (int s = s0; s < s1; ++s) total[s] = rows_total(hist, n_slots, V, s);
+  layout_segments(total, n_tokens, n_slots, s0, s1, bpt, bad_cell, o, L,
+                  [&](int s, int base) { rows_to_cursors(hist, n_slots, V, s, base); });
+  __syncthreads();
+
+  // scatter: same ranges, same order as the count
+  const bool one_round = end - beg <= kRound;
+  for (int base = beg; base < end; base += kRound) {
+    if (!one_round) load_ids(ids, base, end, lane, idv);
+    scatter_round(idv, base, end, lane, n_slots, nbits, row, o.perm);
+  }
+}
+
+// ------------------------------------------------------------ chunked
+// Per-chunk slot counts: cnt[g][s] (global), bad ids per chunk: bad[g].
+__global__ __launch_bounds__(kThreads) void k_seg_count(const int32_t* __restrict__ ids, int32_t n_tokens,
+                                                        int32_t n_slots, int32_t chunk, int32_t* __restrict__ cnt,
+                                                        int32_t* __restrict__ bad_of) {
+  extern __shared__ int32_t lds[];   // [n_slots]
+  __shared__ int bad_cell;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = blockIdx.x;
+  const int cb = g * chunk, ce = min(n_tokens, cb + chunk);
+  for (int i = tid; i < n_slots; i += kThreads) lds[i] = 0;
+  if (tid == 0) bad_cell = 0;
+  __syncthreads();
+  int bad = 0;
+  int idv[kIdBatch];
+  for (int base = cb + wave * kRound; base < ce; base += kWaves * kRound) {
+    load_ids(ids, base, ce, lane, idv);
+    bad += count_round(idv, base, ce, lane, n_slots, lds);
+  }
+  block_add(bad, lane, &bad_cell);
+  __syncthreads();
+  int32_t* dst = cnt + static_cast<size_t>(g) * n_slots;
+  for (int s = tid; s < n_slots; s += kThreads) dst[s] = lds[s];
+  if (tid == 0) bad_of[g] = bad_cell;
+}
+
+// One workgroup: per slot, the exclusive prefix of the chunk counts
+// (coff[g][s] = chunk g's first position within slot s) and the slot total;
+// then the layout; slot_base[s] = first position of slot s in perm.  Thread
+// tid takes slots tid + k * kThreads (k < kBpt) and keeps 32 counter loads in
+// flight: the counters come from other XCDs' L2 slices, so each round trip is
+// long.
+template <int kBpt>
+__global__ __launch_bounds__(kThreads) void k_seg_scan(int32_t n_tokens, int32_t n_slots, int32_t n_chunks,
+                                                       const int32_t* __restrict__ cnt, int32_t* __restrict__ coff,
+                                                       const int32_t* __restrict__ bad_of,
+                                                       int32_t* __restrict__ slot_base, Out o) {
+  extern __shared__ int32_t total[];   // [n_slots]
+  __shared__ LayoutLds L;
+  __shared__ int bad_cell;
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid == 0) bad_cell = 0;
+  __syncthreads();
+  int bad = 0;
+  for (int g = tid; g < n_chunks; g += kThreads) bad += bad_of[g];
+  block_add(bad, lane, &bad_cell);
+  constexpr int kG = 32 / kBpt;
+  int sl[kBpt], run[kBpt];
 #pragma unroll
-      for (int i = 0; i < kIdBatch; ++i) {
-        const int t = base + i * 64 + lane;
-        idv[i] = t < end ? ids[t] : -1;
-      }
+  for (int k = 0; k < kBpt; ++k) {
+    sl[k] = min(tid + k * kThreads, n_slots - 1);
+    run[k] = 0;
+  }
+  for (int g0 = 0; g0 < n_chunks; g0 += kG) {
+    int c[kG][kBpt];
 #pragma unroll
-      for (int i = 0; i < kIdBatch; ++i) {
-        const int t = base + i * 64 + lane;
-        const int id = idv[i];
-        const bool valid = id >= 0 && id < n_slots;
-        const uint64_t peers = match_peers(id, valid, nbits);
-        if (valid) perm[row[id] + __popcll(peers & lt)] = t;
-        if (valid && (__ffsll(static_cast<unsigned long long>(peers)) - 1) == lane) row[id] += __popcll(peers);
+    for (int j = 0; j < kG; ++j) {
+      const int32_t* row = cnt + static_cast<size_t>(min(g0 + j, n_chunks - 1)) * n_slots;
+#pragma unroll
+      for (int k = 0; k < kBpt; ++k) c[j][k] = row[sl[k]];
+    }
+#pragma unroll
+    for (int j = 0; j < kG; ++j) {
+      if (g0 + j < n_chunks) {
+        int32_t* row = coff + static_cast<size_t>(g0 + j) * n_slots;
+#pragma unroll
+        for (int k = 0; k < kBpt; ++k) {
+          if (tid + k * kThreads < n_slots) row[tid + k * kThreads] = run[k];
+          run[k] += c[j][k];
+        }
       }
     }
+  }
+#pragma unroll
+  for (int k = 0; k < kBpt; ++k)
+    if (tid + k * kThreads < n_slots) total[tid + k * kThreads] = run[k];
+  __syncthreads();
+  const int bpt = (n_slots + kThreads - 1) / kThreads;
+  const int s0 = min(n_slots, tid * bpt);
+  const int s1 = min(n_slots, s0 + bpt);
+  layout_segments(total, n_tokens, n_slots, s0, s1, bpt, bad_cell, o, L,
+                  [&](int s, int base) { slot_base[s] = base; });
+}
+
+// Rows, cursors and scatter inside chunk g, starting from the chunk's offsets.
+template <int kBpt>
+__global__ __launch_bounds__(kThreads) void k_seg_scatter(const int32_t* __restrict__ ids, int32_t n_tokens,
+                                                          int32_t n_slots, int32_t V, int32_t nbits, int32_t chunk,
+                                                          const int32_t* __restrict__ cnt,
+                                                          const int32_t* __restrict__ coff,
+                                                          const int32_t* __restrict__ slot_base,
+                                                          int32_t* __restrict__ perm) {
+  extern __shared__ int32_t hist[];   // [V][n_slots]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = blockIdx.x;
+  const int cb = g * chunk, ce = min(n_tokens, cb + chunk);
+  for (int i = tid; i < V * n_slots; i += kThreads) hist[i] = 0;
+  __syncthreads();
+  const int span = ((ce - cb + V - 1) / V + 63) / 64 * 64;
+  const int beg = min(ce, cb + wave * span);
+  const int end = min(ce, beg + span);
+  int32_t* row = hist + min(wave, V - 1) * n_slots;
+  int idv[kIdBatch];
+  for (int base = beg; base < end; base += kRound) {
+    load_ids(ids, base, end, lane, idv);
+    count_round(idv, base, end, lane, n_slots, row);
+  }
+  // this chunk's count, offset and slot base of each slot, all loads at once
+  const size_t gr = static_cast<size_t>(g) * n_slots;
+  int cg[kBpt], base_of[kBpt];
+#pragma unroll
+  for (int k = 0; k < kBpt; ++k) {
+    const int s = min(tid + k * kThreads, n_slots - 1);
+    cg[k] = cnt[gr + s];
+    base_of[k] = slot_base[s] + coff[gr + s];   // slot_base is only written for slots with tokens
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kBpt; ++k) {
+    const int s = tid + k * kThreads;
+    if (s < n_slots && cg[k] > 0) rows_to_cursors(hist, n_slots, V, s, base_of[k]);
+  }
+  __syncthreads();
+  const bool one_round = end - beg <= kRound;
+  for (int base = beg; base < end; base += kRound) {
+    if (!one_round) load_ids(ids, base, end, lane, idv);
+    scatter_round(idv, base, end, lane, n_slots, nbits, row, perm);
   }
 }
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+template <class K>
+bool lds_limit(K* k) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             kLdsWords * 4) == hipSuccess;
+}
+bool set_lds_limit() {   // gfx950 allows 160 KiB of LDS per workgroup; these use up to 64 KiB + static
+  static const bool ok = lds_limit(&k_segments_one) && lds_limit(&k_seg_scatter<1>) &&
+                         lds_limit(&k_seg_scatter<2>) && lds_limit(&k_seg_scatter<4>) &&
+                         lds_limit(&k_seg_scatter<8>);
+  return ok;
+}
+
+// Slots per thread of the chunked kernels, rounded up to 1, 2, 4 or 8.
+int bpt_class(int n_slots) {
+  const int bpt = (n_slots + kThreads - 1) / kThreads;
+  return bpt <= 1 ? 1 : bpt <= 2 ? 2 : bpt <= 4 ? 4 : 8;
+}
 
 }  // namespace
 
 extern "C" {
 
 size_t lora_segments_bytes(int32_t n_tokens, int32_t n_slots) {
-  if (n_tokens < 0 || n_slots < 1) return 0;
+  if (n_tokens < 0 || n_slots < 1 || n_slots > kMaxSlots || n_tokens > (1 << 24)) return 0;
   const int32_t S = max_segs_of(n_tokens, n_slots);
   size_t b = 0;
   b += align256(static_cast<size_t>(n_tokens) * 4);                    // perm
@@ -255,6 +523,7 @@ size_t lora_segments_bytes(int32_t n_tokens, int32_t n_slots) {
   b += align256(LORA_META_WORDS * 4);                                  // meta
   b += align256(static_cast<size_t>(max_units_of(n_tokens, n_slots)) * 8);  // units
   b += align256(static_cast<size_t>(max_tiles_of(n_tokens)) * 8 + 8);  // tiles
+  b += align256(work_words_of(n_tokens, n_slots) * 4);                 // chunked schedule's counts
   return b;
 }
 
@@ -277,37 +546,59 @@ lora_status lora_segments_bind(void* buf, size_t bytes, int32_t n_tokens, int32_
   out->units = reinterpret_cast<int32_t*>(p);
   p += align256(static_cast<size_t>(max_units_of(n_tokens, n_slots)) * 8);
   out->tiles = reinterpret_cast<int32_t*>(p);
+  p += align256(static_cast<size_t>(max_tiles_of(n_tokens)) * 8 + 8);
+  out->work = work_words_of(n_tokens, n_slots) ? reinterpret_cast<int32_t*>(p) : nullptr;
   out->n_tokens = n_tokens;
   out->n_slots = n_slots;
   out->max_segs = S;
   out->max_units = max_units_of(n_tokens, n_slots);
   out->max_tiles = max_tiles_of(n_tokens);
+  out->n_chunks = chunks_of(n_tokens, n_slots);
   return LORA_OK;
 }
 
 lora_status lora_build_segments(const int32_t* ids, const lora_segments* seg, void* stream) {
   if (!seg) return LORA_ERR_ARG;
-  if (seg->n_tokens < 0 || seg->n_slots < 1 || seg->n_slots > kMaxSlots) return LORA_ERR_ARG;
+  if (seg->n_tokens < 0 || seg->n_tokens > (1 << 24) || seg->n_slots < 1 || seg->n_slots > kMaxSlots)
+    return LORA_ERR_ARG;
   if (seg->n_tokens == 0) return LORA_OK;
   if (!ids || !seg->perm || !seg->seg_start || !seg->seg_slot || !seg->meta || !seg->units || !seg->tiles)
     return LORA_ERR_ARG;
-  const int32_t n_slots = seg->n_slots;
-  int32_t V = kLdsWords / n_slots - 1;
-  if (V > kWaves) V = kWaves;
+  const int32_t n = seg->n_tokens, n_slots = seg->n_slots;
+  const int32_t G = chunks_of(n, n_slots);
+  if (seg->n_chunks != G || (G > 0 && !seg->work)) return LORA_ERR_ARG;   // not laid out by lora_segments_bind
+  const int32_t V = rows_of(n_slots);
   if (V < 1) return LORA_ERR_ARG;
   int32_t nbits = 0;
   while ((1 << nbits) < n_slots) ++nbits;
-  const size_t lds = static_cast<size_t>(V + 1) * n_slots * 4;
-  static bool lds_set = false;   // gfx950 allows 160 KiB of LDS per workgroup
-  if (!lds_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_build_segments),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsWords * 4) != hipSuccess)
-      return LORA_ERR_HIP;
-    lds_set = true;
+  if (!set_lds_limit()) return LORA_ERR_HIP;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const Out o{seg->perm, seg->seg_start, seg->seg_slot, seg->meta, seg->units, seg->tiles};
+  if (G == 0) {
+    const size_t lds = static_cast<size_t>(V + 1) * n_slots * 4;
+    hipLaunchKernelGGL(k_segments_one, dim3(1), dim3(kThreads), lds, st, ids, n, n_slots, V, nbits, o);
+  } else {
+    const int32_t chunk = chunk_tokens_of(n, n_slots);
+    int32_t* cnt = seg->work;
+    int32_t* coff = cnt + static_cast<size_t>(G) * n_slots;
+    int32_t* slot_base = coff + static_cast<size_t>(G) * n_slots;
+    int32_t* bad_of = slot_base + n_slots;
+    const size_t row_bytes = static_cast<size_t>(n_slots) * 4;
+    const size_t rows_bytes = static_cast<size_t>(V) * row_bytes;
+    hipLaunchKernelGGL(k_seg_count, dim3(G), dim3(kThreads), row_bytes, st, ids, n, n_slots, chunk, cnt, bad_of);
+#define LORA_SEG_CHUNKED(KB)                                                                                  \
+  hipLaunchKernelGGL(k_seg_scan<KB>, dim3(1), dim3(kThreads), row_bytes, st, n, n_slots, G, cnt, coff, bad_of,   \
+                     slot_base, o);                                                                           \
+  hipLaunchKernelGGL(k_seg_scatter<KB>, dim3(G), dim3(kThreads), rows_bytes, st, ids, n, n_slots, V, nbits,     \
+                     chunk, cnt, coff, slot_base, seg->perm)
+    switch (bpt_class(n_slots)) {
+      case 1: LORA_SEG_CHUNKED(1); break;
+      case 2: LORA_SEG_CHUNKED(2); break;
+      case 4: LORA_SEG_CHUNKED(4); break;
+      default: LORA_SEG_CHUNKED(8); break;
+    }
+#undef LORA_SEG_CHUNKED
   }
-  hipLaunchKernelGGL(k_build_segments, dim3(1), dim3(kThreads), lds, static_cast<hipStream_t>(stream), ids,
-                     seg->n_tokens, n_slots, V, nbits, seg->perm, seg->seg_start, seg->seg_slot, seg->meta,
-                     seg->units, seg->tiles);
   return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 

@@ -4,6 +4,8 @@ Integer and index work is compared bit for bit; floating point within the
 stated tolerances (rel-L2 <= 5e-3 and max-abs <= 2e-2 max|y| for bf16,
 rel-L2 <= 1e-5 for fp32), or bit for bit where the arithmetic is exact.
 """
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -22,10 +24,13 @@ from segmented_gathered_rank_amd.harness import DeviceWorkload, from_device  # n
 
 
 # ----------------------------------------------------------------- segments
-def _gpu_segments(ids, n_slots):
+def _gpu_segments(ids, n_slots, buf=None):
+    """Builds on the GPU into a buffer that starts out as garbage (0xA5 bytes),
+    so that any entry the builder fails to write shows up."""
     dev = torch.device("cuda", 0)
     n = len(ids)
-    buf = torch.zeros(max(sgr.lora_segments_bytes(n, n_slots), 256), dtype=torch.uint8, device=dev)
+    if buf is None:
+        buf = torch.full((max(sgr.lora_segments_bytes(n, n_slots), 256),), 0xA5, dtype=torch.uint8, device=dev)
     seg = sgr.lora_segments_bind(buf, n, n_slots)
     t_ids = torch.tensor(np.asarray(ids, np.int32), dtype=torch.int32, device=dev)
     sgr.lora_build_segments(t_ids, seg)
@@ -51,16 +56,20 @@ SEG_CASES = {
     "many_slots": (np.random.default_rng(9).integers(-1, 8192, 20000), 8192),
     "c5_ids": (np.repeat(W.zipf_ids(np.random.default_rng(5), 128, 1024, 1.2), 256), 1024),
     "long_runs": (np.random.default_rng(3).integers(-1, 6, 5000), 6),
+    # schedule boundaries of the builder: 512 tokens per histogram row on one
+    # workgroup (64 slots -> 16 rows -> 8192 tokens), chunks of >= 1024 above
+    "one_group_max": (np.random.default_rng(21).integers(-1, 64, 8192), 64),
+    "chunked_ragged": (np.random.default_rng(22).integers(-1, 64, 8193), 64),
+    "chunked_bad_ids": (np.random.default_rng(23).integers(-3, 110, 30001), 100),
+    "chunked_one_id": ([3] * 50000, 5),
+    "chunked_all_neg": ([-1] * 20000, 16),
+    "chunked_one_chunk": (np.random.default_rng(24).integers(-1, 8192, 600), 8192),
+    "chunked_runs": (np.repeat(np.random.default_rng(25).integers(0, 300, 1024), 128), 300),
 }
 
 
-@pytest.mark.parametrize("name", sorted(SEG_CASES))
-def test_segments_bit_exact(name):
-    ids, n_slots = SEG_CASES[name]
-    ids = np.asarray(ids, np.int32)
-    say(f"segments case {name}: n={len(ids)} n_slots={n_slots}")
+def _check_segments(ids, n_slots, st, meta, seg, arr):
     ref = lo.build_segments(ids, n_slots)
-    st, meta, seg, arr = _gpu_segments(ids, n_slots)
     assert st == (-8 if ref["n_bad"] else 0)
     n_seg = meta[sgr.META["n_seg"]]
     assert n_seg == ref["n_seg"]
@@ -87,10 +96,39 @@ def test_segments_bit_exact(name):
         if L >= lmin:
             exp_units += [(k, s0 + u) for u in range(0, L, ut)]
             exp_tiles += [(k, s0 + u) for u in range(0, L, tt)]
+    # the library's order: short-segment units, then long-segment units, each in segment order
     assert nus == len(short)
-    assert sorted(map(tuple, units.tolist())) == sorted(exp_units)
-    assert sorted(map(tuple, units[:nus].tolist())) == sorted(short)
-    assert sorted(map(tuple, tiles.tolist())) == sorted(exp_tiles)
+    assert list(map(tuple, units.tolist())) == exp_units
+    assert list(map(tuple, tiles.tolist())) == exp_tiles
+
+
+@pytest.mark.parametrize("name", sorted(SEG_CASES))
+def test_segments_bit_exact(name):
+    ids, n_slots = SEG_CASES[name]
+    ids = np.asarray(ids, np.int32)
+    say(f"segments case {name}: n={len(ids)} n_slots={n_slots} chunks={_chunks(len(ids), n_slots)}")
+    _check_segments(ids, n_slots, *_gpu_segments(ids, n_slots))
+
+
+def _chunks(n, n_slots):
+    """The builder's schedule for a batch: 0 = one workgroup, else its chunks
+    (lora_segments_bind does no device work, so a stand-in address serves)."""
+    seg = sgr.lora_segments()
+    assert sgr._lib.lora_segments_bind(256, 1 << 40, n, n_slots, ctypes.byref(seg)) == 0
+    return seg.n_chunks
+
+
+@pytest.mark.parametrize("n,n_slots", [(3000, 40), (40000, 40), (5000, 8192)])
+def test_segments_rebuild_same_buffer(n, n_slots):
+    """A second batch built into the same buffer (both schedules): nothing of
+    the first batch's layout or scratch leaks into the second."""
+    rng = np.random.default_rng(n + n_slots)
+    a = rng.integers(-1, n_slots, n).astype(np.int32)
+    b = np.sort(rng.integers(-1, n_slots // 2, n)).astype(np.int32)
+    say(f"segments rebuild n={n} n_slots={n_slots} chunks={_chunks(n, n_slots)}")
+    st, meta, seg, arr = _gpu_segments(a, n_slots)
+    _check_segments(a, n_slots, st, meta, seg, arr)
+    _check_segments(b, n_slots, *_gpu_segments(b, n_slots, buf=seg._buf))
 
 
 def test_segments_empty_batch_enqueues_nothing():

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     import segmented_gathered_rank_amd as sgr
-    assert sgr.lora_abi_version() == 1
+    assert sgr.lora_abi_version() == 2
     for code in sgr.STATUS:
         assert sgr.lora_status_str(code) and sgr.lora_status_str(code) != "unknown status"
 
@@ -94,8 +94,34 @@ def test_segments_layout_and_bounds():
         ptrs = [seg.perm, seg.seg_start, seg.seg_slot, seg.meta, seg.units, seg.tiles]
         assert all(p % 256 == 0 for p in ptrs) and ptrs == sorted(ptrs)
         assert seg.tiles + 8 * seg.max_tiles <= fake + nb
+        if seg.n_chunks:   # the large-batch schedule's scratch follows the tiles
+            assert seg.work % 256 == 0 and seg.work >= seg.tiles + 8 * seg.max_tiles
+            assert seg.work + 4 * (2 * seg.n_chunks * s + s + seg.n_chunks) <= fake + nb
+        else:
+            assert seg.work is None
         assert sgr._lib.lora_segments_bind(fake, nb - 1, n, s, ctypes.byref(seg)) == -9
         assert sgr._lib.lora_segments_bind(fake + 16, nb, n, s, ctypes.byref(seg)) == -1
+
+
+def _schedule(n, s):
+    import ctypes
+    import segmented_gathered_rank_amd as sgr
+    seg = sgr.lora_segments()
+    assert sgr._lib.lora_segments_bind(1 << 40, 1 << 40, n, s, ctypes.byref(seg)) == 0
+    return seg.n_chunks
+
+
+def test_segment_builder_schedule():
+    """One workgroup up to 512 tokens per LDS histogram row (rows = min(16,
+    16384 // n_slots - 1)), then chunks of >= 1024 tokens (a multiple of 64),
+    at most 256 of them and at most 2**19 chunk-slot counters."""
+    assert _schedule(8192, 64) == 0 and _schedule(8193, 64) == 9
+    assert _schedule(512, 8192) == 0 and _schedule(513, 8192) == 1 and _schedule(600, 8192) == 1
+    assert _schedule(7680, 1024) == 0 and _schedule(32768, 1024) == 32
+    assert _schedule(20000, 8192) == 20            # 1024-token chunks, under the 2**19 / 8192 = 64 cap
+    assert _schedule(1 << 20, 8192) == 64          # capped by the counters: chunks of 16384 tokens
+    assert _schedule(1 << 24, 1) == 256            # capped at 256 chunks of 65536 tokens
+    assert _schedule(131072, 300) == 128
 
 
 @pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
