@@ -27,7 +27,7 @@
  * rank * (h_in + h_out) / page_elems pages, allocated at the adapter's own
  * rank (no padding to the maximum rank).  Pages need not be contiguous.
  *
- * Adapter ids: -1 means "no adapter" (y untouched).  An id outside
+ * Adapter ids: -1 marks a token without an adapter (y untouched).  An id outside
  * [-1, n_slots) is treated as -1 and counted in the segment meta (word
  * LORA_META_N_BAD); lora_segments_check reports it as LORA_ERR_DEVICE_IDS.
  * A slot with no adapter loaded for a module adds nothing.
@@ -82,7 +82,7 @@ int32_t lora_abi_version(void);
 const char *lora_status_str(lora_status s);
 
 /* ------------------------------------------------------------------------ */
-/* Paged adapter store ("GPU slots": study page, "Memory: slots, tiers and  */
+/* Paged adapter store (GPU slots: study page, "Memory: slots, tiers and   */
 /* paging"; unified paging: "Thousands of adapters", slide 8)               */
 /* ------------------------------------------------------------------------ */
 typedef struct lora_pool lora_pool;   /* opaque, library-owned */
@@ -114,8 +114,8 @@ lora_status lora_pool_create(lora_pool **out, int32_t device, lora_dtype wdtype,
 lora_status lora_pool_destroy(lora_pool *p);
 
 /* Copies one adapter into freshly allocated pages and publishes the
- * (slot, module) entry: "copy a few MB into a GPU slot" (study page,
- * "Strategies compared").  A and B are [rank][h_in] and [rank][h_out] of the
+ * (slot, module) entry (the hot-swap strategy of the study page, section
+ * "Strategies compared": an adapter's weights are copied into a GPU slot).  A and B are [rank][h_in] and [rank][h_out] of the
  * pool's dtype, in host or device memory.  The upload runs on `stream` and
  * the call returns once it has completed, so A and B may be reused at once.
  * Kernels enqueued later on `stream` see the entry.
@@ -144,8 +144,8 @@ lora_status lora_pool_read(const lora_pool *p, int32_t slot, int32_t module,
 
 /* ------------------------------------------------------------------------ */
 /* Segments: tokens grouped by adapter                                      */
-/* ("groups a batch's tokens by adapter": Fastino article; "contiguous      */
-/* segments of tokens sharing an adapter": study page, "The kernel trick")  */
+/* (the Fastino article's kernel sorts a batch by adapter; the study page's */
+/* SGMV runs over runs of tokens with one adapter, "The kernel trick")      */
 /* ------------------------------------------------------------------------ */
 #define LORA_META_WORDS 16
 enum {
@@ -238,8 +238,9 @@ lora_status lora_expand(const lora_pool *p, int32_t module0, int32_t n_modules,
                         void *y, int64_t ld_y, int64_t module_stride_y, lora_dtype ydtype,
                         void *stream);
 
-/* Fused BGMV for decode ("batched gather matrix-vector, one adapter per
- * decode token": study page, "The kernel trick"): shrink and expand in one
+/* Fused BGMV for decode (study page, "The kernel trick": a batched gather
+ * matrix-vector product in which each decode token may bring its own
+ * adapter): shrink and expand in one
  * launch with t kept on chip; tokens that share an adapter share each read
  * of its pages.  Same result as lora_shrink followed by lora_expand.
  * Errors: ARG, SHAPE, DTYPE, HIP. */

@@ -1,8 +1,9 @@
 // GEMV (vector ALU) path: short segments and decode tokens.
 //
 // A work unit is up to kUnitTokens tokens of one segment, i.e. tokens that
-// share one adapter ("BGMV ... one adapter per decode token" and SGMV's
-// segments, study page "The kernel trick").  One 1024-thread workgroup (16
+// share one adapter (the study page's BGMV, where each decode token brings
+// its own adapter, and its SGMV segments; section "The kernel trick: gather,
+// do not merge").  One 1024-thread workgroup (16
 // wave64s) takes a unit and reads each gathered page of its adapter once for
 // all its tokens.  The work is laid out so that every lane issues all of its
 // loads for a phase back to back: a unit costs about three memory round trips

@@ -1,5 +1,6 @@
-// Matrix-core path for long segments (SGMV "for contiguous segments of tokens
-// sharing an adapter, as in prefill": study page, "The kernel trick").  A
+// Matrix-core path for long segments (the study page's SGMV, meant for runs
+// of tokens with one adapter such as a prefill; section "The kernel trick:
+// gather, do not merge").  A
 // segment of L >= kLongMin tokens is a dense grouped contraction, so it is cut
 // into tiles of kTileTokens tokens and run on CDNA4 MFMA.
 //

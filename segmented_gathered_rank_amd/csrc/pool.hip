@@ -1,6 +1,6 @@
 // Paged adapter store: pool creation, adapter upload into pages, eviction.
 //
-// "GPU slots" of the study page ("Memory: slots, tiers and paging") hold the
+// The study page's GPU slots (section "Memory: slots, tiers and paging") hold the
 // hot adapters; S-LoRA's unified paging ("Thousands of adapters", slide 8)
 // stores rank-R adapters in R pages of H elements.  Here a page holds
 // page_elems elements; each rank row of A and of B is cut into whole pages and
