@@ -23,6 +23,7 @@ SegView seg_view(const lora_segments* s) {
   v.meta = s->meta;
   v.units = s->units;
   v.tiles = s->tiles;
+  v.max_units = s->max_units;
   return v;
 }
 
@@ -68,6 +69,14 @@ unsigned grid_of(int32_t bound) {
   return static_cast<unsigned>((bound + 7) / 8 * 8);
 }
 
+// Grid of the GEMV kernels over `max_units` units: a multiple of 16, the
+// period of their unit-to-workgroup map, at most kMaxGrid.
+unsigned gemv_grid_of(int32_t max_units) {
+  if (max_units < 1) max_units = 1;
+  if (max_units > kMaxGrid) max_units = kMaxGrid;
+  return static_cast<unsigned>((max_units + 15) / 16 * 16);
+}
+
 GemvArgs gemv_args(const lora_pool* p, int32_t module0, const SegView& sv, int32_t units_word) {
   GemvArgs g{};
   g.pv = p->view();
@@ -106,7 +115,7 @@ lora_status launch_shrink(const lora_pool* p, int32_t module0, int32_t n_modules
   g.t = t;
   g.ld_t = ld_t;
   g.mst = mst;
-  hipLaunchKernelGGL((k_gemv<1, TI, TI>), dim3(grid_of(seg->max_units), n_modules), dim3(kGemvThreads), 0, s, g);
+  hipLaunchKernelGGL((k_gemv<1, TI, TI>), dim3(gemv_grid_of(seg->max_units), n_modules), dim3(kGemvThreads), 0, s, g);
   if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
   if constexpr (sizeof(TI) == 2) {
     if (use_mfma && seg->max_tiles > 0) {
@@ -192,7 +201,7 @@ lora_status launch_expand(const lora_pool* p, int32_t module0, int32_t n_modules
   g.y = y;
   g.ld_y = ld_y;
   g.msy = msy;
-  hipLaunchKernelGGL((k_gemv<2, TI, TO>), dim3(grid_of(seg->max_units), n_modules), dim3(kGemvThreads), 0, s, g);
+  hipLaunchKernelGGL((k_gemv<2, TI, TO>), dim3(gemv_grid_of(seg->max_units), n_modules), dim3(kGemvThreads), 0, s, g);
   if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
   if constexpr (sizeof(TI) == 2) {
     if (use_mfma && seg->max_tiles > 0) {
@@ -221,7 +230,7 @@ lora_status launch_bgmv(const lora_pool* p, int32_t module0, int32_t n_modules, 
   g.y = y;
   g.ld_y = ld_y;
   g.msy = msy;
-  hipLaunchKernelGGL((k_gemv<0, TI, TO>), dim3(grid_of(seg->max_units), n_modules), dim3(kGemvThreads), 0, s, g);
+  hipLaunchKernelGGL((k_gemv<0, TI, TO>), dim3(gemv_grid_of(seg->max_units), n_modules), dim3(kGemvThreads), 0, s, g);
   return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 

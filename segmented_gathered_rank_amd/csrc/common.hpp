@@ -33,6 +33,8 @@ struct PoolView {
   int64_t page_elems;
   int32_t n_slots;
   int32_t n_modules;
+  int32_t max_rank;           // rank cap of the pool
+  int32_t ppe;                // page-table words per (slot, module): A's ids, then B's from max_rank*ppr_a
 };
 
 struct SegView {
@@ -42,6 +44,7 @@ struct SegView {
   const int32_t* meta;
   const int32_t* units;
   const int32_t* tiles;
+  int32_t max_units;
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -174,9 +177,12 @@ __device__ __forceinline__ float wave_transpose_reduce(float (&v)[64], int lane)
 
 // Work distribution over the 8 XCDs.  Workgroups are dealt to the XCDs
 // round-robin (linear id mod 8) and each XCD has its own L2.  The n work items
-// (known only on the device) are cut into 8 contiguous shares, share x going to
-// the workgroups of XCD x, so consecutive items (the pieces of one segment,
-// which read the same adapter pages) meet in one L2 and every XCD gets work.
+// (known only on the device) are cut into 8 contiguous shares, so consecutive
+// items (the pieces of one segment, which read the same adapter pages) meet
+// in one L2.  Share s goes to XCD (s + plane) % 8, plane being the
+// workgroup's (y, z) index: when n is not a multiple of 8 the short last
+// share lands on a different XCD for each module or split, so the XCDs
+// stay evenly loaded over a launch.
 // Usage: for (XcdIter it(n); it.valid(); it.next()) { int u = it.item; ... }
 // gridDim.x must be a multiple of 8.
 struct XcdIter {
@@ -184,7 +190,8 @@ struct XcdIter {
   __device__ __forceinline__ explicit XcdIter(int n_items) {
     n = n_items;
     per = (n_items + 7) >> 3;
-    xcd = static_cast<int>(blockIdx.x & 7);
+    const int plane = static_cast<int>(blockIdx.y + gridDim.y * blockIdx.z);
+    xcd = static_cast<int>((blockIdx.x - plane) & 7);   // this workgroup's share
     idx = static_cast<int>(blockIdx.x >> 3);
     step = static_cast<int>(gridDim.x >> 3);
     item = xcd * per + idx;

@@ -3,20 +3,26 @@
 // A work unit is up to kUnitTokens tokens of one segment, i.e. tokens that
 // share one adapter (the study page's BGMV, where each decode token brings
 // its own adapter, and its SGMV segments; section "The kernel trick: gather,
-// do not merge").  One 1024-thread workgroup (16
-// wave64s) takes a unit and reads each gathered page of its adapter once for
-// all its tokens.  The work is laid out so that every lane issues all of its
-// loads for a phase back to back: a unit costs about three memory round trips
-// (token ids and page ids; x and A; B and y), which is what bounds a decode
-// step made of many small units.
+// do not merge").  One workgroup of kGemvThreads threads takes a unit and
+// reads each gathered page of its adapter once for all its tokens.  Every
+// lane issues all of its loads for a phase back to back, and a unit has few
+// dependent round trips, which is what bounds a decode step made of many
+// small units:
+//   (1) its work-list record (slot, first token, token count) together with
+//       the unit count;
+//   (2) the slot table entry, every page id the entry can use (the page
+//       table has a fixed layout per (slot, module), so no id waits for the
+//       entry) and the token indices;
+//   (3) the x rows, staged in LDS;
+//   then the A batches and the B batches, each a full load of the workgroup.
 //
 // shrink: t[tb][j] = sum_k x[tok_tb][k] * A[j][k].  The unit's x rows are
 //         staged in LDS (16-byte coalesced loads).  Wave w owns rank rows
-//         w, w+16, ...; a lane takes eight 16-byte chunks of the row (a wave
-//         reads 1 KiB of the row per instruction) and keeps NT partial sums,
-//         folded across the wave by DPP row operations (lane distance < 16)
-//         and ds_bpermute (16, 32): no LDS reduction, no float atomics, a
-//         fixed summation order.
+//         w, w+W, ... (W waves); a lane takes eight 16-byte chunks of the row
+//         (a wave reads 1 KiB of the row per instruction) and keeps NT
+//         partial sums, folded across the wave by DPP row operations (lane
+//         distance < 16) and ds_bpermute (16, 32): no LDS reduction, no float
+//         atomics, a fixed summation order.
 // expand: y[tok_tb][c] = round(y + scale * sum_j t[tb][j] * B[j][c]).  A
 //         thread owns 4 consecutive columns (8-byte loads of bf16, 16-byte of
 //         fp32), loads up to 16 rank rows of B and its y rows at once, and
@@ -39,15 +45,11 @@ namespace lora {
 #ifndef LORA_SHRINK_ROWS
 #define LORA_SHRINK_ROWS 2
 #endif
-#ifndef LORA_EXPAND_PASSES
-#define LORA_EXPAND_PASSES 1
-#endif
 constexpr int kGemvThreads = LORA_GEMV_THREADS;
 constexpr int kGemvWaves = kGemvThreads / 64;
 constexpr int kXSliceBytes = 32768;                 // LDS for the staged x rows of a unit
 constexpr int kShrinkBatch = LORA_SHRINK_BATCH;     // 16-byte chunks of a row in flight per lane
 constexpr int kShrinkRows = LORA_SHRINK_ROWS;       // rank rows a wave streams at once
-constexpr int kExpandPasses = LORA_EXPAND_PASSES;   // column groups a thread updates at once
 template <typename TI>
 constexpr int kExpandBatch = sizeof(TI) == 2 ? LORA_EXPAND_BATCH : 8;   // rank rows of B in flight per thread
 
@@ -129,6 +131,57 @@ __device__ __forceinline__ void shrink_unit(const TI* __restrict__ x, int64_t ld
   const int ppr = h_in / h;
   (void)magic;
   const int n_slices = (h_in + S - 1) / S;
+
+  // base address of rank rows jw + kGemvWaves*q (q < SR) in page p, one per wave
+  auto row_bases = [&](int jw, int p, const TI* (&base)[SR]) {
+#pragma unroll
+    for (int q = 0; q < SR; ++q) {
+      const int j = min(jw + kGemvWaves * q, rank - 1);   // rows past the rank repeat the last
+      const int pid = __builtin_amdgcn_readfirstlane(L.pid[pid0 + j * ppr + p]);
+      base[q] = pages + (static_cast<int64_t>(pid) - p) * h;
+    }
+  };
+  Chunk<TI> raw[SR][kShrinkBatch];
+  auto load_batch = [&](const TI* (&base)[SR], int kb, int kp1) {
+#pragma unroll
+    for (int q = 0; q < SR; ++q)
+#pragma unroll
+      for (int i = 0; i < kShrinkBatch; ++i) {
+        const int k = kb + (lane + 64 * i) * CE;
+        raw[q][i].load_nt(base[q] + static_cast<uint32_t>(min(k, kp1 - CE)));
+      }
+  };
+
+  // acc[q*NT + tb]: this lane's partial sums of rank row jw + kGemvWaves*q, token tb
+  float acc[64];
+#pragma unroll
+  for (int i = 0; i < V; ++i) acc[i] = 0.f;
+  auto compute_batch = [&](int kb, int kp1, int k0) {
+#pragma unroll
+    for (int i = 0; i < kShrinkBatch; ++i) {
+      const int k = kb + (lane + 64 * i) * CE;
+      if (k < kp1) {
+#pragma unroll
+        for (int tb = 0; tb < NT; ++tb) {
+          if (tb < nt) {
+            float xv[CE];
+            Chunk<TI> xc;
+            xc.load(xs + tb * S + (k - k0));
+            xc.unpack(xv);
+#pragma unroll
+            for (int q = 0; q < SR; ++q) {
+              float av[CE];
+              raw[q][i].unpack(av);
+#pragma unroll
+              for (int e = 0; e < CE; ++e) acc[q * NT + tb] = fmaf(av[e], xv[e], acc[q * NT + tb]);
+            }
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);   // keep the x reads of later chunks from piling up
+    }
+  };
+
   if (n_slices == 1) {
     stage_x(x, ld_x, L.toks, nt, 0, h_in, xs);
     __syncthreads();
@@ -136,9 +189,6 @@ __device__ __forceinline__ void shrink_unit(const TI* __restrict__ x, int64_t ld
   // wave w streams rows j0 + w + kGemvWaves*q for q < SR
   for (int j0 = 0; j0 < rank; j0 += kGemvWaves * SR) {
     const int jw = j0 + wave;
-    float acc[64];
-#pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] = 0.f;
     for (int sl = 0; sl < n_slices; ++sl) {
       const int k0 = sl * S;
       const int len = min(S, h_in - k0);
@@ -152,44 +202,10 @@ __device__ __forceinline__ void shrink_unit(const TI* __restrict__ x, int64_t ld
       for (int p = k0 / h; p * h < k0 + len; ++p) {
         const int kp0 = max(k0, p * h), kp1 = min(k0 + len, (p + 1) * h);
         const TI* base[SR];
-#pragma unroll
-        for (int q = 0; q < SR; ++q) {
-          const int j = min(jw + kGemvWaves * q, rank - 1);   // rows past the rank repeat the last
-          const int pid = __builtin_amdgcn_readfirstlane(L.pid[pid0 + j * ppr + p]);
-          base[q] = pages + (static_cast<int64_t>(pid) - p) * h;
-        }
+        row_bases(jw, p, base);
         for (int kb = kp0; kb < kp1; kb += 64 * CE * kShrinkBatch) {
-          Chunk<TI> raw[SR][kShrinkBatch];
-#pragma unroll
-          for (int q = 0; q < SR; ++q)
-#pragma unroll
-            for (int i = 0; i < kShrinkBatch; ++i) {
-              const int k = kb + (lane + 64 * i) * CE;
-              raw[q][i].load_nt(base[q] + static_cast<uint32_t>(min(k, kp1 - CE)));
-            }
-#pragma unroll
-          for (int i = 0; i < kShrinkBatch; ++i) {
-            const int k = kb + (lane + 64 * i) * CE;
-            if (k < kp1) {
-#pragma unroll
-              for (int tb = 0; tb < NT; ++tb) {
-                if (tb < nt) {
-                  float xv[CE];
-                  Chunk<TI> xc;
-                  xc.load(xs + tb * S + (k - k0));
-                  xc.unpack(xv);
-#pragma unroll
-                  for (int q = 0; q < SR; ++q) {
-                    float av[CE];
-                    raw[q][i].unpack(av);
-#pragma unroll
-                    for (int e = 0; e < CE; ++e) acc[q * NT + tb] = fmaf(av[e], xv[e], acc[q * NT + tb]);
-                  }
-                }
-              }
-            }
-            __builtin_amdgcn_sched_barrier(0);   // keep the x reads of later chunks from piling up
-          }
+          load_batch(base, kb, kp1);
+          compute_batch(kb, kp1, k0);
         }
       }
     }
@@ -200,6 +216,8 @@ __device__ __forceinline__ void shrink_unit(const TI* __restrict__ x, int64_t ld
       const int j = jw + kGemvWaves * q;
       if ((lane % G) == 0 && j < rank && tb < nt) L.t[tb * kMaxRank + j] = r;
     }
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
   }
   __syncthreads();
 }
@@ -208,8 +226,7 @@ template <typename TI, typename TO, int NT>
 __device__ __forceinline__ void expand_unit(TO* __restrict__ y, int64_t ld_y, const UnitLds& L, int nt,
                                             const TI* __restrict__ pages, int pid0, int32_t h, uint32_t magic,
                                             int32_t h_out, int32_t rank, float scale) {
-  constexpr int EP = kExpandPasses;    // column groups (of 4 columns) a thread updates at once
-  constexpr int EB = kExpandBatch<TI>; // rank rows of B in flight per group
+  constexpr int EB = kExpandBatch<TI>; // rank rows of B in flight
   const int n_quads = h_out >> 2;
   const int ppr = h_out / h;
   int64_t yoff[NT];
@@ -220,86 +237,82 @@ __device__ __forceinline__ void expand_unit(TO* __restrict__ y, int64_t ld_y, co
   // of 256 they lie in one page, so each rank row has one base address for
   // the wave and every load needs one 32-bit lane offset.
   const bool wave_page = (h % 256) == 0;
-  for (int c0 = threadIdx.x; c0 < n_quads; c0 += kGemvThreads * EP) {
-    int kq[EP], p[EP], off[EP];
+  for (int c0 = threadIdx.x; c0 < n_quads; c0 += kGemvThreads) {
+    const int kq = c0 << 2;
+    int p = page_of(kq, magic, ppr);
+    if (wave_page) p = __builtin_amdgcn_readfirstlane(p);
+    const int off = kq - p * h;
+    Quad<TO> yq[NT];
 #pragma unroll
-    for (int g = 0; g < EP; ++g) {
-      const int c = min(c0 + kGemvThreads * g, n_quads - 1);   // a thread past the end repeats the last group
-      kq[g] = c << 2;
-      p[g] = page_of(kq[g], magic, ppr);
-      if (wave_page) p[g] = __builtin_amdgcn_readfirstlane(p[g]);
-      off[g] = kq[g] - p[g] * h;
-    }
-    Quad<TO> yq[EP][NT];
+    for (int tb = 0; tb < NT; ++tb) yq[tb].load(y + yoff[tb] + kq);
+    float acc[NT][4];
 #pragma unroll
-    for (int g = 0; g < EP; ++g)
+    for (int tb = 0; tb < NT; ++tb)
 #pragma unroll
-      for (int tb = 0; tb < NT; ++tb) yq[g][tb].load(y + yoff[tb] + kq[g]);
-    float acc[EP][NT][4];
-#pragma unroll
-    for (int g = 0; g < EP; ++g)
-#pragma unroll
-      for (int tb = 0; tb < NT; ++tb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[g][tb][e] = 0.f;
+      for (int e = 0; e < 4; ++e) acc[tb][e] = 0.f;
     for (int j0 = 0; j0 < rank; j0 += EB) {
-      Quad<TI> raw[EP][EB];
+      Quad<TI> raw[EB];
 #pragma unroll
       for (int jj = 0; jj < EB; ++jj) {
         const int j = min(j0 + jj, rank - 1);    // rows past the rank repeat the last (their t is 0)
-#pragma unroll
-        for (int g = 0; g < EP; ++g) {
-          int pid = L.pid[pid0 + j * ppr + p[g]];
-          if (wave_page) pid = __builtin_amdgcn_readfirstlane(pid);
-          raw[g][jj].load_nt(pages + static_cast<int64_t>(pid) * h + static_cast<uint32_t>(off[g]));
-        }
+        int pid = L.pid[pid0 + j * ppr + p];
+        if (wave_page) pid = __builtin_amdgcn_readfirstlane(pid);
+        raw[jj].load_nt(pages + static_cast<int64_t>(pid) * h + static_cast<uint32_t>(off));
       }
 #pragma unroll
       for (int jj = 0; jj < EB; ++jj) {
+        float bv[4];
+        raw[jj].unpack(bv);
 #pragma unroll
         for (int tb = 0; tb < NT; ++tb) {
           // t is the same for the whole workgroup: keep it in a scalar register
           const float tv = __builtin_bit_cast(
               float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, L.t[tb * kMaxRank + j0 + jj])));
 #pragma unroll
-          for (int g = 0; g < EP; ++g) {
-            float bv[4];
-            raw[g][jj].unpack(bv);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[g][tb][e] = fmaf(tv, bv[e], acc[g][tb][e]);
-          }
+          for (int e = 0; e < 4; ++e) acc[tb][e] = fmaf(tv, bv[e], acc[tb][e]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
 #pragma unroll
-    for (int g = 0; g < EP; ++g) {
-      if (c0 + kGemvThreads * g >= n_quads) continue;
+    for (int tb = 0; tb < NT; ++tb) {
+      if (tb < nt) {
+        float yv[4];
+        yq[tb].unpack(yv);
 #pragma unroll
-      for (int tb = 0; tb < NT; ++tb) {
-        if (tb < nt) {
-          float yv[4];
-          yq[g][tb].unpack(yv);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) yv[e] = fmaf(scale, acc[g][tb][e], yv[e]);
-          Quad<TO>::store(y + yoff[tb] + kq[g], yv);
-        }
+        for (int e = 0; e < 4; ++e) yv[e] = fmaf(scale, acc[tb][e], yv[e]);
+        Quad<TO>::store(y + yoff[tb] + kq, yv);
       }
     }
   }
 }
 
-// Loads a unit's tokens and page ids (A rows from a_off, B rows from b_off)
-// into LDS and clears its t rows.  Ends with a barrier.
-__device__ __forceinline__ void unit_prologue(const SegView& sv, const PoolView& pv, const SlotEntry& e, int pos,
-                                              int nt, int n_a, int n_b, UnitLds& L) {
+// Loads a unit's tokens and every page id its entry can hold into LDS and
+// clears its t rows.  The page table has a fixed layout per (slot, module):
+// A's ids from `ids` (rank row j, page p at j*ppr_a + p), B's from
+// ids + max_rank*ppr_a; none of these loads waits for the entry.  Begins and
+// ends with a barrier.
+__device__ __forceinline__ void unit_prologue(const SegView& sv, const int32_t* __restrict__ ids, int pos, int nt,
+                                              int n_ids, UnitLds& L) {
   __syncthreads();   // the previous unit is done with LDS
   const int tid = threadIdx.x;
   if (tid < kUnitTokens) L.toks[tid] = tid < nt ? sv.perm[pos + tid] : 0;
-  for (int i = tid; i < n_a; i += kGemvThreads) L.pid[i] = pv.page_ids[e.a_off + i];
-  for (int i = tid; i < n_b; i += kGemvThreads) L.pid[n_a + i] = pv.page_ids[e.b_off + i];
+  for (int i = tid; i < n_ids; i += kGemvThreads) L.pid[i] = ids[i];
   for (int i = tid; i < kUnitTokens * kMaxRank; i += kGemvThreads) L.t[i] = 0.f;
   __syncthreads();
+}
+
+// Unit of workgroup bx of module m, in a grid of a multiple of 16
+// workgroups per module: runs of 2 consecutive units (mostly one segment,
+// so one adapter) stay on one XCD and its L2 (workgroup bx runs on XCD
+// bx % 8), the runs go round-robin over the XCDs, and the round-robin starts
+// one XCD further for each module, so that the XCDs share the units evenly
+// whatever the unit count.  A bijection of [0, gridDim.x) that does not
+// depend on the unit count, so a workgroup can read its work-list record at
+// once.
+__device__ __forceinline__ int unit_of_block(int bx, int m) {
+  const int run = ((bx & 7) - m) & 7, k = bx >> 3;
+  return ((k >> 1) << 4) + (run << 1) + (k & 1);
 }
 
 struct GemvArgs {
@@ -318,28 +331,33 @@ struct GemvArgs {
 };
 
 // MODE 0: fused BGMV (t kept in LDS); 1: shrink only (t to memory); 2: expand only.
+// gridDim.x is a multiple of 16 (see unit_of_block); gridDim.y = modules.
 template <int MODE, typename TI, typename TO>
-__global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvArgs a) {
+__global__ __launch_bounds__(kGemvThreads, 4) void k_gemv(GemvArgs a) {
   __shared__ UnitLds L;
   __shared__ __attribute__((aligned(16))) TI xs[(MODE == 2) ? 8 : kUnitTokens * XSlice<TI>::kElems];
   const int m = blockIdx.y;
-  const int n_units = a.sv.meta[a.units_word];
   const TI* xm = static_cast<const TI*>(a.x) + m * a.msx;
   float* tm = a.t + m * a.mst;
   TO* ym = static_cast<TO*>(a.y) + m * a.msy;
   const TI* pages = static_cast<const TI*>(a.pv.pages);
   const int32_t h = static_cast<int32_t>(a.pv.page_elems);
   const int ppr_a = a.h_in / h, ppr_b = a.h_out / h;
-  for (XcdIter it(n_units); it.valid(); it.next()) {
-    const int u = it.item;
-    const int seg = a.sv.units[2 * u], pos = a.sv.units[2 * u + 1];
-    const int nt = min(kUnitTokens, a.sv.seg_start[seg + 1] - pos);
-    const int slot = a.sv.seg_slot[seg];
-    const SlotEntry e = a.pv.entries[slot * a.pv.n_modules + a.module0 + m];
+  const int ids_a = (MODE == 2) ? 0 : a.pv.max_rank * ppr_a;   // page ids loaded for A
+  const int ids_b = (MODE == 1) ? 0 : a.pv.max_rank * ppr_b;   // ... and for B, after A's
+  const int2* units = reinterpret_cast<const int2*>(a.sv.units);
+  // the unit count and this workgroup's first record travel together
+  const int n_units = a.sv.meta[a.units_word];
+  int u = unit_of_block(blockIdx.x, m);
+  int2 rec = units[min(u, a.sv.max_units - 1)];
+  for (; u < n_units; u += gridDim.x) {
+    if (u >= static_cast<int>(gridDim.x)) rec = units[u];
+    const int slot = rec.x & 0xffff, nt = rec.x >> 16, pos = rec.y;
+    const int ei = slot * a.pv.n_modules + a.module0 + m;
+    const SlotEntry e = a.pv.entries[ei];
+    const int32_t* ids = a.pv.page_ids + static_cast<int64_t>(ei) * a.pv.ppe;
+    unit_prologue(a.sv, (MODE == 2) ? ids + a.pv.max_rank * ppr_a : ids, pos, nt, ids_a + ids_b, L);
     if (e.rank <= 0) continue;
-    const int n_a = (MODE == 2) ? 0 : e.rank * ppr_a;
-    const int n_b = (MODE == 1) ? 0 : e.rank * ppr_b;
-    unit_prologue(a.sv, a.pv, e, pos, nt, n_a, n_b, L);
     if constexpr (MODE != 2) {
       if (nt == 1) shrink_unit<TI, 1>(xm, a.ld_x, L, nt, pages, 0, h, a.magic, a.h_in, e.rank, xs);
       else if (nt == 2) shrink_unit<TI, 2>(xm, a.ld_x, L, nt, pages, 0, h, a.magic, a.h_in, e.rank, xs);
@@ -359,9 +377,9 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvArgs a) {
       __syncthreads();
     }
     if constexpr (MODE != 1) {
-      if (nt == 1) expand_unit<TI, TO, 1>(ym, a.ld_y, L, nt, pages, n_a, h, a.magic, a.h_out, e.rank, e.scale);
-      else if (nt == 2) expand_unit<TI, TO, 2>(ym, a.ld_y, L, nt, pages, n_a, h, a.magic, a.h_out, e.rank, e.scale);
-      else expand_unit<TI, TO, 4>(ym, a.ld_y, L, nt, pages, n_a, h, a.magic, a.h_out, e.rank, e.scale);
+      if (nt == 1) expand_unit<TI, TO, 1>(ym, a.ld_y, L, nt, pages, ids_a, h, a.magic, a.h_out, e.rank, e.scale);
+      else if (nt == 2) expand_unit<TI, TO, 2>(ym, a.ld_y, L, nt, pages, ids_a, h, a.magic, a.h_out, e.rank, e.scale);
+      else expand_unit<TI, TO, 4>(ym, a.ld_y, L, nt, pages, ids_a, h, a.magic, a.h_out, e.rank, e.scale);
     }
   }
 }

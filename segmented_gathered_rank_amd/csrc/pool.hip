@@ -21,8 +21,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_upload(T* __restrict__ pages, const T* __restrict__ src,
                                                 const int32_t* __restrict__ plist, int32_t n_plist,
                                                 int64_t page_elems, int32_t* __restrict__ page_ids,
-                                                int32_t ids_off, SlotEntry* __restrict__ entry,
-                                                SlotEntry value) {
+                                                int32_t ids_off, int32_t n_a, int32_t b_gap,
+                                                SlotEntry* __restrict__ entry, SlotEntry value) {
   const int32_t piece = blockIdx.x;
   if (piece >= n_plist) return;
   const int32_t page = plist[piece];
@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void k_upload(T* __restrict__ pages, const T* 
     *reinterpret_cast<u32x4*>(d + e) = *reinterpret_cast<const u32x4*>(s + e);
   }
   if (threadIdx.x == 0) {
-    page_ids[ids_off + piece] = page;
+    page_ids[ids_off + piece + (piece >= n_a ? b_gap : 0)] = page;
     if (piece == 0) *entry = value;
   }
 }
@@ -189,7 +189,12 @@ lora_status lora_pool_load(lora_pool* p, int32_t slot, int32_t module, int32_t r
   const size_t ids_at = (a_bytes + b_bytes + 255) / 256 * 256;
   char* st = static_cast<char*>(p->d_staging);
   const int32_t ids_off = static_cast<int32_t>(ei * p->max_pages_per_entry);
-  SlotEntry value{rank, scale, ids_off, ids_off + static_cast<int32_t>(rank * ppr_a)};
+  // A's page ids from ids_off (rank row j, page p at j*ppr_a + p); B's from
+  // ids_off + max_rank*ppr_a whatever the rank, so kernels can fetch both
+  // lists without waiting for the entry.
+  const int32_t n_a = static_cast<int32_t>(rank * ppr_a);
+  const int32_t b_gap = static_cast<int32_t>((p->max_rank - rank) * ppr_a);
+  SlotEntry value{rank, scale, ids_off, ids_off + n_a + b_gap};
 
   DeviceGuard g(p->device);
   bool ok = g.ok &&
@@ -202,12 +207,12 @@ lora_status lora_pool_load(lora_pool* p, int32_t slot, int32_t module, int32_t r
       hipLaunchKernelGGL(k_upload<__bf16>, dim3(static_cast<unsigned>(n_plist)), dim3(256), 0, s,
                          static_cast<__bf16*>(p->d_pages), reinterpret_cast<const __bf16*>(st),
                          reinterpret_cast<const int32_t*>(st + ids_at), static_cast<int32_t>(n_plist), h,
-                         p->d_page_ids, ids_off, p->d_entries + ei, value);
+                         p->d_page_ids, ids_off, n_a, b_gap, p->d_entries + ei, value);
     } else {
       hipLaunchKernelGGL(k_upload<float>, dim3(static_cast<unsigned>(n_plist)), dim3(256), 0, s,
                          static_cast<float*>(p->d_pages), reinterpret_cast<const float*>(st),
                          reinterpret_cast<const int32_t*>(st + ids_at), static_cast<int32_t>(n_plist), h,
-                         p->d_page_ids, ids_off, p->d_entries + ei, value);
+                         p->d_page_ids, ids_off, n_a, b_gap, p->d_entries + ei, value);
     }
     ok = hipGetLastError() == hipSuccess && hipStreamSynchronize(s) == hipSuccess;
   }

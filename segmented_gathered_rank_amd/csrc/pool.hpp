@@ -41,6 +41,8 @@ struct lora_pool {
     v.page_elems = page_elems;
     v.n_slots = n_slots;
     v.n_modules = n_modules;
+    v.max_rank = max_rank;
+    v.ppe = max_pages_per_entry;
     return v;
   }
 };

@@ -173,6 +173,12 @@ struct Out {
   int32_t *perm, *seg_start, *seg_slot, *meta, *units, *tiles;
 };
 
+// GEMV work unit u of a segment of `run` tokens of `slot` that starts at
+// position `first` of perm: (slot + 65536 * tokens in the unit, position).
+__device__ __forceinline__ int2 unit_record(int slot, int run, int u, int first) {
+  return make_int2(slot + (min(kUnitTokens, run - u * kUnitTokens) << 16), first + u * kUnitTokens);
+}
+
 struct LayoutLds {
   int wsum[kWaves][6];   // per wave: inclusive counter totals, max segment length
   int woff[kWaves][5];   // per wave: exclusive offsets
@@ -261,7 +267,7 @@ __device__ void layout_segments(const int32_t* total, int n_tokens, int n_slots,
       o.seg_start[off[1]] = off[0];
       base_of(s, off[0]);
       if (run < kLongMin) {   // at most kLongMin / kUnitTokens entries: written by this lane
-        for (int u = 0; u < nu; ++u) units[off[2] + u] = make_int2(off[1], off[0] + u * kUnitTokens);
+        for (int u = 0; u < nu; ++u) units[off[2] + u] = unit_record(s, run, u, off[0]);
       }
     }
     // long segments: the whole wave writes each one's entries, lane by lane
@@ -270,12 +276,13 @@ __device__ void layout_segments(const int32_t* total, int n_tokens, int n_slots,
       const int src = lowest_lane(lm);
       lm &= lm - 1;
       const int r = __builtin_amdgcn_readlane(run, src);
+      const int slot = __builtin_amdgcn_readlane(s, src);
       const int ssi = __builtin_amdgcn_readlane(off[1], src);
       const int sb = __builtin_amdgcn_readlane(off[0], src);
       const int u0 = long_at + __builtin_amdgcn_readlane(off[3], src);
       const int t0 = __builtin_amdgcn_readlane(off[4], src);
       const int lnu = (r + kUnitTokens - 1) / kUnitTokens;
-      for (int u = lane; u < lnu; u += 64) units[u0 + u] = make_int2(ssi, sb + u * kUnitTokens);
+      for (int u = lane; u < lnu; u += 64) units[u0 + u] = unit_record(slot, r, u, sb);
       const int ntl = (r + kTileTokens - 1) / kTileTokens;
       for (int u = lane; u < ntl; u += 64) tiles[t0 + u] = make_int2(ssi, sb + u * kTileTokens);
     }

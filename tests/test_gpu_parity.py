@@ -86,15 +86,17 @@ def _check_segments(ids, n_slots, st, meta, seg, arr):
     tiles = arr(seg.tiles, 2 * ntl).reshape(-1, 2)
     lens = np.diff(ref["seg_start"])
     exp_units, exp_tiles = [], []
+
+    def unit(k, L, u):   # (slot + 65536 * tokens in the unit, first position)
+        return (int(ref["seg_slot"][k]) + 65536 * min(ut, L - u), int(ref["seg_start"][k]) + u)
     for k, L in enumerate(lens):
-        s0 = ref["seg_start"][k]
         if L < lmin:
-            exp_units += [(k, s0 + u) for u in range(0, L, ut)]
+            exp_units += [unit(k, L, u) for u in range(0, L, ut)]
     short = list(exp_units)
     for k, L in enumerate(lens):
         s0 = ref["seg_start"][k]
         if L >= lmin:
-            exp_units += [(k, s0 + u) for u in range(0, L, ut)]
+            exp_units += [unit(k, L, u) for u in range(0, L, ut)]
             exp_tiles += [(k, s0 + u) for u in range(0, L, tt)]
     # the library's order: short-segment units, then long-segment units, each in segment order
     assert nus == len(short)
