@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "LoRA-apply tokens/s; achieved HBM GB/s (BGMV) and MFMA TFLOP/s (SGMV) vs peak"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak of MI355X
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 
 
@@ -137,6 +138,49 @@ def pmc_summary(args):
     print(json.dumps(out))
 
 
+def copy_gbps(mib=1024, reps=10):
+    """Measured device-to-device copy bandwidth (read + write bytes per second):
+    the streaming rate this GPU reaches, a second denominator beside the spec peak."""
+    import torch
+    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return 2.0 * (mib << 20) / (ms * 1e-3) / 1e9
+
+
+def base_gemm_ms(wl, reps=10):
+    """The shared base products y0 = x W of every module (bf16, hipBLASLt through
+    torch.matmul) on random data of the workload's shapes: the denominator of the
+    adapter overhead.  Not part of the library or of the timed step."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(0)
+    ops = [(torch.randn(wl.n_tokens, m.h_in, device="cuda", dtype=torch.bfloat16, generator=g),
+            torch.randn(m.h_in, m.h_out, device="cuda", dtype=torch.bfloat16, generator=g)) for m in wl.modules]
+    for x, w in ops:
+        torch.matmul(x, w)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        for x, w in ops:
+            torch.matmul(x, w)
+    b.record()
+    torch.cuda.synchronize()
+    flops = sum(2.0 * wl.n_tokens * m.h_in * m.h_out for m in wl.modules)
+    ms = a.elapsed_time(b) / reps
+    del ops
+    return ms, flops
+
+
 def cpu_baseline(wl, seconds):
     """The oracle, untouched, on one core: whole steps (all modules, all tokens) until `seconds`."""
     from threadpoolctl import threadpool_limits
@@ -238,6 +282,22 @@ def main():
 
     bound_bytes = work["bytes"]
     achieved = bound_bytes / (kern_avg * 1e-3) / 1e9
+    if args.calibrate_copy_mib <= 0:   # in counter runs the calibration copy must stay the largest copy
+        extra["copy_GBps"] = round(copy_gbps(), 1)
+        extra["frac_of_copy_GBps"] = round(achieved / extra["copy_GBps"], 4)
+    if mode == "sgmv":   # the matrix-core path: what its arithmetic intensity allows at the HBM peak
+        ai = work["flops"] / work["bytes"]
+        attainable = min(MFMA_BF16_PEAK_TFLOPS, ai * HBM_PEAK_GBS / 1e3)
+        extra["mfma_peak_tflops"] = MFMA_BF16_PEAK_TFLOPS
+        extra["arith_intensity_flop_per_byte"] = round(ai, 2)
+        extra["attainable_tflops"] = round(attainable, 2)
+        extra["frac_of_peak_tflops"] = round(extra["achieved_tflops"] / MFMA_BF16_PEAK_TFLOPS, 5)
+        extra["frac_of_attainable_tflops"] = round(extra["achieved_tflops"] / attainable, 4)
+    if args.workload == "encoder_step":
+        gms, gflops = base_gemm_ms(wl)
+        extra["base_gemm_ms"] = round(gms, 4)
+        extra["base_gemm_tflops"] = round(gflops / (gms * 1e-3) / 1e12, 1)
+        extra["lora_apply_over_base_gemm"] = round(kern_avg / gms, 4)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(args.workload),
                 "kernel": "k_bgmv" if mode == "bgmv" else "shrink+expand",

@@ -169,7 +169,8 @@ typedef struct {
     int32_t *seg_start;  /* [max_segs + 1] offsets into perm; seg_start[n_seg] = n_active          */
     int32_t *seg_slot;   /* [max_segs] slot of each segment, ascending                             */
     int32_t *meta;       /* [LORA_META_WORDS]                                                      */
-    int32_t *units;      /* [2 * max_units] (slot + 65536 * tokens, position in perm) per GEMV unit */
+    int32_t *units;      /* [2 * max_units] GEMV units: (slot + 65536 * tokens + 2^24 * [segment  */
+                         /* spans several units], position in perm)                               */
     int32_t *tiles;      /* [2 * max_tiles] (segment, position in perm) per matrix-core tile       */
     int32_t *work;       /* builder scratch of large batches (n_chunks > 0), else NULL             */
     int32_t n_tokens, n_slots, max_segs, max_units, max_tiles;

@@ -69,12 +69,14 @@ unsigned grid_of(int32_t bound) {
   return static_cast<unsigned>((bound + 7) / 8 * 8);
 }
 
-// Grid of the GEMV kernels over `max_units` units: a multiple of 16, the
-// period of their unit-to-workgroup map, at most kMaxGrid.
+// Grid of the GEMV kernels over `max_units` units: a multiple of 8*kUnitRun,
+// the period of their unit-to-workgroup map, at most kMaxGrid.
 unsigned gemv_grid_of(int32_t max_units) {
+  constexpr int period = 8 * kUnitRun;
+  static_assert(kMaxGrid % period == 0, "the grid cap must be a whole number of periods");
   if (max_units < 1) max_units = 1;
   if (max_units > kMaxGrid) max_units = kMaxGrid;
-  return static_cast<unsigned>((max_units + 15) / 16 * 16);
+  return static_cast<unsigned>((max_units + period - 1) / period * period);
 }
 
 GemvArgs gemv_args(const lora_pool* p, int32_t module0, const SegView& sv, int32_t units_word) {

@@ -45,11 +45,15 @@ namespace lora {
 #ifndef LORA_SHRINK_ROWS
 #define LORA_SHRINK_ROWS 2
 #endif
+#ifndef LORA_UNIT_RUN
+#define LORA_UNIT_RUN 2
+#endif
 constexpr int kGemvThreads = LORA_GEMV_THREADS;
 constexpr int kGemvWaves = kGemvThreads / 64;
 constexpr int kXSliceBytes = 32768;                 // LDS for the staged x rows of a unit
 constexpr int kShrinkBatch = LORA_SHRINK_BATCH;     // 16-byte chunks of a row in flight per lane
 constexpr int kShrinkRows = LORA_SHRINK_ROWS;       // rank rows a wave streams at once
+constexpr int kUnitRun = LORA_UNIT_RUN;             // consecutive units one XCD takes (a power of 2)
 template <typename TI>
 constexpr int kExpandBatch = sizeof(TI) == 2 ? LORA_EXPAND_BATCH : 8;   // rank rows of B in flight per thread
 
@@ -118,7 +122,10 @@ __device__ __forceinline__ void stage_x(const TI* __restrict__ x, int64_t ld_x, 
   }
 }
 
-template <typename TI, int NT>
+// KEEP: the unit's segment spans several units, whose workgroups read the
+// same pages, so they are loaded through the caches; a page read by one
+// unit only is streamed with non-temporal loads.
+template <typename TI, int NT, bool KEEP>
 __device__ __forceinline__ void shrink_unit(const TI* __restrict__ x, int64_t ld_x, UnitLds& L, int nt,
                                             const TI* __restrict__ pages, int pid0, int32_t h, uint32_t magic,
                                             int32_t h_in, int32_t rank, TI* xs) {
@@ -148,7 +155,8 @@ __device__ __forceinline__ void shrink_unit(const TI* __restrict__ x, int64_t ld
 #pragma unroll
       for (int i = 0; i < kShrinkBatch; ++i) {
         const int k = kb + (lane + 64 * i) * CE;
-        raw[q][i].load_nt(base[q] + static_cast<uint32_t>(min(k, kp1 - CE)));
+        if constexpr (KEEP) raw[q][i].load(base[q] + static_cast<uint32_t>(min(k, kp1 - CE)));
+        else raw[q][i].load_nt(base[q] + static_cast<uint32_t>(min(k, kp1 - CE)));
       }
   };
 
@@ -222,7 +230,7 @@ __device__ __forceinline__ void shrink_unit(const TI* __restrict__ x, int64_t ld
   __syncthreads();
 }
 
-template <typename TI, typename TO, int NT>
+template <typename TI, typename TO, int NT, bool KEEP>
 __device__ __forceinline__ void expand_unit(TO* __restrict__ y, int64_t ld_y, const UnitLds& L, int nt,
                                             const TI* __restrict__ pages, int pid0, int32_t h, uint32_t magic,
                                             int32_t h_out, int32_t rank, float scale) {
@@ -257,7 +265,8 @@ __device__ __forceinline__ void expand_unit(TO* __restrict__ y, int64_t ld_y, co
         const int j = min(j0 + jj, rank - 1);    // rows past the rank repeat the last (their t is 0)
         int pid = L.pid[pid0 + j * ppr + p];
         if (wave_page) pid = __builtin_amdgcn_readfirstlane(pid);
-        raw[jj].load_nt(pages + static_cast<int64_t>(pid) * h + static_cast<uint32_t>(off));
+        if constexpr (KEEP) raw[jj].load(pages + static_cast<int64_t>(pid) * h + static_cast<uint32_t>(off));
+        else raw[jj].load_nt(pages + static_cast<int64_t>(pid) * h + static_cast<uint32_t>(off));
       }
 #pragma unroll
       for (int jj = 0; jj < EB; ++jj) {
@@ -302,17 +311,17 @@ __device__ __forceinline__ void unit_prologue(const SegView& sv, const int32_t* 
   __syncthreads();
 }
 
-// Unit of workgroup bx of module m, in a grid of a multiple of 16
-// workgroups per module: runs of 2 consecutive units (mostly one segment,
-// so one adapter) stay on one XCD and its L2 (workgroup bx runs on XCD
-// bx % 8), the runs go round-robin over the XCDs, and the round-robin starts
-// one XCD further for each module, so that the XCDs share the units evenly
-// whatever the unit count.  A bijection of [0, gridDim.x) that does not
-// depend on the unit count, so a workgroup can read its work-list record at
-// once.
+// Unit of workgroup bx of module m, in a grid of a multiple of 8*kUnitRun
+// workgroups per module: runs of kUnitRun consecutive units (mostly one
+// segment, so one adapter) stay on one XCD and its L2 (workgroup bx runs on
+// XCD bx % 8), the runs go round-robin over the XCDs, and the round-robin
+// starts one XCD further for each module, so that the XCDs share the units
+// evenly whatever the unit count.  A bijection of [0, gridDim.x) that does
+// not depend on the unit count, so a workgroup can read its work-list
+// record at once.
 __device__ __forceinline__ int unit_of_block(int bx, int m) {
   const int run = ((bx & 7) - m) & 7, k = bx >> 3;
-  return ((k >> 1) << 4) + (run << 1) + (k & 1);
+  return (k / kUnitRun) * (8 * kUnitRun) + run * kUnitRun + (k % kUnitRun);
 }
 
 struct GemvArgs {
@@ -331,7 +340,7 @@ struct GemvArgs {
 };
 
 // MODE 0: fused BGMV (t kept in LDS); 1: shrink only (t to memory); 2: expand only.
-// gridDim.x is a multiple of 16 (see unit_of_block); gridDim.y = modules.
+// gridDim.x is a multiple of 8*kUnitRun (see unit_of_block); gridDim.y = modules.
 template <int MODE, typename TI, typename TO>
 __global__ __launch_bounds__(kGemvThreads, 4) void k_gemv(GemvArgs a) {
   __shared__ UnitLds L;
@@ -352,16 +361,25 @@ __global__ __launch_bounds__(kGemvThreads, 4) void k_gemv(GemvArgs a) {
   int2 rec = units[min(u, a.sv.max_units - 1)];
   for (; u < n_units; u += gridDim.x) {
     if (u >= static_cast<int>(gridDim.x)) rec = units[u];
-    const int slot = rec.x & 0xffff, nt = rec.x >> 16, pos = rec.y;
+    const int slot = rec.x & 0xffff, nt = (rec.x >> 16) & 0xff, pos = rec.y;
+    const bool keep = (rec.x >> 24) & 1;
     const int ei = slot * a.pv.n_modules + a.module0 + m;
     const SlotEntry e = a.pv.entries[ei];
     const int32_t* ids = a.pv.page_ids + static_cast<int64_t>(ei) * a.pv.ppe;
     unit_prologue(a.sv, (MODE == 2) ? ids + a.pv.max_rank * ppr_a : ids, pos, nt, ids_a + ids_b, L);
     if (e.rank <= 0) continue;
     if constexpr (MODE != 2) {
-      if (nt == 1) shrink_unit<TI, 1>(xm, a.ld_x, L, nt, pages, 0, h, a.magic, a.h_in, e.rank, xs);
-      else if (nt == 2) shrink_unit<TI, 2>(xm, a.ld_x, L, nt, pages, 0, h, a.magic, a.h_in, e.rank, xs);
-      else shrink_unit<TI, 4>(xm, a.ld_x, L, nt, pages, 0, h, a.magic, a.h_in, e.rank, xs);
+#define LORA_SHRINK_CALL(N, K) shrink_unit<TI, N, K>(xm, a.ld_x, L, nt, pages, 0, h, a.magic, a.h_in, e.rank, xs)
+      if (keep) {
+        if (nt == 1) LORA_SHRINK_CALL(1, true);
+        else if (nt == 2) LORA_SHRINK_CALL(2, true);
+        else LORA_SHRINK_CALL(4, true);
+      } else {
+        if (nt == 1) LORA_SHRINK_CALL(1, false);
+        else if (nt == 2) LORA_SHRINK_CALL(2, false);
+        else LORA_SHRINK_CALL(4, false);
+      }
+#undef LORA_SHRINK_CALL
     }
     if constexpr (MODE == 1) {
       for (int i = threadIdx.x; i < nt * e.rank; i += kGemvThreads) {
@@ -377,9 +395,18 @@ __global__ __launch_bounds__(kGemvThreads, 4) void k_gemv(GemvArgs a) {
       __syncthreads();
     }
     if constexpr (MODE != 1) {
-      if (nt == 1) expand_unit<TI, TO, 1>(ym, a.ld_y, L, nt, pages, ids_a, h, a.magic, a.h_out, e.rank, e.scale);
-      else if (nt == 2) expand_unit<TI, TO, 2>(ym, a.ld_y, L, nt, pages, ids_a, h, a.magic, a.h_out, e.rank, e.scale);
-      else expand_unit<TI, TO, 4>(ym, a.ld_y, L, nt, pages, ids_a, h, a.magic, a.h_out, e.rank, e.scale);
+#define LORA_EXPAND_CALL(N, K) \
+  expand_unit<TI, TO, N, K>(ym, a.ld_y, L, nt, pages, ids_a, h, a.magic, a.h_out, e.rank, e.scale)
+      if (keep) {
+        if (nt == 1) LORA_EXPAND_CALL(1, true);
+        else if (nt == 2) LORA_EXPAND_CALL(2, true);
+        else LORA_EXPAND_CALL(4, true);
+      } else {
+        if (nt == 1) LORA_EXPAND_CALL(1, false);
+        else if (nt == 2) LORA_EXPAND_CALL(2, false);
+        else LORA_EXPAND_CALL(4, false);
+      }
+#undef LORA_EXPAND_CALL
     }
   }
 }

@@ -174,9 +174,11 @@ struct Out {
 };
 
 // GEMV work unit u of a segment of `run` tokens of `slot` that starts at
-// position `first` of perm: (slot + 65536 * tokens in the unit, position).
+// position `first` of perm: (slot + 65536 * tokens in the unit + 2^24 if the
+// segment has more than one unit, position).
 __device__ __forceinline__ int2 unit_record(int slot, int run, int u, int first) {
-  return make_int2(slot + (min(kUnitTokens, run - u * kUnitTokens) << 16), first + u * kUnitTokens);
+  return make_int2(slot + (min(kUnitTokens, run - u * kUnitTokens) << 16) + ((run > kUnitTokens) ? (1 << 24) : 0),
+                   first + u * kUnitTokens);
 }
 
 struct LayoutLds {

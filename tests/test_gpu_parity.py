@@ -87,8 +87,8 @@ def _check_segments(ids, n_slots, st, meta, seg, arr):
     lens = np.diff(ref["seg_start"])
     exp_units, exp_tiles = [], []
 
-    def unit(k, L, u):   # (slot + 65536 * tokens in the unit, first position)
-        return (int(ref["seg_slot"][k]) + 65536 * min(ut, L - u), int(ref["seg_start"][k]) + u)
+    def unit(k, L, u):   # (slot + 65536 * tokens in the unit + 2^24 * [several units], first position)
+        return (int(ref["seg_slot"][k]) + 65536 * min(ut, L - u) + (1 << 24) * (L > ut), int(ref["seg_start"][k]) + u)
     for k, L in enumerate(lens):
         if L < lmin:
             exp_units += [unit(k, L, u) for u in range(0, L, ut)]
