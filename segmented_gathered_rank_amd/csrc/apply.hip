@@ -209,9 +209,16 @@ lora_status launch_expand(const lora_pool* p, int32_t module0, int32_t n_modules
     if (use_mfma && seg->max_tiles > 0) {
       const int32_t ldr = ldr_of(p);
       const size_t ysz = sizeof(TO);
-      const size_t lds = (static_cast<size_t>(kTileTokens) * (ldr + 1) * 4 + 15) / 16 * 16 +
-                         (static_cast<size_t>(ldr) * (kExpandCols + 8) * 2 + 15) / 16 * 16 +
-                         static_cast<size_t>(kTileTokens) * (kExpandCols + 16 / ysz) * ysz;
+      const size_t lds = expand_lds_bytes(ldr, static_cast<int>(ysz));
+      static size_t lds_allowed = 64 * 1024;   // up to 78 KiB at rank 64 with fp32 y (gfx950: 160 KiB)
+      if (lds > lds_allowed) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_expand_mfma<TO>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)) != hipSuccess) {
+          (void)hipGetLastError();
+          return LORA_ERR_HIP;
+        }
+        lds_allowed = lds;
+      }
       const int32_t col_groups = (h_out / kExpandCols + kExpandBlocks - 1) / kExpandBlocks;
       hipLaunchKernelGGL((k_expand_mfma<TO>), dim3(grid_of(seg->max_tiles), col_groups, n_modules),
                          dim3(kMfmaThreads), lds, s, pv, module0, sv, t, ld_t, mst, static_cast<TO*>(y), ld_y, msy,

@@ -15,8 +15,10 @@
 //   them in split order (deterministic; the launch boundary orders the writes
 //   and reads, so no device-wide fence is needed inside a kernel).
 // expand (fp32 t, bf16 B, y bf16 or fp32): Y[64 x 128] += s * T[64 x r] B[r x 128]
-//   with v_mfma_f32_32x32x2_f32, so t stays in fp32; formed transposed so that
-//   y moves between HBM and registers directly (see k_expand_mfma).
+//   with v_mfma_f32_32x32x16_bf16.  t is split into three bf16 parts whose sum
+//   is t exactly, so the matrix cores multiply by t itself (three MFMAs per K
+//   step of 16 instead of eight fp32 32x32x2 steps); formed transposed so that
+//   the accumulators map onto y rows (see k_expand_mfma).
 #pragma once
 
 #include "common.hpp"
@@ -245,24 +247,32 @@ __global__ __launch_bounds__(kMfmaThreads) void k_shrink_reduce(ShrinkArgs a) {
 // and an LDS tile with coalesced 16-byte row accesses (a wave covers whole
 // rows), and between LDS and the MFMA layout with 8- or 16-byte accesses.
 // T (fp32) is staged once per tile, the B block (bf16) once per column block.
+// LDS of k_expand_mfma for pool rank cap ldr and y element size ysz: the
+// three bf16 parts of the T tile [3][64][r16+8], the transposed B block
+// [128][r16+8] (bf16) and the y block [64][128 + 16/ysz].
+__host__ __device__ inline int expand_r16(int ldr) { return (ldr + 15) & ~15; }
+__host__ __device__ inline size_t expand_lds_bytes(int ldr, int ysz) {
+  const size_t ld = static_cast<size_t>(expand_r16(ldr) + 8);
+  return 3 * kTileTokens * ld * 2 + static_cast<size_t>(kExpandCols) * ld * 2 +
+         static_cast<size_t>(kTileTokens) * (kExpandCols + 16 / ysz) * ysz;
+}
+
 template <typename TO>
-__global__ __launch_bounds__(kMfmaThreads) void k_expand_mfma(PoolView pv, int32_t module0, SegView sv,
-                                                             const float* __restrict__ t, int64_t ld_t,
-                                                             int64_t mst, TO* __restrict__ y, int64_t ld_y,
-                                                             int64_t msy, int32_t h_out, int32_t ldr) {
+__global__ __launch_bounds__(kMfmaThreads, sizeof(TO) == 2 ? 3 : 2) void k_expand_mfma(PoolView pv, int32_t module0, SegView sv,
+                                                                const float* __restrict__ t, int64_t ld_t,
+                                                                int64_t mst, TO* __restrict__ y, int64_t ld_y,
+                                                                int64_t msy, int32_t h_out, int32_t ldr) {
   constexpr int TN = kExpandCols;
-  constexpr int BLD = TN + 8;                         // B_s row stride (bf16)
   constexpr int YLD = TN + 16 / sizeof(TO);           // Y_s row stride (elements)
   constexpr int YCPR = TN * sizeof(TO) / 16;          // 16-byte chunks per y row of the block
   constexpr int YCH = kTileTokens * YCPR / kMfmaThreads;   // y chunks per thread
   constexpr int YV = 16 / sizeof(TO);                 // elements per 16-byte chunk
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int TLD = ldr + 1;                            // T_s row stride (floats)
-  float* T_s = reinterpret_cast<float*>(smem);                                              // [64][TLD]
-  size_t o = (static_cast<size_t>(kTileTokens) * TLD * 4 + 15) & ~static_cast<size_t>(15);
-  __bf16* B_s = reinterpret_cast<__bf16*>(smem + o);                                        // [ldr][BLD]
-  o += (static_cast<size_t>(ldr) * BLD * 2 + 15) & ~static_cast<size_t>(15);
-  TO* Y_s = reinterpret_cast<TO*>(smem + o);                                                // [64][YLD]
+  const int r16 = expand_r16(ldr);
+  const int LD = r16 + 8;                             // row stride of T3_s and BT_s (bf16)
+  __bf16* T3_s = reinterpret_cast<__bf16*>(smem);                                  // [3][64][LD]
+  __bf16* BT_s = T3_s + 3 * kTileTokens * LD;                                      // [TN][LD]
+  TO* Y_s = reinterpret_cast<TO*>(BT_s + TN * LD);                                 // [64][YLD]
   __shared__ int32_t toks_s[kTileTokens];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -283,12 +293,49 @@ __global__ __launch_bounds__(kMfmaThreads) void k_expand_mfma(PoolView pv, int32
     const SlotEntry e = pv.entries[slot * pv.n_modules + module0 + m];
     if (e.rank <= 0) continue;
     const int rank = e.rank;
-    const int r2 = (rank + 1) & ~1;
+    const int rk = (rank + 15) & ~15;          // contraction length: rank rounded up to the MFMA's K
     __syncthreads();   // the previous tile is done with LDS
     if (tid < kTileTokens) toks_s[tid] = tid < len ? sv.perm[pos + tid] : -1;
     __syncthreads();
     const int first = toks_s[0];
-    // T tile [64][r2] (fp32): thread -> row tid/4, columns (tid%4) + 4q; loads issued together
+    // y block cb [64][TN]: coalesced 16-byte chunks, rows without a token read the first token's;
+    // B block [rk <= 32 rows][TN] (bf16): rank row j, columns c0..c0+TN of that row
+    u32x4 yv[YCH], bv[2];
+    auto issue = [&](int cb, u32x4 (&yq)[YCH], u32x4 (&bq)[2]) {
+      const int c0 = (blockIdx.y * kExpandBlocks + cb) * TN;
+      const int p = c0 / h;                    // the column block lies inside page p of each row
+      const int off = c0 - p * h;
+#pragma unroll
+      for (int q = 0; q < YCH; ++q) {
+        const int idx = tid + kMfmaThreads * q;
+        const int r = idx / YCPR, c = (idx % YCPR) * YV;
+        const int tk = toks_s[r];
+        yq[q] = ld16<LORA_NT_ROWS != 0>(
+            reinterpret_cast<const u32x4*>(ym + static_cast<int64_t>(tk >= 0 ? tk : first) * ld_y + c0 + c));
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int idx = min(tid + kMfmaThreads * q, rk * (TN / 8) - 1);
+        const int j = idx / (TN / 8), c = (idx % (TN / 8)) * 8;
+        bq[q] = *reinterpret_cast<const u32x4*>(
+            pages + static_cast<int64_t>(pv.page_ids[e.b_off + min(j, rank - 1) * ppr + p]) * h + off + c);
+      }
+    };
+    // B chunk (row j, columns c..c+7) into the transposed block, zero for rows past the rank
+    auto put_b = [&](int j, int c, u32x4 v) {
+      if (j >= rank) v = u32x4{0u, 0u, 0u, 0u};
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        BT_s[(c + 2 * i) * LD + j] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(w[i] & 0xffffu));
+        BT_s[(c + 2 * i + 1) * LD + j] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(w[i] >> 16));
+      }
+    };
+    const int n_cb = min(kExpandBlocks, (h_out - static_cast<int>(blockIdx.y) * kExpandBlocks * TN + TN - 1) / TN);
+    // T tile: t = hi + mid + lo, three bf16 values whose sum is t exactly (3 x 8 significand
+    // bits cover fp32's 24), so the bf16 matrix cores multiply by t itself.  Thread -> row
+    // tid/4, columns (tid%4) + 4q; its loads go out with block 0's.  Later blocks load at the
+    // top of their own step: a second register stage would cost the third wave per SIMD.
     {
       const int r = tid >> 2, jq = tid & 3;
       const int tk = toks_s[r];
@@ -296,37 +343,30 @@ __global__ __launch_bounds__(kMfmaThreads) void k_expand_mfma(PoolView pv, int32
       float tv[kMaxRank / 4];
 #pragma unroll
       for (int q = 0; q < kMaxRank / 4; ++q) tv[q] = trow[min(jq + 4 * q, rank - 1)];
+      if (n_cb > 0) issue(0, yv, bv);
 #pragma unroll
       for (int q = 0; q < kMaxRank / 4; ++q) {
         const int j = jq + 4 * q;
-        if (j < r2) T_s[r * TLD + j] = (tk >= 0 && j < rank) ? tv[q] : 0.f;
+        if (j < rk) {
+          const float v = (tk >= 0 && j < rank) ? tv[q] : 0.f;
+          const __bf16 hi = static_cast<__bf16>(v);
+          const float r1 = v - static_cast<float>(hi);
+          const __bf16 mid = static_cast<__bf16>(r1);
+          const __bf16 lo = static_cast<__bf16>(r1 - static_cast<float>(mid));
+          T3_s[r * LD + j] = hi;
+          T3_s[(kTileTokens + r) * LD + j] = mid;
+          T3_s[(2 * kTileTokens + r) * LD + j] = lo;
+        }
       }
     }
+#pragma unroll
     for (int cb = 0; cb < kExpandBlocks; ++cb) {
+      if (cb >= n_cb) break;                   // uniform
       const int c0 = (blockIdx.y * kExpandBlocks + cb) * TN;
-      if (c0 >= h_out) break;                  // uniform
-      const int p = c0 / h;                    // the column block lies inside page p of each row
+      const int p = c0 / h;
       const int off = c0 - p * h;
-      // y block [64][TN]: coalesced 16-byte chunks, rows without a token read the first token's
-      u32x4 yv[YCH];
-#pragma unroll
-      for (int q = 0; q < YCH; ++q) {
-        const int idx = tid + kMfmaThreads * q;
-        const int r = idx / YCPR, c = (idx % YCPR) * YV;
-        const int tk = toks_s[r];
-        yv[q] = ld16<LORA_NT_ROWS != 0>(
-            reinterpret_cast<const u32x4*>(ym + static_cast<int64_t>(tk >= 0 ? tk : first) * ld_y + c0 + c));
-      }
-      // B block [r2][TN] (bf16): rank row j, columns c0..c0+TN of that row
-      u32x4 bv[2];
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int idx = min(tid + kMfmaThreads * q, r2 * (TN / 8) - 1);
-        const int j = idx / (TN / 8), c = (idx % (TN / 8)) * 8;
-        bv[q] = *reinterpret_cast<const u32x4*>(
-            pages + static_cast<int64_t>(pv.page_ids[e.b_off + min(j, rank - 1) * ppr + p]) * h + off + c);
-      }
-      __syncthreads();                         // the previous block's B_s / Y_s reads are done
+      if (cb > 0) issue(cb, yv, bv);
+      __syncthreads();                         // the previous block's BT_s / Y_s reads are done
 #pragma unroll
       for (int q = 0; q < YCH; ++q) {
         const int idx = tid + kMfmaThreads * q;
@@ -336,30 +376,35 @@ __global__ __launch_bounds__(kMfmaThreads) void k_expand_mfma(PoolView pv, int32
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int idx = tid + kMfmaThreads * q;
-        if (idx < r2 * (TN / 8)) {
-          const int j = idx / (TN / 8), c = (idx % (TN / 8)) * 8;
-          *reinterpret_cast<u32x4*>(&B_s[j * BLD + c]) = (j < rank) ? bv[q] : u32x4{0u, 0u, 0u, 0u};
-        }
+        if (idx < rk * (TN / 8)) put_b(idx / (TN / 8), (idx % (TN / 8)) * 8, bv[q]);
       }
-      for (int base = 2 * kMfmaThreads; base < r2 * (TN / 8); base += kMfmaThreads) {   // ranks above 16
+      for (int base = 2 * kMfmaThreads; base < rk * (TN / 8); base += kMfmaThreads) {   // ranks above 32
         const int idx = base + tid;
-        if (idx < r2 * (TN / 8)) {
+        if (idx < rk * (TN / 8)) {
           const int j = idx / (TN / 8), c = (idx % (TN / 8)) * 8;
-          u32x4 v = *reinterpret_cast<const u32x4*>(
-              pages + static_cast<int64_t>(pv.page_ids[e.b_off + min(j, rank - 1) * ppr + p]) * h + off + c);
-          *reinterpret_cast<u32x4*>(&B_s[j * BLD + c]) = (j < rank) ? v : u32x4{0u, 0u, 0u, 0u};
+          put_b(j, c, *reinterpret_cast<const u32x4*>(
+                          pages + static_cast<int64_t>(pv.page_ids[e.b_off + min(j, rank - 1) * ppr + p]) * h +
+                          off + c));
         }
       }
       __syncthreads();
 
+      // Y^T[col][token] += B^T[col][j] T^T[j][token] on v_mfma_f32_32x32x16_bf16: A = B^T
+      // (lane -> column l%32 of the wave's 32, j = 8(l/32)..+8), B = one part of T^T (lane ->
+      // token l%32 or 32 + l%32, same j), K = 16 per step
       f32x16 acc0 = {}, acc1 = {};
-      for (int kk = 0; kk < r2; kk += 2) {
-        const int kr = kk + kh;
-        const float a = static_cast<float>(B_s[kr * BLD + wave * 32 + l32]);   // B^T[col][k]
-        const float b0 = T_s[l32 * TLD + kr];                                  // T^T[k][token]
-        const float b1 = T_s[(32 + l32) * TLD + kr];
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b0, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b1, acc1, 0, 0, 0);
+#pragma unroll 1
+      for (int kk = 0; kk < rk; kk += 16) {
+        const int j0 = kk + 8 * kh;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&BT_s[(wave * 32 + l32) * LD + j0]);
+#pragma unroll
+        for (int part = 0; part < 3; ++part) {
+          const __bf16* tp = T3_s + part * kTileTokens * LD;
+          const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(&tp[l32 * LD + j0]);
+          const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(&tp[(32 + l32) * LD + j0]);
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc1, 0, 0, 0);
+        }
       }
       // epilogue in LDS: lane l, register 4i+j: column 32w + 8i + 4(l/32) + j, token l%32 (+32)
       const float s = e.scale;
