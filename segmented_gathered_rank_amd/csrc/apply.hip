@@ -69,14 +69,24 @@ unsigned grid_of(int32_t bound) {
   return static_cast<unsigned>((bound + 7) / 8 * 8);
 }
 
-// Grid of the GEMV kernels over `max_units` units: a multiple of 8*kUnitRun,
-// the period of their unit-to-workgroup map, at most kMaxGrid.
-unsigned gemv_grid_of(int32_t max_units) {
+// Grid of the GEMV kernels over at most `units` units: a multiple of
+// 8*kUnitRun, the period of their unit-to-workgroup map, and at most
+// kGemvMaxGrid (4 workgroups per CU fill the chip; more units loop).  A
+// launch that finds no units costs about one dispatch of its grid.
+constexpr int kGemvMaxGrid = 1024;
+unsigned gemv_grid_of(int32_t units) {
   constexpr int period = 8 * kUnitRun;
-  static_assert(kMaxGrid % period == 0, "the grid cap must be a whole number of periods");
-  if (max_units < 1) max_units = 1;
-  if (max_units > kMaxGrid) max_units = kMaxGrid;
-  return static_cast<unsigned>((max_units + period - 1) / period * period);
+  static_assert(kGemvMaxGrid % period == 0, "the grid cap must be a whole number of periods");
+  if (units < 1) units = 1;
+  if (units > kGemvMaxGrid) units = kGemvMaxGrid;
+  return static_cast<unsigned>((units + period - 1) / period * period);
+}
+
+// Upper bound of the units of segments shorter than kLongMin tokens: one
+// such segment per slot at most, each of at most ceil((kLongMin-1)/kUnitTokens) units.
+int32_t max_short_units_of(const lora_segments* seg) {
+  const int64_t by_slots = static_cast<int64_t>(seg->n_slots) * ((kLongMin - 1 + kUnitTokens - 1) / kUnitTokens);
+  return static_cast<int32_t>(by_slots < seg->max_units ? by_slots : seg->max_units);
 }
 
 GemvArgs gemv_args(const lora_pool* p, int32_t module0, const SegView& sv, int32_t units_word) {
@@ -117,7 +127,8 @@ lora_status launch_shrink(const lora_pool* p, int32_t module0, int32_t n_modules
   g.t = t;
   g.ld_t = ld_t;
   g.mst = mst;
-  hipLaunchKernelGGL((k_gemv<1, TI, TI>), dim3(gemv_grid_of(seg->max_units), n_modules), dim3(kGemvThreads), 0, s, g);
+  const int32_t gemv_units = use_mfma ? max_short_units_of(seg) : seg->max_units;   // what units_word can count
+  hipLaunchKernelGGL((k_gemv<1, TI, TI>), dim3(gemv_grid_of(gemv_units), n_modules), dim3(kGemvThreads), 0, s, g);
   if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
   if constexpr (sizeof(TI) == 2) {
     if (use_mfma && seg->max_tiles > 0) {
@@ -203,7 +214,8 @@ lora_status launch_expand(const lora_pool* p, int32_t module0, int32_t n_modules
   g.y = y;
   g.ld_y = ld_y;
   g.msy = msy;
-  hipLaunchKernelGGL((k_gemv<2, TI, TO>), dim3(gemv_grid_of(seg->max_units), n_modules), dim3(kGemvThreads), 0, s, g);
+  const int32_t gemv_units = use_mfma ? max_short_units_of(seg) : seg->max_units;   // what units_word can count
+  hipLaunchKernelGGL((k_gemv<2, TI, TO>), dim3(gemv_grid_of(gemv_units), n_modules), dim3(kGemvThreads), 0, s, g);
   if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
   if constexpr (sizeof(TI) == 2) {
     if (use_mfma && seg->max_tiles > 0) {
