@@ -5,6 +5,8 @@
 // the pool is bf16 and its page and output widths tile evenly.  Both work
 // lists come from the segment builder and stay on the device; grids are sized
 // by their upper bounds and idle workgroups exit at once.
+#include <algorithm>
+
 #include "gemv_kernels.hpp"
 #include "mfma_kernels.hpp"
 #include "pool.hpp"
@@ -95,6 +97,7 @@ GemvArgs gemv_args(const lora_pool* p, int32_t module0, const SegView& sv, int32
   g.sv = sv;
   g.module0 = module0;
   g.units_word = units_word;
+  g.parts = 1;
   g.h_in = static_cast<int32_t>(p->h_in[module0]);
   g.h_out = static_cast<int32_t>(p->h_out[module0]);
   g.magic = static_cast<uint32_t>(((uint64_t(1) << 32) + p->page_elems - 1) / p->page_elems);
@@ -128,7 +131,9 @@ lora_status launch_shrink(const lora_pool* p, int32_t module0, int32_t n_modules
   g.ld_t = ld_t;
   g.mst = mst;
   const int32_t gemv_units = use_mfma ? max_short_units_of(seg) : seg->max_units;   // what units_word can count
-  hipLaunchKernelGGL((k_gemv<1, TI, TI>), dim3(gemv_grid_of(gemv_units), n_modules), dim3(kGemvThreads), 0, s, g);
+  g.parts = (p->max_rank + kPartRows - 1) / kPartRows;   // a work item per 16 rank rows of a unit
+  hipLaunchKernelGGL((k_gemv<1, TI, TI>), dim3(gemv_grid_of(gemv_units * g.parts), n_modules), dim3(kGemvThreads), 0,
+                     s, g);
   if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
   if constexpr (sizeof(TI) == 2) {
     if (use_mfma && seg->max_tiles > 0) {
@@ -215,7 +220,11 @@ lora_status launch_expand(const lora_pool* p, int32_t module0, int32_t n_modules
   g.ld_y = ld_y;
   g.msy = msy;
   const int32_t gemv_units = use_mfma ? max_short_units_of(seg) : seg->max_units;   // what units_word can count
-  hipLaunchKernelGGL((k_gemv<2, TI, TO>), dim3(gemv_grid_of(gemv_units), n_modules), dim3(kGemvThreads), 0, s, g);
+  // a work item per column range of at least 64 quads, as many ranges as 16-row blocks of rank
+  const int32_t col_ranges = static_cast<int32_t>(p->h_out[module0] / 4 / 64);
+  g.parts = std::max(1, std::min((p->max_rank + kPartRows - 1) / kPartRows, col_ranges));
+  hipLaunchKernelGGL((k_gemv<2, TI, TO>), dim3(gemv_grid_of(gemv_units * g.parts), n_modules), dim3(kGemvThreads), 0,
+                     s, g);
   if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
   if constexpr (sizeof(TI) == 2) {
     if (use_mfma && seg->max_tiles > 0) {

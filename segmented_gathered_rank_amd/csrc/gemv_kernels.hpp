@@ -54,6 +54,7 @@ constexpr int kXSliceBytes = 32768;                 // LDS for the staged x rows
 constexpr int kShrinkBatch = LORA_SHRINK_BATCH;     // 16-byte chunks of a row in flight per lane
 constexpr int kShrinkRows = LORA_SHRINK_ROWS;       // rank rows a wave streams at once
 constexpr int kUnitRun = LORA_UNIT_RUN;             // consecutive units one XCD takes (a power of 2)
+constexpr int kPartRows = 16;                       // rank rows per work item of the shrink-only kernel
 template <typename TI>
 constexpr int kExpandBatch = sizeof(TI) == 2 ? LORA_EXPAND_BATCH : 8;   // rank rows of B in flight per thread
 
@@ -128,7 +129,7 @@ __device__ __forceinline__ void stage_x(const TI* __restrict__ x, int64_t ld_x, 
 template <typename TI, int NT, bool KEEP>
 __device__ __forceinline__ void shrink_unit(const TI* __restrict__ x, int64_t ld_x, UnitLds& L, int nt,
                                             const TI* __restrict__ pages, int pid0, int32_t h, uint32_t magic,
-                                            int32_t h_in, int32_t rank, TI* xs) {
+                                            int32_t h_in, int32_t j_begin, int32_t j_end, TI* xs) {
   constexpr int S = XSlice<TI>::kElems;
   constexpr int CE = 16 / sizeof(TI);  // elements per 16-byte chunk
   constexpr int SR = kShrinkRows;      // rank rows a wave streams at once
@@ -143,7 +144,7 @@ __device__ __forceinline__ void shrink_unit(const TI* __restrict__ x, int64_t ld
   auto row_bases = [&](int jw, int p, const TI* (&base)[SR]) {
 #pragma unroll
     for (int q = 0; q < SR; ++q) {
-      const int j = min(jw + kGemvWaves * q, rank - 1);   // rows past the rank repeat the last
+      const int j = min(jw + kGemvWaves * q, j_end - 1);  // rows past the range repeat its last
       const int pid = __builtin_amdgcn_readfirstlane(L.pid[pid0 + j * ppr + p]);
       base[q] = pages + (static_cast<int64_t>(pid) - p) * h;
     }
@@ -194,8 +195,8 @@ __device__ __forceinline__ void shrink_unit(const TI* __restrict__ x, int64_t ld
     stage_x(x, ld_x, L.toks, nt, 0, h_in, xs);
     __syncthreads();
   }
-  // wave w streams rows j0 + w + kGemvWaves*q for q < SR
-  for (int j0 = 0; j0 < rank; j0 += kGemvWaves * SR) {
+  // wave w streams rows j0 + w + kGemvWaves*q for q < SR, rank rows [j_begin, j_end)
+  for (int j0 = j_begin; j0 < j_end; j0 += kGemvWaves * SR) {
     const int jw = j0 + wave;
     for (int sl = 0; sl < n_slices; ++sl) {
       const int k0 = sl * S;
@@ -205,7 +206,7 @@ __device__ __forceinline__ void shrink_unit(const TI* __restrict__ x, int64_t ld
         stage_x(x, ld_x, L.toks, nt, k0, len, xs);
         __syncthreads();
       }
-      if (jw >= rank) continue;          // wave-uniform
+      if (jw >= j_end) continue;         // wave-uniform
       // pages of the rows that overlap [k0, k0+len): one base address per row for the whole wave
       for (int p = k0 / h; p * h < k0 + len; ++p) {
         const int kp0 = max(k0, p * h), kp1 = min(k0 + len, (p + 1) * h);
@@ -217,12 +218,12 @@ __device__ __forceinline__ void shrink_unit(const TI* __restrict__ x, int64_t ld
         }
       }
     }
-    if (jw < rank) {
+    if (jw < j_end) {
       const float r = wave_transpose_reduce<V>(acc, lane);
       const int idx = lane / G;
       const int q = idx / NT, tb = idx - q * NT;
       const int j = jw + kGemvWaves * q;
-      if ((lane % G) == 0 && j < rank && tb < nt) L.t[tb * kMaxRank + j] = r;
+      if ((lane % G) == 0 && j < j_end && tb < nt) L.t[tb * kMaxRank + j] = r;
     }
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0.f;
@@ -233,7 +234,7 @@ __device__ __forceinline__ void shrink_unit(const TI* __restrict__ x, int64_t ld
 template <typename TI, typename TO, int NT, bool KEEP>
 __device__ __forceinline__ void expand_unit(TO* __restrict__ y, int64_t ld_y, const UnitLds& L, int nt,
                                             const TI* __restrict__ pages, int pid0, int32_t h, uint32_t magic,
-                                            int32_t h_out, int32_t rank, float scale) {
+                                            int32_t h_out, int32_t rank, float scale, int q_begin, int q_end) {
   constexpr int EB = kExpandBatch<TI>; // rank rows of B in flight
   const int n_quads = h_out >> 2;
   const int ppr = h_out / h;
@@ -245,7 +246,8 @@ __device__ __forceinline__ void expand_unit(TO* __restrict__ y, int64_t ld_y, co
   // of 256 they lie in one page, so each rank row has one base address for
   // the wave and every load needs one 32-bit lane offset.
   const bool wave_page = (h % 256) == 0;
-  for (int c0 = threadIdx.x; c0 < n_quads; c0 += kGemvThreads) {
+  (void)n_quads;
+  for (int c0 = q_begin + threadIdx.x; c0 < q_end; c0 += kGemvThreads) {
     const int kq = c0 << 2;
     int p = page_of(kq, magic, ppr);
     if (wave_page) p = __builtin_amdgcn_readfirstlane(p);
@@ -329,6 +331,7 @@ struct GemvArgs {
   SegView sv;
   int32_t module0;
   int32_t units_word;   // meta word holding the unit count to process
+  int32_t parts;        // work items per unit (1 for MODE 0): rank-row blocks (MODE 1) or column ranges (MODE 2)
   int32_t h_in, h_out;
   uint32_t magic;       // reciprocal of the page size
   const void* x;
@@ -357,10 +360,15 @@ __global__ __launch_bounds__(kGemvThreads, 4) void k_gemv(GemvArgs a) {
   const int2* units = reinterpret_cast<const int2*>(a.sv.units);
   // the unit count and this workgroup's first record travel together
   const int n_units = a.sv.meta[a.units_word];
-  int u = unit_of_block(blockIdx.x, m);
-  int2 rec = units[min(u, a.sv.max_units - 1)];
-  for (; u < n_units; u += gridDim.x) {
-    if (u >= static_cast<int>(gridDim.x)) rec = units[u];
+  // work item it = unit * parts + part; high-rank units of the two-kernel path split into parts
+  // so that a unit's serial batches spread over several workgroups
+  const int parts = a.parts;
+  const int n_items = n_units * parts;
+  int it = unit_of_block(blockIdx.x, m);
+  int2 rec = units[min(it / parts, a.sv.max_units - 1)];
+  for (; it < n_items; it += gridDim.x) {
+    const int u = it / parts, part = it - u * parts;
+    if (it >= static_cast<int>(gridDim.x)) rec = units[u];
     const int slot = rec.x & 0xffff, nt = (rec.x >> 16) & 0xff, pos = rec.y;
     const bool keep = (rec.x >> 24) & 1;
     const int ei = slot * a.pv.n_modules + a.module0 + m;
@@ -368,8 +376,13 @@ __global__ __launch_bounds__(kGemvThreads, 4) void k_gemv(GemvArgs a) {
     const int32_t* ids = a.pv.page_ids + static_cast<int64_t>(ei) * a.pv.ppe;
     unit_prologue(a.sv, (MODE == 2) ? ids + a.pv.max_rank * ppr_a : ids, pos, nt, ids_a + ids_b, L);
     if (e.rank <= 0) continue;
+    // rank rows of this part (shrink-only kernel) or all of them
+    const int j_begin = (MODE == 1) ? part * kPartRows : 0;
+    const int j_end = (MODE == 1) ? min(e.rank, j_begin + kPartRows) : e.rank;
+    if (j_begin >= j_end) continue;       // uniform: this part has no rows of this rank
     if constexpr (MODE != 2) {
-#define LORA_SHRINK_CALL(N, K) shrink_unit<TI, N, K>(xm, a.ld_x, L, nt, pages, 0, h, a.magic, a.h_in, e.rank, xs)
+#define LORA_SHRINK_CALL(N, K) \
+  shrink_unit<TI, N, K>(xm, a.ld_x, L, nt, pages, 0, h, a.magic, a.h_in, j_begin, j_end, xs)
       if (keep) {
         if (nt == 1) LORA_SHRINK_CALL(1, true);
         else if (nt == 2) LORA_SHRINK_CALL(2, true);
@@ -382,8 +395,9 @@ __global__ __launch_bounds__(kGemvThreads, 4) void k_gemv(GemvArgs a) {
 #undef LORA_SHRINK_CALL
     }
     if constexpr (MODE == 1) {
-      for (int i = threadIdx.x; i < nt * e.rank; i += kGemvThreads) {
-        const int tb = i / e.rank, j = i - tb * e.rank;
+      const int nr = j_end - j_begin;
+      for (int i = threadIdx.x; i < nt * nr; i += kGemvThreads) {
+        const int tb = i / nr, j = j_begin + (i - tb * nr);
         tm[static_cast<int64_t>(L.toks[tb]) * a.ld_t + j] = L.t[tb * kMaxRank + j];
       }
     }
@@ -395,8 +409,14 @@ __global__ __launch_bounds__(kGemvThreads, 4) void k_gemv(GemvArgs a) {
       __syncthreads();
     }
     if constexpr (MODE != 1) {
+      // column quads of this part: ranges of whole waves (64 quads), the last one ragged
+      const int n_quads = a.h_out >> 2;
+      const int per = (MODE == 2) ? ((n_quads + parts - 1) / parts + 63) / 64 * 64 : n_quads;
+      const int q_begin = (MODE == 2) ? part * per : 0;
+      const int q_end = min(n_quads, q_begin + per);
+      if (q_begin >= q_end) continue;     // uniform
 #define LORA_EXPAND_CALL(N, K) \
-  expand_unit<TI, TO, N, K>(ym, a.ld_y, L, nt, pages, ids_a, h, a.magic, a.h_out, e.rank, e.scale)
+  expand_unit<TI, TO, N, K>(ym, a.ld_y, L, nt, pages, ids_a, h, a.magic, a.h_out, e.rank, e.scale, q_begin, q_end)
       if (keep) {
         if (nt == 1) LORA_EXPAND_CALL(1, true);
         else if (nt == 2) LORA_EXPAND_CALL(2, true);
