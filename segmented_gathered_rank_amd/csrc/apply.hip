@@ -16,6 +16,10 @@ using namespace lora;
 namespace {
 
 constexpr int kMaxGrid = 4096;   // persistent grids loop over work beyond this
+#ifndef LORA_SHRINK_WG_TARGET
+#define LORA_SHRINK_WG_TARGET 512
+#endif
+constexpr int kShrinkWgTarget = LORA_SHRINK_WG_TARGET;   // matrix-core shrink: split K below this many workgroups
 
 SegView seg_view(const lora_segments* s) {
   SegView v;
@@ -142,7 +146,7 @@ lora_status launch_shrink(const lora_pool* p, int32_t module0, int32_t n_modules
       const int32_t per_wg = shared ? n_modules : 1;
       // enough workgroups for 256 CUs: split K when tiles alone are too few
       const int32_t est_tiles = (seg->n_tokens + kTileTokens - 1) / kTileTokens;
-      int32_t ks = 512 / (est_tiles * groups > 0 ? est_tiles * groups : 1);
+      int32_t ks = kShrinkWgTarget / (est_tiles * groups > 0 ? est_tiles * groups : 1);
       if (ks > kMaxSplits) ks = kMaxSplits;
       if (ks > h_in / 256) ks = h_in / 256;
       if (ks < 1) ks = 1;

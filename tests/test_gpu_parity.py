@@ -274,6 +274,35 @@ def test_c3_reduced_mixed_paths():
         dw.close()
 
 
+def test_c3_delta_tight_fp32_output_matrix_cores():
+    """y0 = 0 in fp32 on a batch whose long segments run on the matrix cores: the
+    bf16 MFMA expand multiplies by t itself (t as three exact bf16 parts), so the
+    adapter term matches the oracle at fp32 accuracy."""
+    wl = W.c3_sgmv_prefill(h=512, units=(2, 8), total_units=32)
+    assert max(wl.notes["segment_lengths"]) >= 64
+    for mode in ("sgmv", "bgmv"):
+        dw = DeviceWorkload(wl, y_dtype="f32")
+        dw.zero_y()
+        dw.sgmv_step() if mode == "sgmv" else dw.bgmv_step()
+        torch.cuda.synchronize()
+        for m in range(4):
+            got = from_device(dw.y_of(m)).astype(np.float64)
+            assert rel_l2(got, lo.lora_delta(wl, m)) <= 1e-5, (mode, m)
+        dw.close()
+
+
+def test_wide_rows_in_several_pages():
+    """h = 8192 (the GEMV shrink stages x in two slices) with pages of 2048
+    elements (four pages per adapter row), on both GEMV paths."""
+    import dataclasses
+    wl = dataclasses.replace(W.c2_bgmv_decode(h=8192, n_tokens=24, n_slots=8), page_elems=2048)
+    say("wide rows, 4 pages per row")
+    for mode in ("bgmv", "sgmv"):
+        dw, ys = run(wl, mode)
+        assert_close(ys[0], lo.apply_to_y0(wl, 0), "bf16", f"wide {mode}")
+        dw.close()
+
+
 def test_c3_t_tight():
     wl = W.c3_sgmv_prefill(h=512, units=(2, 8), total_units=32)
     dw = DeviceWorkload(wl)
