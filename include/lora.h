@@ -171,7 +171,7 @@ typedef struct {
     int32_t *meta;       /* [LORA_META_WORDS]                                                      */
     int32_t *units;      /* [2 * max_units] GEMV units: (slot + 65536 * tokens + 2^24 * [segment  */
                          /* spans several units], position in perm)                               */
-    int32_t *tiles;      /* [2 * max_tiles] (segment, position in perm) per matrix-core tile       */
+    int32_t *tiles;      /* [2 * max_tiles] matrix-core tiles: (slot + 65536 * tokens, position)    */
     int32_t *work;       /* builder scratch of large batches (n_chunks > 0), else NULL             */
     int32_t n_tokens, n_slots, max_segs, max_units, max_tiles;
     int32_t n_chunks;    /* 0: one-workgroup build; else the large-batch build's token chunks      */

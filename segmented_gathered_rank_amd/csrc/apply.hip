@@ -30,6 +30,7 @@ SegView seg_view(const lora_segments* s) {
   v.units = s->units;
   v.tiles = s->tiles;
   v.max_units = s->max_units;
+  v.max_tiles = s->max_tiles;
   return v;
 }
 
@@ -73,6 +74,16 @@ unsigned grid_of(int32_t bound) {
   if (bound < 1) bound = 1;
   if (bound > kMaxGrid) bound = kMaxGrid;
   return static_cast<unsigned>((bound + 7) / 8 * 8);
+}
+
+// Grid of the matrix-core kernels over at most `max_tiles` tiles: a multiple of
+// 8*kTileRun, the period of their tile-to-workgroup map, at most kMaxGrid.
+unsigned tile_grid_of(int32_t max_tiles) {
+  constexpr int period = 8 * kTileRun;
+  static_assert(kMaxGrid % period == 0, "the grid cap must be a whole number of periods");
+  if (max_tiles < 1) max_tiles = 1;
+  if (max_tiles > kMaxGrid) max_tiles = kMaxGrid;
+  return static_cast<unsigned>((max_tiles + period - 1) / period * period);
 }
 
 // Grid of the GEMV kernels over at most `units` units: a multiple of
@@ -180,7 +191,7 @@ lora_status launch_shrink(const lora_pool* p, int32_t module0, int32_t n_modules
       const size_t lds = static_cast<size_t>(per_wg) * a.ldr * (kc + 8) * 2 +
                          static_cast<size_t>(per_wg) * a.max_pids * 4;
       a.part = ks > 1 ? static_cast<float*>(ws) : nullptr;
-      const dim3 grid(grid_of(seg->max_tiles), ks, groups), block(kMfmaThreads);
+      const dim3 grid(tile_grid_of(seg->max_tiles), ks, groups), block(kMfmaThreads);
       const int ntiles = a.ldr <= 16 ? 1 : a.ldr <= 32 ? 2 : 4;
 #define LORA_SHRINK_LAUNCH(M, NT) hipLaunchKernelGGL((k_shrink_mfma<M, NT>), grid, block, lds, s, a)
 #define LORA_SHRINK_NT(M)                                 \
@@ -199,7 +210,7 @@ lora_status launch_shrink(const lora_pool* p, int32_t module0, int32_t n_modules
 #undef LORA_SHRINK_LAUNCH
       if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
       if (ks > 1) {
-        hipLaunchKernelGGL(k_shrink_reduce, dim3(grid_of(seg->max_tiles), n_modules), block, 0, s, a);
+        hipLaunchKernelGGL(k_shrink_reduce, dim3(tile_grid_of(seg->max_tiles), n_modules), block, 0, s, a);
         if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
       }
     }
@@ -245,9 +256,9 @@ lora_status launch_expand(const lora_pool* p, int32_t module0, int32_t n_modules
         lds_allowed = lds;
       }
       const int32_t col_groups = (h_out / kExpandCols + kExpandBlocks - 1) / kExpandBlocks;
-      hipLaunchKernelGGL((k_expand_mfma<TO>), dim3(grid_of(seg->max_tiles), col_groups, n_modules),
+      hipLaunchKernelGGL((k_expand_mfma<TO>), dim3(tile_grid_of(seg->max_tiles), col_groups, n_modules),
                          dim3(kMfmaThreads), lds, s, pv, module0, sv, t, ld_t, mst, static_cast<TO*>(y), ld_y, msy,
-                         h_out, ldr);
+                         h_out, ldr, static_cast<int32_t>(p->max_rank * (p->h_in[module0] / p->page_elems)));
       if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
     }
   }

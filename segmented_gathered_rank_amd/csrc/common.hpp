@@ -45,6 +45,7 @@ struct SegView {
   const int32_t* units;
   const int32_t* tiles;
   int32_t max_units;
+  int32_t max_tiles;
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -175,33 +176,20 @@ __device__ __forceinline__ float wave_transpose_reduce(float (&v)[64], int lane)
   return s;
 }
 
-// Work distribution over the 8 XCDs.  Workgroups are dealt to the XCDs
-// round-robin (linear id mod 8) and each XCD has its own L2.  The n work items
-// (known only on the device) are cut into 8 contiguous shares, so consecutive
-// items (the pieces of one segment, which read the same adapter pages) meet
-// in one L2.  Share s goes to XCD (s + plane) % 8, plane being the
-// workgroup's (y, z) index: when n is not a multiple of 8 the short last
-// share lands on a different XCD for each module or split, so the XCDs
-// stay evenly loaded over a launch.
-// Usage: for (XcdIter it(n); it.valid(); it.next()) { int u = it.item; ... }
-// gridDim.x must be a multiple of 8.
-struct XcdIter {
-  int item, idx, per, n, step, xcd;
-  __device__ __forceinline__ explicit XcdIter(int n_items) {
-    n = n_items;
-    per = (n_items + 7) >> 3;
-    const int plane = static_cast<int>(blockIdx.y + gridDim.y * blockIdx.z);
-    xcd = static_cast<int>((blockIdx.x - plane) & 7);   // this workgroup's share
-    idx = static_cast<int>(blockIdx.x >> 3);
-    step = static_cast<int>(gridDim.x >> 3);
-    item = xcd * per + idx;
-  }
-  __device__ __forceinline__ bool valid() const { return idx < per && item < n; }
-  __device__ __forceinline__ void next() {
-    idx += step;
-    item = xcd * per + idx;
-  }
-};
+// Work item of workgroup bx of plane `plane` (a module or a split), in a grid
+// of a multiple of 8*R workgroups: runs of R consecutive items (mostly pieces
+// of one segment, so one adapter) stay on one XCD and its L2 (workgroup bx
+// runs on XCD bx % 8), the runs go round-robin over the XCDs, and the
+// round-robin starts one XCD further for each plane, so that the XCDs share
+// the items evenly whatever their count.  A bijection of [0, gridDim.x) that
+// does not depend on the item count, so a workgroup can read its work-list
+// record together with that count.
+template <int R>
+__device__ __forceinline__ int item_of_block(int bx, int plane) {
+  const int run = ((bx & 7) - plane) & 7, k = bx >> 3;
+  return (k / R) * (8 * R) + run * R + (k % R);
+}
+constexpr int kTileRun = 2;   // consecutive matrix-core tiles one XCD takes
 
 // Upper bounds of the segment work lists (host and device agree on them).
 __host__ __device__ inline int32_t max_segs_of(int32_t n_tokens, int32_t n_slots) {

@@ -313,18 +313,8 @@ __device__ __forceinline__ void unit_prologue(const SegView& sv, const int32_t* 
   __syncthreads();
 }
 
-// Unit of workgroup bx of module m, in a grid of a multiple of 8*kUnitRun
-// workgroups per module: runs of kUnitRun consecutive units (mostly one
-// segment, so one adapter) stay on one XCD and its L2 (workgroup bx runs on
-// XCD bx % 8), the runs go round-robin over the XCDs, and the round-robin
-// starts one XCD further for each module, so that the XCDs share the units
-// evenly whatever the unit count.  A bijection of [0, gridDim.x) that does
-// not depend on the unit count, so a workgroup can read its work-list
-// record at once.
-__device__ __forceinline__ int unit_of_block(int bx, int m) {
-  const int run = ((bx & 7) - m) & 7, k = bx >> 3;
-  return (k / kUnitRun) * (8 * kUnitRun) + run * kUnitRun + (k % kUnitRun);
-}
+// Unit of workgroup bx of module m (see item_of_block): runs of kUnitRun units per XCD.
+__device__ __forceinline__ int unit_of_block(int bx, int m) { return item_of_block<kUnitRun>(bx, m); }
 
 struct GemvArgs {
   PoolView pv;

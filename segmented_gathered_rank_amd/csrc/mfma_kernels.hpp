@@ -91,19 +91,27 @@ __global__ __launch_bounds__(kMfmaThreads) void k_shrink_mfma(ShrinkArgs a) {
   const int kq = (lane >> 4) * 8;        // this lane's k offset inside a 32-wide step
   const int mrow = wave * 16 + (lane & 15);
 
-  for (XcdIter it(n_tiles); it.valid(); it.next()) {
-    const int tile = it.item;
-    const int seg = a.sv.tiles[2 * tile], pos = a.sv.tiles[2 * tile + 1];
-    const int len = min(kTileTokens, a.sv.seg_start[seg + 1] - pos);
-    const int slot = a.sv.seg_slot[seg];
+  // the tile count and this workgroup's first tile record travel together; the
+  // entries, the A page ids (fixed table layout: rank row j, page p at j*ppr + p)
+  // and the token ids then load in one round trip
+  const int2* tiles = reinterpret_cast<const int2*>(a.sv.tiles);
+  int tile = item_of_block<kTileRun>(blockIdx.x, static_cast<int>(blockIdx.y + gridDim.y * blockIdx.z));
+  int2 rec = tiles[min(tile, a.sv.max_tiles - 1)];
+  const int n_ids = min(a.ldr, a.pv.max_rank) * ppr;
+  for (; tile < n_tiles; tile += gridDim.x) {
+    if (tile >= static_cast<int>(gridDim.x)) rec = tiles[tile];
+    const int slot = rec.x & 0xffff, len = rec.x >> 16, pos = rec.y;
     SlotEntry e[MODS];
 #pragma unroll
     for (int mi = 0; mi < MODS; ++mi) e[mi] = a.pv.entries[slot * a.pv.n_modules + a.module0 + grp * MODS + mi];
     __syncthreads();
     if (tid < kTileTokens) toks_s[tid] = tid < len ? a.sv.perm[pos + tid] : -1;
 #pragma unroll
-    for (int mi = 0; mi < MODS; ++mi)
-      for (int i = tid; i < e[mi].rank * ppr; i += kMfmaThreads) pid_s[mi * a.max_pids + i] = a.pv.page_ids[e[mi].a_off + i];
+    for (int mi = 0; mi < MODS; ++mi) {
+      const int32_t* ids =
+          a.pv.page_ids + static_cast<int64_t>(slot * a.pv.n_modules + a.module0 + grp * MODS + mi) * a.pv.ppe;
+      for (int i = tid; i < n_ids; i += kMfmaThreads) pid_s[mi * a.max_pids + i] = ids[i];
+    }
     __syncthreads();
     const int tok = toks_s[mrow];
     const __bf16* xrow = a.x + grp * a.msx + static_cast<int64_t>(tok < 0 ? 0 : tok) * a.ld_x + kq;
@@ -217,11 +225,12 @@ __global__ __launch_bounds__(kMfmaThreads) void k_shrink_reduce(ShrinkArgs a) {
   const int n_tiles = a.sv.meta[LORA_META_N_TILES];
   const int gm = blockIdx.y;                        // group * mods_per_wg + module in group
   const int64_t tile_block = static_cast<int64_t>(kTileTokens) * a.ldr;
-  for (XcdIter it(n_tiles); it.valid(); it.next()) {
-    const int tile = it.item;
-    const int seg = a.sv.tiles[2 * tile], pos = a.sv.tiles[2 * tile + 1];
-    const int len = min(kTileTokens, a.sv.seg_start[seg + 1] - pos);
-    const int slot = a.sv.seg_slot[seg];
+  const int2* tiles = reinterpret_cast<const int2*>(a.sv.tiles);
+  int tile = item_of_block<kTileRun>(blockIdx.x, static_cast<int>(blockIdx.y + gridDim.y * blockIdx.z));
+  int2 rec = tiles[min(tile, a.sv.max_tiles - 1)];
+  for (; tile < n_tiles; tile += gridDim.x) {
+    if (tile >= static_cast<int>(gridDim.x)) rec = tiles[tile];
+    const int slot = rec.x & 0xffff, len = rec.x >> 16, pos = rec.y;
     const int rank = a.pv.entries[slot * a.pv.n_modules + a.module0 + gm].rank;
     const float* pp = a.part + (static_cast<int64_t>(tile) * gridDim.y + gm) * a.ks_count * tile_block;
     float* tm = a.t + gm * a.mst;
@@ -261,7 +270,8 @@ template <typename TO>
 __global__ __launch_bounds__(kMfmaThreads, sizeof(TO) == 2 ? 3 : 2) void k_expand_mfma(PoolView pv, int32_t module0, SegView sv,
                                                                 const float* __restrict__ t, int64_t ld_t,
                                                                 int64_t mst, TO* __restrict__ y, int64_t ld_y,
-                                                                int64_t msy, int32_t h_out, int32_t ldr) {
+                                                                int64_t msy, int32_t h_out, int32_t ldr,
+                                                                int32_t b_ids_at) {
   constexpr int TN = kExpandCols;
   constexpr int YLD = TN + 16 / sizeof(TO);           // Y_s row stride (elements)
   constexpr int YCPR = TN * sizeof(TO) / 16;          // 16-byte chunks per y row of the block
@@ -274,6 +284,7 @@ __global__ __launch_bounds__(kMfmaThreads, sizeof(TO) == 2 ? 3 : 2) void k_expan
   __bf16* BT_s = T3_s + 3 * kTileTokens * LD;                                      // [TN][LD]
   TO* Y_s = reinterpret_cast<TO*>(BT_s + TN * LD);                                 // [64][YLD]
   __shared__ int32_t toks_s[kTileTokens];
+  __shared__ int32_t bids_s[kMaxEntryPages];   // B page ids of the tile's (slot, module): row j, page p at j*ppr + p
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = blockIdx.z;
@@ -285,18 +296,26 @@ __global__ __launch_bounds__(kMfmaThreads, sizeof(TO) == 2 ? 3 : 2) void k_expan
   const int ppr = h_out / h;
   const int l32 = lane & 31, kh = lane >> 5;
 
-  for (XcdIter it(n_tiles); it.valid(); it.next()) {
-    const int tile = it.item;
-    const int seg = sv.tiles[2 * tile], pos = sv.tiles[2 * tile + 1];
-    const int len = min(kTileTokens, sv.seg_start[seg + 1] - pos);
-    const int slot = sv.seg_slot[seg];
-    const SlotEntry e = pv.entries[slot * pv.n_modules + module0 + m];
-    if (e.rank <= 0) continue;
-    const int rank = e.rank;
-    const int rk = (rank + 15) & ~15;          // contraction length: rank rounded up to the MFMA's K
+  // the tile count and this workgroup's first tile record travel together; the
+  // entry, the B page ids (fixed table layout, from b_ids_at) and the token ids
+  // then load in one round trip, and t, y and the B rows in the next
+  const int2* tiles = reinterpret_cast<const int2*>(sv.tiles);
+  int tile = item_of_block<kTileRun>(blockIdx.x, static_cast<int>(blockIdx.y + gridDim.y * blockIdx.z));
+  int2 rec = tiles[min(tile, sv.max_tiles - 1)];
+  const int n_bids = pv.max_rank * ppr;
+  for (; tile < n_tiles; tile += gridDim.x) {
+    if (tile >= static_cast<int>(gridDim.x)) rec = tiles[tile];
+    const int slot = rec.x & 0xffff, len = rec.x >> 16, pos = rec.y;
+    const int ei = slot * pv.n_modules + module0 + m;
+    const SlotEntry e = pv.entries[ei];
+    const int32_t* bids = pv.page_ids + static_cast<int64_t>(ei) * pv.ppe + b_ids_at;
     __syncthreads();   // the previous tile is done with LDS
     if (tid < kTileTokens) toks_s[tid] = tid < len ? sv.perm[pos + tid] : -1;
+    for (int i = tid; i < n_bids; i += kMfmaThreads) bids_s[i] = bids[i];
     __syncthreads();
+    if (e.rank <= 0) continue;                 // uniform
+    const int rank = e.rank;
+    const int rk = (rank + 15) & ~15;          // contraction length: rank rounded up to the MFMA's K
     const int first = toks_s[0];
     // y block cb [64][TN]: coalesced 16-byte chunks, rows without a token read the first token's;
     // B block [rk <= 32 rows][TN] (bf16): rank row j, columns c0..c0+TN of that row
@@ -317,8 +336,8 @@ __global__ __launch_bounds__(kMfmaThreads, sizeof(TO) == 2 ? 3 : 2) void k_expan
       for (int q = 0; q < 2; ++q) {
         const int idx = min(tid + kMfmaThreads * q, rk * (TN / 8) - 1);
         const int j = idx / (TN / 8), c = (idx % (TN / 8)) * 8;
-        bq[q] = *reinterpret_cast<const u32x4*>(
-            pages + static_cast<int64_t>(pv.page_ids[e.b_off + min(j, rank - 1) * ppr + p]) * h + off + c);
+        bq[q] = *reinterpret_cast<const u32x4*>(pages + static_cast<int64_t>(bids_s[min(j, rank - 1) * ppr + p]) * h +
+                                                off + c);
       }
     };
     // B chunk (row j, columns c..c+7) into the transposed block, zero for rows past the rank
@@ -383,8 +402,7 @@ __global__ __launch_bounds__(kMfmaThreads, sizeof(TO) == 2 ? 3 : 2) void k_expan
         if (idx < rk * (TN / 8)) {
           const int j = idx / (TN / 8), c = (idx % (TN / 8)) * 8;
           put_b(j, c, *reinterpret_cast<const u32x4*>(
-                          pages + static_cast<int64_t>(pv.page_ids[e.b_off + min(j, rank - 1) * ppr + p]) * h +
-                          off + c));
+                          pages + static_cast<int64_t>(bids_s[min(j, rank - 1) * ppr + p]) * h + off + c));
         }
       }
       __syncthreads();

@@ -279,14 +279,14 @@ __device__ void layout_segments(const int32_t* total, int n_tokens, int n_slots,
       lm &= lm - 1;
       const int r = __builtin_amdgcn_readlane(run, src);
       const int slot = __builtin_amdgcn_readlane(s, src);
-      const int ssi = __builtin_amdgcn_readlane(off[1], src);
       const int sb = __builtin_amdgcn_readlane(off[0], src);
       const int u0 = long_at + __builtin_amdgcn_readlane(off[3], src);
       const int t0 = __builtin_amdgcn_readlane(off[4], src);
       const int lnu = (r + kUnitTokens - 1) / kUnitTokens;
       for (int u = lane; u < lnu; u += 64) units[u0 + u] = unit_record(slot, r, u, sb);
       const int ntl = (r + kTileTokens - 1) / kTileTokens;
-      for (int u = lane; u < ntl; u += 64) tiles[t0 + u] = make_int2(ssi, sb + u * kTileTokens);
+      for (int u = lane; u < ntl; u += 64)
+        tiles[t0 + u] = make_int2(slot + (min(kTileTokens, r - u * kTileTokens) << 16), sb + u * kTileTokens);
     }
     if (run > 0) {
       if (run >= kLongMin) {

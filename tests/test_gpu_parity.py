@@ -97,7 +97,7 @@ def _check_segments(ids, n_slots, st, meta, seg, arr):
         s0 = ref["seg_start"][k]
         if L >= lmin:
             exp_units += [unit(k, L, u) for u in range(0, L, ut)]
-            exp_tiles += [(k, s0 + u) for u in range(0, L, tt)]
+            exp_tiles += [(int(ref["seg_slot"][k]) + 65536 * min(tt, L - u), int(s0 + u)) for u in range(0, L, tt)]
     # the library's order: short-segment units, then long-segment units, each in segment order
     assert nus == len(short)
     assert list(map(tuple, units.tolist())) == exp_units
