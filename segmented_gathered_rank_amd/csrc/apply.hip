@@ -37,7 +37,9 @@ SegView seg_view(const lora_segments* s) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Checks shared by the apply calls.  `need_out` also checks equal h_out.
-lora_status check_call(const lora_pool* p, int32_t module0, int32_t n_modules, const lora_segments* seg) {
+// same_out: the call also needs equal h_out (expand and BGMV; the shrink only reads h_in).
+lora_status check_call(const lora_pool* p, int32_t module0, int32_t n_modules, const lora_segments* seg,
+                       bool same_out) {
   if (!p || !seg) return LORA_ERR_ARG;
   if (n_modules < 1 || module0 < 0 || module0 + n_modules > p->n_modules) return LORA_ERR_ARG;
   if (seg->n_tokens < 0 || seg->n_slots < 1 || seg->n_slots > p->n_slots) return LORA_ERR_ARG;
@@ -47,7 +49,7 @@ lora_status check_call(const lora_pool* p, int32_t module0, int32_t n_modules, c
   if (seg->max_units != max_units_of(seg->n_tokens, seg->n_slots) || seg->max_tiles != max_tiles_of(seg->n_tokens))
     return LORA_ERR_ARG;
   for (int32_t m = module0 + 1; m < module0 + n_modules; ++m) {
-    if (p->h_in[m] != p->h_in[module0] || p->h_out[m] != p->h_out[module0]) return LORA_ERR_SHAPE;
+    if (p->h_in[m] != p->h_in[module0] || (same_out && p->h_out[m] != p->h_out[module0])) return LORA_ERR_SHAPE;
   }
   return LORA_OK;
 }
@@ -291,7 +293,7 @@ size_t lora_shrink_workspace_bytes(const lora_pool* p, int32_t n_tokens, int32_t
 lora_status lora_shrink(const lora_pool* p, int32_t module0, int32_t n_modules, const void* x, int64_t ld_x,
                         int64_t module_stride_x, const lora_segments* seg, float* t, int64_t ld_t,
                         int64_t module_stride_t, void* ws, size_t ws_bytes, void* stream) {
-  lora_status st = check_call(p, module0, n_modules, seg);
+  lora_status st = check_call(p, module0, n_modules, seg, false);
   if (st != LORA_OK) return st;
   const int32_t n = seg->n_tokens;
   st = check_operand(x, ld_x, module_stride_x, p->h_in[module0], p->elem_bytes(), n, n_modules, false, true);
@@ -313,7 +315,7 @@ lora_status lora_shrink(const lora_pool* p, int32_t module0, int32_t n_modules, 
 lora_status lora_expand(const lora_pool* p, int32_t module0, int32_t n_modules, const float* t, int64_t ld_t,
                         int64_t module_stride_t, const lora_segments* seg, void* y, int64_t ld_y,
                         int64_t module_stride_y, lora_dtype ydtype, void* stream) {
-  lora_status st = check_call(p, module0, n_modules, seg);
+  lora_status st = check_call(p, module0, n_modules, seg, true);
   if (st != LORA_OK) return st;
   if (ydtype != LORA_F32 && ydtype != LORA_BF16) return LORA_ERR_DTYPE;
   const int32_t n = seg->n_tokens;
@@ -343,7 +345,7 @@ lora_status lora_expand(const lora_pool* p, int32_t module0, int32_t n_modules, 
 lora_status lora_apply_bgmv(const lora_pool* p, int32_t module0, int32_t n_modules, const void* x, int64_t ld_x,
                             int64_t module_stride_x, const lora_segments* seg, void* y, int64_t ld_y,
                             int64_t module_stride_y, lora_dtype ydtype, void* stream) {
-  lora_status st = check_call(p, module0, n_modules, seg);
+  lora_status st = check_call(p, module0, n_modules, seg, true);
   if (st != LORA_OK) return st;
   if (ydtype != LORA_F32 && ydtype != LORA_BF16) return LORA_ERR_DTYPE;
   const int32_t n = seg->n_tokens;

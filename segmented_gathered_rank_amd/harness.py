@@ -73,11 +73,20 @@ class DeviceWorkload:
                 e += 1
             self.groups.append((m, e))
             m = e
-        self.y, self.t = [], []
+        self.y = []
         for (m0, m1) in self.groups:
-            y = torch.empty((m1 - m0, n, mods[m0].h_out), dtype=ydt, device=self.dev)
-            self.y.append(y)
-            self.t.append(torch.zeros((m1 - m0, n, self.ld_t), dtype=torch.float32, device=self.dev))
+            self.y.append(torch.empty((m1 - m0, n, mods[m0].h_out), dtype=ydt, device=self.dev))
+        # shrink groups: consecutive modules with equal h_in, one shrink call each (t of all
+        # modules is one tensor, so any run of modules has a uniform t stride)
+        self.in_groups: List[Tuple[int, int]] = []
+        m = 0
+        while m < len(mods):
+            e = m + 1
+            while e < len(mods) and mods[e].h_in == mods[m].h_in:
+                e += 1
+            self.in_groups.append((m, e))
+            m = e
+        self.t = torch.zeros((len(mods), n, self.ld_t), dtype=torch.float32, device=self.dev)
         self.reset_y()
 
         self.pool = None
@@ -122,10 +131,7 @@ class DeviceWorkload:
         raise IndexError(module)
 
     def t_of(self, module: int) -> torch.Tensor:
-        for gi, (m0, m1) in enumerate(self.groups):
-            if m0 <= module < m1:
-                return self.t[gi][module - m0]
-        raise IndexError(module)
+        return self.t[module]
 
     # ---------------------------------------------------------------- calls
     def _x_runs(self, m0: int, m1: int):
@@ -155,20 +161,20 @@ class DeviceWorkload:
 
     def shrink(self, stream=None):
         mods = self.wl.modules
-        for gi, (m0, m1) in enumerate(self.groups):
+        t = self.t
+        for (m0, m1) in self.in_groups:
             h_in = mods[m0].h_in
-            t = self.t[gi]
             for (a, b, xo, msx) in self._x_runs(m0, m1):
-                tp = t.data_ptr() + (a - m0) * t.stride(0) * 4
-                lora_shrink(self.pool, a, b - a, self._xp(xo), h_in, msx, self.seg, tp, self.ld_t, t.stride(0),
+                lora_shrink(self.pool, a, b - a, self._xp(xo), h_in, msx, self.seg, t[a], self.ld_t, t.stride(0),
                             self.ws, self.ws_bytes, stream)
 
     def expand(self, stream=None):
         ydt = LORA_BF16 if self.y_dtype == "bf16" else LORA_F32
         mods = self.wl.modules
+        t = self.t
         for gi, (m0, m1) in enumerate(self.groups):
-            y, t = self.y[gi], self.t[gi]
-            lora_expand(self.pool, m0, m1 - m0, t, self.ld_t, t.stride(0), self.seg, y, mods[m0].h_out,
+            y = self.y[gi]
+            lora_expand(self.pool, m0, m1 - m0, t[m0], self.ld_t, t.stride(0), self.seg, y, mods[m0].h_out,
                         y.stride(0), ydt, stream)
 
     def bgmv(self, stream=None):
