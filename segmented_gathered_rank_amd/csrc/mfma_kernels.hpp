@@ -234,17 +234,37 @@ __global__ __launch_bounds__(kMfmaThreads) void k_shrink_reduce(ShrinkArgs a) {
     const int rank = a.pv.entries[slot * a.pv.n_modules + a.module0 + gm].rank;
     const float* pp = a.part + (static_cast<int64_t>(tile) * gridDim.y + gm) * a.ks_count * tile_block;
     float* tm = a.t + gm * a.mst;
-    for (int idx = threadIdx.x; idx < len * rank; idx += kMfmaThreads) {
-      const int r = idx / rank, j = idx - r * rank;
-      float part[kMaxSplits];
+    // items: (token row r, 4 rank columns from 4q); two items per thread at a time, with
+    // every split's 16-byte load of both in flight together
+    const int nq = (rank + 3) >> 2;
+    const int n_items = len * nq;
+    constexpr int U = 2;
+    for (int i0 = threadIdx.x; i0 < n_items; i0 += U * kMfmaThreads) {
+      f32x4 part[U][kMaxSplits];
 #pragma unroll
-      for (int q = 0; q < kMaxSplits; ++q)    // all splits' loads in flight together
-        part[q] = pp[min(q, a.ks_count - 1) * tile_block + r * a.ldr + j];
-      float sum = 0.f;
+      for (int u = 0; u < U; ++u) {
+        const int idx = min(i0 + u * kMfmaThreads, n_items - 1);
+        const int r = idx / nq, j = (idx - r * nq) * 4;
 #pragma unroll
-      for (int q = 0; q < kMaxSplits; ++q)
-        if (q < a.ks_count) sum += part[q];
-      tm[static_cast<int64_t>(a.sv.perm[pos + r]) * a.ld_t + j] = sum;
+        for (int q = 0; q < kMaxSplits; ++q)
+          part[u][q] = *reinterpret_cast<const f32x4*>(pp + min(q, a.ks_count - 1) * tile_block + r * a.ldr + j);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int idx = i0 + u * kMfmaThreads;
+        if (idx >= n_items) continue;
+        const int r = idx / nq, j = (idx - r * nq) * 4;
+        f32x4 sum = part[u][0];
+#pragma unroll
+        for (int q = 1; q < kMaxSplits; ++q)
+          if (q < a.ks_count) sum += part[u][q];   // splits added in order
+        float* dst = tm + static_cast<int64_t>(a.sv.perm[pos + r]) * a.ld_t + j;
+        if (j + 4 <= rank) {
+          *reinterpret_cast<f32x4*>(dst) = sum;
+        } else {                                    // columns past the rank are not written
+          for (int e = 0; e < rank - j; ++e) dst[e] = sum[e];
+        }
+      }
     }
   }
 }
