@@ -61,9 +61,15 @@ struct ShrinkArgs {
   float* part;                // [tiles][groups][mods_per_wg][ks_count][64][ldr]
 };
 
-constexpr int kShrinkSteps = 16;   // 32-wide k steps of x prefetched per lane
-constexpr int kMaxSplits = 8;      // K splits of the shrink at most
-constexpr int kStageBatch = 8;     // 16-byte chunks of A each thread loads at once when staging
+#ifndef LORA_SHRINK_STEPS
+#define LORA_SHRINK_STEPS 16
+#endif
+#ifndef LORA_STAGE_BATCH
+#define LORA_STAGE_BATCH 8
+#endif
+constexpr int kShrinkSteps = LORA_SHRINK_STEPS;   // 32-wide k steps of x prefetched per lane
+constexpr int kMaxSplits = 8;                     // K splits of the shrink at most
+constexpr int kStageBatch = LORA_STAGE_BATCH;     // 16-byte chunks of A each thread loads at once when staging
 
 // Shrink tile: 64 tokens x one K split, for mods_per_wg modules.  Per K
 // sub-chunk the adapter's A rows (all modules) are staged in LDS once and read
