@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 3
+#define LORA_ABI_VERSION 4
 
 typedef int32_t lora_status;
 enum {
@@ -250,6 +250,36 @@ lora_status lora_apply_bgmv(const lora_pool *p, int32_t module0, int32_t n_modul
                             const lora_segments *seg,
                             void *y, int64_t ld_y, int64_t module_stride_y, lora_dtype ydtype,
                             void *stream);
+
+/* Base product and adapter term in one matrix-core pass, for batches whose
+ * tokens come in runs of one adapter, such as prefills (study page, "The
+ * kernel trick: gather, do not merge": one shared base matmul plus each
+ * token's low-rank update, whose cost is about 2r/d of the base):
+ *   y_i[c] = round(sum_k x_i[k] W[k][c] + scale_a * sum_{j<rank_a} t_i[j] B_a[j][c]),
+ *   t_i[j] = sum_k x_i[k] A_a[j][k],
+ * with a = ids[i]; a token whose id is -1, outside [0, n_slots) or of an
+ * empty slot gets x_i W alone.  Unlike the other apply calls, y is written,
+ * not added to: the call computes the base product itself.
+ *   module: pool module whose adapters apply; h_in, h_out are its widths.
+ *   x [n_tokens][ld_x] bf16, 16-byte aligned rows.
+ *   w [h_out][ld_w] bf16: W transposed, row c holds the weights of output
+ *     column c (the row-major layout of a linear layer's weight), 16-byte
+ *     aligned rows.
+ *   ids [n_tokens] int32 per-token slot ids, or NULL for x W alone.  Ids are
+ *     read in token order; no segment build is needed.
+ *   y [n_tokens][ld_y] bf16, 8-byte aligned rows; written for every token.
+ * Tiles of 256 tokens x 256 columns run on bf16 MFMA with fp32
+ * accumulation; each element of y is rounded once.  The adapter part of a
+ * tile costs about 16/256 of its base part per 16 rank rows of each
+ * distinct adapter among its 256 tokens, so batches whose tiles mix many
+ * adapters (decode) belong on lora_apply_bgmv after a plain GEMM.
+ * The pool must be bf16 and h_in / page_elems at most 32.
+ * Errors: ARG (null pointer, bad module, n_tokens < 0, a leading dimension
+ * below the width, misalignment), DTYPE (pool not bf16), SHAPE, HIP. */
+lora_status lora_fused_gemm(const lora_pool *p, int32_t module,
+                            const void *x, int64_t ld_x, const void *w, int64_t ld_w,
+                            const int32_t *ids, int32_t n_tokens,
+                            void *y, int64_t ld_y, void *stream);
 
 #ifdef __cplusplus
 }

@@ -20,7 +20,7 @@ __all__ = [
     "lora_pool_load", "lora_pool_evict", "lora_pool_stats", "lora_pool_read",
     "lora_segments_bytes", "lora_segments_bind", "lora_build_segments",
     "lora_segments_check", "lora_shrink_workspace_bytes", "lora_shrink",
-    "lora_expand", "lora_apply_bgmv",
+    "lora_expand", "lora_apply_bgmv", "lora_fused_gemm",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblora_mi355x.so")
@@ -91,6 +91,7 @@ _SIGS = {
     "lora_shrink": (_I32, [_P, _I32, _I32, _P, _I64, _I64, _SEGP, _P, _I64, _I64, _P, _SZ, _P]),
     "lora_expand": (_I32, [_P, _I32, _I32, _P, _I64, _I64, _SEGP, _P, _I64, _I64, _I32, _P]),
     "lora_apply_bgmv": (_I32, [_P, _I32, _I32, _P, _I64, _I64, _SEGP, _P, _I64, _I64, _I32, _P]),
+    "lora_fused_gemm": (_I32, [_P, _I32, _P, _I64, _P, _I64, _P, _I32, _P, _I64, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -235,3 +236,9 @@ def lora_apply_bgmv(pool: int, module0: int, n_modules: int, x, ld_x: int, modul
                     stream=None) -> None:
     _check(_lib.lora_apply_bgmv(pool, module0, n_modules, _ptr(x), ld_x, module_stride_x, ctypes.byref(seg),
                                 _ptr(y), ld_y, module_stride_y, ydtype, _stream(stream)), "lora_apply_bgmv")
+
+
+def lora_fused_gemm(pool: int, module: int, x, ld_x: int, w, ld_w: int, ids, n_tokens: int, y, ld_y: int,
+                    stream=None) -> None:
+    _check(_lib.lora_fused_gemm(pool, module, _ptr(x), ld_x, _ptr(w), ld_w, _ptr(ids), n_tokens, _ptr(y), ld_y,
+                                _stream(stream)), "lora_fused_gemm")

@@ -7,6 +7,7 @@
 // by their upper bounds and idle workgroups exit at once.
 #include <algorithm>
 
+#include "fused_gemm.hpp"
 #include "gemv_kernels.hpp"
 #include "mfma_kernels.hpp"
 #include "pool.hpp"
@@ -370,6 +371,49 @@ lora_status lora_apply_bgmv(const lora_pool* p, int32_t module0, int32_t n_modul
                                       module_stride_y, s);
   return launch_bgmv<float, float>(p, module0, n_modules, x, ld_x, module_stride_x, seg, y, ld_y, module_stride_y,
                                    s);
+}
+
+lora_status lora_fused_gemm(const lora_pool* p, int32_t module, const void* x, int64_t ld_x, const void* w,
+                            int64_t ld_w, const int32_t* ids, int32_t n_tokens, void* y, int64_t ld_y,
+                            void* stream) {
+  if (!p || module < 0 || module >= p->n_modules || n_tokens < 0) return LORA_ERR_ARG;
+  if (p->dtype != LORA_BF16) return LORA_ERR_DTYPE;
+  const int64_t h_in = p->h_in[module], h_out = p->h_out[module];
+  if (h_in / p->page_elems > kFgMaxPpr || p->n_slots > kFgMaxSlots) return LORA_ERR_SHAPE;
+  if (!x || !w || !y) return LORA_ERR_ARG;
+  if (ld_x < h_in || ld_w < h_in || ld_y < h_out) return LORA_ERR_ARG;
+  // a tile's 256 rows of x or W^T are addressed with 32-bit byte offsets
+  if (ld_x > (int64_t(1) << 22) || ld_w > (int64_t(1) << 22)) return LORA_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(w) || (ld_x * 2) % 16 != 0 || (ld_w * 2) % 16 != 0) return LORA_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(y) & 7u) != 0 || (ld_y * 2) % 8 != 0) return LORA_ERR_ARG;
+  if (n_tokens == 0) return LORA_OK;
+  DeviceGuard g(p->device);
+  if (!g.ok) return LORA_ERR_HIP;
+  FusedArgs fa{};
+  fa.pv = p->view();
+  fa.x = static_cast<const __bf16*>(x);
+  fa.w = static_cast<const __bf16*>(w);
+  fa.ids = ids;
+  fa.y = static_cast<__bf16*>(y);
+  fa.ld_x = ld_x;
+  fa.ld_w = ld_w;
+  fa.ld_y = ld_y;
+  fa.n = n_tokens;
+  fa.h_in = static_cast<int32_t>(h_in);
+  fa.h_out = static_cast<int32_t>(h_out);
+  fa.module = module;
+  const int64_t n_rt = (static_cast<int64_t>(n_tokens) + kFgBM - 1) / kFgBM;
+  fa.n_ct = static_cast<int32_t>((h_out + kFgBN - 1) / kFgBN);
+  const int64_t tiles = n_rt * fa.n_ct;
+  if (tiles > (int64_t(1) << 30)) return LORA_ERR_SHAPE;
+  fa.n_tiles = static_cast<int32_t>(tiles);
+  const unsigned grid = static_cast<unsigned>((tiles + 7) / 8 * 8);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (ids)
+    hipLaunchKernelGGL((k_fused_gemm<true>), dim3(grid), dim3(kFgThreads), 0, s, fa);
+  else
+    hipLaunchKernelGGL((k_fused_gemm<false>), dim3(grid), dim3(kFgThreads), 0, s, fa);
+  return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
 }  // extern "C"

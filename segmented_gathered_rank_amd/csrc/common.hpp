@@ -35,6 +35,7 @@ struct PoolView {
   int32_t n_modules;
   int32_t max_rank;           // rank cap of the pool
   int32_t ppe;                // page-table words per (slot, module): A's ids, then B's from max_rank*ppr_a
+  int32_t zero_page;          // a page of zeros (index n_pages)
 };
 
 struct SegView {

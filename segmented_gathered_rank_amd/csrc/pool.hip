@@ -140,12 +140,15 @@ lora_status lora_pool_create(lora_pool** out, int32_t device, lora_dtype wdtype,
   const size_t ab = ((static_cast<size_t>(max_rank) * (max_in + max_out) * eb) + 255) / 256 * 256;
   p->staging_bytes = ab + static_cast<size_t>(max_ppe) * 4 + 256;
   const size_t n_entries = static_cast<size_t>(n_slots) * n_modules;
-  bool ok = hipMalloc(&p->d_pages, static_cast<size_t>(n_pages) * page_elems * eb) == hipSuccess &&
+  // one page past the allocator's: all zeros, read by kernels in place of rows an adapter does not have
+  const size_t page_bytes = static_cast<size_t>(page_elems) * eb;
+  bool ok = hipMalloc(&p->d_pages, static_cast<size_t>(n_pages + 1) * page_bytes) == hipSuccess &&
             hipMalloc(reinterpret_cast<void**>(&p->d_entries), n_entries * sizeof(SlotEntry)) == hipSuccess &&
             hipMalloc(reinterpret_cast<void**>(&p->d_page_ids),
                       static_cast<size_t>(table > 0 ? table : 1) * 4) == hipSuccess &&
             hipMalloc(&p->d_staging, p->staging_bytes) == hipSuccess;
-  ok = ok && fill_zero(p->d_entries, n_entries * sizeof(SlotEntry), nullptr) &&
+  ok = ok && fill_zero(static_cast<char*>(p->d_pages) + static_cast<size_t>(n_pages) * page_bytes, page_bytes, nullptr) &&
+       fill_zero(p->d_entries, n_entries * sizeof(SlotEntry), nullptr) &&
        fill_zero(p->d_page_ids, static_cast<size_t>(table) * 4, nullptr) &&
        hipDeviceSynchronize() == hipSuccess;
   if (!ok) {

@@ -42,6 +42,7 @@ struct lora_pool {
     v.n_slots = n_slots;
     v.n_modules = n_modules;
     v.max_rank = max_rank;
+    v.zero_page = static_cast<int32_t>(n_pages);
     v.ppe = max_pages_per_entry;
     return v;
   }

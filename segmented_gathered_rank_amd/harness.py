@@ -15,7 +15,7 @@ from typing import List, Optional, Tuple
 import numpy as np
 import torch
 
-from . import (LORA_BF16, LORA_F32, lora_apply_bgmv, lora_build_segments, lora_expand,
+from . import (LORA_BF16, LORA_F32, lora_apply_bgmv, lora_build_segments, lora_expand, lora_fused_gemm,
                lora_pool_create, lora_pool_destroy, lora_pool_load, lora_segments_bind,
                lora_segments_bytes, lora_shrink, lora_shrink_workspace_bytes)
 
@@ -186,6 +186,23 @@ class DeviceWorkload:
                 yp = y.data_ptr() + (a - m0) * y.stride(0) * y.element_size()
                 lora_apply_bgmv(self.pool, a, b - a, self._xp(xo), mods[m0].h_in, msx, self.seg, yp,
                                 mods[m0].h_out, y.stride(0), ydt, stream)
+
+    def upload_weights(self):
+        """W^T of every module ([h_out][h_in], the layout lora_fused_gemm reads)."""
+        self.wT = []
+        for m in range(len(self.wl.modules)):
+            W = self.wl.W[m]
+            self.wT.append(None if W is None else to_device(np.ascontiguousarray(W.T), self.wl.dtype, self.dev))
+
+    def fused(self, stream=None, adapters: bool = True, modules=None):
+        """y = x W (+ the adapter term) per module in one lora_fused_gemm call each."""
+        mods = self.wl.modules
+        if not hasattr(self, "wT"):
+            self.upload_weights()
+        for m in (range(len(mods)) if modules is None else modules):
+            h_in, h_out = mods[m].h_in, mods[m].h_out
+            lora_fused_gemm(self.pool, m, self._xp(self.x_off[mods[m].x_group]), h_in, self.wT[m], h_in,
+                            self.ids if adapters else None, self.n, self.y_of(m), h_out, stream)
 
     def sgmv_step(self, stream=None):
         self.build_segments(stream)

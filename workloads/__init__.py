@@ -36,7 +36,7 @@ import numpy as np
 __all__ = [
     "Module", "Workload", "to_bf16_bits", "zipf_ids", "finite_zipf_cdf",
     "c0_worked_example", "c1_tiny_f32", "c2_bgmv_decode", "c3_sgmv_prefill",
-    "c4_mixed_rank", "c5_encoder_step", "fingerprint_rank1", "integer_exact",
+    "c4_mixed_rank", "c5_encoder_step", "fused_tiles", "fingerprint_rank1", "integer_exact",
     "BY_NAME",
 ]
 
@@ -319,6 +319,34 @@ def c5_encoder_step(seed: int = 5, n_seq: int = 128, seq_len: int = 256,
                                   [[rank] * 4] * n_slots, [2.0] * n_slots,
                                   1.0, 0.02, 0.02, draw_w)
     return Workload("c5_encoder_step", "bf16", h, n_slots, mods, ids, xs, y0, Ws, ad)
+
+
+# --------------------------------------------------------------------------
+# fused base + adapter tiles
+# --------------------------------------------------------------------------
+def fused_tiles(seed: int = 14, h_in: int = 320, h_out: int = 384, page: int = 64,
+                decode_tokens: int = 88) -> Workload:
+    """Small bf16 workload for the fused base-plus-adapter path: tiles of 256
+    tokens with a ragged last tile, a ragged last column tile (384 = 256 + 128),
+    12 slots of ranks 1..64 in 64-element pages (several 16-row units per
+    adapter), and three token regions:
+      tokens   0..255: one run of slot 1 (rank 16);
+      tokens 256..511: runs of slot 3 (rank 32) x 100, id -1 x 30, slot 5
+                       (rank 64) x 60, slot 0 (rank 8) x 66;
+      tokens 512..   : per-token ids uniform over {-1, 0..11, 12} (12 is out
+                       of range), like decode tokens.
+    x ~ N(0,1); W ~ N(0, 0.005) so that the adapter term is a large share of
+    y; A, B ~ N(0, 0.02); scale 32/r; bf16."""
+    rng = np.random.default_rng(seed)
+    ranks = [8, 16, 24, 32, 48, 64, 16, 16, 5, 1, 40, 16]
+    n_slots = len(ranks)
+    ids = np.concatenate([
+        np.full(256, 1), np.full(100, 3), np.full(30, -1), np.full(60, 5), np.full(66, 0),
+        rng.integers(-1, n_slots + 1, size=decode_tokens)]).astype(np.int32)
+    mods = [Module("proj", h_in, h_out, 0)]
+    xs, Ws, ad, y0 = _draw_values(rng, "bf16", ids.shape[0], mods, 1, [[r] for r in ranks],
+                                  [32.0 / r for r in ranks], 1.0, 0.005, 0.02)
+    return Workload("fused_tiles", "bf16", page, n_slots, mods, ids, xs, y0, Ws, ad)
 
 
 # --------------------------------------------------------------------------
