@@ -38,7 +38,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="bgmv_decode_x128",
-                    choices=["bgmv_decode_x128", "bgmv_decode", "sgmv_prefill", "mixed_rank", "encoder_step"])
+                    choices=["bgmv_decode_x128", "bgmv_decode", "sgmv_prefill", "mixed_rank", "encoder_step",
+                             "encoder_fused", "prefill_fused"])
     ap.add_argument("--path", choices=["auto", "bgmv", "sgmv"], default="auto",
                     help="force the fused BGMV or the shrink+expand path (default: the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -71,12 +72,22 @@ def make_workload(name):
     if name == "mixed_rank":
         return W.c4_mixed_rank(draw_w=False), "sgmv", {
             "workload": "mixed_rank", "tokens": 1072, "ranks": "8/16/32/64", "slots": 64, "h": 4096}
+    if name == "encoder_fused":
+        return W.c5_encoder_step(), "fused", {
+            "workload": "encoder_fused", "tokens": 32768, "slots": 1024, "rank": 16,
+            "modules": "qkv 768->2304, o 768->768, up 768->3072, down 3072->768",
+            "step": "y = x W + adapter term per module, one lora_fused_gemm call each"}
+    if name == "prefill_fused":
+        return W.c3_sgmv_prefill(), "fused", {
+            "workload": "prefill_fused", "tokens": 4096, "segments": 8, "h": 4096, "rank": 16,
+            "modules": "q,k,v,o (q,k,v share x)",
+            "step": "y = x W + adapter term per module, one lora_fused_gemm call each"}
     return W.c5_encoder_step(draw_w=False), "sgmv", {
         "workload": "encoder_step", "tokens": 32768, "slots": 1024, "rank": 16,
         "modules": "qkv 768->2304, o 768->768, up 768->3072, down 3072->768"}
 
 
-KERNEL_SOURCES = ["common.hpp", "gemv_kernels.hpp", "mfma_kernels.hpp", "apply.hip", "segments.hip"]
+KERNEL_SOURCES = ["common.hpp", "gemv_kernels.hpp", "mfma_kernels.hpp", "fused_gemm.hpp", "apply.hip", "segments.hip"]
 
 
 def kernel_source_sha():
@@ -159,26 +170,36 @@ def copy_gbps(mib=1024, reps=10):
 
 def base_gemm_ms(wl, reps=10):
     """The shared base products y0 = x W of every module (bf16, hipBLASLt through
-    torch.matmul) on random data of the workload's shapes: the denominator of the
+    torch.matmul into preallocated outputs) on random data of the workload's
+    shapes, the faster of the two weight layouts: the denominator of the
     adapter overhead.  Not part of the library or of the timed step."""
     import torch
     g = torch.Generator(device="cuda").manual_seed(0)
-    ops = [(torch.randn(wl.n_tokens, m.h_in, device="cuda", dtype=torch.bfloat16, generator=g),
-            torch.randn(m.h_in, m.h_out, device="cuda", dtype=torch.bfloat16, generator=g)) for m in wl.modules]
-    for x, w in ops:
-        torch.matmul(x, w)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(reps):
-        for x, w in ops:
-            torch.matmul(x, w)
-    b.record()
-    torch.cuda.synchronize()
     flops = sum(2.0 * wl.n_tokens * m.h_in * m.h_out for m in wl.modules)
-    ms = a.elapsed_time(b) / reps
-    del ops
-    return ms, flops
+    best = None
+    for transposed in (False, True):   # W stored [h_in][h_out], or as a linear layer's [h_out][h_in]
+        ops = []
+        for m in wl.modules:
+            x = torch.randn(wl.n_tokens, m.h_in, device="cuda", dtype=torch.bfloat16, generator=g)
+            if transposed:
+                w = torch.randn(m.h_out, m.h_in, device="cuda", dtype=torch.bfloat16, generator=g).t()
+            else:
+                w = torch.randn(m.h_in, m.h_out, device="cuda", dtype=torch.bfloat16, generator=g)
+            ops.append((x, w, torch.empty(wl.n_tokens, m.h_out, device="cuda", dtype=torch.bfloat16)))
+        for x, w, y in ops:
+            torch.matmul(x, w, out=y)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            for x, w, y in ops:
+                torch.matmul(x, w, out=y)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        best = ms if best is None else min(best, ms)
+        del ops
+    return best, flops
 
 
 def cpu_baseline(wl, seconds):
@@ -197,6 +218,61 @@ def cpu_baseline(wl, seconds):
     return {"value": wl.n_tokens * steps / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{steps} whole step(s): {wl.n_tokens} tokens x {wl.n_modules} modules, fp64 "
                       f"per-token loop, {el:.1f} s on one core (BLAS threads = 1)"}
+
+
+def fused_work(wl):
+    """Algorithmic flops and bytes of one fused step: every module's base
+    product (x read, W read, y written once) plus its adapter term (each
+    distinct adapter's A and B pages read once)."""
+    import numpy as np
+    flops = byts = 0
+    used = sorted(set(int(i) for i in np.unique(wl.ids) if 0 <= i < wl.n_slots))
+    for m, mod in enumerate(wl.modules):
+        n = wl.n_tokens
+        flops += 2.0 * n * mod.h_in * mod.h_out
+        byts += 2 * (n * mod.h_in + mod.h_in * mod.h_out + n * mod.h_out)
+        for i in range(n):
+            a = wl.adapters[int(wl.ids[i])][m] if 0 <= wl.ids[i] < wl.n_slots else None
+            if a is not None:
+                flops += 2.0 * a[0] * (mod.h_in + mod.h_out)
+        for s in used:
+            a = wl.adapters[s][m]
+            if a is not None:
+                byts += 2 * a[0] * (mod.h_in + mod.h_out)
+    return flops, byts
+
+
+def cpu_baseline_fused(wl, seconds):
+    """The oracle, untouched, on one core: y = x W + adapter term for whole
+    tokens (all modules) of the workload, 64 tokens at a time, until `seconds`."""
+    from threadpoolctl import threadpool_limits
+    from oracle import lora_oracle as lo
+    done, t0 = 0, time.perf_counter()
+    with threadpool_limits(1):
+        while done < wl.n_tokens:
+            toks = range(done, min(wl.n_tokens, done + 64))
+            for m in range(wl.n_modules):
+                lo.lora_forward(wl, m, toks)
+            done += len(toks)
+            if time.perf_counter() - t0 >= seconds:
+                break
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"the first {done} of {wl.n_tokens} tokens x {wl.n_modules} modules, fp64 per-token "
+                      f"x W plus adapter term, {el:.1f} s on one core (BLAS threads = 1)"}
+
+
+def time_ms(fn, reps=10):
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
 
 
 def main():
@@ -221,12 +297,18 @@ def main():
     stream = torch.cuda.current_stream()
     work = accounting.step_work(wl, fused=(mode == "bgmv"))
 
+    if mode == "fused":
+        dw.upload_weights()
+
     def step(ev=None):
-        dw.build_segments()
+        if mode != "fused":
+            dw.build_segments()
         if ev is not None:
             ev[0].record(stream)
         if mode == "bgmv":
             dw.bgmv()
+        elif mode == "fused":
+            dw.fused()
         else:
             dw.shrink()
             dw.expand()
@@ -279,6 +361,34 @@ def main():
         extra["single_module_call_us"] = float(np.median(lat) * 1e3)
         extra["single_module_bytes"] = work["per_module"][0]["bytes"]
         extra["single_module_GBps"] = work["per_module"][0]["bytes"] / (np.median(lat) * 1e-3) / 1e9
+
+    if mode == "fused":
+        flops, byts = fused_work(wl)
+        tf = flops / (kern_avg * 1e-3) / 1e12
+        base_ours = time_ms(lambda: dw.fused(adapters=False))
+        gms, _ = base_gemm_ms(wl)
+        unfused = time_ms(lambda: dw.sgmv_step())
+        extra = {"fused_ms_mean": kern_avg, "fused_ms_min": float(np.min(kern_ms)), "flops_per_step": flops,
+                 "algorithmic_bytes_per_step": byts, "arith_intensity_flop_per_byte": round(flops / byts, 1),
+                 "base_only_ms": round(base_ours, 4), "adapter_overhead_in_kernel": round(kern_avg / base_ours - 1, 4),
+                 "hipblaslt_base_ms": round(gms, 4), "unfused_lora_step_ms": round(unfused, 4),
+                 "hipblaslt_plus_unfused_ms": round(gms + unfused, 4),
+                 "fused_over_hipblaslt_plus_unfused": round(kern_avg / (gms + unfused), 4),
+                 "fused_over_hipblaslt_base": round(kern_avg / gms, 4)}
+        roofline = {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": load_traffic(args.workload),
+                    "kernel": "k_fused_gemm", "flops_per_launch_set": flops}
+        out = {
+            "metric": METRIC, "value": round(wl.n_tokens / (ms_step * 1e-3), 1), "unit": "tokens/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic", "config": config, "roofline": roofline, "extra": extra,
+        }
+        dw.close()
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline_fused(wl, args.cpu_seconds)
+        print(json.dumps(out), flush=True)
+        return
 
     bound_bytes = work["bytes"]
     achieved = bound_bytes / (kern_avg * 1e-3) / 1e9
