@@ -281,6 +281,58 @@ lora_status lora_fused_gemm(const lora_pool *p, int32_t module,
                             const int32_t *ids, int32_t n_tokens,
                             void *y, int64_t ld_y, void *stream);
 
+/* ---- Adapter tiers: GPU slots <- host memory <- cold store ----------------
+ * Study page "Multi-LoRA Serving", section "Memory: slots, tiers and paging"
+ * and its cache simulation: the engine keeps a fixed number of adapters in
+ * GPU slots, a larger least-recently-used set in host memory (a swap is then
+ * a PCIe copy, not a download), and loads the rest from a cold store.
+ * Policy per request for adapter id a (a >= 0; adapter ids are the caller's,
+ * slot ids are the pool's):
+ *   GPU tier, least recently used order: a hit refreshes a; a miss gives a
+ *   the lowest free slot, else the slot of the least recently used adapter,
+ *   which leaves the GPU tier;
+ *   host tier, consulted only on a GPU miss, same rule: a hit is a host copy
+ *   (LORA_TIER_HOST), a miss a cold load (LORA_TIER_COLD).
+ * The state is host-side and not thread-safe: one caller at a time. */
+typedef struct lora_tiers lora_tiers;   /* opaque, library-owned */
+enum { LORA_TIER_GPU = 0, LORA_TIER_HOST = 1, LORA_TIER_COLD = 2 };
+
+/* Cold store callback: writes adapter `adapter`'s rows for `module` into A
+ * ([*rank][h_in], room for max_rank rows) and B ([*rank][h_out]) in the
+ * pool's dtype, and sets *rank (0 = no adapter for this module) and *scale.
+ * Returns 0 on success; anything else fails the acquire with LORA_ERR_ARG. */
+typedef int32_t (*lora_fetch_fn)(void *ctx, int32_t adapter, int32_t module, int32_t *rank, float *scale,
+                                 void *A, void *B);
+
+/* gpu_slots >= 1 (the pool's n_slots when used with lora_tiers_acquire),
+ * host_slots >= 0.  Errors: ARG. */
+lora_status lora_tiers_create(lora_tiers **out, int32_t gpu_slots, int32_t host_slots);
+/* Frees the tiers and their host buffers.  Waits for nothing: no upload from
+ * them may be pending (synchronize the acquire streams first). */
+lora_status lora_tiers_destroy(lora_tiers *t);
+/* Policy only: n requests in order.  [host] out arrays, each optional:
+ * tier[i], slot[i] (GPU slot after the request), evicted[i] (adapter that
+ * left the GPU tier, -1 none).  Errors: ARG (negative id). */
+lora_status lora_tiers_touch(lora_tiers *t, const int32_t *ids, int32_t n,
+                             int32_t *tier, int32_t *slot, int32_t *evicted);
+/* [host] counts since creation. */
+lora_status lora_tiers_stats(const lora_tiers *t, int64_t *gpu_hits, int64_t *host_hits, int64_t *cold_loads);
+/* [host] *slot = GPU slot of adapter id, -1 if not resident. */
+lora_status lora_tiers_slot_of(const lora_tiers *t, int32_t id, int32_t *slot);
+/* The policy driving a pool for one batch of n requests ([host] ids, [host]
+ * slots out, the slot id to give the apply kernels for each request).  For
+ * each GPU miss: the displaced adapter is evicted from the slot and the new
+ * adapter's A and B rows of every module are uploaded to it on `stream`,
+ * asynchronously, straight from page-locked host buffers that the tiers own
+ * (allocated on the first acquire: host_slots x all modules at max_rank);
+ * a cold load first calls fetch to fill the buffer.  Kernels of the batch go
+ * on the same stream after the call.  All modules of a slot change together.
+ * Errors: ARG (bad id, no host tier, another pool), SLOT (more distinct
+ * adapters in the batch than slots), RANK, NO_PAGES, HIP; after an error the
+ * tiers may disagree with the pool: destroy both. */
+lora_status lora_tiers_acquire(lora_tiers *t, lora_pool *p, const int32_t *ids, int32_t n,
+                               lora_fetch_fn fetch, void *ctx, int32_t *slots, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

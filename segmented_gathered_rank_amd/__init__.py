@@ -21,6 +21,8 @@ __all__ = [
     "lora_segments_bytes", "lora_segments_bind", "lora_build_segments",
     "lora_segments_check", "lora_shrink_workspace_bytes", "lora_shrink",
     "lora_expand", "lora_apply_bgmv", "lora_fused_gemm",
+    "LORA_TIER_GPU", "LORA_TIER_HOST", "LORA_TIER_COLD", "lora_tiers_create", "lora_tiers_destroy",
+    "lora_tiers_touch", "lora_tiers_stats", "lora_tiers_slot_of", "lora_tiers_acquire",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblora_mi355x.so")
@@ -92,6 +94,12 @@ _SIGS = {
     "lora_expand": (_I32, [_P, _I32, _I32, _P, _I64, _I64, _SEGP, _P, _I64, _I64, _I32, _P]),
     "lora_apply_bgmv": (_I32, [_P, _I32, _I32, _P, _I64, _I64, _SEGP, _P, _I64, _I64, _I32, _P]),
     "lora_fused_gemm": (_I32, [_P, _I32, _P, _I64, _P, _I64, _P, _I32, _P, _I64, _P]),
+    "lora_tiers_create": (_I32, [ctypes.POINTER(_P), _I32, _I32]),
+    "lora_tiers_destroy": (_I32, [_P]),
+    "lora_tiers_touch": (_I32, [_P, _P, _I32, _P, _P, _P]),
+    "lora_tiers_stats": (_I32, [_P, ctypes.POINTER(_I64), ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
+    "lora_tiers_slot_of": (_I32, [_P, _I32, ctypes.POINTER(_I32)]),
+    "lora_tiers_acquire": (_I32, [_P, _P, _P, _I32, _P, _P, _P, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -242,3 +250,80 @@ def lora_fused_gemm(pool: int, module: int, x, ld_x: int, w, ld_w: int, ids, n_t
                     stream=None) -> None:
     _check(_lib.lora_fused_gemm(pool, module, _ptr(x), ld_x, _ptr(w), ld_w, _ptr(ids), n_tokens, _ptr(y), ld_y,
                                 _stream(stream)), "lora_fused_gemm")
+
+
+# ------------------------------------------------------------------ adapter tiers
+LORA_TIER_GPU, LORA_TIER_HOST, LORA_TIER_COLD = 0, 1, 2
+LORA_FETCH_FN = ctypes.CFUNCTYPE(_I32, _P, _I32, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_F), _P, _P)
+
+
+def lora_tiers_create(gpu_slots: int, host_slots: int) -> int:
+    out = _P()
+    _check(_lib.lora_tiers_create(ctypes.byref(out), gpu_slots, host_slots), "lora_tiers_create")
+    return out.value
+
+
+def lora_tiers_destroy(tiers: int) -> None:
+    _check(_lib.lora_tiers_destroy(tiers), "lora_tiers_destroy")
+
+
+def lora_tiers_touch(tiers: int, ids):
+    """Policy only: returns (tier, slot, evicted) int32 arrays, one entry per request."""
+    import numpy as np
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    n = ids.shape[0]
+    tier, slot, ev = (np.empty(n, np.int32) for _ in range(3))
+    _check(_lib.lora_tiers_touch(tiers, _ptr(ids), n, _ptr(tier), _ptr(slot), _ptr(ev)), "lora_tiers_touch")
+    return tier, slot, ev
+
+
+def lora_tiers_stats(tiers: int) -> dict:
+    g, h, c = _I64(), _I64(), _I64()
+    _check(_lib.lora_tiers_stats(tiers, ctypes.byref(g), ctypes.byref(h), ctypes.byref(c)), "lora_tiers_stats")
+    return {"gpu_hits": g.value, "host_hits": h.value, "cold_loads": c.value}
+
+
+def lora_tiers_slot_of(tiers: int, adapter: int) -> int:
+    s = _I32()
+    _check(_lib.lora_tiers_slot_of(tiers, adapter, ctypes.byref(s)), "lora_tiers_slot_of")
+    return s.value
+
+
+def lora_tiers_acquire(tiers: int, pool: int, ids, fetch, stream=None):
+    """One batch through the tiers: returns the slot id of each request (int32
+    array) after scheduling the uploads of GPU misses on `stream`.  fetch(adapter,
+    module) -> None (no adapter for that module) or (rank, scale, A, B) with A
+    [rank][h_in] and B [rank][h_out] host arrays in the pool's storage dtype
+    (bf16 as uint16 bits)."""
+    import numpy as np
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    n = ids.shape[0]
+    slots = np.empty(n, np.int32)
+    errors = []
+
+    def _cb(ctx, adapter, module, rank, scale, a_ptr, b_ptr):
+        try:
+            got = fetch(int(adapter), int(module))
+            if got is None:
+                rank[0] = 0
+                scale[0] = 0.0
+                return 0
+            r, s, A, B = got
+            A = np.ascontiguousarray(A)
+            B = np.ascontiguousarray(B)
+            ctypes.memmove(a_ptr, A.ctypes.data, A.nbytes)
+            ctypes.memmove(b_ptr, B.ctypes.data, B.nbytes)
+            rank[0] = int(r)
+            scale[0] = float(s)
+            return 0
+        except Exception as e:  # reported after the call returns
+            errors.append(e)
+            return 1
+
+    cb = LORA_FETCH_FN(_cb)
+    st = _lib.lora_tiers_acquire(tiers, pool, _ptr(ids), n, ctypes.cast(cb, _P), None, _ptr(slots),
+                                 _stream(stream))
+    if errors:
+        raise errors[0]
+    _check(st, "lora_tiers_acquire")
+    return slots

@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "liblora_mi355x.so")
-SOURCES = ["pool.hip", "segments.hip", "apply.hip"]
+SOURCES = ["pool.hip", "segments.hip", "apply.hip", "tiers.hip"]
 ARCH = "gfx950"
 
 

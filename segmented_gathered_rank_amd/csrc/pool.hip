@@ -15,10 +15,12 @@ using namespace lora;
 
 namespace {
 
-// Copies one upload (A rows then B rows, contiguous in `src`) into its pages
-// and publishes the slot-table entry.  One workgroup per page.
+// Copies one upload (A's rank rows from src_a, B's from src_b, page by page)
+// into its pages and publishes the slot-table entry.  One workgroup per page.
+// The sources may be device memory or page-locked host memory.
 template <typename T>
-__global__ __launch_bounds__(256) void k_upload(T* __restrict__ pages, const T* __restrict__ src,
+__global__ __launch_bounds__(256) void k_upload(T* __restrict__ pages, const T* __restrict__ src_a,
+                                                const T* __restrict__ src_b,
                                                 const int32_t* __restrict__ plist, int32_t n_plist,
                                                 int64_t page_elems, int32_t* __restrict__ page_ids,
                                                 int32_t ids_off, int32_t n_a, int32_t b_gap,
@@ -26,7 +28,8 @@ __global__ __launch_bounds__(256) void k_upload(T* __restrict__ pages, const T* 
   const int32_t piece = blockIdx.x;
   if (piece >= n_plist) return;
   const int32_t page = plist[piece];
-  const T* s = src + static_cast<int64_t>(piece) * page_elems;
+  const T* s = piece < n_a ? src_a + static_cast<int64_t>(piece) * page_elems
+                           : src_b + static_cast<int64_t>(piece - n_a) * page_elems;
   T* d = pages + static_cast<int64_t>(page) * page_elems;
   constexpr int kVec = 16 / sizeof(T);
   for (int64_t e = static_cast<int64_t>(threadIdx.x) * kVec; e < page_elems; e += 256 * kVec) {
@@ -71,6 +74,45 @@ void free_device(lora_pool* p) {
 }
 
 }  // namespace
+
+lora_status pool_upload_async(lora_pool* p, int32_t slot, int32_t module, int32_t rank, const void* a,
+                              const void* b, float scale, int32_t* plist, hipStream_t s) {
+  if (slot < 0 || slot >= p->n_slots || module < 0 || module >= p->n_modules) return LORA_ERR_SLOT;
+  if (rank < 1 || rank > p->max_rank) return LORA_ERR_RANK;
+  const size_t ei = static_cast<size_t>(slot) * p->n_modules + module;
+  if (p->entries[ei].rank != 0) return LORA_ERR_SLOT;
+  const int64_t h = p->page_elems;
+  const int64_t ppr_a = p->h_in[module] / h, ppr_b = p->h_out[module] / h;
+  const int64_t n_plist = rank * (ppr_a + ppr_b);
+  std::vector<int32_t> pages;
+  if (!p->alloc.allocate(n_plist, pages)) return LORA_ERR_NO_PAGES;
+  std::memcpy(plist, pages.data(), pages.size() * 4);
+  const int32_t ids_off = static_cast<int32_t>(ei * p->max_pages_per_entry);
+  const int32_t n_a = static_cast<int32_t>(rank * ppr_a);
+  const int32_t b_gap = static_cast<int32_t>((p->max_rank - rank) * ppr_a);
+  SlotEntry value{rank, scale, ids_off, ids_off + n_a + b_gap};
+  if (p->dtype == LORA_BF16) {
+    hipLaunchKernelGGL(k_upload<__bf16>, dim3(static_cast<unsigned>(n_plist)), dim3(256), 0, s,
+                       static_cast<__bf16*>(p->d_pages), static_cast<const __bf16*>(a),
+                       static_cast<const __bf16*>(b), plist, static_cast<int32_t>(n_plist), h, p->d_page_ids,
+                       ids_off, n_a, b_gap, p->d_entries + ei, value);
+  } else {
+    hipLaunchKernelGGL(k_upload<float>, dim3(static_cast<unsigned>(n_plist)), dim3(256), 0, s,
+                       static_cast<float*>(p->d_pages), static_cast<const float*>(a), static_cast<const float*>(b),
+                       plist, static_cast<int32_t>(n_plist), h, p->d_page_ids, ids_off, n_a, b_gap,
+                       p->d_entries + ei, value);
+  }
+  if (hipGetLastError() != hipSuccess) {
+    p->alloc.release(pages);
+    return LORA_ERR_HIP;
+  }
+  auto& e = p->entries[ei];
+  e.rank = rank;
+  e.scale = scale;
+  e.pages = std::move(pages);
+  ++p->loads;
+  return LORA_OK;
+}
 
 extern "C" {
 
@@ -209,11 +251,13 @@ lora_status lora_pool_load(lora_pool* p, int32_t slot, int32_t module, int32_t r
     if (p->dtype == LORA_BF16) {
       hipLaunchKernelGGL(k_upload<__bf16>, dim3(static_cast<unsigned>(n_plist)), dim3(256), 0, s,
                          static_cast<__bf16*>(p->d_pages), reinterpret_cast<const __bf16*>(st),
+                         reinterpret_cast<const __bf16*>(st + a_bytes),
                          reinterpret_cast<const int32_t*>(st + ids_at), static_cast<int32_t>(n_plist), h,
                          p->d_page_ids, ids_off, n_a, b_gap, p->d_entries + ei, value);
     } else {
       hipLaunchKernelGGL(k_upload<float>, dim3(static_cast<unsigned>(n_plist)), dim3(256), 0, s,
                          static_cast<float*>(p->d_pages), reinterpret_cast<const float*>(st),
+                         reinterpret_cast<const float*>(st + a_bytes),
                          reinterpret_cast<const int32_t*>(st + ids_at), static_cast<int32_t>(n_plist), h,
                          p->d_page_ids, ids_off, n_a, b_gap, p->d_entries + ei, value);
     }

@@ -65,3 +65,11 @@ struct DeviceGuard {
 };
 
 }  // namespace lora
+
+// Asynchronous upload of one (slot, module) entry on stream s: A's rank rows
+// from a, B's from b (device memory or page-locked host memory), the page
+// list written to plist (rank * (h_in + h_out) / page_elems ints, readable by
+// the device).  The caller keeps a, b and plist unchanged until the stream
+// passes the upload.  Same checks and bookkeeping as lora_pool_load.
+lora_status pool_upload_async(lora_pool* p, int32_t slot, int32_t module, int32_t rank, const void* a,
+                              const void* b, float scale, int32_t* plist, hipStream_t s);

@@ -37,6 +37,7 @@ __all__ = [
     "Module", "Workload", "to_bf16_bits", "zipf_ids", "finite_zipf_cdf",
     "c0_worked_example", "c1_tiny_f32", "c2_bgmv_decode", "c3_sgmv_prefill",
     "c4_mixed_rank", "c5_encoder_step", "fused_tiles", "fingerprint_rank1", "integer_exact",
+    "lcg_uniforms", "request_trace", "tier_batches",
     "BY_NAME",
 ]
 
@@ -319,6 +320,57 @@ def c5_encoder_step(seed: int = 5, n_seq: int = 128, seq_len: int = 256,
                                   [[rank] * 4] * n_slots, [2.0] * n_slots,
                                   1.0, 0.02, 0.02, draw_w)
     return Workload("c5_encoder_step", "bf16", h, n_slots, mods, ids, xs, y0, Ws, ad)
+
+
+# --------------------------------------------------------------------------
+# request traces for the adapter tiers
+# --------------------------------------------------------------------------
+def lcg_uniforms(seed: int, count: int) -> np.ndarray:
+    """``count`` draws in [0, 1) of the 32-bit linear congruential generator
+    the study page's cache simulation uses (section "Memory: slots, tiers and
+    paging"): state <- (1664525 state + 1013904223) mod 2^32, draw = state / 2^32
+    (the state after the step)."""
+    out = np.empty(count, dtype=np.float64)
+    s = seed & 0xFFFFFFFF
+    for i in range(count):
+        s = (s * 1664525 + 1013904223) & 0xFFFFFFFF
+        out[i] = s / 4294967296.0
+    return out
+
+
+def request_trace(seed: int = 11, n_adapters: int = 500, n_requests: int = 50_000,
+                  s: float = 1.1) -> np.ndarray:
+    """Adapter id of each request, finite Zipf(s) over ``n_adapters`` (id 0
+    hottest), drawn by inverse CDF from ``lcg_uniforms(seed)``: the smallest id
+    whose cumulative weight reaches the draw.  The defaults are the study
+    page's cache-simulation example (500 adapters, 50,000 requests, s = 1.1,
+    seed 11)."""
+    cdf = finite_zipf_cdf(n_adapters, s)
+    u = lcg_uniforms(seed, n_requests)
+    return np.minimum(np.searchsorted(cdf, u, side="left"), n_adapters - 1).astype(np.int32)
+
+
+def tier_batches(seed: int = 21, n_batches: int = 10, batch: int = 32, n_adapters: int = 12,
+                 per_batch: int = 4, h_in: int = 256, h_out: int = 384, page: int = 64) -> Workload:
+    """Consecutive decode batches served through adapter tiers: ``n_adapters``
+    adapters (ranks 8 and 16, slots indexed by adapter id), each batch of
+    ``batch`` tokens draws its tokens' ids from ``per_batch`` adapters picked
+    at random (about one token in eight has id -1).  Batch b is tokens
+    [b batch, (b+1) batch).  bf16; x ~ N(0,1); W, A, B ~ N(0, 0.02); scale 2."""
+    rng = np.random.default_rng(seed)
+    ids = []
+    for _ in range(n_batches):
+        pick = rng.choice(n_adapters, size=per_batch, replace=False)
+        b = pick[rng.integers(0, per_batch, size=batch)]
+        b[rng.random(batch) < 0.125] = -1
+        ids.append(b)
+    ids = np.concatenate(ids).astype(np.int32)
+    mods = [Module("proj", h_in, h_out, 0)]
+    ranks = [[8 if a % 3 == 0 else 16] for a in range(n_adapters)]
+    xs, Ws, ad, y0 = _draw_values(rng, "bf16", ids.shape[0], mods, 1, ranks, [2.0] * n_adapters,
+                                  1.0, 0.02, 0.02, draw_w=False)
+    return Workload("tier_batches", "bf16", page, n_adapters, mods, ids, xs, y0, Ws, ad,
+                    notes={"batch": batch})
 
 
 # --------------------------------------------------------------------------
