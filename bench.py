@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="bgmv_decode_x128",
                     choices=["bgmv_decode_x128", "bgmv_decode", "sgmv_prefill", "mixed_rank", "encoder_step",
-                             "encoder_fused", "prefill_fused"])
+                             "encoder_fused", "prefill_fused", "tiers_trace"])
     ap.add_argument("--path", choices=["auto", "bgmv", "sgmv"], default="auto",
                     help="force the fused BGMV or the shrink+expand path (default: the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -275,6 +275,79 @@ def time_ms(fn, reps=10):
     return a.elapsed_time(b) / reps
 
 
+def tiers_trace(args):
+    """The study page's request trace (500 rank-16 adapters of 4096 x 4096,
+    Zipf(1.1), 50,000 requests, LCG seed 11) served in decode batches of 32
+    requests through 32 GPU slots and a 500-adapter host tier: per batch one
+    lora_tiers_acquire (uploads of GPU misses from page-locked host memory,
+    cold loads from numpy arrays through the fetch callback), a segment build
+    and one fused BGMV.  Against the same loop with all 500 adapters resident
+    in a 500-slot pool.  Wall clock over the whole trace, host work included."""
+    import numpy as np
+    import torch
+    import segmented_gathered_rank_amd as sgr
+    import workloads as W
+    from workloads import _store, _normal
+    n_ad, gpu_slots, host_slots, bsz, h, r = 500, 32, 500, 32, 4096, 16
+    trace = W.request_trace()
+    rng = np.random.default_rng(7)
+    A = [_store(_normal(rng, 0.02, (r, h)), "bf16") for _ in range(n_ad)]
+    B = [_store(_normal(rng, 0.02, (r, h)), "bf16") for _ in range(n_ad)]
+    dev = torch.device("cuda", 0)
+    x = torch.randn(bsz, h, device=dev).to(torch.bfloat16)
+    y = torch.zeros(bsz, h, device=dev, dtype=torch.bfloat16)
+
+    def run(tiered):
+        slots = gpu_slots if tiered else n_ad
+        pool = sgr.lora_pool_create(0, sgr.LORA_BF16, h, slots * 2 * r, slots, 1, [h], [h], r)
+        seg_buf = torch.zeros(max(sgr.lora_segments_bytes(bsz, slots), 256), dtype=torch.uint8, device=dev)
+        seg = sgr.lora_segments_bind(seg_buf, bsz, slots)
+        tiers = sgr.lora_tiers_create(gpu_slots, host_slots) if tiered else None
+        if not tiered:
+            for a in range(n_ad):
+                sgr.lora_pool_load(pool, a, 0, r, A[a], B[a], 2.0)
+        fetch = lambda a, m: (r, 2.0, A[a], B[a])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for b0 in range(0, len(trace), bsz):
+            req = trace[b0:b0 + bsz]
+            ids = sgr.lora_tiers_acquire(tiers, pool, req, fetch) if tiered else req
+            d_ids = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).to(dev, non_blocking=False)
+            sgr.lora_build_segments(d_ids, seg)
+            sgr.lora_apply_bgmv(pool, 0, 1, x, h, 0, seg, y, h, 0, sgr.LORA_BF16)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        st = sgr.lora_tiers_stats(tiers) if tiered else None
+        if tiered:
+            sgr.lora_tiers_destroy(tiers)
+        sgr.lora_pool_destroy(pool)
+        return wall, st
+
+    run(True)   # warm-up of both paths (library, allocator, page-locked buffers)
+    run(False)
+    t_res, _ = run(False)
+    t_tier, st = run(True)
+    n = len(trace)
+    misses = st["host_hits"] + st["cold_loads"]
+    adapter_bytes = 2 * r * 2 * h
+    out = {
+        "metric": METRIC, "value": round(n / t_tier, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": n // bsz, "warmup": 0, "ms_per_step": round(t_tier * 1e3 / (n // bsz), 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "tiers_trace", "adapters": n_ad, "gpu_slots": gpu_slots, "host_slots": host_slots,
+                   "requests": n, "batch": bsz, "h": h, "rank": r, "ids": "the study page's LCG trace, Zipf(1.1)"},
+        "roofline": None,
+        "extra": {"gpu_hit_pct": round(100.0 * st["gpu_hits"] / n, 1),
+                  "host_hit_pct": round(100.0 * st["host_hits"] / n, 1), "cold_loads": st["cold_loads"],
+                  "resident_tokens_per_s": round(n / t_res, 1), "tiered_over_resident_time": round(t_tier / t_res, 3),
+                  "upload_us_per_miss": round((t_tier - t_res) / max(misses, 1) * 1e6, 2),
+                  "upload_GBps_per_miss": round(adapter_bytes * misses / max(t_tier - t_res, 1e-9) / 1e9, 2),
+                  "note": "wall clock of the serve loop, host work included; upload cost = extra time over the "
+                          "resident loop per GPU miss"},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -284,6 +357,9 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path (see DESIGN.md, 'Sharding').",
               file=sys.stderr)
         sys.exit(2)
+    if args.workload == "tiers_trace":
+        tiers_trace(args)
+        return
     import numpy as np
     import torch
     from segmented_gathered_rank_amd import accounting
