@@ -10,7 +10,10 @@
 namespace lora {
 
 // Work decomposition fixed by the library (recorded in the segment meta).
-constexpr int kUnitTokens = 4;     // tokens per GEMV work unit
+#ifndef LORA_UNIT_TOKENS
+#define LORA_UNIT_TOKENS 4
+#endif
+constexpr int kUnitTokens = LORA_UNIT_TOKENS;     // tokens per GEMV work unit
 constexpr int kTileTokens = 64;    // tokens per matrix-core tile
 constexpr int kLongMin = 64;       // segments this long or longer use matrix-core tiles
 constexpr int kMaxRank = LORA_MAX_RANK;

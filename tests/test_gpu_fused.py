@@ -171,3 +171,18 @@ def test_fused_argument_errors():
         sgr.lora_fused_gemm(dw1.pool, 0, dw1._xp(0), 64, dw1._xp(0), 64, dw1.ids, 16, dw1.y_of(0), 64)
     assert ei.value.status == -6
     dw1.close()
+
+
+def test_fused_rejects_rows_of_too_many_pages():
+    """h_in / page_elems above 32 (A page ids per rank row held in LDS): SHAPE, nothing launched."""
+    import torch
+    import segmented_gathered_rank_amd as sgr
+    pool = sgr.lora_pool_create(0, sgr.LORA_BF16, 64, 64, 2, 1, [64 * 33], [64], 4)
+    x = torch.zeros(4, 64 * 33, dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros(64, 64 * 33, dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros(4, 64, dtype=torch.bfloat16, device="cuda")
+    ids = torch.zeros(4, dtype=torch.int32, device="cuda")
+    with pytest.raises(sgr.LoraError) as ei:
+        sgr.lora_fused_gemm(pool, 0, x, 64 * 33, w, 64 * 33, ids, 4, y, 64)
+    assert ei.value.status == -2
+    sgr.lora_pool_destroy(pool)

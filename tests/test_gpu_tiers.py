@@ -70,3 +70,28 @@ def test_acquire_serves_batches_through_four_slots():
     assert ps["loaded_slots"] <= n_slots and ps["evicts"] > 0
     sgr.lora_tiers_destroy(tiers)
     sgr.lora_pool_destroy(pool)
+
+
+def test_acquire_errors():
+    import segmented_gathered_rank_amd as sgr
+    wl = W.tier_batches(seed=22)
+    mod = wl.modules[0]
+    pool = sgr.lora_pool_create(0, sgr.LORA_BF16, wl.page_elems, 4 * 16 * 10, 4, 1, [mod.h_in], [mod.h_out], 16)
+    fetch = lambda a, m: (wl.adapters[a][m][0], wl.adapters[a][m][1], wl.adapters[a][m][2], wl.adapters[a][m][3])
+    tiers = sgr.lora_tiers_create(4, 6)
+    with pytest.raises(sgr.LoraError) as ei:           # five adapters for four slots
+        sgr.lora_tiers_acquire(tiers, pool, [0, 1, 2, 3, 4], fetch)
+    assert ei.value.status == -5
+    assert sgr.lora_tiers_stats(tiers) == {"gpu_hits": 0, "host_hits": 0, "cold_loads": 0}   # nothing touched
+
+    def bad(a, m):
+        raise RuntimeError("cold store unavailable")
+    with pytest.raises(RuntimeError):
+        sgr.lora_tiers_acquire(tiers, pool, [5], bad)
+    sgr.lora_tiers_destroy(tiers)
+    no_host = sgr.lora_tiers_create(4, 0)                # uploads need a host tier
+    with pytest.raises(sgr.LoraError) as ei:
+        sgr.lora_tiers_acquire(no_host, pool, [1], fetch)
+    assert ei.value.status == -1
+    sgr.lora_tiers_destroy(no_host)
+    sgr.lora_pool_destroy(pool)
