@@ -46,7 +46,7 @@ namespace lora {
 #define LORA_SHRINK_ROWS 2
 #endif
 #ifndef LORA_UNIT_RUN
-#define LORA_UNIT_RUN 2
+#define LORA_UNIT_RUN 8
 #endif
 constexpr int kGemvThreads = LORA_GEMV_THREADS;
 constexpr int kGemvWaves = kGemvThreads / 64;
