@@ -52,6 +52,9 @@ def parse():
                     help="summarize two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) instead of benchmarking")
     ap.add_argument("--pmc-kernel", default="k_gemvILi0E", help="substring of the kernel to summarize")
     ap.add_argument("--pmc-out", default=None, help="write the traffic summary JSON here")
+    ap.add_argument("--pmc-per-step", type=int, default=0,
+                    help="the step makes this many launches of the kernel (one per module): average over all "
+                         "of them and report HBM bytes per step")
     return ap.parse_args()
 
 
@@ -111,7 +114,9 @@ def load_traffic(workload):
             t = json.load(fh)
     except (OSError, ValueError):
         return None
-    return t.get("hbm_bytes_per_launch") if t.get("kernel_source_sha") == kernel_source_sha() else None
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("hbm_bytes_per_step", t.get("hbm_bytes_per_launch"))
 
 
 def pmc_summary(args):
@@ -132,7 +137,8 @@ def pmc_summary(args):
         copies = [float(r["Counter_Value"]) for r in rs if "copyBuffer" in r["Kernel_Name"]]
         match = [r for r in rs if args.pmc_kernel in r["Kernel_Name"]]
         big = max((int(r["Grid_Size"]) for r in match), default=0)     # the bench's own launch shape
-        target = [float(r["Counter_Value"]) for r in match if int(r["Grid_Size"]) == big]
+        target = [float(r["Counter_Value"]) for r in match
+                  if args.pmc_per_step > 0 or int(r["Grid_Size"]) == big]
         if not copies or not target:
             raise SystemExit(f"{name}: no copy or no target dispatch found in {d}")
         ref_kib = args.calibrate_copy_mib * 1024.0
@@ -143,6 +149,9 @@ def pmc_summary(args):
                     res["WRITE_SIZE"]["kernel_kib_mean"] * res["WRITE_SIZE"]["scale"])
     out = {"workload": args.workload, "kernel": args.pmc_kernel, "kernel_source_sha": kernel_source_sha(),
            "hbm_bytes_per_launch": hbm, "counters": res}
+    if args.pmc_per_step > 0:   # every launch of the step, averaged, times the launches per step
+        out["hbm_bytes_per_step"] = hbm * args.pmc_per_step
+        out["launches_per_step"] = args.pmc_per_step
     if args.pmc_out:
         with open(args.pmc_out, "w") as fh:
             json.dump(out, fh, indent=1)
@@ -451,6 +460,8 @@ def main():
                  "hipblaslt_plus_unfused_ms": round(gms + unfused, 4),
                  "fused_over_hipblaslt_plus_unfused": round(kern_avg / (gms + unfused), 4),
                  "fused_over_hipblaslt_base": round(kern_avg / gms, 4)}
+        # traffic: counter-measured HBM bytes of one step (all its launches), against
+        # algorithmic_bytes_per_step
         roofline = {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": load_traffic(args.workload),
                     "kernel": "k_fused_gemm", "flops_per_launch_set": flops}
