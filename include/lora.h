@@ -332,6 +332,21 @@ lora_status lora_tiers_slot_of(const lora_tiers *t, int32_t id, int32_t *slot);
  * tiers may disagree with the pool: destroy both. */
 lora_status lora_tiers_acquire(lora_tiers *t, lora_pool *p, const int32_t *ids, int32_t n,
                                lora_fetch_fn fetch, void *ctx, int32_t *slots, void *stream);
+/* Marks the end of the kernels of the batch last acquired: call it after
+ * enqueueing them on `stream`.  Prefetches wait for the batch before it. */
+lora_status lora_tiers_batch_done(lora_tiers *t, void *stream);
+/* Forecast ("Thousands of adapters", slide 9: a forecast from the waiting
+ * queue and an asynchronous copy): uploads, on copy_stream, the adapters of
+ * [host] ids that are not resident, in order, as long as a slot can be
+ * freed without displacing an adapter of the batch in flight (the last
+ * acquire).  copy_stream first waits for the kernels of the batch before
+ * the one in flight (the second-latest lora_tiers_batch_done).  The next
+ * acquire makes its stream wait for these uploads, and finds the adapters
+ * resident.  Prefetches are not requests: the hit counters do not change.
+ * [host] *issued = adapters uploaded (optional).
+ * Errors: as lora_tiers_acquire. */
+lora_status lora_tiers_prefetch(lora_tiers *t, lora_pool *p, const int32_t *ids, int32_t n,
+                                lora_fetch_fn fetch, void *ctx, void *copy_stream, int32_t *issued);
 
 #ifdef __cplusplus
 }

@@ -23,6 +23,7 @@ __all__ = [
     "lora_expand", "lora_apply_bgmv", "lora_fused_gemm",
     "LORA_TIER_GPU", "LORA_TIER_HOST", "LORA_TIER_COLD", "lora_tiers_create", "lora_tiers_destroy",
     "lora_tiers_touch", "lora_tiers_stats", "lora_tiers_slot_of", "lora_tiers_acquire",
+    "lora_tiers_batch_done", "lora_tiers_prefetch",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblora_mi355x.so")
@@ -100,6 +101,8 @@ _SIGS = {
     "lora_tiers_stats": (_I32, [_P, ctypes.POINTER(_I64), ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
     "lora_tiers_slot_of": (_I32, [_P, _I32, ctypes.POINTER(_I32)]),
     "lora_tiers_acquire": (_I32, [_P, _P, _P, _I32, _P, _P, _P, _P]),
+    "lora_tiers_batch_done": (_I32, [_P, _P]),
+    "lora_tiers_prefetch": (_I32, [_P, _P, _P, _I32, _P, _P, _P, ctypes.POINTER(_I32)]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -327,3 +330,47 @@ def lora_tiers_acquire(tiers: int, pool: int, ids, fetch, stream=None):
         raise errors[0]
     _check(st, "lora_tiers_acquire")
     return slots
+
+
+def _fetch_cb(fetch, errors):
+    import numpy as np
+
+    def _cb(ctx, adapter, module, rank, scale, a_ptr, b_ptr):
+        try:
+            got = fetch(int(adapter), int(module))
+            if got is None:
+                rank[0] = 0
+                scale[0] = 0.0
+                return 0
+            r, s, A, B = got
+            A = np.ascontiguousarray(A)
+            B = np.ascontiguousarray(B)
+            ctypes.memmove(a_ptr, A.ctypes.data, A.nbytes)
+            ctypes.memmove(b_ptr, B.ctypes.data, B.nbytes)
+            rank[0] = int(r)
+            scale[0] = float(s)
+            return 0
+        except Exception as e:  # reported after the call returns
+            errors.append(e)
+            return 1
+    return LORA_FETCH_FN(_cb)
+
+
+def lora_tiers_batch_done(tiers: int, stream=None) -> None:
+    _check(_lib.lora_tiers_batch_done(tiers, _stream(stream)), "lora_tiers_batch_done")
+
+
+def lora_tiers_prefetch(tiers: int, pool: int, ids, fetch, stream=None) -> int:
+    """Uploads the non-resident adapters of ids on `stream` (a copy stream);
+    returns how many were issued.  fetch as for lora_tiers_acquire."""
+    import numpy as np
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    errors = []
+    cb = _fetch_cb(fetch, errors)
+    issued = _I32()
+    st = _lib.lora_tiers_prefetch(tiers, pool, _ptr(ids), ids.shape[0], ctypes.cast(cb, _P), None,
+                                  _stream(stream), ctypes.byref(issued))
+    if errors:
+        raise errors[0]
+    _check(st, "lora_tiers_prefetch")
+    return issued.value

@@ -17,6 +17,13 @@
 // every module from page-locked host buffers (the host tier), asynchronously
 // on the caller's stream.  A host-tier miss first asks the caller's fetch
 // function to fill a host buffer (the cold store is the caller's).
+//
+// lora_tiers_prefetch is the forecast of "Thousands of adapters" (slide 9: a
+// forecast from the waiting queue and an asynchronous copy): while the batch
+// in flight computes, the adapters of the next batch are uploaded on a copy
+// stream.  It never displaces an adapter of the batch in flight, and it
+// waits for the kernels of earlier batches (lora_tiers_batch_done marks
+// them) before it reuses a slot.
 #include <hip/hip_runtime.h>
 
 #include <new>
@@ -105,20 +112,30 @@ struct lora_tiers {
   std::vector<float> scale;     // [host entry][module]
   std::vector<hipEvent_t> done; // [host entry]: last upload that read the entry's buffer
   std::vector<uint8_t> pending;
+  // prefetch: adapters of the batch in flight (never displaced by a prefetch),
+  // the end of the two latest batches' kernels, and the end of the latest prefetch
+  std::vector<int32_t> inflight;
+  hipEvent_t batch_ev[2] = {nullptr, nullptr};
+  int batches_done = 0;
+  hipEvent_t prefetch_ev = nullptr;
+  bool prefetch_pending = false;
+  int64_t prefetched = 0;
 };
 
 namespace {
 
 // One request: tier, GPU slot after it, adapter displaced from the GPU tier,
 // and the host entry of the adapter (-1 if the host tier keeps nothing).
-void touch_one(lora_tiers* t, int32_t id, int32_t* tier, int32_t* slot, int32_t* evicted, int32_t* host_entry) {
+// count = false: a prefetch, not a request (the hit counters stay).
+void touch_one(lora_tiers* t, int32_t id, int32_t* tier, int32_t* slot, int32_t* evicted, int32_t* host_entry,
+               bool count = true) {
   bool hit = false;
   int32_t out = -1;
   *slot = t->gpu.access(id, &hit, &out);
   *evicted = (hit || out == id) ? -1 : out;
   *host_entry = -1;
   if (hit) {
-    ++t->gpu_hits;
+    if (count) ++t->gpu_hits;
     *tier = LORA_TIER_GPU;
     return;
   }
@@ -126,10 +143,10 @@ void touch_one(lora_tiers* t, int32_t id, int32_t* tier, int32_t* slot, int32_t*
   int32_t h_out = -1;
   *host_entry = t->host.access(id, &h_hit, &h_out);
   if (h_hit) {
-    ++t->host_hits;
+    if (count) ++t->host_hits;
     *tier = LORA_TIER_HOST;
   } else {
-    ++t->cold;
+    if (count) ++t->cold;
     *tier = LORA_TIER_COLD;
   }
 }
@@ -155,6 +172,8 @@ lora_status lora_tiers_destroy(lora_tiers* t) {
   lora_status st = LORA_OK;
   for (size_t e = 0; e < t->done.size(); ++e)
     if (t->done[e] && hipEventDestroy(t->done[e]) != hipSuccess) st = LORA_ERR_HIP;
+  for (hipEvent_t ev : {t->batch_ev[0], t->batch_ev[1], t->prefetch_ev})
+    if (ev && hipEventDestroy(ev) != hipSuccess) st = LORA_ERR_HIP;
   if (t->pinned && hipHostFree(t->pinned) != hipSuccess) st = LORA_ERR_HIP;
   delete t;
   return st;
@@ -190,86 +209,172 @@ lora_status lora_tiers_slot_of(const lora_tiers* t, int32_t id, int32_t* slot) {
   return LORA_OK;
 }
 
+namespace {
+
+size_t a_bytes_of(const lora_pool* p, int32_t m) { return static_cast<size_t>(p->max_rank) * p->h_in[m] * p->elem_bytes(); }
+size_t b_bytes_of(const lora_pool* p, int32_t m) { return static_cast<size_t>(p->max_rank) * p->h_out[m] * p->elem_bytes(); }
+size_t ids_bytes_of(const lora_pool* p) { return (static_cast<size_t>(p->max_pages_per_entry) * 4 + 15) / 16 * 16; }
+
+// Binds the tiers to pool p on first use: host buffers for every module at the
+// rank cap plus its page list, one per host entry, page-locked.
+lora_status bind_pool(lora_tiers* t, lora_pool* p) {
+  if (t->pool) return t->pool == p ? LORA_OK : LORA_ERR_ARG;
+  if (static_cast<int64_t>(t->gpu.key.size()) != p->n_slots) return LORA_ERR_SLOT;
+  if (t->host.key.empty()) return LORA_ERR_ARG;   // uploads come from host buffers
+  size_t per = 0;
+  for (int32_t m = 0; m < p->n_modules; ++m) per += a_bytes_of(p, m) + b_bytes_of(p, m) + ids_bytes_of(p);
+  const size_t nh = t->host.key.size();
+  if (hipHostMalloc(&t->pinned, per * nh, hipHostMallocDefault) != hipSuccess) {
+    t->pinned = nullptr;
+    return LORA_ERR_HIP;
+  }
+  t->pool = p;
+  t->entry_bytes = per;
+  t->rank.assign(nh * p->n_modules, 0);
+  t->scale.assign(nh * p->n_modules, 0.f);
+  t->done.assign(nh, nullptr);
+  t->pending.assign(nh, 0);
+  for (size_t e = 0; e < nh; ++e)
+    if (hipEventCreateWithFlags(&t->done[e], hipEventDisableTiming) != hipSuccess) return LORA_ERR_HIP;
+  for (hipEvent_t* ev : {&t->batch_ev[0], &t->batch_ev[1], &t->prefetch_ev})
+    if (hipEventCreateWithFlags(ev, hipEventDisableTiming) != hipSuccess) return LORA_ERR_HIP;
+  return LORA_OK;
+}
+
+// A GPU miss of adapter id in slot `slot`, host entry he: fill the host
+// buffer from the cold store if needed, evict the slot's previous adapter,
+// upload the new one on stream s (asynchronously, from the host buffer).
+lora_status serve_miss(lora_tiers* t, lora_pool* p, int32_t id, int32_t tier, int32_t slot, int32_t he,
+                       lora_fetch_fn fetch, void* ctx, hipStream_t s) {
+  const int32_t nm = p->n_modules;
+  // the entry's buffers (rows, page lists) may still feed an earlier upload
+  if (t->pending[he] && hipEventSynchronize(t->done[he]) != hipSuccess) return LORA_ERR_HIP;
+  t->pending[he] = 0;
+  char* buf = static_cast<char*>(t->pinned) + static_cast<size_t>(he) * t->entry_bytes;
+  if (tier == LORA_TIER_COLD) {   // the caller's cold store fills the host buffer
+    char* q = buf;
+    for (int32_t m = 0; m < nm; ++m) {
+      int32_t r = 0;
+      float sc = 0.f;
+      if (fetch(ctx, id, m, &r, &sc, q, q + a_bytes_of(p, m)) != 0) return LORA_ERR_ARG;
+      if (r < 0 || r > p->max_rank) return LORA_ERR_RANK;
+      t->rank[static_cast<size_t>(he) * nm + m] = r;
+      t->scale[static_cast<size_t>(he) * nm + m] = sc;
+      q += a_bytes_of(p, m) + b_bytes_of(p, m) + ids_bytes_of(p);
+    }
+  }
+  // the slot's previous adapter leaves (stream-ordered), the new one is copied in
+  bool loaded = false;
+  for (int32_t m = 0; m < nm; ++m) loaded = loaded || p->entries[static_cast<size_t>(slot) * nm + m].rank > 0;
+  if (loaded) {
+    const lora_status st = lora_pool_evict(p, slot, s);
+    if (st != LORA_OK) return st;
+  }
+  char* q = buf;
+  for (int32_t m = 0; m < nm; ++m) {
+    const int32_t r = t->rank[static_cast<size_t>(he) * nm + m];
+    if (r > 0) {
+      const lora_status st =
+          pool_upload_async(p, slot, m, r, q, q + a_bytes_of(p, m), t->scale[static_cast<size_t>(he) * nm + m],
+                            reinterpret_cast<int32_t*>(q + a_bytes_of(p, m) + b_bytes_of(p, m)), s);
+      if (st != LORA_OK) return st;
+    }
+    q += a_bytes_of(p, m) + b_bytes_of(p, m) + ids_bytes_of(p);
+  }
+  if (hipEventRecord(t->done[he], s) != hipSuccess) return LORA_ERR_HIP;
+  t->pending[he] = 1;
+  return LORA_OK;
+}
+
+}  // namespace
+
 lora_status lora_tiers_acquire(lora_tiers* t, lora_pool* p, const int32_t* ids, int32_t n,
                                lora_fetch_fn fetch, void* ctx, int32_t* slots, void* stream) {
   if (!t || !p || n < 0 || (n > 0 && (!ids || !slots)) || !fetch) return LORA_ERR_ARG;
   if (static_cast<int64_t>(t->gpu.key.size()) != p->n_slots) return LORA_ERR_SLOT;
-  if (t->host.key.empty()) return LORA_ERR_ARG;   // uploads come from host buffers
+  if (t->host.key.empty()) return LORA_ERR_ARG;
   if (t->pool && t->pool != p) return LORA_ERR_ARG;
   for (int32_t i = 0; i < n; ++i)
     if (ids[i] < 0) return LORA_ERR_ARG;
+  std::vector<int32_t> distinct;
   {   // a batch may not need more adapters than there are slots
     std::unordered_map<int32_t, int> seen;
-    for (int32_t i = 0; i < n; ++i) seen[ids[i]] = 1;
-    if (static_cast<int64_t>(seen.size()) > p->n_slots) return LORA_ERR_SLOT;
+    for (int32_t i = 0; i < n; ++i)
+      if (seen.emplace(ids[i], 1).second) distinct.push_back(ids[i]);
+    if (static_cast<int64_t>(distinct.size()) > p->n_slots) return LORA_ERR_SLOT;
   }
-  const int32_t nm = p->n_modules;
-  const size_t eb = p->elem_bytes();
-  auto a_bytes = [&](int32_t m) { return static_cast<size_t>(p->max_rank) * p->h_in[m] * eb; };
-  auto b_bytes = [&](int32_t m) { return static_cast<size_t>(p->max_rank) * p->h_out[m] * eb; };
-  const size_t ids_bytes = (static_cast<size_t>(p->max_pages_per_entry) * 4 + 15) / 16 * 16;
   DeviceGuard g(p->device);
   if (!g.ok) return LORA_ERR_HIP;
-  if (!t->pool) {   // host buffers for this pool: every module at the rank cap, plus its page list
-    size_t per = 0;
-    for (int32_t m = 0; m < nm; ++m) per += a_bytes(m) + b_bytes(m) + ids_bytes;
-    const size_t nh = t->host.key.size();
-    if (hipHostMalloc(&t->pinned, per * nh, hipHostMallocDefault) != hipSuccess) {
-      t->pinned = nullptr;
-      return LORA_ERR_HIP;
-    }
-    t->pool = p;
-    t->entry_bytes = per;
-    t->rank.assign(nh * nm, 0);
-    t->scale.assign(nh * nm, 0.f);
-    t->done.assign(nh, nullptr);
-    t->pending.assign(nh, 0);
-    for (size_t e = 0; e < nh; ++e)
-      if (hipEventCreateWithFlags(&t->done[e], hipEventDisableTiming) != hipSuccess) return LORA_ERR_HIP;
-  }
+  lora_status st = bind_pool(t, p);
+  if (st != LORA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (t->prefetch_pending) {   // this batch's kernels come after the prefetched uploads
+    if (hipStreamWaitEvent(s, t->prefetch_ev, 0) != hipSuccess) return LORA_ERR_HIP;
+    t->prefetch_pending = false;
+  }
   for (int32_t i = 0; i < n; ++i) {
     int32_t tier, slot, ev, he;
     touch_one(t, ids[i], &tier, &slot, &ev, &he);
     slots[i] = slot;
     if (tier == LORA_TIER_GPU) continue;
-    // the entry's buffers (rows, page lists) may still feed an earlier upload
-    if (t->pending[he] && hipEventSynchronize(t->done[he]) != hipSuccess) return LORA_ERR_HIP;
-    t->pending[he] = 0;
-    char* buf = static_cast<char*>(t->pinned) + static_cast<size_t>(he) * t->entry_bytes;
-    if (tier == LORA_TIER_COLD) {   // the caller's cold store fills the host buffer
-      char* q = buf;
-      for (int32_t m = 0; m < nm; ++m) {
-        int32_t r = 0;
-        float sc = 0.f;
-        if (fetch(ctx, ids[i], m, &r, &sc, q, q + a_bytes(m)) != 0) return LORA_ERR_ARG;
-        if (r < 0 || r > p->max_rank) return LORA_ERR_RANK;
-        t->rank[static_cast<size_t>(he) * nm + m] = r;
-        t->scale[static_cast<size_t>(he) * nm + m] = sc;
-        q += a_bytes(m) + b_bytes(m) + ids_bytes;
-      }
-    }
-    // the slot's previous adapter leaves (stream-ordered), the new one is copied in
-    bool loaded = false;
-    for (int32_t m = 0; m < nm; ++m) loaded = loaded || p->entries[static_cast<size_t>(slot) * nm + m].rank > 0;
-    if (loaded) {
-      const lora_status st = lora_pool_evict(p, slot, stream);
-      if (st != LORA_OK) return st;
-    }
-    char* q = buf;
-    for (int32_t m = 0; m < nm; ++m) {
-      const int32_t r = t->rank[static_cast<size_t>(he) * nm + m];
-      if (r > 0) {
-        const lora_status st =
-            pool_upload_async(p, slot, m, r, q, q + a_bytes(m), t->scale[static_cast<size_t>(he) * nm + m],
-                              reinterpret_cast<int32_t*>(q + a_bytes(m) + b_bytes(m)), s);
-        if (st != LORA_OK) return st;
-      }
-      q += a_bytes(m) + b_bytes(m) + ids_bytes;
-    }
-    if (hipEventRecord(t->done[he], s) != hipSuccess) return LORA_ERR_HIP;
-    t->pending[he] = 1;
+    st = serve_miss(t, p, ids[i], tier, slot, he, fetch, ctx, s);
+    if (st != LORA_OK) return st;
   }
+  t->inflight = std::move(distinct);
+  return LORA_OK;
+}
+
+lora_status lora_tiers_batch_done(lora_tiers* t, void* stream) {
+  if (!t) return LORA_ERR_ARG;
+  if (!t->pool) return LORA_OK;   // nothing acquired yet
+  DeviceGuard g(t->pool->device);
+  if (!g.ok) return LORA_ERR_HIP;
+  // keep the latest two: a prefetch waits for the batch before the one in flight
+  std::swap(t->batch_ev[0], t->batch_ev[1]);
+  if (hipEventRecord(t->batch_ev[1], static_cast<hipStream_t>(stream)) != hipSuccess) return LORA_ERR_HIP;
+  ++t->batches_done;
+  return LORA_OK;
+}
+
+lora_status lora_tiers_prefetch(lora_tiers* t, lora_pool* p, const int32_t* ids, int32_t n, lora_fetch_fn fetch,
+                                void* ctx, void* copy_stream, int32_t* issued) {
+  if (!t || !p || n < 0 || (n > 0 && !ids) || !fetch) return LORA_ERR_ARG;
+  if (issued) *issued = 0;
+  for (int32_t i = 0; i < n; ++i)
+    if (ids[i] < 0) return LORA_ERR_ARG;
+  DeviceGuard g(p->device);
+  if (!g.ok) return LORA_ERR_HIP;
+  lora_status st = bind_pool(t, p);
+  if (st != LORA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(copy_stream);
+  // slots may still be read by kernels of batches before the one in flight
+  // (with fewer than two batches done there are none)
+  if (t->batches_done >= 2 && hipStreamWaitEvent(s, t->batch_ev[0], 0) != hipSuccess) return LORA_ERR_HIP;
+  std::unordered_map<int32_t, int> pinned;
+  for (int32_t a : t->inflight) pinned[a] = 1;
+  int32_t free_slots = static_cast<int32_t>(t->gpu.key.size()) - static_cast<int32_t>(pinned.size());
+  int32_t count = 0;
+  for (int32_t i = 0; i < n && free_slots > 0; ++i) {
+    const int32_t id = ids[i];
+    if (t->gpu.where.count(id)) continue;   // resident: nothing to do (its recency is left alone)
+    // the least recently used adapter must not be one of the batch in flight:
+    // those were touched last, so it is not while fewer than free_slots uploads happen
+    const int32_t victim = t->gpu.tail >= 0 && t->gpu.free_.empty() ? t->gpu.key[t->gpu.tail] : -1;
+    if (victim >= 0 && pinned.count(victim)) break;
+    int32_t tier, slot, ev, he;
+    touch_one(t, id, &tier, &slot, &ev, &he, false);
+    st = serve_miss(t, p, id, tier, slot, he, fetch, ctx, s);
+    if (st != LORA_OK) return st;
+    pinned[id] = 1;
+    --free_slots;
+    ++count;
+  }
+  if (count > 0) {
+    if (hipEventRecord(t->prefetch_ev, s) != hipSuccess) return LORA_ERR_HIP;
+    t->prefetch_pending = true;
+    t->prefetched += count;
+  }
+  if (issued) *issued = count;
   return LORA_OK;
 }
 

@@ -95,3 +95,58 @@ def test_acquire_errors():
     assert ei.value.status == -1
     sgr.lora_tiers_destroy(no_host)
     sgr.lora_pool_destroy(pool)
+
+
+def test_prefetch_on_a_copy_stream():
+    """The next batch's adapters are uploaded on a second stream while the
+    current batch computes (the slide-9 forecast, here the exact next batch).
+    Every batch still matches the oracle, and more requests find their adapter
+    on the GPU than without the forecast."""
+    import torch
+    import segmented_gathered_rank_amd as sgr
+    from segmented_gathered_rank_amd.harness import from_device, to_device
+    wl = W.tier_batches(seed=23, n_batches=12)
+    bsz = wl.notes["batch"]
+    mod = wl.modules[0]
+    n_slots, host_slots = 8, 6
+    say(f"prefetch: {wl.n_slots} adapters, {n_slots} GPU slots, host tier {host_slots}")
+    pages = n_slots * 16 * (mod.h_in + mod.h_out) // wl.page_elems
+    pool = sgr.lora_pool_create(0, sgr.LORA_BF16, wl.page_elems, pages, n_slots, 1, [mod.h_in], [mod.h_out], 16)
+    tiers = sgr.lora_tiers_create(n_slots, host_slots)
+
+    def fetch(adapter, module):
+        a = wl.adapters[adapter][module]
+        return None if a is None else (a[0], a[1], a[2], a[3])
+
+    dev = torch.device("cuda", 0)
+    compute = torch.cuda.current_stream()
+    copy = torch.cuda.Stream()
+    x = to_device(wl.x[0], "bf16", dev)
+    y = to_device(wl.y0[0], "bf16", dev)
+    seg_buf = torch.zeros(max(sgr.lora_segments_bytes(bsz, n_slots), 256), dtype=torch.uint8, device=dev)
+    seg = sgr.lora_segments_bind(seg_buf, bsz, n_slots)
+    nb = wl.n_tokens // bsz
+    reqs = [wl.ids[b * bsz:(b + 1) * bsz][wl.ids[b * bsz:(b + 1) * bsz] >= 0] for b in range(nb)]
+    issued = 0
+    for b in range(nb):
+        ids = wl.ids[b * bsz:(b + 1) * bsz]
+        slots = sgr.lora_tiers_acquire(tiers, pool, reqs[b], fetch, compute)
+        tok_slots = np.full(bsz, -1, np.int32)
+        tok_slots[ids >= 0] = slots
+        d_ids = torch.from_numpy(tok_slots).to(dev)
+        sgr.lora_build_segments(d_ids, seg, compute)
+        sgr.lora_apply_bgmv(pool, 0, 1, x[b * bsz:], mod.h_in, 0, seg, y[b * bsz:], mod.h_out, 0, sgr.LORA_BF16,
+                            compute)
+        sgr.lora_tiers_batch_done(tiers, compute)
+        if b + 1 < nb:
+            issued += sgr.lora_tiers_prefetch(tiers, pool, reqs[b + 1], fetch, copy)
+    torch.cuda.synchronize()
+    got = lo.decode(from_device(y), "bf16")
+    assert_close(got, lo.apply_to_y0(wl, 0), "bf16", "tiers with prefetch")
+    st = sgr.lora_tiers_stats(tiers)
+    plain = T.simulate([int(a) for r in reqs for a in r], n_slots, host_slots)
+    plain_hits = sum(t == T.GPU_HIT for t in plain["tier"])
+    say(f"  GPU hits {st['gpu_hits']} with the forecast ({issued} uploads issued), {plain_hits} without")
+    assert issued > 0 and st["gpu_hits"] > plain_hits
+    sgr.lora_tiers_destroy(tiers)
+    sgr.lora_pool_destroy(pool)
