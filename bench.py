@@ -291,7 +291,9 @@ def tiers_trace(args):
     lora_tiers_acquire (uploads of GPU misses from page-locked host memory,
     cold loads from numpy arrays through the fetch callback), a segment build
     and one fused BGMV.  Against the same loop with all 500 adapters resident
-    in a 500-slot pool.  Wall clock over the whole trace, host work included."""
+    in a 500-slot pool, and with a forecast: after each batch the next batch's
+    adapters are prefetched on a copy stream.  Wall clock over the whole
+    trace, host work included."""
     import numpy as np
     import torch
     import segmented_gathered_rank_amd as sgr
@@ -306,7 +308,7 @@ def tiers_trace(args):
     x = torch.randn(bsz, h, device=dev).to(torch.bfloat16)
     y = torch.zeros(bsz, h, device=dev, dtype=torch.bfloat16)
 
-    def run(tiered):
+    def run(tiered, prefetch=False):
         slots = gpu_slots if tiered else n_ad
         pool = sgr.lora_pool_create(0, sgr.LORA_BF16, h, slots * 2 * r, slots, 1, [h], [h], r)
         seg_buf = torch.zeros(max(sgr.lora_segments_bytes(bsz, slots), 256), dtype=torch.uint8, device=dev)
@@ -316,6 +318,7 @@ def tiers_trace(args):
             for a in range(n_ad):
                 sgr.lora_pool_load(pool, a, 0, r, A[a], B[a], 2.0)
         fetch = lambda a, m: (r, 2.0, A[a], B[a])
+        copy = torch.cuda.Stream() if prefetch else None
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for b0 in range(0, len(trace), bsz):
@@ -324,6 +327,9 @@ def tiers_trace(args):
             d_ids = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).to(dev, non_blocking=False)
             sgr.lora_build_segments(d_ids, seg)
             sgr.lora_apply_bgmv(pool, 0, 1, x, h, 0, seg, y, h, 0, sgr.LORA_BF16)
+            if prefetch:   # the forecast: the next batch of the queue
+                sgr.lora_tiers_batch_done(tiers)
+                sgr.lora_tiers_prefetch(tiers, pool, trace[b0 + bsz:b0 + 2 * bsz], fetch, copy)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         st = sgr.lora_tiers_stats(tiers) if tiered else None
@@ -336,6 +342,7 @@ def tiers_trace(args):
     run(False)
     t_res, _ = run(False)
     t_tier, st = run(True)
+    t_pf, st_pf = run(True, prefetch=True)
     n = len(trace)
     misses = st["host_hits"] + st["cold_loads"]
     adapter_bytes = 2 * r * 2 * h
@@ -351,6 +358,10 @@ def tiers_trace(args):
                   "resident_tokens_per_s": round(n / t_res, 1), "tiered_over_resident_time": round(t_tier / t_res, 3),
                   "upload_us_per_miss": round((t_tier - t_res) / max(misses, 1) * 1e6, 2),
                   "upload_GBps_per_miss": round(adapter_bytes * misses / max(t_tier - t_res, 1e-9) / 1e9, 2),
+                  "prefetch_tokens_per_s": round(n / t_pf, 1),
+                  "prefetch_gpu_hit_pct": round(100.0 * st_pf["gpu_hits"] / n, 1),
+                  "prefetch_host_hit_pct": round(100.0 * st_pf["host_hits"] / n, 1),
+                  "prefetch_cold_loads": st_pf["cold_loads"],
                   "note": "wall clock of the serve loop, host work included; upload cost = extra time over the "
                           "resident loop per GPU miss"},
     }
