@@ -21,6 +21,9 @@ constexpr int kMaxGrid = 4096;   // persistent grids loop over work beyond this
 #define LORA_SHRINK_WG_TARGET 512
 #endif
 constexpr int kShrinkWgTarget = LORA_SHRINK_WG_TARGET;   // matrix-core shrink: split K below this many workgroups
+// LDS for the matrix-core shrink's staged A rows and page ids: three
+// workgroups fit in a CU's 160 KiB
+constexpr size_t kStreamLdsBudget = 52 * 1024;
 
 SegView seg_view(const lora_segments* s) {
   SegView v;
@@ -184,19 +187,21 @@ lora_status launch_shrink(const lora_pool* p, int32_t module0, int32_t n_modules
       a.k_per_split = kps;
       a.ldr = ldr_of(p);
       a.magic = static_cast<uint32_t>(((uint64_t(1) << 32) + p->page_elems - 1) / p->page_elems);
-      // staged A per sub-chunk: at most kStageBatch 16-byte chunks per thread (32 KiB)
-      int32_t kc = (kMfmaThreads * kStageBatch * 8 / (per_wg * a.ldr)) / 32 * 32;
-      if (kc > 32 * kShrinkSteps) kc = 32 * kShrinkSteps;
-      if (kc > kps) kc = kps;
-      if (kc < 32) kc = 32;
-      a.kc = kc;
       a.max_pids = p->max_pages_per_entry;
-      const size_t lds = static_cast<size_t>(per_wg) * a.ldr * (kc + 8) * 2 +
-                         static_cast<size_t>(per_wg) * a.max_pids * 4;
+      const int ntiles = a.ldr <= 16 ? 1 : a.ldr <= 32 ? 2 : 4;
+      // A rows staged in LDS at once: the whole split when they fit the LDS budget,
+      // else equal sub-ranges (multiples of 32) that do
+      const size_t ids_bytes = static_cast<size_t>(per_wg) * a.max_pids * 4;
+      const size_t row_bytes = static_cast<size_t>(per_wg) * 16 * ntiles * 2;   // per k of A rows
+      int32_t kc_max = static_cast<int32_t>((kStreamLdsBudget - ids_bytes) / row_bytes) - 8;
+      kc_max = std::max(32, kc_max / 32 * 32);
+      const int32_t n_sub = (kps + kc_max - 1) / kc_max;
+      a.kc = ((kps + n_sub - 1) / n_sub + 31) / 32 * 32;
+      const size_t lds = stream_lds_bytes(per_wg, ntiles, a.kc, a.max_pids);
       a.part = ks > 1 ? static_cast<float*>(ws) : nullptr;
       const dim3 grid(tile_grid_of(seg->max_tiles), ks, groups), block(kMfmaThreads);
-      const int ntiles = a.ldr <= 16 ? 1 : a.ldr <= 32 ? 2 : 4;
-#define LORA_SHRINK_LAUNCH(M, NT) hipLaunchKernelGGL((k_shrink_mfma<M, NT>), grid, block, lds, s, a)
+#define LORA_SHRINK_LAUNCH(M, NT) \
+  hipLaunchKernelGGL((k_shrink_stream<M, NT, kStreamDepth>), grid, block, lds, s, a)
 #define LORA_SHRINK_NT(M)                                 \
   do {                                                    \
     if (ntiles == 1) LORA_SHRINK_LAUNCH(M, 1);            \

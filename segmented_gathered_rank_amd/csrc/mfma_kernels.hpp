@@ -7,8 +7,10 @@
 // shrink (bf16 in, fp32 accumulate): T[64 x r] = X[64 x K] * A^T[K x r] with
 //   v_mfma_f32_16x16x32_bf16.  Wave w owns tokens 16w..16w+15 of the tile;
 //   one MFMA takes a 16 x 32 slice of X (each lane 8 consecutive bf16 of one
-//   token row) and a 32 x 16 slice of A^T (each lane 8 consecutive bf16 of one
-//   rank row), so both operands stream straight from row-major memory.  When
+//   token row, loaded straight from row-major memory: a wave's load covers 64
+//   bytes of 16 rows, and the next step's load the rest of their 128-byte
+//   lines) and a 32 x 16 slice of A^T (each lane 8 consecutive bf16 of one
+//   rank row, from the A rows staged in LDS).  When
 //   several modules share x (q, k, v), one workgroup computes all of them from
 //   one read of the x slice.  K may be split across workgroups to fill the
 //   chip; the partial tiles then go to a workspace and a second launch adds
@@ -38,9 +40,6 @@ constexpr int kExpandCols = 128;       // output columns per expand block
 constexpr int kExpandBlocks = LORA_EXPAND_BLOCKS;   // column blocks per expand workgroup
 
 __device__ __forceinline__ bf16x8 ld_bf16x8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
-__device__ __forceinline__ bf16x8 ld_bf16x8_nt(const __bf16* p) {
-  return ld16<LORA_NT_ROWS != 0>(reinterpret_cast<const bf16x8*>(p));
-}
 
 struct ShrinkArgs {
   PoolView pv;
@@ -55,35 +54,31 @@ struct ShrinkArgs {
   uint32_t magic;             // reciprocal of the page size
   int32_t ks_count;           // K splits (grid y)
   int32_t k_per_split;        // multiple of 32
-  int32_t kc;                 // K staged in LDS at a time (multiple of 32, <= 32 * kShrinkSteps)
+  int32_t kc;                 // K of A rows staged in LDS at a time (multiple of 32)
   int32_t ldr;                // rank rows per module in LDS and columns of a partial tile (multiple of 16)
   int32_t max_pids;           // page ids per entry in LDS
   float* part;                // [tiles][groups][mods_per_wg][ks_count][64][ldr]
 };
 
-#ifndef LORA_SHRINK_STEPS
-#define LORA_SHRINK_STEPS 16
-#endif
 #ifndef LORA_STAGE_BATCH
 #define LORA_STAGE_BATCH 8
 #endif
-constexpr int kShrinkSteps = LORA_SHRINK_STEPS;   // 32-wide k steps of x prefetched per lane
 constexpr int kMaxSplits = 8;                     // K splits of the shrink at most
 constexpr int kStageBatch = LORA_STAGE_BATCH;     // 16-byte chunks of A each thread loads at once when staging
 
-// Shrink tile: 64 tokens x one K split, for mods_per_wg modules.  Per K
-// sub-chunk the adapter's A rows (all modules) are staged in LDS once and read
-// by the 4 waves; each wave first issues all its x loads for the sub-chunk
-// (up to kShrinkSteps 16-byte loads per lane), so the x stream overlaps the A
-// staging and the previous sub-chunk's MFMAs.
-template <int MODS, int NTILES>
-__global__ __launch_bounds__(kMfmaThreads) void k_shrink_mfma(ShrinkArgs a) {
-  static_assert(MODS >= 1 && MODS <= kShrinkMaxModules && NTILES >= 1 && NTILES <= 4, "tile shape");
+// Streaming shrink tile: 64 tokens x one K split, for MODS modules that share
+// the x slice.  The A rows of the split (every module, rank rows padded to
+// the tile width) are staged in LDS once, while the first x loads are
+// already in flight.  After that one barrier the four waves are independent:
+// wave w owns tokens 16w..16w+15 and streams its x fragments straight from
+// memory, D steps of 32 k ahead of the matrix cores, to the end of the split
+// with no further barrier; A comes from LDS.  A split whose A rows do not fit
+// in LDS is run as consecutive sub-ranges of a.kc elements, each staged the
+// same way.
+template <int MODS, int NTILES, int D>
+__global__ __launch_bounds__(kMfmaThreads) void k_shrink_stream(ShrinkArgs a) {
+  static_assert(MODS >= 1 && MODS <= kShrinkMaxModules && NTILES >= 1 && NTILES <= 4 && D >= 1, "tile shape");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int ALD = a.kc + 8;                                   // A_s row stride (bf16)
-  __bf16* A_s = reinterpret_cast<__bf16*>(smem);              // [mods][ldr][ALD]
-  int32_t* pid_s = reinterpret_cast<int32_t*>(smem + static_cast<size_t>(MODS) * a.ldr * ALD * 2);
-  __shared__ int32_t toks_s[kTileTokens];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ks = blockIdx.y;
   const int grp = blockIdx.z;
@@ -91,15 +86,16 @@ __global__ __launch_bounds__(kMfmaThreads) void k_shrink_mfma(ShrinkArgs a) {
   const int n_tiles = a.sv.meta[LORA_META_N_TILES];
   const int32_t h = static_cast<int32_t>(a.pv.page_elems);
   const __bf16* pages = static_cast<const __bf16*>(a.pv.pages);
-  const int k_begin = ks * a.k_per_split;
-  const int k_end = min(a.h_in, k_begin + a.k_per_split);
+  const int k_split = ks * a.k_per_split;
+  const int k_split_end = min(a.h_in, k_split + a.k_per_split);
+  const int ALD = a.kc + 8;                                   // A_s row stride (bf16)
+  __bf16* A_s = reinterpret_cast<__bf16*>(smem);              // [MODS][16*NTILES][ALD]
+  int32_t* pid_s = reinterpret_cast<int32_t*>(smem + static_cast<size_t>(MODS) * 16 * NTILES * ALD * 2);
+  __shared__ int32_t toks_s[kTileTokens];
   const int ppr = a.h_in / h;
   const int kq = (lane >> 4) * 8;        // this lane's k offset inside a 32-wide step
   const int mrow = wave * 16 + (lane & 15);
 
-  // the tile count and this workgroup's first tile record travel together; the
-  // entries, the A page ids (fixed table layout: rank row j, page p at j*ppr + p)
-  // and the token ids then load in one round trip
   const int2* tiles = reinterpret_cast<const int2*>(a.sv.tiles);
   int tile = item_of_block<kTileRun>(blockIdx.x, static_cast<int>(blockIdx.y + gridDim.y * blockIdx.z));
   int2 rec = tiles[min(tile, a.sv.max_tiles - 1)];
@@ -107,10 +103,10 @@ __global__ __launch_bounds__(kMfmaThreads) void k_shrink_mfma(ShrinkArgs a) {
   for (; tile < n_tiles; tile += gridDim.x) {
     if (tile >= static_cast<int>(gridDim.x)) rec = tiles[tile];
     const int slot = rec.x & 0xffff, len = rec.x >> 16, pos = rec.y;
-    SlotEntry e[MODS];
+    int rank[MODS];
 #pragma unroll
-    for (int mi = 0; mi < MODS; ++mi) e[mi] = a.pv.entries[slot * a.pv.n_modules + a.module0 + grp * MODS + mi];
-    __syncthreads();
+    for (int mi = 0; mi < MODS; ++mi) rank[mi] = a.pv.entries[slot * a.pv.n_modules + a.module0 + grp * MODS + mi].rank;
+    __syncthreads();                     // the previous tile is done with toks_s and pid_s
     if (tid < kTileTokens) toks_s[tid] = tid < len ? a.sv.perm[pos + tid] : -1;
 #pragma unroll
     for (int mi = 0; mi < MODS; ++mi) {
@@ -119,72 +115,87 @@ __global__ __launch_bounds__(kMfmaThreads) void k_shrink_mfma(ShrinkArgs a) {
       for (int i = tid; i < n_ids; i += kMfmaThreads) pid_s[mi * a.max_pids + i] = ids[i];
     }
     __syncthreads();
+    // rows without a token read row 0 of x: an output row depends only on its own x row,
+    // and those rows are never stored
     const int tok = toks_s[mrow];
-    const __bf16* xrow = a.x + grp * a.msx + static_cast<int64_t>(tok < 0 ? 0 : tok) * a.ld_x + kq;
-
     f32x4 acc[MODS][NTILES];
 #pragma unroll
     for (int mi = 0; mi < MODS; ++mi)
 #pragma unroll
       for (int nt = 0; nt < NTILES; ++nt) acc[mi][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int kc0 = k_begin; kc0 < k_end; kc0 += a.kc) {
-      const int kc1 = min(k_end, kc0 + a.kc);
-      const int nsteps = (kc1 - kc0) >> 5;
-      // 1) this thread's share of the sub-chunk's A rows [mods][ldr][kc1-kc0]
-      //    (at most kStageBatch 16-byte chunks: the host sizes kc for that).
-      //    Rows past a module's rank read its last row: they only feed output
-      //    columns past the rank, which are never stored.
-      const int cpr = (kc1 - kc0) >> 3;                       // 16-byte chunks per row
-      const int n_chunks = MODS * a.ldr * cpr;
+    for (int k_begin = k_split; k_begin < k_split_end; k_begin += a.kc) {
+    const int klen = min(a.kc, k_split_end - k_begin);
+    const int n = klen >> 5;               // 32-wide steps of the sub-range
+    const __bf16* xrow = a.x + grp * a.msx + static_cast<int64_t>(tok < 0 ? 0 : tok) * a.ld_x + k_begin + kq;
+    if (k_begin != k_split) __syncthreads();   // every wave is done with the previous sub-range's A
+
+    // x prologue: steps 0..D-1 (a split shorter than D steps repeats its last step)
+    bf16x8 xb[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) xb[i] = ld_bf16x8(xrow + 32 * min(i, n - 1));
+    // A rows of the split into LDS, kStageBatch 16-byte chunks per thread at a time.  Rows
+    // past a module's rank read its last row: they only feed output columns past the rank,
+    // which are never stored.
+    const int cpr = klen >> 3;                                  // 16-byte chunks per row
+    const int n_chunks = MODS * 16 * NTILES * cpr;
+    for (int c0 = 0; c0 < n_chunks; c0 += kMfmaThreads * kStageBatch) {
       u32x4 av[kStageBatch];
 #pragma unroll
       for (int q = 0; q < kStageBatch; ++q) {
-        const int idx = min(tid + kMfmaThreads * q, n_chunks - 1);
+        const int idx = min(c0 + tid + kMfmaThreads * q, n_chunks - 1);
         const int row = idx / cpr, c = idx - row * cpr;
-        const int mi = row / a.ldr, j = row - mi * a.ldr;
+        const int mi = row / (16 * NTILES), j = row - mi * (16 * NTILES);
         int rank_mi = 0;
 #pragma unroll
         for (int m2 = 0; m2 < MODS; ++m2)
-          if (m2 == mi) rank_mi = e[m2].rank;
+          if (m2 == mi) rank_mi = rank[m2];
         const int jj = max(0, min(j, rank_mi - 1));
-        const int k = kc0 + c * 8;
+        const int k = k_begin + c * 8;
         const int pg = ppr == 1 ? 0 : static_cast<int>(__umulhi(static_cast<uint32_t>(k), a.magic));
         const int pid = rank_mi > 0 ? pid_s[mi * a.max_pids + jj * ppr + pg] : 0;
         av[q] = *reinterpret_cast<const u32x4*>(pages + static_cast<int64_t>(pid) * h + (k - pg * h));
       }
-      // 2) the x fragments of the sub-chunk, unconditional (no branch, so no
-      //    wait between them): steps past the sub-chunk repeat its last step and
-      //    rows without a token read row 0; an output row depends only on its
-      //    own x row, and those rows are never stored.
-      bf16x8 xf[kShrinkSteps];
-#pragma unroll
-      for (int i = 0; i < kShrinkSteps; ++i) xf[i] = ld_bf16x8_nt(xrow + min(kc0 + 32 * i, kc1 - 32));
-      // 3) write A to LDS once the previous sub-chunk's reads are done
-      __syncthreads();
 #pragma unroll
       for (int q = 0; q < kStageBatch; ++q) {
-        const int idx = tid + kMfmaThreads * q;
+        const int idx = c0 + tid + kMfmaThreads * q;
         if (idx < n_chunks) {
           const int row = idx / cpr, c = idx - row * cpr;
           *reinterpret_cast<u32x4*>(A_s + static_cast<size_t>(row) * ALD + c * 8) = av[q];
         }
       }
-      __syncthreads();
+    }
+    __syncthreads();
+
+    // this lane's A row of each (module, 16-column tile) in LDS
+    const __bf16* arow = A_s + static_cast<size_t>(lane & 15) * ALD + kq;
+    auto consume = [&](int i, int s) {
 #pragma unroll
-      for (int i = 0; i < kShrinkSteps; ++i) {
-        if (i >= nsteps) continue;             // fixed trip count: xf stays in registers
+      for (int mi = 0; mi < MODS; ++mi)
 #pragma unroll
-        for (int mi = 0; mi < MODS; ++mi) {
-#pragma unroll
-          for (int nt = 0; nt < NTILES; ++nt) {
-            if (nt * 16 >= e[mi].rank) continue;
-            const bf16x8 af = *reinterpret_cast<const bf16x8*>(
-                A_s + static_cast<size_t>(mi * a.ldr + nt * 16 + (lane & 15)) * ALD + 32 * i + kq);
-            acc[mi][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[i], af, acc[mi][nt], 0, 0, 0);
+        for (int nt = 0; nt < NTILES; ++nt)
+          if (nt * 16 < rank[mi]) {
+            const bf16x8 af = *reinterpret_cast<const bf16x8*>(arow + static_cast<size_t>(mi * 16 * NTILES + nt * 16) * ALD + 32 * s);
+            acc[mi][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb[i], af, acc[mi][nt], 0, 0, 0);
           }
-        }
+    };
+    int s0 = 0;
+    for (; s0 + 2 * D <= n; s0 += D) {   // every refill is in range
+#pragma unroll
+      for (int i = 0; i < D; ++i) {
+        consume(i, s0 + i);
+        xb[i] = ld_bf16x8(xrow + 32 * (s0 + D + i));
       }
+    }
+    // the last 1..2D-1 steps: buffer i holds step s0+i, then step s0+D+i
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      if (s0 + i < n) consume(i, s0 + i);
+      if (s0 + D + i < n) xb[i] = ld_bf16x8(xrow + 32 * (s0 + D + i));
+    }
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+      if (s0 + D + i < n) consume(i, s0 + D + i);
     }
 
     // D layout: lane l holds rows 4*(l>>4)+i (token rows of this wave), column l&15 (rank)
@@ -196,17 +207,16 @@ __global__ __launch_bounds__(kMfmaThreads) void k_shrink_mfma(ShrinkArgs a) {
 #pragma unroll
         for (int nt = 0; nt < NTILES; ++nt) {
           const int j = nt * 16 + (lane & 15);
-          if (nt * 16 >= e[mi].rank) continue;
+          if (nt * 16 >= rank[mi]) continue;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int tk = toks_s[rbase + i];
-            if (tk >= 0 && j < e[mi].rank) tm[static_cast<int64_t>(tk) * a.ld_t + j] = acc[mi][nt][i];
+            if (tk >= 0 && j < rank[mi]) tm[static_cast<int64_t>(tk) * a.ld_t + j] = acc[mi][nt][i];
           }
         }
       }
       continue;
     }
-
     // split K: this split's partial tile goes to the workspace; k_shrink_reduce
     // (the next launch on the stream) adds the splits in order
     const int64_t tile_block = static_cast<int64_t>(kTileTokens) * a.ldr;
@@ -216,7 +226,7 @@ __global__ __launch_bounds__(kMfmaThreads) void k_shrink_mfma(ShrinkArgs a) {
       float* pp = a.part + ((base_tg + mi) * a.ks_count + ks) * tile_block;
 #pragma unroll
       for (int nt = 0; nt < NTILES; ++nt) {
-        if (nt * 16 >= e[mi].rank) continue;
+        if (nt * 16 >= rank[mi]) continue;
         const int j = nt * 16 + (lane & 15);
 #pragma unroll
         for (int i = 0; i < 4; ++i) pp[(rbase + i) * a.ldr + j] = acc[mi][nt][i];
@@ -224,6 +234,19 @@ __global__ __launch_bounds__(kMfmaThreads) void k_shrink_mfma(ShrinkArgs a) {
     }
   }
 }
+
+// LDS of k_shrink_stream: a sub-range's A rows [mods][16*ntiles][kc + 8] bf16 and
+// the tile's A page ids [mods][max_pids].
+__host__ __device__ inline size_t stream_lds_bytes(int mods, int ntiles, int kc, int max_pids) {
+  return static_cast<size_t>(mods) * 16 * ntiles * (kc + 8) * 2 + static_cast<size_t>(mods) * max_pids * 4;
+}
+
+// Prefetch depth of k_shrink_stream: 32-wide steps of x in flight per wave
+// (16 bytes per lane each).
+#ifndef LORA_STREAM_DEPTH
+#define LORA_STREAM_DEPTH 8
+#endif
+constexpr int kStreamDepth = LORA_STREAM_DEPTH;
 
 // Sum of the K splits of each tile, in split order: t[tok][j] = sum_q part[q].
 // One workgroup per (tile, module); grid (tiles, groups * mods_per_wg).
