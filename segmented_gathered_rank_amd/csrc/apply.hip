@@ -153,10 +153,9 @@ lora_status launch_shrink(const lora_pool* p, int32_t module0, int32_t n_modules
   g.mst = mst;
   const int32_t gemv_units = use_mfma ? max_short_units_of(seg) : seg->max_units;   // what units_word can count
   g.parts = (p->max_rank + kPartRows - 1) / kPartRows;   // a work item per 16 rank rows of a unit
-  hipLaunchKernelGGL((k_gemv<1, TI, TI>), dim3(gemv_grid_of(gemv_units * g.parts), n_modules), dim3(kGemvThreads), 0,
-                     s, g);
-  if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
+  const unsigned gx = gemv_grid_of(gemv_units * g.parts);
   if constexpr (sizeof(TI) == 2) {
+    // long segments on matrix-core tiles and short units on the GEMV path, in one launch
     if (use_mfma && seg->max_tiles > 0) {
       const bool shared = (msx == 0 && n_modules > 1 && n_modules <= kShrinkMaxModules);
       const int32_t groups = shared ? 1 : n_modules;
@@ -197,11 +196,14 @@ lora_status launch_shrink(const lora_pool* p, int32_t module0, int32_t n_modules
       kc_max = std::max(32, kc_max / 32 * 32);
       const int32_t n_sub = (kps + kc_max - 1) / kc_max;
       a.kc = ((kps + n_sub - 1) / n_sub + 31) / 32 * 32;
-      const size_t lds = stream_lds_bytes(per_wg, ntiles, a.kc, a.max_pids);
+      const size_t lds = std::max(stream_lds_bytes(per_wg, ntiles, a.kc, a.max_pids), gemv_lds_bytes<1, __bf16>());
       a.part = ks > 1 ? static_cast<float*>(ws) : nullptr;
-      const dim3 grid(tile_grid_of(seg->max_tiles), ks, groups), block(kMfmaThreads);
-#define LORA_SHRINK_LAUNCH(M, NT) \
-  hipLaunchKernelGGL((k_shrink_stream<M, NT, kStreamDepth>), grid, block, lds, s, a)
+      const int tnx = static_cast<int>(tile_grid_of(seg->max_tiles));
+      const dim3 grid(static_cast<unsigned>(tnx * ks * groups) + gx * static_cast<unsigned>(n_modules)),
+          block(kMfmaThreads);
+#define LORA_SHRINK_LAUNCH(M, NT)                                                                        \
+  hipLaunchKernelGGL((k_shrink_mixed<M, NT, kStreamDepth>), grid, block, lds, s, a, g, tnx, ks, groups, \
+                     static_cast<int>(gx), n_modules)
 #define LORA_SHRINK_NT(M)                                 \
   do {                                                    \
     if (ntiles == 1) LORA_SHRINK_LAUNCH(M, 1);            \
@@ -221,9 +223,11 @@ lora_status launch_shrink(const lora_pool* p, int32_t module0, int32_t n_modules
         hipLaunchKernelGGL(k_shrink_reduce, dim3(tile_grid_of(seg->max_tiles), n_modules), block, 0, s, a);
         if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
       }
+      return LORA_OK;
     }
   }
-  return LORA_OK;
+  hipLaunchKernelGGL((k_gemv<1, TI, TI>), dim3(gx, n_modules), dim3(kGemvThreads), 0, s, g);
+  return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
 template <typename TI, typename TO>
@@ -246,31 +250,44 @@ lora_status launch_expand(const lora_pool* p, int32_t module0, int32_t n_modules
   // a work item per column range of at least 64 quads, as many ranges as 16-row blocks of rank
   const int32_t col_ranges = static_cast<int32_t>(p->h_out[module0] / 4 / 64);
   g.parts = std::max(1, std::min((p->max_rank + kPartRows - 1) / kPartRows, col_ranges));
-  hipLaunchKernelGGL((k_gemv<2, TI, TO>), dim3(gemv_grid_of(gemv_units * g.parts), n_modules), dim3(kGemvThreads), 0,
-                     s, g);
-  if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
+  const unsigned gx = gemv_grid_of(gemv_units * g.parts);
   if constexpr (sizeof(TI) == 2) {
+    // long segments on matrix-core tiles and short units on the GEMV path, in one launch
     if (use_mfma && seg->max_tiles > 0) {
-      const int32_t ldr = ldr_of(p);
-      const size_t ysz = sizeof(TO);
-      const size_t lds = expand_lds_bytes(ldr, static_cast<int>(ysz));
+      ExpandArgs ea;
+      ea.pv = pv;
+      ea.sv = sv;
+      ea.t = t;
+      ea.ld_t = ld_t;
+      ea.mst = mst;
+      ea.y = y;
+      ea.ld_y = ld_y;
+      ea.msy = msy;
+      ea.module0 = module0;
+      ea.h_out = h_out;
+      ea.ldr = ldr_of(p);
+      ea.b_ids_at = static_cast<int32_t>(p->max_rank * (p->h_in[module0] / p->page_elems));
+      const size_t lds =
+          std::max(expand_lds_bytes(ea.ldr, static_cast<int>(sizeof(TO))), gemv_lds_bytes<2, __bf16>());
       static size_t lds_allowed = 64 * 1024;   // up to 78 KiB at rank 64 with fp32 y (gfx950: 160 KiB)
       if (lds > lds_allowed) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_expand_mfma<TO>),
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_expand_mixed<TO>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)) != hipSuccess) {
           (void)hipGetLastError();
           return LORA_ERR_HIP;
         }
         lds_allowed = lds;
       }
-      const int32_t col_groups = (h_out / kExpandCols + kExpandBlocks - 1) / kExpandBlocks;
-      hipLaunchKernelGGL((k_expand_mfma<TO>), dim3(tile_grid_of(seg->max_tiles), col_groups, n_modules),
-                         dim3(kMfmaThreads), lds, s, pv, module0, sv, t, ld_t, mst, static_cast<TO*>(y), ld_y, msy,
-                         h_out, ldr, static_cast<int32_t>(p->max_rank * (p->h_in[module0] / p->page_elems)));
-      if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
+      const int tnx = static_cast<int>(tile_grid_of(seg->max_tiles));
+      const int col_groups = (h_out / kExpandCols + kExpandBlocks - 1) / kExpandBlocks;
+      const dim3 grid(static_cast<unsigned>(tnx * col_groups * n_modules) + gx * static_cast<unsigned>(n_modules));
+      hipLaunchKernelGGL((k_expand_mixed<TO>), grid, dim3(kMfmaThreads), lds, s, ea, g, tnx, col_groups, n_modules,
+                         static_cast<int>(gx), n_modules);
+      return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
     }
   }
-  return LORA_OK;
+  hipLaunchKernelGGL((k_gemv<2, TI, TO>), dim3(gx, n_modules), dim3(kGemvThreads), 0, s, g);
+  return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
 template <typename TI, typename TO>

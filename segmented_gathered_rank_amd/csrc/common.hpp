@@ -195,6 +195,24 @@ __device__ __forceinline__ int item_of_block(int bx, int plane) {
 }
 constexpr int kTileRun = 2;   // consecutive matrix-core tiles one XCD takes
 
+// A workgroup's coordinates in the grid of its kernel body.  A body that
+// has a launch of its own takes the launch's; one that shares a launch with
+// another body takes those of its part of the launch, laid out x fastest as
+// the hardware dispatches (so a part that starts at a multiple of 8 keeps
+// the XCD of every block: block i goes to XCD i % 8).
+struct Blk {
+  int x, y, z, nx, ny, nz;
+};
+__device__ __forceinline__ Blk blk_of_launch() {
+  return Blk{static_cast<int>(blockIdx.x), static_cast<int>(blockIdx.y), static_cast<int>(blockIdx.z),
+             static_cast<int>(gridDim.x),  static_cast<int>(gridDim.y),  static_cast<int>(gridDim.z)};
+}
+// Block `lin` of a grid nx x ny x nz.
+__device__ __forceinline__ Blk blk_of_linear(int lin, int nx, int ny, int nz) {
+  const int x = lin % nx, yz = lin / nx;
+  return Blk{x, yz % ny, yz / ny, nx, ny, nz};
+}
+
 // Upper bounds of the segment work lists (host and device agree on them).
 __host__ __device__ inline int32_t max_segs_of(int32_t n_tokens, int32_t n_slots) {
   return n_tokens < n_slots ? n_tokens : n_slots;

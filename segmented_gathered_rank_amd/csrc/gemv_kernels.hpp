@@ -332,13 +332,19 @@ struct GemvArgs {
   int64_t ld_y, msy;
 };
 
+// LDS of the GEMV body: the unit's tables, then (shrink modes) its staged x rows.
+template <int MODE, typename TI>
+constexpr size_t gemv_xs_offset() { return (sizeof(UnitLds) + 15) / 16 * 16; }
+template <int MODE, typename TI>
+constexpr size_t gemv_lds_bytes() {
+  return gemv_xs_offset<MODE, TI>() + ((MODE == 2) ? 16 : kUnitTokens * XSlice<TI>::kElems * sizeof(TI));
+}
+
 // MODE 0: fused BGMV (t kept in LDS); 1: shrink only (t to memory); 2: expand only.
-// gridDim.x is a multiple of 8*kUnitRun (see unit_of_block); gridDim.y = modules.
+// b.nx is a multiple of 8*kUnitRun (see unit_of_block); b.ny = modules.
 template <int MODE, typename TI, typename TO>
-__global__ __launch_bounds__(kGemvThreads, 4) void k_gemv(GemvArgs a) {
-  __shared__ UnitLds L;
-  __shared__ __attribute__((aligned(16))) TI xs[(MODE == 2) ? 8 : kUnitTokens * XSlice<TI>::kElems];
-  const int m = blockIdx.y;
+__device__ __forceinline__ void gemv_body(const GemvArgs& a, const Blk b, UnitLds& L, TI* xs) {
+  const int m = b.y;
   const TI* xm = static_cast<const TI*>(a.x) + m * a.msx;
   float* tm = a.t + m * a.mst;
   TO* ym = static_cast<TO*>(a.y) + m * a.msy;
@@ -354,11 +360,11 @@ __global__ __launch_bounds__(kGemvThreads, 4) void k_gemv(GemvArgs a) {
   // so that a unit's serial batches spread over several workgroups
   const int parts = a.parts;
   const int n_items = n_units * parts;
-  int it = unit_of_block(blockIdx.x, m);
+  int it = unit_of_block(b.x, m);
   int2 rec = units[min(it / parts, a.sv.max_units - 1)];
-  for (; it < n_items; it += gridDim.x) {
+  for (; it < n_items; it += b.nx) {
     const int u = it / parts, part = it - u * parts;
-    if (it >= static_cast<int>(gridDim.x)) rec = units[u];
+    if (it >= b.nx) rec = units[u];
     const int slot = rec.x & 0xffff, nt = (rec.x >> 16) & 0xff, pos = rec.y;
     const bool keep = (rec.x >> 24) & 1;
     const int ei = slot * a.pv.n_modules + a.module0 + m;
@@ -419,6 +425,13 @@ __global__ __launch_bounds__(kGemvThreads, 4) void k_gemv(GemvArgs a) {
 #undef LORA_EXPAND_CALL
     }
   }
+}
+
+template <int MODE, typename TI, typename TO>
+__global__ __launch_bounds__(kGemvThreads, 4) void k_gemv(GemvArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[gemv_lds_bytes<MODE, TI>()];
+  gemv_body<MODE, TI, TO>(a, blk_of_launch(), *reinterpret_cast<UnitLds*>(lds),
+                          reinterpret_cast<TI*>(lds + gemv_xs_offset<MODE, TI>()));
 }
 
 }  // namespace lora

@@ -20,7 +20,7 @@
 //   with v_mfma_f32_32x32x16_bf16.  t is split into three bf16 parts whose sum
 //   is t exactly, so the matrix cores multiply by t itself (three MFMAs per K
 //   step of 16 instead of eight fp32 32x32x2 steps); formed transposed so that
-//   the accumulators map onto y rows (see k_expand_mfma).
+//   the accumulators map onto y rows (see expand_mfma_body).
 #pragma once
 
 #include "common.hpp"
@@ -75,14 +75,14 @@ constexpr int kStageBatch = LORA_STAGE_BATCH;     // 16-byte chunks of A each th
 // with no further barrier; A comes from LDS.  A split whose A rows do not fit
 // in LDS is run as consecutive sub-ranges of a.kc elements, each staged the
 // same way.
+// Grid (b): x over tiles, y over K splits, z over module groups.
 template <int MODS, int NTILES, int D>
-__global__ __launch_bounds__(kMfmaThreads) void k_shrink_stream(ShrinkArgs a) {
+__device__ __forceinline__ void shrink_stream_body(const ShrinkArgs& a, const Blk b, unsigned char* smem) {
   static_assert(MODS >= 1 && MODS <= kShrinkMaxModules && NTILES >= 1 && NTILES <= 4 && D >= 1, "tile shape");
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ks = blockIdx.y;
-  const int grp = blockIdx.z;
-  const int groups = gridDim.z;
+  const int ks = b.y;
+  const int grp = b.z;
+  const int groups = b.nz;
   const int n_tiles = a.sv.meta[LORA_META_N_TILES];
   const int32_t h = static_cast<int32_t>(a.pv.page_elems);
   const __bf16* pages = static_cast<const __bf16*>(a.pv.pages);
@@ -97,11 +97,11 @@ __global__ __launch_bounds__(kMfmaThreads) void k_shrink_stream(ShrinkArgs a) {
   const int mrow = wave * 16 + (lane & 15);
 
   const int2* tiles = reinterpret_cast<const int2*>(a.sv.tiles);
-  int tile = item_of_block<kTileRun>(blockIdx.x, static_cast<int>(blockIdx.y + gridDim.y * blockIdx.z));
+  int tile = item_of_block<kTileRun>(b.x, b.y + b.ny * b.z);
   int2 rec = tiles[min(tile, a.sv.max_tiles - 1)];
   const int n_ids = min(a.ldr, a.pv.max_rank) * ppr;
-  for (; tile < n_tiles; tile += gridDim.x) {
-    if (tile >= static_cast<int>(gridDim.x)) rec = tiles[tile];
+  for (; tile < n_tiles; tile += b.nx) {
+    if (tile >= b.nx) rec = tiles[tile];
     const int slot = rec.x & 0xffff, len = rec.x >> 16, pos = rec.y;
     int rank[MODS];
 #pragma unroll
@@ -235,13 +235,13 @@ __global__ __launch_bounds__(kMfmaThreads) void k_shrink_stream(ShrinkArgs a) {
   }
 }
 
-// LDS of k_shrink_stream: a sub-range's A rows [mods][16*ntiles][kc + 8] bf16 and
+// LDS of shrink_stream_body: a sub-range's A rows [mods][16*ntiles][kc + 8] bf16 and
 // the tile's A page ids [mods][max_pids].
 __host__ __device__ inline size_t stream_lds_bytes(int mods, int ntiles, int kc, int max_pids) {
   return static_cast<size_t>(mods) * 16 * ntiles * (kc + 8) * 2 + static_cast<size_t>(mods) * max_pids * 4;
 }
 
-// Prefetch depth of k_shrink_stream: 32-wide steps of x in flight per wave
+// Prefetch depth of shrink_stream_body: 32-wide steps of x in flight per wave
 // (16 bytes per lane each).
 #ifndef LORA_STREAM_DEPTH
 #define LORA_STREAM_DEPTH 8
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(kMfmaThreads) void k_shrink_reduce(ShrinkArgs a) {
 // and an LDS tile with coalesced 16-byte row accesses (a wave covers whole
 // rows), and between LDS and the MFMA layout with 8- or 16-byte accesses.
 // T (fp32) is staged once per tile, the B block (bf16) once per column block.
-// LDS of k_expand_mfma for pool rank cap ldr and y element size ysz: the
+// LDS of expand_mfma_body for pool rank cap ldr and y element size ysz: the
 // three bf16 parts of the T tile [3][64][r16+8], the transposed B block
 // [128][r16+8] (bf16) and the y block [64][128 + 16/ysz].
 __host__ __device__ inline int expand_r16(int ldr) { return (ldr + 15) & ~15; }
@@ -315,18 +315,33 @@ __host__ __device__ inline size_t expand_lds_bytes(int ldr, int ysz) {
          static_cast<size_t>(kTileTokens) * (kExpandCols + 16 / ysz) * ysz;
 }
 
+struct ExpandArgs {
+  PoolView pv;
+  SegView sv;
+  const float* t;
+  int64_t ld_t, mst;          // mst: t offset between modules
+  void* y;
+  int64_t ld_y, msy;          // msy: y offset between modules
+  int32_t module0;
+  int32_t h_out;
+  int32_t ldr;                // rank cap of the pool rounded up to 16
+  int32_t b_ids_at;           // offset of B's page ids in a (slot, module) page table
+};
+
+// Grid (b): x over tiles, y over groups of kExpandBlocks column blocks, z over modules.
 template <typename TO>
-__global__ __launch_bounds__(kMfmaThreads, sizeof(TO) == 2 ? 3 : 2) void k_expand_mfma(PoolView pv, int32_t module0, SegView sv,
-                                                                const float* __restrict__ t, int64_t ld_t,
-                                                                int64_t mst, TO* __restrict__ y, int64_t ld_y,
-                                                                int64_t msy, int32_t h_out, int32_t ldr,
-                                                                int32_t b_ids_at) {
+__device__ __forceinline__ void expand_mfma_body(const ExpandArgs& ea, const Blk b, unsigned char* smem) {
+  const PoolView& pv = ea.pv;
+  const SegView& sv = ea.sv;
+  const int32_t module0 = ea.module0, h_out = ea.h_out, ldr = ea.ldr, b_ids_at = ea.b_ids_at;
+  const int64_t ld_t = ea.ld_t, mst = ea.mst, ld_y = ea.ld_y, msy = ea.msy;
+  const float* __restrict__ t = ea.t;
+  TO* __restrict__ y = static_cast<TO*>(ea.y);
   constexpr int TN = kExpandCols;
   constexpr int YLD = TN + 16 / sizeof(TO);           // Y_s row stride (elements)
   constexpr int YCPR = TN * sizeof(TO) / 16;          // 16-byte chunks per y row of the block
   constexpr int YCH = kTileTokens * YCPR / kMfmaThreads;   // y chunks per thread
   constexpr int YV = 16 / sizeof(TO);                 // elements per 16-byte chunk
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int r16 = expand_r16(ldr);
   const int LD = r16 + 8;                             // row stride of T3_s and BT_s (bf16)
   __bf16* T3_s = reinterpret_cast<__bf16*>(smem);                                  // [3][64][LD]
@@ -336,7 +351,7 @@ __global__ __launch_bounds__(kMfmaThreads, sizeof(TO) == 2 ? 3 : 2) void k_expan
   __shared__ int32_t bids_s[kMaxEntryPages];   // B page ids of the tile's (slot, module): row j, page p at j*ppr + p
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int m = blockIdx.z;
+  const int m = b.z;
   const int n_tiles = sv.meta[LORA_META_N_TILES];
   const int32_t h = static_cast<int32_t>(pv.page_elems);
   const __bf16* pages = static_cast<const __bf16*>(pv.pages);
@@ -349,11 +364,11 @@ __global__ __launch_bounds__(kMfmaThreads, sizeof(TO) == 2 ? 3 : 2) void k_expan
   // entry, the B page ids (fixed table layout, from b_ids_at) and the token ids
   // then load in one round trip, and t, y and the B rows in the next
   const int2* tiles = reinterpret_cast<const int2*>(sv.tiles);
-  int tile = item_of_block<kTileRun>(blockIdx.x, static_cast<int>(blockIdx.y + gridDim.y * blockIdx.z));
+  int tile = item_of_block<kTileRun>(b.x, b.y + b.ny * b.z);
   int2 rec = tiles[min(tile, sv.max_tiles - 1)];
   const int n_bids = pv.max_rank * ppr;
-  for (; tile < n_tiles; tile += gridDim.x) {
-    if (tile >= static_cast<int>(gridDim.x)) rec = tiles[tile];
+  for (; tile < n_tiles; tile += b.nx) {
+    if (tile >= b.nx) rec = tiles[tile];
     const int slot = rec.x & 0xffff, len = rec.x >> 16, pos = rec.y;
     const int ei = slot * pv.n_modules + module0 + m;
     const SlotEntry e = pv.entries[ei];
@@ -370,7 +385,7 @@ __global__ __launch_bounds__(kMfmaThreads, sizeof(TO) == 2 ? 3 : 2) void k_expan
     // B block [rk <= 32 rows][TN] (bf16): rank row j, columns c0..c0+TN of that row
     u32x4 yv[YCH], bv[2];
     auto issue = [&](int cb, u32x4 (&yq)[YCH], u32x4 (&bq)[2]) {
-      const int c0 = (blockIdx.y * kExpandBlocks + cb) * TN;
+      const int c0 = (b.y * kExpandBlocks + cb) * TN;
       const int p = c0 / h;                    // the column block lies inside page p of each row
       const int off = c0 - p * h;
 #pragma unroll
@@ -399,7 +414,7 @@ __global__ __launch_bounds__(kMfmaThreads, sizeof(TO) == 2 ? 3 : 2) void k_expan
         BT_s[(c + 2 * i + 1) * LD + j] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(w[i] >> 16));
       }
     };
-    const int n_cb = min(kExpandBlocks, (h_out - static_cast<int>(blockIdx.y) * kExpandBlocks * TN + TN - 1) / TN);
+    const int n_cb = min(kExpandBlocks, (h_out - b.y * kExpandBlocks * TN + TN - 1) / TN);
     // T tile: t = hi + mid + lo, three bf16 values whose sum is t exactly (3 x 8 significand
     // bits cover fp32's 24), so the bf16 matrix cores multiply by t itself.  Thread -> row
     // tid/4, columns (tid%4) + 4q; its loads go out with block 0's.  Later blocks load at the
@@ -430,7 +445,7 @@ __global__ __launch_bounds__(kMfmaThreads, sizeof(TO) == 2 ? 3 : 2) void k_expan
 #pragma unroll
     for (int cb = 0; cb < kExpandBlocks; ++cb) {
       if (cb >= n_cb) break;                   // uniform
-      const int c0 = (blockIdx.y * kExpandBlocks + cb) * TN;
+      const int c0 = (b.y * kExpandBlocks + cb) * TN;
       const int p = c0 / h;
       const int off = c0 - p * h;
       if (cb > 0) issue(cb, yv, bv);
@@ -503,6 +518,43 @@ __global__ __launch_bounds__(kMfmaThreads, sizeof(TO) == 2 ? 3 : 2) void k_expan
               *reinterpret_cast<const u32x4*>(Y_s + r * YLD + c);
       }
     }
+  }
+}
+
+// A mixed batch in one launch (decode tokens and short segments next to long
+// segments, the study page's "one kernel for a mixed batch"): the first
+// tnx*tny*tnz workgroups run matrix-core tiles, the rest run GEMV work items
+// (a grid of gnx x gny, gny = modules).  Both parts start at multiples of 8 workgroups,
+// so each keeps its XCD-aware map, and both take their LDS from the launch's
+// dynamic LDS, sized for the larger of the two.
+template <int MODS, int NTILES, int D>
+__global__ __launch_bounds__(kMfmaThreads) void k_shrink_mixed(ShrinkArgs a, GemvArgs g, int tnx, int tny, int tnz,
+                                                               int gnx, int gny) {
+  static_assert(kMfmaThreads == kGemvThreads, "both parts run on one workgroup size");
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int lin = static_cast<int>(blockIdx.x), tile_blocks = tnx * tny * tnz;
+  if (lin < tile_blocks) {
+    shrink_stream_body<MODS, NTILES, D>(a, blk_of_linear(lin, tnx, tny, tnz), smem);
+  } else {
+    gemv_body<1, __bf16, __bf16>(g, blk_of_linear(lin - tile_blocks, gnx, gny, 1),
+                                 *reinterpret_cast<UnitLds*>(smem),
+                                 reinterpret_cast<__bf16*>(smem + gemv_xs_offset<1, __bf16>()));
+  }
+}
+
+template <typename TO>
+__global__ __launch_bounds__(kMfmaThreads, sizeof(TO) == 2 ? 3 : 2) void k_expand_mixed(ExpandArgs ea, GemvArgs g,
+                                                                                      int tnx, int tny, int tnz,
+                                                                                      int gnx, int gny) {
+  static_assert(kMfmaThreads == kGemvThreads, "both parts run on one workgroup size");
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int lin = static_cast<int>(blockIdx.x), tile_blocks = tnx * tny * tnz;
+  if (lin < tile_blocks) {
+    expand_mfma_body<TO>(ea, blk_of_linear(lin, tnx, tny, tnz), smem);
+  } else {
+    gemv_body<2, __bf16, TO>(g, blk_of_linear(lin - tile_blocks, gnx, gny, 1),
+                             *reinterpret_cast<UnitLds*>(smem),
+                             reinterpret_cast<__bf16*>(smem + gemv_xs_offset<2, __bf16>()));
   }
 }
 
