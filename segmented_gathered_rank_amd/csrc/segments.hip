@@ -38,7 +38,8 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kLdsWords = 16384;      // 64 KiB: histogram rows (+ one row of totals)
-constexpr int kIdBatch = 16;          // 64-token batches a wave loads at once
+constexpr int kIdBatch = 4;           // 64-token batches a wave loads at once (a small unroll keeps the
+                                      // kernel short: it runs cold in one CU's instruction cache)
 constexpr int kRound = 64 * kIdBatch; // tokens a wave loads at once
 constexpr int kChunkTokens = 1024;    // chunked schedule: tokens per workgroup (minimum)
 constexpr int kChunkWords = 1 << 19;  // chunked schedule: bound on chunks * n_slots
