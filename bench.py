@@ -90,14 +90,22 @@ def make_workload(name):
         "modules": "qkv 768->2304, o 768->768, up 768->3072, down 3072->768"}
 
 
-KERNEL_SOURCES = ["common.hpp", "gemv_kernels.hpp", "mfma_kernels.hpp", "fused_gemm.hpp", "apply.hip", "segments.hip"]
+# HIP sources that build the kernel whose HBM traffic a workload's counters measured, and
+# its launch (apply.hip sizes the grids): a change to any of them voids the stored counters.
+KERNEL_SOURCES = {
+    "bgmv_decode_x128": ["common.hpp", "gemv_kernels.hpp", "apply.hip"],
+    "encoder_fused": ["common.hpp", "fused_gemm.hpp", "apply.hip"],
+    "prefill_fused": ["common.hpp", "fused_gemm.hpp", "apply.hip"],
+}
+ALL_KERNEL_SOURCES = ["common.hpp", "gemv_kernels.hpp", "mfma_kernels.hpp", "fused_gemm.hpp", "apply.hip",
+                      "segments.hip"]
 
 
-def kernel_source_sha():
-    """sha256 over the HIP sources of the apply kernels (identifies the kernel version)."""
+def kernel_source_sha(workload):
+    """sha256 over the HIP sources of the workload's measured kernel (identifies its version)."""
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES.get(workload, ALL_KERNEL_SOURCES):
         with open(os.path.join(ROOT, "segmented_gathered_rank_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -114,7 +122,7 @@ def load_traffic(workload):
             t = json.load(fh)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha") != kernel_source_sha():
+    if t.get("kernel_source_sha") != kernel_source_sha(workload):
         return None
     return t.get("hbm_bytes_per_step", t.get("hbm_bytes_per_launch"))
 
@@ -147,7 +155,7 @@ def pmc_summary(args):
                      "scale": ref_kib / max(copies)}
     hbm = 1024.0 * (res["FETCH_SIZE"]["kernel_kib_mean"] * res["FETCH_SIZE"]["scale"] +
                     res["WRITE_SIZE"]["kernel_kib_mean"] * res["WRITE_SIZE"]["scale"])
-    out = {"workload": args.workload, "kernel": args.pmc_kernel, "kernel_source_sha": kernel_source_sha(),
+    out = {"workload": args.workload, "kernel": args.pmc_kernel, "kernel_source_sha": kernel_source_sha(args.workload),
            "hbm_bytes_per_launch": hbm, "counters": res}
     if args.pmc_per_step > 0:   # every launch of the step, averaged, times the launches per step
         out["hbm_bytes_per_step"] = hbm * args.pmc_per_step
