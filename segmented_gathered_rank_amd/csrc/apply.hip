@@ -278,8 +278,13 @@ lora_status launch_expand(const lora_pool* p, int32_t module0, int32_t n_modules
         }
         lds_allowed = lds;
       }
+      // column blocks in groups of kExpandBlocks, the last one short: a workgroup's tile
+      // prologue and t staging serve all its blocks, so even but smaller groups are slower
+      // (768 columns as 3 + 3 blocks: 28.4 us against 26.7 us as 4 + 2)
+      const int n_blocks = h_out / kExpandCols;
+      ea.blocks = kExpandBlocks;
       const int tnx = static_cast<int>(tile_grid_of(seg->max_tiles));
-      const int col_groups = (h_out / kExpandCols + kExpandBlocks - 1) / kExpandBlocks;
+      const int col_groups = (n_blocks + ea.blocks - 1) / ea.blocks;
       const dim3 grid(static_cast<unsigned>(tnx * col_groups * n_modules) + gx * static_cast<unsigned>(n_modules));
       hipLaunchKernelGGL((k_expand_mixed<TO>), grid, dim3(kMfmaThreads), lds, s, ea, g, tnx, col_groups, n_modules,
                          static_cast<int>(gx), n_modules);

@@ -298,7 +298,7 @@ __global__ __launch_bounds__(kMfmaThreads) void k_shrink_reduce(ShrinkArgs a) {
   }
 }
 
-// Expand tile: 64 tokens x kExpandBlocks blocks of kExpandCols columns of one
+// Expand tile: 64 tokens x up to kExpandBlocks blocks of kExpandCols columns of one
 // module.  The product is formed transposed, Y^T[cols x tokens] += B^T[cols x r]
 // T^T[r x tokens] (v_mfma_f32_32x32x2_f32: lane l holds token l%32 and, for
 // i = 0..3, columns 8i + 4(l/32) .. +3 of its wave's 32).  y moves between HBM
@@ -326,9 +326,10 @@ struct ExpandArgs {
   int32_t h_out;
   int32_t ldr;                // rank cap of the pool rounded up to 16
   int32_t b_ids_at;           // offset of B's page ids in a (slot, module) page table
+  int32_t blocks;             // column blocks per workgroup (<= kExpandBlocks)
 };
 
-// Grid (b): x over tiles, y over groups of kExpandBlocks column blocks, z over modules.
+// Grid (b): x over tiles, y over groups of ea.blocks column blocks, z over modules.
 template <typename TO>
 __device__ __forceinline__ void expand_mfma_body(const ExpandArgs& ea, const Blk b, unsigned char* smem) {
   const PoolView& pv = ea.pv;
@@ -385,7 +386,7 @@ __device__ __forceinline__ void expand_mfma_body(const ExpandArgs& ea, const Blk
     // B block [rk <= 32 rows][TN] (bf16): rank row j, columns c0..c0+TN of that row
     u32x4 yv[YCH], bv[2];
     auto issue = [&](int cb, u32x4 (&yq)[YCH], u32x4 (&bq)[2]) {
-      const int c0 = (b.y * kExpandBlocks + cb) * TN;
+      const int c0 = (b.y * ea.blocks + cb) * TN;
       const int p = c0 / h;                    // the column block lies inside page p of each row
       const int off = c0 - p * h;
 #pragma unroll
@@ -414,7 +415,7 @@ __device__ __forceinline__ void expand_mfma_body(const ExpandArgs& ea, const Blk
         BT_s[(c + 2 * i + 1) * LD + j] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(w[i] >> 16));
       }
     };
-    const int n_cb = min(kExpandBlocks, (h_out - b.y * kExpandBlocks * TN + TN - 1) / TN);
+    const int n_cb = min(ea.blocks, (h_out - b.y * ea.blocks * TN + TN - 1) / TN);
     // T tile: t = hi + mid + lo, three bf16 values whose sum is t exactly (3 x 8 significand
     // bits cover fp32's 24), so the bf16 matrix cores multiply by t itself.  Thread -> row
     // tid/4, columns (tid%4) + 4q; its loads go out with block 0's.  Later blocks load at the
@@ -445,7 +446,7 @@ __device__ __forceinline__ void expand_mfma_body(const ExpandArgs& ea, const Blk
 #pragma unroll
     for (int cb = 0; cb < kExpandBlocks; ++cb) {
       if (cb >= n_cb) break;                   // uniform
-      const int c0 = (b.y * kExpandBlocks + cb) * TN;
+      const int c0 = (b.y * ea.blocks + cb) * TN;
       const int p = c0 / h;
       const int off = c0 - p * h;
       if (cb > 0) issue(cb, yv, bv);

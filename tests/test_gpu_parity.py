@@ -274,6 +274,19 @@ def test_c3_reduced_mixed_paths():
         dw.close()
 
 
+@pytest.mark.parametrize("rank", [32, 64])
+def test_shared_x_high_rank_sub_ranges(rank):
+    """q, k, v share x on pools of rank 32 and 64 at h = 4096: the matrix-core shrink runs two or
+    four 16-column tiles per module for three modules at once, K split across workgroups, and
+    each split's A rows staged in LDS as two or four sub-ranges; short segments share the launch."""
+    wl = W.c3_sgmv_prefill(h=4096, rank=rank, units=(2, 8), total_units=32)
+    say(f"shared x, rank {rank}, lengths {wl.notes['segment_lengths'].tolist()}")
+    dw, ys = run(wl, "sgmv")
+    for m in range(4):
+        assert_close(ys[m], lo.apply_to_y0(wl, m), "bf16", f"rank {rank} m{m}")
+    dw.close()
+
+
 def test_c3_delta_tight_fp32_output_matrix_cores():
     """y0 = 0 in fp32 on a batch whose long segments run on the matrix cores: the
     bf16 MFMA expand multiplies by t itself (t as three exact bf16 parts), so the
