@@ -6,6 +6,9 @@
 // lists come from the segment builder and stay on the device; grids are sized
 // by their upper bounds and idle workgroups exit at once.
 #include <algorithm>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "fused_gemm.hpp"
 #include "gemv_kernels.hpp"
@@ -230,6 +233,53 @@ lora_status launch_shrink(const lora_pool* p, int32_t module0, int32_t n_modules
   return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
+// Column blocks per workgroup of the matrix-core expand.  A launch runs in
+// about ceil(workgroups / resident workgroups) rounds, and a round lasts
+// about (blocks per workgroup + 2) block times: a workgroup's tile prologue
+// and t staging cost about two blocks.  The group size (kept even across a
+// tile's groups) that minimizes that product is taken, the larger on a tie.  Measured on the
+// encoder layer and prefill projections it picks the fastest of 4, 6 and 8
+// blocks for every shape (768 columns: 6 blocks, 25.6 us against 27.8 us
+// with 4 and 2; 3072 columns: 8 blocks, 71.5 us against 74.8 us).
+int expand_group_blocks(int n_blocks, int tiles, int n_modules, int resident) {
+  int best_g = 1;
+  int64_t best = INT64_MAX;
+  for (int g = 1; g <= kExpandBlocks; ++g) {
+    const int groups = (n_blocks + g - 1) / g;
+    const int gb = (n_blocks + groups - 1) / groups;
+    const int64_t wgs = static_cast<int64_t>(tiles) * groups * n_modules;
+    const int64_t cost = ((wgs + resident - 1) / resident) * (gb + 2);
+    if (cost <= best) {   // ties go to the larger group: fewer prologues
+      best = cost;
+      best_g = gb;
+    }
+  }
+  return best_g;
+}
+
+// Workgroups of k_expand_mixed<TO> resident on the whole device at `lds` bytes
+// of dynamic LDS (occupancy per CU times CUs), cached per device and LDS size;
+// 0 on a HIP error.
+template <typename TO>
+int expand_resident_groups(int device, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::pair<int, size_t>, int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(device, lds);
+  const auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&k_expand_mixed<TO>),
+                                                   kMfmaThreads, lds) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  const int resident = std::max(1, per_cu) * std::max(1, cus);
+  cache.emplace(key, resident);
+  return resident;
+}
+
 template <typename TI, typename TO>
 lora_status launch_expand(const lora_pool* p, int32_t module0, int32_t n_modules, const float* t, int64_t ld_t,
                           int64_t mst, const lora_segments* seg, void* y, int64_t ld_y, int64_t msy,
@@ -278,11 +328,11 @@ lora_status launch_expand(const lora_pool* p, int32_t module0, int32_t n_modules
         }
         lds_allowed = lds;
       }
-      // column blocks in groups of kExpandBlocks, the last one short: a workgroup's tile
-      // prologue and t staging serve all its blocks, so even but smaller groups are slower
-      // (768 columns as 3 + 3 blocks: 28.4 us against 26.7 us as 4 + 2)
       const int n_blocks = h_out / kExpandCols;
-      ea.blocks = kExpandBlocks;
+      const int resident = expand_resident_groups<TO>(p->device, lds);
+      if (resident <= 0) return LORA_ERR_HIP;
+      ea.blocks = expand_group_blocks(n_blocks, (seg->n_tokens + kTileTokens - 1) / kTileTokens, n_modules,
+                                      resident);
       const int tnx = static_cast<int>(tile_grid_of(seg->max_tiles));
       const int col_groups = (n_blocks + ea.blocks - 1) / ea.blocks;
       const dim3 grid(static_cast<unsigned>(tnx * col_groups * n_modules) + gx * static_cast<unsigned>(n_modules));

@@ -35,9 +35,9 @@ constexpr int kMfmaThreads = 256;
 constexpr int kShrinkMaxModules = 4;   // modules sharing one x slice in a workgroup
 constexpr int kExpandCols = 128;       // output columns per expand block
 #ifndef LORA_EXPAND_BLOCKS
-#define LORA_EXPAND_BLOCKS 4
+#define LORA_EXPAND_BLOCKS 8
 #endif
-constexpr int kExpandBlocks = LORA_EXPAND_BLOCKS;   // column blocks per expand workgroup
+constexpr int kExpandBlocks = LORA_EXPAND_BLOCKS;   // column blocks per expand workgroup, at most
 
 __device__ __forceinline__ bf16x8 ld_bf16x8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
@@ -443,8 +443,8 @@ __device__ __forceinline__ void expand_mfma_body(const ExpandArgs& ea, const Blk
         }
       }
     }
-#pragma unroll
-    for (int cb = 0; cb < kExpandBlocks; ++cb) {
+#pragma unroll 2
+    for (int cb = 0; cb < kExpandBlocks; ++cb) {   // unrolled in pairs: a full unroll spills
       if (cb >= n_cb) break;                   // uniform
       const int c0 = (b.y * ea.blocks + cb) * TN;
       const int p = c0 / h;
