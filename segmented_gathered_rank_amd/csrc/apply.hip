@@ -233,6 +233,23 @@ lora_status launch_shrink(const lora_pool* p, int32_t module0, int32_t n_modules
   return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
+// Raises kernel `fn`'s dynamic LDS limit on `device` to at least `lds` bytes
+// (the default is 64 KiB).  Safe to call from several host threads.
+bool allow_dynamic_lds(const void* fn, int device, size_t lds) {
+  if (lds <= 64 * 1024) return true;
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, size_t> allowed;
+  std::lock_guard<std::mutex> lock(mu);
+  size_t& cur = allowed[std::make_pair(fn, device)];
+  if (lds <= cur) return true;
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  cur = lds;
+  return true;
+}
+
 // Column blocks per workgroup of the matrix-core expand.  A launch runs in
 // about ceil(workgroups / resident workgroups) rounds, and a round lasts
 // about (blocks per workgroup + 2) block times: a workgroup's tile prologue
@@ -319,15 +336,8 @@ lora_status launch_expand(const lora_pool* p, int32_t module0, int32_t n_modules
       ea.b_ids_at = static_cast<int32_t>(p->max_rank * (p->h_in[module0] / p->page_elems));
       const size_t lds =
           std::max(expand_lds_bytes(ea.ldr, static_cast<int>(sizeof(TO))), gemv_lds_bytes<2, __bf16>());
-      static size_t lds_allowed = 64 * 1024;   // up to 78 KiB at rank 64 with fp32 y (gfx950: 160 KiB)
-      if (lds > lds_allowed) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_expand_mixed<TO>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)) != hipSuccess) {
-          (void)hipGetLastError();
-          return LORA_ERR_HIP;
-        }
-        lds_allowed = lds;
-      }
+      // up to 78 KiB at rank 64 with fp32 y (gfx950: 160 KiB per workgroup)
+      if (!allow_dynamic_lds(reinterpret_cast<const void*>(&k_expand_mixed<TO>), p->device, lds)) return LORA_ERR_HIP;
       const int n_blocks = h_out / kExpandCols;
       const int resident = expand_resident_groups<TO>(p->device, lds);
       if (resident <= 0) return LORA_ERR_HIP;

@@ -304,6 +304,20 @@ def test_c3_delta_tight_fp32_output_matrix_cores():
         dw.close()
 
 
+def test_mixed_rank_fp32_output_large_lds():
+    """The mixed-rank batch (ranks up to 64) with y0 = 0 in fp32: the matrix-core expand then
+    needs 78 KiB of LDS (above the 64 KiB default, so the library raises the kernel's limit),
+    and the adapter term of every token, prefill or decode, matches the oracle at fp32 accuracy."""
+    wl = W.c4_mixed_rank(h=1024, draw_w=False)
+    dw = DeviceWorkload(wl, y_dtype="f32")
+    dw.zero_y()
+    dw.sgmv_step()
+    torch.cuda.synchronize()
+    got = from_device(dw.y_of(0)).astype(np.float64)
+    assert rel_l2(got, lo.lora_delta(wl, 0)) <= 1e-5
+    dw.close()
+
+
 def test_wide_rows_in_several_pages():
     """h = 8192 (the GEMV shrink stages x in two slices) with pages of 2048
     elements (four pages per adapter row), on both GEMV paths."""
