@@ -155,7 +155,7 @@ lora_status launch_shrink(const lora_pool* p, int32_t module0, int32_t n_modules
   g.ld_t = ld_t;
   g.mst = mst;
   const int32_t gemv_units = use_mfma ? max_short_units_of(seg) : seg->max_units;   // what units_word can count
-  g.parts = (p->max_rank + kPartRows - 1) / kPartRows;   // a work item per 16 rank rows of a unit
+  g.parts = (p->max_rank + kPartRows - 1) / kPartRows;   // a work item per kPartRows rank rows of a unit
   const unsigned gx = gemv_grid_of(gemv_units * g.parts);
   if constexpr (sizeof(TI) == 2) {
     // long segments on matrix-core tiles and short units on the GEMV path, in one launch
@@ -316,7 +316,7 @@ lora_status launch_expand(const lora_pool* p, int32_t module0, int32_t n_modules
   const int32_t gemv_units = use_mfma ? max_short_units_of(seg) : seg->max_units;   // what units_word can count
   // a work item per column range of at least 64 quads, as many ranges as 16-row blocks of rank
   const int32_t col_ranges = static_cast<int32_t>(p->h_out[module0] / 4 / 64);
-  g.parts = std::max(1, std::min((p->max_rank + kPartRows - 1) / kPartRows, col_ranges));
+  g.parts = std::max(1, std::min((p->max_rank + 15) / 16, col_ranges));
   const unsigned gx = gemv_grid_of(gemv_units * g.parts);
   if constexpr (sizeof(TI) == 2) {
     // long segments on matrix-core tiles and short units on the GEMV path, in one launch

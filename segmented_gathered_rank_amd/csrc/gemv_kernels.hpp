@@ -54,7 +54,8 @@ constexpr int kXSliceBytes = 32768;                 // LDS for the staged x rows
 constexpr int kShrinkBatch = LORA_SHRINK_BATCH;     // 16-byte chunks of a row in flight per lane
 constexpr int kShrinkRows = LORA_SHRINK_ROWS;       // rank rows a wave streams at once
 constexpr int kUnitRun = LORA_UNIT_RUN;             // consecutive units one XCD takes (a power of 2)
-constexpr int kPartRows = 16;                       // rank rows per work item of the shrink-only kernel
+constexpr int kPartRows = 8;                        // rank rows per work item of the shrink-only kernel:
+                                                    // one pass of the 4 waves (2 rows each)
 template <typename TI>
 constexpr int kExpandBatch = sizeof(TI) == 2 ? LORA_EXPAND_BATCH : 8;   // rank rows of B in flight per thread
 
