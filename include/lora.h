@@ -222,7 +222,10 @@ size_t lora_shrink_workspace_bytes(const lora_pool *p, int32_t n_tokens, int32_t
  * for splitting the matrix-core contraction over K when there are too few
  * tiles to fill the GPU; with ws_bytes == 0 no split is made.  Calls that
  * share a workspace must be ordered on one stream.
- * Errors: ARG, SHAPE, DTYPE, HIP. */
+ * On bf16 pools the call is one launch (plus one for the K splits) that
+ * runs long segments on matrix-core tiles and short ones on the GEMV path.
+ * Errors: ARG, SHAPE (also: a batch whose launch would exceed 2^31 - 1
+ * workgroups; nothing is launched), DTYPE, HIP. */
 lora_status lora_shrink(const lora_pool *p, int32_t module0, int32_t n_modules,
                         const void *x, int64_t ld_x, int64_t module_stride_x,
                         const lora_segments *seg,
@@ -232,7 +235,10 @@ lora_status lora_shrink(const lora_pool *p, int32_t module0, int32_t n_modules,
 /* Expand: y_i[c] = round(y_i[c] + scale_a * sum_{j<rank_a} t[i][j] B_a[j][c])
  * for tokens with a valid id ("expand" of the study page's demo, fused into
  * the update of y).  Other rows of y are not touched.
- * Errors: ARG, SHAPE, DTYPE, HIP. */
+ * On bf16 pools the call is one launch that runs long segments on
+ * matrix-core tiles and short ones on the GEMV path.
+ * Errors: ARG, SHAPE (also: a batch whose launch would exceed 2^31 - 1
+ * workgroups; nothing is launched), DTYPE, HIP. */
 lora_status lora_expand(const lora_pool *p, int32_t module0, int32_t n_modules,
                         const float *t, int64_t ld_t, int64_t module_stride_t,
                         const lora_segments *seg,

@@ -6,6 +6,7 @@
 // lists come from the segment builder and stay on the device; grids are sized
 // by their upper bounds and idle workgroups exit at once.
 #include <algorithm>
+#include <cstdint>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -202,8 +203,9 @@ lora_status launch_shrink(const lora_pool* p, int32_t module0, int32_t n_modules
       const size_t lds = std::max(stream_lds_bytes(per_wg, ntiles, a.kc, a.max_pids), gemv_lds_bytes<1, __bf16>());
       a.part = ks > 1 ? static_cast<float*>(ws) : nullptr;
       const int tnx = static_cast<int>(tile_grid_of(seg->max_tiles));
-      const dim3 grid(static_cast<unsigned>(tnx * ks * groups) + gx * static_cast<unsigned>(n_modules)),
-          block(kMfmaThreads);
+      const int64_t n_blocks = static_cast<int64_t>(tnx) * ks * groups + static_cast<int64_t>(gx) * n_modules;
+      if (n_blocks > INT32_MAX) return LORA_ERR_SHAPE;   // beyond one launch's grid (nothing launched yet)
+      const dim3 grid(static_cast<unsigned>(n_blocks)), block(kMfmaThreads);
 #define LORA_SHRINK_LAUNCH(M, NT)                                                                        \
   hipLaunchKernelGGL((k_shrink_mixed<M, NT, kStreamDepth>), grid, block, lds, s, a, g, tnx, ks, groups, \
                      static_cast<int>(gx), n_modules)
@@ -345,7 +347,9 @@ lora_status launch_expand(const lora_pool* p, int32_t module0, int32_t n_modules
                                       resident);
       const int tnx = static_cast<int>(tile_grid_of(seg->max_tiles));
       const int col_groups = (n_blocks + ea.blocks - 1) / ea.blocks;
-      const dim3 grid(static_cast<unsigned>(tnx * col_groups * n_modules) + gx * static_cast<unsigned>(n_modules));
+      const int64_t n_wgs = static_cast<int64_t>(tnx) * col_groups * n_modules + static_cast<int64_t>(gx) * n_modules;
+      if (n_wgs > INT32_MAX) return LORA_ERR_SHAPE;   // beyond one launch's grid (nothing launched yet)
+      const dim3 grid(static_cast<unsigned>(n_wgs));
       hipLaunchKernelGGL((k_expand_mixed<TO>), grid, dim3(kMfmaThreads), lds, s, ea, g, tnx, col_groups, n_modules,
                          static_cast<int>(gx), n_modules);
       return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
