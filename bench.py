@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--path", choices=["auto", "bgmv", "sgmv"], default="auto",
                     help="force the fused BGMV or the shrink+expand path (default: the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="input sets the steps cycle through (each with its own pool, x and y); default: enough "
+                         "that one cycle moves more than twice the 256 MB Infinity Cache")
     ap.add_argument("--single-module", action="store_true",
                     help="also time one-module calls of the decode batch (replayed from a captured graph)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -56,6 +59,9 @@ def parse():
                     help="the step makes this many launches of the kernel (one per module): average over all "
                          "of them and report HBM bytes per step")
     return ap.parse_args()
+
+
+ROTATE = {"sgmv_prefill": 2, "mixed_rank": 16}
 
 
 def make_workload(name):
@@ -397,25 +403,33 @@ def main():
     if args.path != "auto":
         mode = args.path
         config["path"] = mode
-    dw = DeviceWorkload(wl, device=0)
+    # input sets the steps cycle through, so that a cycle's distinct bytes exceed twice the
+    # 256 MB Infinity Cache and the kernels read from HBM: the decode batch covers that with its
+    # 128 modules in one launch, the prefill step (346 MB) takes 2 sets, the mixed batch (43 MB) 16
+    rotate = args.rotate if args.rotate > 0 else ROTATE.get(args.workload, 1)
+    dws = [DeviceWorkload(wl, device=0) for _ in range(rotate)]
+    dw = dws[0]
+    config["input_sets"] = rotate
     stream = torch.cuda.current_stream()
     work = accounting.step_work(wl, fused=(mode == "bgmv"))
 
     if mode == "fused":
-        dw.upload_weights()
+        for d in dws:
+            d.upload_weights()
 
-    def step(ev=None):
+    def step(ev=None, i=0):
+        d = dws[i % rotate]
         if mode != "fused":
-            dw.build_segments()
+            d.build_segments()
         if ev is not None:
             ev[0].record(stream)
         if mode == "bgmv":
-            dw.bgmv()
+            d.bgmv()
         elif mode == "fused":
-            dw.fused()
+            d.fused()
         else:
-            dw.shrink()
-            dw.expand()
+            d.shrink()
+            d.expand()
         if ev is not None:
             ev[1].record(stream)
 
@@ -425,13 +439,13 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(None, i)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs[i])
+        step(evs[i], args.warmup + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kern_ms = [a.elapsed_time(b) for a, b in evs]
@@ -490,7 +504,8 @@ def main():
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic", "config": config, "roofline": roofline, "extra": extra,
         }
-        dw.close()
+        for d in dws:
+            d.close()
         if not args.no_cpu_baseline:
             out["cpu_baseline"] = cpu_baseline_fused(wl, args.cpu_seconds)
         print(json.dumps(out), flush=True)
@@ -524,7 +539,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic", "config": config, "roofline": roofline, "extra": extra,
     }
-    dw.close()
+    for d in dws:
+        d.close()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
