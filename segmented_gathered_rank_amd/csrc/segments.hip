@@ -182,11 +182,30 @@ __device__ __forceinline__ int2 unit_record(int slot, int run, int u, int first)
                    first + u * kUnitTokens);
 }
 
+// Long segments whose unit and tile records the whole workgroup writes
+// together; a batch with more falls back to each owning wave writing its own.
+constexpr int kLongDesc = 512;
+
 struct LayoutLds {
-  int wsum[kWaves][6];   // per wave: inclusive counter totals, max segment length
-  int woff[kWaves][5];   // per wave: exclusive offsets
-  int tot[5];
+  int wsum[kWaves][7];   // per wave: inclusive counter totals, max segment length
+  int woff[kWaves][6];   // per wave: exclusive offsets
+  int tot[6];
+  // long segment d: slot, length, first position, first unit (after the short
+  // units) and first tile; ld_u0 / ld_t0 end with the totals
+  int ld_slot[kLongDesc], ld_run[kLongDesc], ld_first[kLongDesc];
+  int ld_u0[kLongDesc + 1], ld_t0[kLongDesc + 1];
 };
+
+// Largest d < n with a[d] <= v, for a strictly increasing a with a[0] <= v.
+__device__ __forceinline__ int last_at_most(const int* a, int n, int v) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a[mid] <= v) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
 
 // Block-wide layout from the per-slot totals `total` (LDS).  Thread tid owns
 // slots [s0, s1) (consecutive, in slot order, the same partition the caller
@@ -196,7 +215,7 @@ template <class BaseFn>
 __device__ void layout_segments(const int32_t* total, int n_tokens, int n_slots, int s0, int s1, int bpt,
                                 int bad_total, const Out& o, LayoutLds& L, BaseFn base_of) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int own[5] = {0, 0, 0, 0, 0};   // tokens, segments, short units, long units, tiles
+  int own[6] = {0, 0, 0, 0, 0, 0};   // tokens, segments, short units, long units, tiles, long segments
   int mx = 0;
   for (int s = s0; s < s1; ++s) {
     const int run = total[s];
@@ -207,35 +226,38 @@ __device__ void layout_segments(const int32_t* total, int n_tokens, int n_slots,
       if (run >= kLongMin) {
         own[3] += nu;
         own[4] += (run + kTileTokens - 1) / kTileTokens;
+        own[5] += 1;
       } else {
         own[2] += nu;
       }
       mx = max(mx, run);
     }
   }
-  int incl[5];
+  int incl[6];
 #pragma unroll
-  for (int q = 0; q < 5; ++q) incl[q] = wave_scan<false>(own[q]);
+  for (int q = 0; q < 6; ++q) incl[q] = wave_scan<false>(own[q]);
   const int wmx = lane63(wave_scan<true>(mx));
   if (lane == 63) {
 #pragma unroll
-    for (int q = 0; q < 5; ++q) L.wsum[wave][q] = incl[q];
-    L.wsum[wave][5] = wmx;
+    for (int q = 0; q < 6; ++q) L.wsum[wave][q] = incl[q];
+    L.wsum[wave][6] = wmx;
   }
   __syncthreads();
   if (wave == 0) {
-    int tq[5];
+    int tq[6];
 #pragma unroll
-    for (int q = 0; q < 5; ++q) {
+    for (int q = 0; q < 6; ++q) {
       const int v = lane < kWaves ? L.wsum[lane][q] : 0;
       const int c = wave_scan<false>(v);
       if (lane < kWaves) L.woff[lane][q] = c - v;
       tq[q] = lane63(c);
     }
-    const int m = lane63(wave_scan<true>(lane < kWaves ? L.wsum[lane][5] : 0));
+    const int m = lane63(wave_scan<true>(lane < kWaves ? L.wsum[lane][6] : 0));
     if (lane == 0) {
 #pragma unroll
-      for (int q = 0; q < 5; ++q) L.tot[q] = tq[q];
+      for (int q = 0; q < 6; ++q) L.tot[q] = tq[q];
+      L.ld_u0[min(tq[5], kLongDesc)] = tq[3];
+      L.ld_t0[min(tq[5], kLongDesc)] = tq[4];
       int32_t* meta = o.meta;
       meta[LORA_META_N_SEG] = tq[1];
       meta[LORA_META_N_ACTIVE] = tq[0];
@@ -255,10 +277,12 @@ __device__ void layout_segments(const int32_t* total, int n_tokens, int n_slots,
   }
   __syncthreads();
 
-  int off[5];
+  int off[6];
 #pragma unroll
-  for (int q = 0; q < 5; ++q) off[q] = L.woff[wave][q] + incl[q] - own[q];
+  for (int q = 0; q < 6; ++q) off[q] = L.woff[wave][q] + incl[q] - own[q];
   const int long_at = L.tot[2];   // long-segment units follow all short ones
+  const int n_long = L.tot[5];
+  const bool spread = n_long <= kLongDesc;   // uniform
   int2* units = reinterpret_cast<int2*>(o.units);
   int2* tiles = reinterpret_cast<int2*>(o.tiles);
   for (int b = 0; b < bpt; ++b) {
@@ -271,10 +295,16 @@ __device__ void layout_segments(const int32_t* total, int n_tokens, int n_slots,
       base_of(s, off[0]);
       if (run < kLongMin) {   // at most kLongMin / kUnitTokens entries: written by this lane
         for (int u = 0; u < nu; ++u) units[off[2] + u] = unit_record(s, run, u, off[0]);
+      } else if (spread) {    // described here, written below by the whole workgroup
+        L.ld_slot[off[5]] = s;
+        L.ld_run[off[5]] = run;
+        L.ld_first[off[5]] = off[0];
+        L.ld_u0[off[5]] = off[3];
+        L.ld_t0[off[5]] = off[4];
       }
     }
-    // long segments: the whole wave writes each one's entries, lane by lane
-    uint64_t lm = __ballot(run >= kLongMin);
+    // long segments, when too many to describe: the whole wave writes each one's entries
+    uint64_t lm = spread ? 0ull : __ballot(run >= kLongMin);
     while (lm) {
       const int src = lowest_lane(lm);
       lm &= lm - 1;
@@ -293,11 +323,28 @@ __device__ void layout_segments(const int32_t* total, int n_tokens, int n_slots,
       if (run >= kLongMin) {
         off[3] += nu;
         off[4] += (run + kTileTokens - 1) / kTileTokens;
+        off[5] += 1;
       } else {
         off[2] += nu;
       }
       off[0] += run;
       off[1] += 1;
+    }
+  }
+  // the long segments' unit and tile records, spread over the workgroup: record i
+  // belongs to the last segment whose first record is at most i
+  if (spread && n_long > 0) {   // uniform
+    __syncthreads();
+    const int n_lu = L.tot[3], n_t = L.tot[4];
+    for (int i = threadIdx.x; i < n_lu; i += kThreads) {
+      const int d = last_at_most(L.ld_u0, n_long, i);
+      units[long_at + i] = unit_record(L.ld_slot[d], L.ld_run[d], i - L.ld_u0[d], L.ld_first[d]);
+    }
+    for (int i = threadIdx.x; i < n_t; i += kThreads) {
+      const int d = last_at_most(L.ld_t0, n_long, i);
+      const int u = i - L.ld_t0[d], r = L.ld_run[d];
+      tiles[i] = make_int2(L.ld_slot[d] + (min(kTileTokens, r - u * kTileTokens) << 16),
+                           L.ld_first[d] + u * kTileTokens);
     }
   }
 }

@@ -65,6 +65,11 @@ SEG_CASES = {
     "chunked_all_neg": ([-1] * 20000, 16),
     "chunked_one_chunk": (np.random.default_rng(24).integers(-1, 8192, 600), 8192),
     "chunked_runs": (np.repeat(np.random.default_rng(25).integers(0, 300, 1024), 128), 300),
+    # long segments whose records the whole workgroup writes (one workgroup; chunked), and more
+    # long segments than the builder describes at once (each wave writes its own)
+    "one_group_many_long": (np.repeat(np.random.default_rng(26).permutation(100), 64 + 5), 100),
+    "chunked_many_long": (np.repeat(np.random.default_rng(27).permutation(400), 130), 400),
+    "chunked_too_many_long": (np.repeat(np.random.default_rng(28).permutation(1500), 70), 1500),
 }
 
 
