@@ -418,8 +418,8 @@ __device__ __forceinline__ void expand_mfma_body(const ExpandArgs& ea, const Blk
     const int n_cb = min(ea.blocks, (h_out - b.y * ea.blocks * TN + TN - 1) / TN);
     // T tile: t = hi + mid + lo, three bf16 values whose sum is t exactly (3 x 8 significand
     // bits cover fp32's 24), so the bf16 matrix cores multiply by t itself.  Thread -> row
-    // tid/4, columns (tid%4) + 4q; its loads go out with block 0's.  Later blocks load at the
-    // top of their own step: a second register stage would cost the third wave per SIMD.
+    // tid/4, columns (tid%4) + 4q; its loads go out with block 0's.  Each later block's loads
+    // are issued as soon as the block before it is staged in LDS.
     {
       const int r = tid >> 2, jq = tid & 3;
       const int tk = toks_s[r];
@@ -449,7 +449,6 @@ __device__ __forceinline__ void expand_mfma_body(const ExpandArgs& ea, const Blk
       const int c0 = (b.y * ea.blocks + cb) * TN;
       const int p = c0 / h;
       const int off = c0 - p * h;
-      if (cb > 0) issue(cb, yv, bv);
       __syncthreads();                         // the previous block's BT_s / Y_s reads are done
 #pragma unroll
       for (int q = 0; q < YCH; ++q) {
@@ -470,6 +469,9 @@ __device__ __forceinline__ void expand_mfma_body(const ExpandArgs& ea, const Blk
                           pages + static_cast<int64_t>(bids_s[min(j, rank - 1) * ppr + p]) * h + off + c));
         }
       }
+      // the next block's y and B loads fly during this block's matrix-core work, epilogue and
+      // store (same registers, now free: no occupancy cost)
+      if (cb + 1 < n_cb) issue(cb + 1, yv, bv);
       __syncthreads();
 
       // Y^T[col][token] += B^T[col][j] T^T[j][token] on v_mfma_f32_32x32x16_bf16: A = B^T
