@@ -388,7 +388,8 @@ def main():
         pmc_summary(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (see DESIGN.md, 'Sharding').",
+        print("bench.py measures one GPU: the library has no multi-GPU path (tokens shard across data-parallel "
+              "replicas with no exchange; tensor-parallel row splits would add one all-reduce of t).",
               file=sys.stderr)
         sys.exit(2)
     if args.workload == "tiers_trace":
