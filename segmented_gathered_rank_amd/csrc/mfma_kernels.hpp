@@ -41,6 +41,12 @@ constexpr int kExpandBlocks = LORA_EXPAND_BLOCKS;   // column blocks per expand 
 
 __device__ __forceinline__ bf16x8 ld_bf16x8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
+typedef __attribute__((address_space(3))) void* lds_addr_t;
+__device__ __forceinline__ lds_addr_t to_lds(void* p) {
+  return reinterpret_cast<lds_addr_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+
 struct ShrinkArgs {
   PoolView pv;
   SegView sv;
@@ -134,38 +140,71 @@ __device__ __forceinline__ void shrink_stream_body(const ShrinkArgs& a, const Bl
     bf16x8 xb[D];
 #pragma unroll
     for (int i = 0; i < D; ++i) xb[i] = ld_bf16x8(xrow + 32 * min(i, n - 1));
-    // A rows of the split into LDS, kStageBatch 16-byte chunks per thread at a time.  Rows
-    // past a module's rank read its last row: they only feed output columns past the rank,
-    // which are never stored.
+    // A rows of the split into LDS.  Rows past a module's rank read its last row: they only
+    // feed output columns past the rank, which are never stored.
     const int cpr = klen >> 3;                                  // 16-byte chunks per row
-    const int n_chunks = MODS * 16 * NTILES * cpr;
-    for (int c0 = 0; c0 < n_chunks; c0 += kMfmaThreads * kStageBatch) {
-      u32x4 av[kStageBatch];
+    // through registers, kStageBatch chunks per thread at a time, every lane busy
+    auto stage_regs = [&]() {
+      const int n_chunks = MODS * 16 * NTILES * cpr;
+      for (int c0 = 0; c0 < n_chunks; c0 += kMfmaThreads * kStageBatch) {
+        u32x4 av[kStageBatch];
 #pragma unroll
-      for (int q = 0; q < kStageBatch; ++q) {
-        const int idx = min(c0 + tid + kMfmaThreads * q, n_chunks - 1);
-        const int row = idx / cpr, c = idx - row * cpr;
+        for (int q = 0; q < kStageBatch; ++q) {
+          const int idx = min(c0 + tid + kMfmaThreads * q, n_chunks - 1);
+          const int row = idx / cpr, c = idx - row * cpr;
+          const int mi = row / (16 * NTILES), j = row - mi * (16 * NTILES);
+          int rank_mi = 0;
+#pragma unroll
+          for (int m2 = 0; m2 < MODS; ++m2)
+            if (m2 == mi) rank_mi = rank[m2];
+          const int jj = max(0, min(j, rank_mi - 1));
+          const int k = k_begin + c * 8;
+          const int pg = ppr == 1 ? 0 : static_cast<int>(__umulhi(static_cast<uint32_t>(k), a.magic));
+          const int pid = rank_mi > 0 ? pid_s[mi * a.max_pids + jj * ppr + pg] : 0;
+          av[q] = *reinterpret_cast<const u32x4*>(pages + static_cast<int64_t>(pid) * h + (k - pg * h));
+        }
+#pragma unroll
+        for (int q = 0; q < kStageBatch; ++q) {
+          const int idx = c0 + tid + kMfmaThreads * q;
+          if (idx < n_chunks) {
+            const int row = idx / cpr, c = idx - row * cpr;
+            *reinterpret_cast<u32x4*>(A_s + static_cast<size_t>(row) * ALD + c * 8) = av[q];
+          }
+        }
+      }
+    };
+    // straight from memory into LDS (global_load_lds, no registers), all rows in one round
+    // trip, for rows of 1 KiB or more.  Wave w takes rows w, w + 4, ...; one instruction
+    // moves up to 64 chunks of a row (lane i lands at byte 16 i of the instruction's LDS
+    // base; lanes past the row stay idle).  Only shapes whose A slice fits such rows in the
+    // LDS budget (modules x 16-column tiles <= 3) compile it: the others would lose a wave.
+    auto stage_dma = [&]() {
+      for (int row = wave; row < MODS * 16 * NTILES; row += kMfmaThreads / 64) {
         const int mi = row / (16 * NTILES), j = row - mi * (16 * NTILES);
         int rank_mi = 0;
 #pragma unroll
         for (int m2 = 0; m2 < MODS; ++m2)
           if (m2 == mi) rank_mi = rank[m2];
         const int jj = max(0, min(j, rank_mi - 1));
-        const int k = k_begin + c * 8;
-        const int pg = ppr == 1 ? 0 : static_cast<int>(__umulhi(static_cast<uint32_t>(k), a.magic));
-        const int pid = rank_mi > 0 ? pid_s[mi * a.max_pids + jj * ppr + pg] : 0;
-        av[q] = *reinterpret_cast<const u32x4*>(pages + static_cast<int64_t>(pid) * h + (k - pg * h));
-      }
-#pragma unroll
-      for (int q = 0; q < kStageBatch; ++q) {
-        const int idx = c0 + tid + kMfmaThreads * q;
-        if (idx < n_chunks) {
-          const int row = idx / cpr, c = idx - row * cpr;
-          *reinterpret_cast<u32x4*>(A_s + static_cast<size_t>(row) * ALD + c * 8) = av[q];
+        for (int c0 = 0; c0 < cpr; c0 += 64) {
+          const int c = c0 + lane;
+          if (c < cpr) {
+            const int k = k_begin + c * 8;
+            const int pg = ppr == 1 ? 0 : static_cast<int>(__umulhi(static_cast<uint32_t>(k), a.magic));
+            const int pid = rank_mi > 0 ? pid_s[mi * a.max_pids + jj * ppr + pg] : 0;
+            __builtin_amdgcn_global_load_lds(pages + static_cast<int64_t>(pid) * h + (k - pg * h),
+                                             to_lds(A_s + static_cast<size_t>(row) * ALD + c0 * 8), 16, 0, 0);
+          }
         }
       }
+    };
+    if constexpr (MODS * NTILES <= 3) {
+      if (cpr >= 64) stage_dma();   // uniform
+      else stage_regs();
+    } else {
+      stage_regs();
     }
-    __syncthreads();
+    __syncthreads();   // A has landed (the barrier waits for the loads into LDS)
 
     // this lane's A row of each (module, 16-column tile) in LDS
     const __bf16* arow = A_s + static_cast<size_t>(lane & 15) * ALD + kq;
@@ -443,8 +482,8 @@ __device__ __forceinline__ void expand_mfma_body(const ExpandArgs& ea, const Blk
         }
       }
     }
-#pragma unroll 2
-    for (int cb = 0; cb < kExpandBlocks; ++cb) {   // unrolled in pairs: a full unroll spills
+#pragma unroll 1
+    for (int cb = 0; cb < kExpandBlocks; ++cb) {   // not unrolled: a full unroll spills
       if (cb >= n_cb) break;                   // uniform
       const int c0 = (b.y * ea.blocks + cb) * TN;
       const int p = c0 / h;
