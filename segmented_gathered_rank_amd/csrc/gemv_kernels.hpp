@@ -331,6 +331,8 @@ struct GemvArgs {
   int64_t ld_t, mst;
   void* y;
   int64_t ld_y, msy;
+  int32_t module_group;   // MODE 0 on a 1-D grid: modules per dispatch group (0: the grid is units x modules)
+  int32_t group_nx;       // ... and each module's unit workgroups
 };
 
 // LDS of the GEMV body: the unit's tables, then (shrink modes) its staged x rows.
@@ -342,9 +344,10 @@ constexpr size_t gemv_lds_bytes() {
 }
 
 // MODE 0: fused BGMV (t kept in LDS); 1: shrink only (t to memory); 2: expand only.
-// b.nx is a multiple of 8*kUnitRun (see unit_of_block); b.ny = modules.
+// b.nx is a multiple of 8*kUnitRun (see unit_of_block); b.ny = modules.  it0 >= 0
+// names the workgroup's first work item in place of unit_of_block.
 template <int MODE, typename TI, typename TO>
-__device__ __forceinline__ void gemv_body(const GemvArgs& a, const Blk b, UnitLds& L, TI* xs) {
+__device__ __forceinline__ void gemv_body(const GemvArgs& a, const Blk b, UnitLds& L, TI* xs, int it0 = -1) {
   const int m = b.y;
   const TI* xm = static_cast<const TI*>(a.x) + m * a.msx;
   float* tm = a.t + m * a.mst;
@@ -361,7 +364,7 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a, const Blk b, UnitLd
   // so that a unit's serial batches spread over several workgroups
   const int parts = a.parts;
   const int n_items = n_units * parts;
-  int it = unit_of_block(b.x, m);
+  int it = it0 >= 0 ? it0 : unit_of_block(b.x, m);
   int2 rec = units[min(it / parts, a.sv.max_units - 1)];
   for (; it < n_items; it += b.nx) {
     const int u = it / parts, part = it - u * parts;
@@ -428,11 +431,26 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a, const Blk b, UnitLd
   }
 }
 
+// With a.module_group > 0 (MODE 0) the grid is 1-D, modules x group_nx workgroups,
+// in groups of module_group modules (the last may be shorter); inside a group
+// the modules vary fastest, so the workgroups in flight at any time cover a few
+// modules at once and, for a group of a multiple of 8 modules, every workgroup
+// of module m runs on XCD m % 8.
 template <int MODE, typename TI, typename TO>
 __global__ __launch_bounds__(kGemvThreads, 4) void k_gemv(GemvArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[gemv_lds_bytes<MODE, TI>()];
-  gemv_body<MODE, TI, TO>(a, blk_of_launch(), *reinterpret_cast<UnitLds*>(lds),
-                          reinterpret_cast<TI*>(lds + gemv_xs_offset<MODE, TI>()));
+  Blk b = blk_of_launch();
+  int it0 = -1;
+  if (MODE == 0 && a.module_group > 0) {
+    const int nx = a.group_nx, nm = static_cast<int>(gridDim.x) / nx, gm = a.module_group;
+    const int lin = static_cast<int>(blockIdx.x);
+    const int g = lin / (gm * nx), local = lin - g * gm * nx;
+    const int size = min(gm, nm - g * gm);
+    b = Blk{0, g * gm + local % size, 0, nx, nm, 1};
+    it0 = local / size;
+  }
+  gemv_body<MODE, TI, TO>(a, b, *reinterpret_cast<UnitLds*>(lds),
+                          reinterpret_cast<TI*>(lds + gemv_xs_offset<MODE, TI>()), it0);
 }
 
 }  // namespace lora

@@ -463,6 +463,17 @@ def test_bad_ids_leave_rows_untouched():
         dw.close()
 
 
+@pytest.mark.parametrize("n_modules", [33, 40])
+def test_bgmv_module_groups_with_short_tail(n_modules):
+    """A bgmv over 32 or more modules runs its modules in groups of 32: one full
+    group and a short last one (1 or 8 modules) must each match the oracle."""
+    wl = W.c2_bgmv_decode(n_modules=n_modules, h=512, n_tokens=40)
+    dw, ys = run(wl, "bgmv")
+    for m in range(n_modules):
+        assert_close(ys[m], lo.apply_to_y0(wl, m), "bf16", f"bgmv m{m}")
+    dw.close()
+
+
 def test_multi_module_one_launch():
     """Eight decode modules with their own x and y in one bgmv launch and one sgmv pass."""
     wl = W.c2_bgmv_decode(n_modules=8, h=512, n_tokens=48)
