@@ -474,6 +474,17 @@ def test_bgmv_module_groups_with_short_tail(n_modules):
     dw.close()
 
 
+def test_c2_decode_128_modules_full_size_sampled():
+    """The default decode launch: 64 tokens over 128 modules of 4096 x 4096 in one
+    bgmv (four groups of 32 modules); modules at every group edge against the oracle."""
+    wl = W.c2_bgmv_decode(n_modules=128, draw_w=False)
+    say("C2 x128 full")
+    dw, ys = run(wl, "bgmv")
+    for m in (0, 1, 31, 32, 63, 64, 95, 96, 126, 127):
+        assert_close(ys[m], lo.apply_to_y0(wl, m), "bf16", f"C2x128 m{m}")
+    dw.close()
+
+
 def test_multi_module_one_launch():
     """Eight decode modules with their own x and y in one bgmv launch and one sgmv pass."""
     wl = W.c2_bgmv_decode(n_modules=8, h=512, n_tokens=48)
