@@ -463,10 +463,11 @@ def test_bad_ids_leave_rows_untouched():
         dw.close()
 
 
-@pytest.mark.parametrize("n_modules", [33, 40])
+@pytest.mark.parametrize("n_modules", [12, 24, 33, 40])
 def test_bgmv_module_groups_with_short_tail(n_modules):
-    """A bgmv over 32 or more modules runs its modules in groups of 32: one full
-    group and a short last one (1 or 8 modules) must each match the oracle."""
+    """A bgmv over 8 or more modules runs its modules in groups of up to 32: one
+    group of 12 or 24, or a full group and a short last one (1 or 8 modules),
+    must each match the oracle."""
     wl = W.c2_bgmv_decode(n_modules=n_modules, h=512, n_tokens=40)
     dw, ys = run(wl, "bgmv")
     for m in range(n_modules):
