@@ -61,7 +61,10 @@ def parse():
     return ap.parse_args()
 
 
-ROTATE = {"sgmv_prefill": 2, "mixed_rank": 16}
+# Input sets per workload.  One set of the 128-module decode batch moves 0.87 GB per
+# step, yet back-to-back launches over it ran 17% faster than over two alternating
+# sets (three sets: the same as two): the Infinity Cache still held part of it.
+ROTATE = {"bgmv_decode_x128": 2, "sgmv_prefill": 2, "mixed_rank": 16}
 
 
 def make_workload(name):
