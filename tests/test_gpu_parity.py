@@ -463,27 +463,30 @@ def test_bad_ids_leave_rows_untouched():
         dw.close()
 
 
+@pytest.mark.parametrize("mode", ["bgmv", "sgmv"])
 @pytest.mark.parametrize("n_modules", [12, 24, 33, 40])
-def test_bgmv_module_groups_with_short_tail(n_modules):
-    """A bgmv over 8 or more modules runs its modules in groups of up to 32: one
-    group of 12 or 24, or a full group and a short last one (1 or 8 modules),
-    must each match the oracle."""
+def test_module_groups_with_short_tail(n_modules, mode):
+    """A GEMV launch over 8 or more modules runs its modules in groups of up to
+    32: one group of 12 or 24, or a full group and a short last one (1 or 8
+    modules), must each match the oracle."""
     wl = W.c2_bgmv_decode(n_modules=n_modules, h=512, n_tokens=40)
-    dw, ys = run(wl, "bgmv")
+    dw, ys = run(wl, mode)
     for m in range(n_modules):
-        assert_close(ys[m], lo.apply_to_y0(wl, m), "bf16", f"bgmv m{m}")
+        assert_close(ys[m], lo.apply_to_y0(wl, m), "bf16", f"{mode} m{m}")
     dw.close()
 
 
 def test_c2_decode_128_modules_full_size_sampled():
-    """The default decode launch: 64 tokens over 128 modules of 4096 x 4096 in one
-    bgmv (four groups of 32 modules); modules at every group edge against the oracle."""
+    """The default decode batch: 64 tokens over 128 modules of 4096 x 4096 in one
+    bgmv, and through shrink and expand (four groups of 32 modules); modules at
+    every group edge against the oracle."""
     wl = W.c2_bgmv_decode(n_modules=128, draw_w=False)
-    say("C2 x128 full")
-    dw, ys = run(wl, "bgmv")
-    for m in (0, 1, 31, 32, 63, 64, 95, 96, 126, 127):
-        assert_close(ys[m], lo.apply_to_y0(wl, m), "bf16", f"C2x128 m{m}")
-    dw.close()
+    for mode in ("bgmv", "sgmv"):
+        say(f"C2 x128 full {mode}")
+        dw, ys = run(wl, mode)
+        for m in (0, 1, 31, 32, 63, 64, 95, 96, 126, 127):
+            assert_close(ys[m], lo.apply_to_y0(wl, m), "bf16", f"C2x128 {mode} m{m}")
+        dw.close()
 
 
 def test_multi_module_one_launch():
