@@ -107,6 +107,13 @@ constexpr int kGemvMaxGrid = 1024;
 // measured 4% faster at 128 modules, 15% at 32, 10% at 24, 6% at 16, even at 8.
 constexpr int kBgmvModuleGroup = 32;
 constexpr int kBgmvGroupedFrom = 8;
+
+// The GEMV part of a mixed shrink or expand launch (gx workgroups per module,
+// after the tiles) takes its modules in the same groups from that count on.
+void set_module_groups(GemvArgs& g, unsigned gx, int32_t n_modules) {
+  g.module_group = n_modules >= kBgmvGroupedFrom ? std::min(kBgmvModuleGroup, n_modules) : 0;
+  g.group_nx = static_cast<int32_t>(gx);
+}
 unsigned gemv_grid_of(int32_t units) {
   constexpr int period = 8 * kUnitRun;
   static_assert(kGemvMaxGrid % period == 0, "the grid cap must be a whole number of periods");
@@ -212,6 +219,7 @@ lora_status launch_shrink(const lora_pool* p, int32_t module0, int32_t n_modules
       const int64_t n_blocks = static_cast<int64_t>(tnx) * ks * groups + static_cast<int64_t>(gx) * n_modules;
       if (n_blocks > INT32_MAX) return LORA_ERR_SHAPE;   // beyond one launch's grid (nothing launched yet)
       const dim3 grid(static_cast<unsigned>(n_blocks)), block(kMfmaThreads);
+      set_module_groups(g, gx, n_modules);
 #define LORA_SHRINK_LAUNCH(M, NT)                                                                        \
   hipLaunchKernelGGL((k_shrink_mixed<M, NT, kStreamDepth>), grid, block, lds, s, a, g, tnx, ks, groups, \
                      static_cast<int>(gx), n_modules)
@@ -356,6 +364,7 @@ lora_status launch_expand(const lora_pool* p, int32_t module0, int32_t n_modules
       const int64_t n_wgs = static_cast<int64_t>(tnx) * col_groups * n_modules + static_cast<int64_t>(gx) * n_modules;
       if (n_wgs > INT32_MAX) return LORA_ERR_SHAPE;   // beyond one launch's grid (nothing launched yet)
       const dim3 grid(static_cast<unsigned>(n_wgs));
+      set_module_groups(g, gx, n_modules);
       hipLaunchKernelGGL((k_expand_mixed<TO>), grid, dim3(kMfmaThreads), lds, s, ea, g, tnx, col_groups, n_modules,
                          static_cast<int>(gx), n_modules);
       return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;

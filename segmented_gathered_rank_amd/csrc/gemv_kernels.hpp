@@ -331,7 +331,7 @@ struct GemvArgs {
   int64_t ld_t, mst;
   void* y;
   int64_t ld_y, msy;
-  int32_t module_group;   // MODE 0 on a 1-D grid: modules per dispatch group (0: the grid is units x modules)
+  int32_t module_group;   // modules per dispatch group of the GEMV grid (0: one module after another)
   int32_t group_nx;       // ... and each module's unit workgroups
 };
 
@@ -431,24 +431,29 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a, const Blk b, UnitLd
   }
 }
 
-// With a.module_group > 0 (MODE 0) the grid is 1-D, modules x group_nx workgroups,
-// in groups of module_group modules (the last may be shorter); inside a group
-// the modules vary fastest, so the workgroups in flight at any time cover a few
-// modules at once and, for a group of a multiple of 8 modules, every workgroup
-// of module m runs on XCD m % 8.
+// Workgroup lin of a 1-D GEMV grid of nm modules x nx workgroups taken in
+// groups of gm modules (the last may be shorter), the modules varying fastest
+// inside a group: the workgroups in flight at any time cover a few modules at
+// once and, for a group of a multiple of 8 modules laid out from a multiple of
+// 8 workgroups, every workgroup of module m runs on XCD m % 8.  Returns its
+// coordinates and sets it0 to its first work item.
+__device__ __forceinline__ Blk blk_of_module_groups(int lin, int nx, int nm, int gm, int& it0) {
+  const int g = lin / (gm * nx), local = lin - g * gm * nx;
+  const int size = min(gm, nm - g * gm);
+  it0 = local / size;
+  return Blk{0, g * gm + local % size, 0, nx, nm, 1};
+}
+
+// With a.module_group > 0 (MODE 0) the grid is 1-D, modules x group_nx
+// workgroups in groups of module_group modules (blk_of_module_groups).
 template <int MODE, typename TI, typename TO>
 __global__ __launch_bounds__(kGemvThreads, 4) void k_gemv(GemvArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[gemv_lds_bytes<MODE, TI>()];
   Blk b = blk_of_launch();
   int it0 = -1;
-  if (MODE == 0 && a.module_group > 0) {
-    const int nx = a.group_nx, nm = static_cast<int>(gridDim.x) / nx, gm = a.module_group;
-    const int lin = static_cast<int>(blockIdx.x);
-    const int g = lin / (gm * nx), local = lin - g * gm * nx;
-    const int size = min(gm, nm - g * gm);
-    b = Blk{0, g * gm + local % size, 0, nx, nm, 1};
-    it0 = local / size;
-  }
+  if (MODE == 0 && a.module_group > 0)
+    b = blk_of_module_groups(static_cast<int>(blockIdx.x), a.group_nx,
+                             static_cast<int>(gridDim.x) / a.group_nx, a.module_group, it0);
   gemv_body<MODE, TI, TO>(a, b, *reinterpret_cast<UnitLds*>(lds),
                           reinterpret_cast<TI*>(lds + gemv_xs_offset<MODE, TI>()), it0);
 }

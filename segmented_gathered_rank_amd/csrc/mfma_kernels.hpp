@@ -578,9 +578,11 @@ __global__ __launch_bounds__(kMfmaThreads) void k_shrink_mixed(ShrinkArgs a, Gem
   if (lin < tile_blocks) {
     shrink_stream_body<MODS, NTILES, D>(a, blk_of_linear(lin, tnx, tny, tnz), smem);
   } else {
-    gemv_body<1, __bf16, __bf16>(g, blk_of_linear(lin - tile_blocks, gnx, gny, 1),
-                                 *reinterpret_cast<UnitLds*>(smem),
-                                 reinterpret_cast<__bf16*>(smem + gemv_xs_offset<1, __bf16>()));
+    int it0 = -1;
+    const Blk b = g.module_group > 0 ? blk_of_module_groups(lin - tile_blocks, gnx, gny, g.module_group, it0)
+                                     : blk_of_linear(lin - tile_blocks, gnx, gny, 1);
+    gemv_body<1, __bf16, __bf16>(g, b, *reinterpret_cast<UnitLds*>(smem),
+                                 reinterpret_cast<__bf16*>(smem + gemv_xs_offset<1, __bf16>()), it0);
   }
 }
 
@@ -594,9 +596,11 @@ __global__ __launch_bounds__(kMfmaThreads, sizeof(TO) == 2 ? 3 : 2) void k_expan
   if (lin < tile_blocks) {
     expand_mfma_body<TO>(ea, blk_of_linear(lin, tnx, tny, tnz), smem);
   } else {
-    gemv_body<2, __bf16, TO>(g, blk_of_linear(lin - tile_blocks, gnx, gny, 1),
-                             *reinterpret_cast<UnitLds*>(smem),
-                             reinterpret_cast<__bf16*>(smem + gemv_xs_offset<2, __bf16>()));
+    int it0 = -1;
+    const Blk b = g.module_group > 0 ? blk_of_module_groups(lin - tile_blocks, gnx, gny, g.module_group, it0)
+                                     : blk_of_linear(lin - tile_blocks, gnx, gny, 1);
+    gemv_body<2, __bf16, TO>(g, b, *reinterpret_cast<UnitLds*>(smem),
+                             reinterpret_cast<__bf16*>(smem + gemv_xs_offset<2, __bf16>()), it0);
   }
 }
 
