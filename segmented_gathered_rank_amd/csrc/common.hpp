@@ -70,6 +70,13 @@ __device__ __forceinline__ V ld16(const V* p) {
   else return *p;
 }
 
+// LDS address of a pointer into shared memory, for the direct global-to-LDS loads
+// (global_load_lds: each lane's 16 bytes land at the wave's LDS base + 16 * lane).
+typedef __attribute__((address_space(3))) void* lds_addr_t;
+__device__ __forceinline__ lds_addr_t to_lds(void* p) {
+  return reinterpret_cast<lds_addr_t>(reinterpret_cast<uintptr_t>(p));
+}
+
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 

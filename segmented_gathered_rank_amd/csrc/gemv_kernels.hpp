@@ -58,6 +58,11 @@ constexpr int kPartRows = 8;                        // rank rows per work item o
                                                     // one pass of the 4 waves (2 rows each)
 template <typename TI>
 constexpr int kExpandBatch = sizeof(TI) == 2 ? LORA_EXPAND_BATCH : 8;   // rank rows of B in flight per thread
+// The fused BGMV reads x and updates y with streaming accesses: each x row and
+// each y element is touched by one work item only.
+#ifndef LORA_BGMV_NT_XY
+#define LORA_BGMV_NT_XY 1
+#endif
 
 template <typename TI>
 struct XSlice {
@@ -92,6 +97,17 @@ template <> struct Quad<__bf16> {
                    static_cast<__bf16>(f[3])};
     *reinterpret_cast<uint2*>(p) = __builtin_bit_cast(uint2, h);
   }
+  // streaming (non-temporal) load and store, for y elements touched once
+  __device__ __forceinline__ void load_stream(const __bf16* p) {
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    lo = v.x;
+    hi = v.y;
+  }
+  static __device__ __forceinline__ void store_stream(__bf16* p, const float (&f)[4]) {
+    __bf16 h[4] = {static_cast<__bf16>(f[0]), static_cast<__bf16>(f[1]), static_cast<__bf16>(f[2]),
+                   static_cast<__bf16>(f[3])};
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x2, h), reinterpret_cast<u32x2*>(p));
+  }
 };
 template <> struct Quad<float> {
   f32x4 v;
@@ -102,6 +118,12 @@ template <> struct Quad<float> {
   static __device__ __forceinline__ void store(float* p, const float (&f)[4]) {
     *reinterpret_cast<f32x4*>(p) = f32x4{f[0], f[1], f[2], f[3]};
   }
+  __device__ __forceinline__ void load_stream(const float* p) {
+    v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  }
+  static __device__ __forceinline__ void store_stream(float* p, const float (&f)[4]) {
+    __builtin_nontemporal_store(f32x4{f[0], f[1], f[2], f[3]}, reinterpret_cast<f32x4*>(p));
+  }
 };
 
 struct UnitLds {
@@ -110,8 +132,9 @@ struct UnitLds {
   int32_t toks[kUnitTokens];
 };
 
-// Copies x[tok][k0 .. k0+len) of the unit's tokens into xs[tb][0 .. len).
-template <typename TI>
+// Copies x[tok][k0 .. k0+len) of the unit's tokens into xs[tb][0 .. len);
+// NT: streaming loads (the rows are read by this work item only).
+template <typename TI, bool NT>
 __device__ __forceinline__ void stage_x(const TI* __restrict__ x, int64_t ld_x, const int32_t* toks, int nt,
                                         int k0, int len, TI* xs) {
   constexpr int V = 16 / sizeof(TI);
@@ -120,14 +143,14 @@ __device__ __forceinline__ void stage_x(const TI* __restrict__ x, int64_t ld_x, 
   for (int i = threadIdx.x; i < nt * per_tok; i += kGemvThreads) {
     const int tb = i / per_tok, c = (i - tb * per_tok) * V;
     *reinterpret_cast<u32x4*>(xs + tb * S + c) =
-        *reinterpret_cast<const u32x4*>(x + static_cast<int64_t>(toks[tb]) * ld_x + k0 + c);
+        ld16<NT>(reinterpret_cast<const u32x4*>(x + static_cast<int64_t>(toks[tb]) * ld_x + k0 + c));
   }
 }
 
 // KEEP: the unit's segment spans several units, whose workgroups read the
 // same pages, so they are loaded through the caches; a page read by one
 // unit only is streamed with non-temporal loads.
-template <typename TI, int NT, bool KEEP>
+template <typename TI, int NT, bool KEEP, bool NTX>
 __device__ __forceinline__ void shrink_unit(const TI* __restrict__ x, int64_t ld_x, UnitLds& L, int nt,
                                             const TI* __restrict__ pages, int pid0, int32_t h, uint32_t magic,
                                             int32_t h_in, int32_t j_begin, int32_t j_end, TI* xs) {
@@ -193,7 +216,7 @@ __device__ __forceinline__ void shrink_unit(const TI* __restrict__ x, int64_t ld
   };
 
   if (n_slices == 1) {
-    stage_x(x, ld_x, L.toks, nt, 0, h_in, xs);
+    stage_x<TI, NTX>(x, ld_x, L.toks, nt, 0, h_in, xs);
     __syncthreads();
   }
   // wave w streams rows j0 + w + kGemvWaves*q for q < SR, rank rows [j_begin, j_end)
@@ -204,7 +227,7 @@ __device__ __forceinline__ void shrink_unit(const TI* __restrict__ x, int64_t ld
       const int len = min(S, h_in - k0);
       if (n_slices > 1) {
         __syncthreads();
-        stage_x(x, ld_x, L.toks, nt, k0, len, xs);
+        stage_x<TI, NTX>(x, ld_x, L.toks, nt, k0, len, xs);
         __syncthreads();
       }
       if (jw >= j_end) continue;         // wave-uniform
@@ -232,7 +255,9 @@ __device__ __forceinline__ void shrink_unit(const TI* __restrict__ x, int64_t ld
   __syncthreads();
 }
 
-template <typename TI, typename TO, int NT, bool KEEP>
+// NTY: y is read and written with streaming accesses (each element is touched
+// by this work item only).
+template <typename TI, typename TO, int NT, bool KEEP, bool NTY>
 __device__ __forceinline__ void expand_unit(TO* __restrict__ y, int64_t ld_y, const UnitLds& L, int nt,
                                             const TI* __restrict__ pages, int pid0, int32_t h, uint32_t magic,
                                             int32_t h_out, int32_t rank, float scale, int q_begin, int q_end) {
@@ -255,7 +280,10 @@ __device__ __forceinline__ void expand_unit(TO* __restrict__ y, int64_t ld_y, co
     const int off = kq - p * h;
     Quad<TO> yq[NT];
 #pragma unroll
-    for (int tb = 0; tb < NT; ++tb) yq[tb].load(y + yoff[tb] + kq);
+    for (int tb = 0; tb < NT; ++tb) {
+      if constexpr (NTY) yq[tb].load_stream(y + yoff[tb] + kq);
+      else yq[tb].load(y + yoff[tb] + kq);
+    }
     float acc[NT][4];
 #pragma unroll
     for (int tb = 0; tb < NT; ++tb)
@@ -293,7 +321,8 @@ __device__ __forceinline__ void expand_unit(TO* __restrict__ y, int64_t ld_y, co
         yq[tb].unpack(yv);
 #pragma unroll
         for (int e = 0; e < 4; ++e) yv[e] = fmaf(scale, acc[tb][e], yv[e]);
-        Quad<TO>::store(y + yoff[tb] + kq, yv);
+        if constexpr (NTY) Quad<TO>::store_stream(y + yoff[tb] + kq, yv);
+        else Quad<TO>::store(y + yoff[tb] + kq, yv);
       }
     }
   }
@@ -343,12 +372,13 @@ constexpr size_t gemv_lds_bytes() {
   return gemv_xs_offset<MODE, TI>() + ((MODE == 2) ? 16 : kUnitTokens * XSlice<TI>::kElems * sizeof(TI));
 }
 
-// MODE 0: fused BGMV (t kept in LDS); 1: shrink only (t to memory); 2: expand only.
-// b.nx is a multiple of 8*kUnitRun (see unit_of_block); b.ny = modules.  it0 >= 0
-// names the workgroup's first work item in place of unit_of_block.
+// One work item of the GEMV path: unit `rec` (see the segment builder's unit
+// records) of module m, part `part` of it.  MODE 0: fused BGMV (t kept in
+// LDS); 1: shrink only (t to memory, part = block of kPartRows rank rows); 2:
+// expand only (t from memory, part = column range of `parts`).  Begins with a
+// barrier (the previous item is done with LDS).
 template <int MODE, typename TI, typename TO>
-__device__ __forceinline__ void gemv_body(const GemvArgs& a, const Blk b, UnitLds& L, TI* xs, int it0 = -1) {
-  const int m = b.y;
+__device__ __forceinline__ void gemv_item(const GemvArgs& a, int m, int2 rec, int part, UnitLds& L, TI* xs) {
   const TI* xm = static_cast<const TI*>(a.x) + m * a.msx;
   float* tm = a.t + m * a.mst;
   TO* ym = static_cast<TO*>(a.y) + m * a.msy;
@@ -357,6 +387,76 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a, const Blk b, UnitLd
   const int ppr_a = a.h_in / h, ppr_b = a.h_out / h;
   const int ids_a = (MODE == 2) ? 0 : a.pv.max_rank * ppr_a;   // page ids loaded for A
   const int ids_b = (MODE == 1) ? 0 : a.pv.max_rank * ppr_b;   // ... and for B, after A's
+  const int slot = rec.x & 0xffff, nt = (rec.x >> 16) & 0xff, pos = rec.y;
+  const bool keep = (rec.x >> 24) & 1;
+  const int ei = slot * a.pv.n_modules + a.module0 + m;
+  const SlotEntry e = a.pv.entries[ei];
+  const int32_t* ids = a.pv.page_ids + static_cast<int64_t>(ei) * a.pv.ppe;
+  unit_prologue(a.sv, (MODE == 2) ? ids + a.pv.max_rank * ppr_a : ids, pos, nt, ids_a + ids_b, L);
+  if (e.rank <= 0) return;
+  // rank rows of this part (shrink-only kernel) or all of them
+  const int j_begin = (MODE == 1) ? part * kPartRows : 0;
+  const int j_end = (MODE == 1) ? min(e.rank, j_begin + kPartRows) : e.rank;
+  if (j_begin >= j_end) return;         // uniform: this part has no rows of this rank
+  if constexpr (MODE != 2) {
+    constexpr bool ntx = MODE == 0 && LORA_BGMV_NT_XY != 0;
+#define LORA_SHRINK_CALL(N, K) \
+  shrink_unit<TI, N, K, ntx>(xm, a.ld_x, L, nt, pages, 0, h, a.magic, a.h_in, j_begin, j_end, xs)
+    if (keep) {
+      if (nt == 1) LORA_SHRINK_CALL(1, true);
+      else if (nt == 2) LORA_SHRINK_CALL(2, true);
+      else LORA_SHRINK_CALL(4, true);
+    } else {
+      if (nt == 1) LORA_SHRINK_CALL(1, false);
+      else if (nt == 2) LORA_SHRINK_CALL(2, false);
+      else LORA_SHRINK_CALL(4, false);
+    }
+#undef LORA_SHRINK_CALL
+  }
+  if constexpr (MODE == 1) {
+    const int nr = j_end - j_begin;
+    for (int i = threadIdx.x; i < nt * nr; i += kGemvThreads) {
+      const int tb = i / nr, j = j_begin + (i - tb * nr);
+      tm[static_cast<int64_t>(L.toks[tb]) * a.ld_t + j] = L.t[tb * kMaxRank + j];
+    }
+  }
+  if constexpr (MODE == 2) {
+    for (int i = threadIdx.x; i < nt * e.rank; i += kGemvThreads) {
+      const int tb = i / e.rank, j = i - tb * e.rank;
+      L.t[tb * kMaxRank + j] = tm[static_cast<int64_t>(L.toks[tb]) * a.ld_t + j];
+    }
+    __syncthreads();
+  }
+  if constexpr (MODE != 1) {
+    // column quads of this part: ranges of whole waves (64 quads), the last one ragged
+    const int n_quads = a.h_out >> 2;
+    const int per = (MODE == 2) ? ((n_quads + a.parts - 1) / a.parts + 63) / 64 * 64 : n_quads;
+    const int q_begin = (MODE == 2) ? part * per : 0;
+    const int q_end = min(n_quads, q_begin + per);
+    if (q_begin >= q_end) return;       // uniform
+    constexpr bool nty = MODE == 0 && LORA_BGMV_NT_XY != 0;
+#define LORA_EXPAND_CALL(N, K)                                                                               \
+  expand_unit<TI, TO, N, K, nty>(ym, a.ld_y, L, nt, pages, ids_a, h, a.magic, a.h_out, e.rank, e.scale, q_begin, \
+                                 q_end)
+    if (keep) {
+      if (nt == 1) LORA_EXPAND_CALL(1, true);
+      else if (nt == 2) LORA_EXPAND_CALL(2, true);
+      else LORA_EXPAND_CALL(4, true);
+    } else {
+      if (nt == 1) LORA_EXPAND_CALL(1, false);
+      else if (nt == 2) LORA_EXPAND_CALL(2, false);
+      else LORA_EXPAND_CALL(4, false);
+    }
+#undef LORA_EXPAND_CALL
+  }
+}
+
+// The work items of module b.y for one workgroup of a grid of b.nx workgroups per
+// module.  b.nx is a multiple of 8*kUnitRun (see unit_of_block).  it0 >= 0 names
+// the workgroup's first work item in place of unit_of_block.
+template <int MODE, typename TI, typename TO>
+__device__ __forceinline__ void gemv_body(const GemvArgs& a, const Blk b, UnitLds& L, TI* xs, int it0 = -1) {
+  const int m = b.y;
   const int2* units = reinterpret_cast<const int2*>(a.sv.units);
   // the unit count and this workgroup's first record travel together
   const int n_units = a.sv.meta[a.units_word];
@@ -369,65 +469,7 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a, const Blk b, UnitLd
   for (; it < n_items; it += b.nx) {
     const int u = it / parts, part = it - u * parts;
     if (it >= b.nx) rec = units[u];
-    const int slot = rec.x & 0xffff, nt = (rec.x >> 16) & 0xff, pos = rec.y;
-    const bool keep = (rec.x >> 24) & 1;
-    const int ei = slot * a.pv.n_modules + a.module0 + m;
-    const SlotEntry e = a.pv.entries[ei];
-    const int32_t* ids = a.pv.page_ids + static_cast<int64_t>(ei) * a.pv.ppe;
-    unit_prologue(a.sv, (MODE == 2) ? ids + a.pv.max_rank * ppr_a : ids, pos, nt, ids_a + ids_b, L);
-    if (e.rank <= 0) continue;
-    // rank rows of this part (shrink-only kernel) or all of them
-    const int j_begin = (MODE == 1) ? part * kPartRows : 0;
-    const int j_end = (MODE == 1) ? min(e.rank, j_begin + kPartRows) : e.rank;
-    if (j_begin >= j_end) continue;       // uniform: this part has no rows of this rank
-    if constexpr (MODE != 2) {
-#define LORA_SHRINK_CALL(N, K) \
-  shrink_unit<TI, N, K>(xm, a.ld_x, L, nt, pages, 0, h, a.magic, a.h_in, j_begin, j_end, xs)
-      if (keep) {
-        if (nt == 1) LORA_SHRINK_CALL(1, true);
-        else if (nt == 2) LORA_SHRINK_CALL(2, true);
-        else LORA_SHRINK_CALL(4, true);
-      } else {
-        if (nt == 1) LORA_SHRINK_CALL(1, false);
-        else if (nt == 2) LORA_SHRINK_CALL(2, false);
-        else LORA_SHRINK_CALL(4, false);
-      }
-#undef LORA_SHRINK_CALL
-    }
-    if constexpr (MODE == 1) {
-      const int nr = j_end - j_begin;
-      for (int i = threadIdx.x; i < nt * nr; i += kGemvThreads) {
-        const int tb = i / nr, j = j_begin + (i - tb * nr);
-        tm[static_cast<int64_t>(L.toks[tb]) * a.ld_t + j] = L.t[tb * kMaxRank + j];
-      }
-    }
-    if constexpr (MODE == 2) {
-      for (int i = threadIdx.x; i < nt * e.rank; i += kGemvThreads) {
-        const int tb = i / e.rank, j = i - tb * e.rank;
-        L.t[tb * kMaxRank + j] = tm[static_cast<int64_t>(L.toks[tb]) * a.ld_t + j];
-      }
-      __syncthreads();
-    }
-    if constexpr (MODE != 1) {
-      // column quads of this part: ranges of whole waves (64 quads), the last one ragged
-      const int n_quads = a.h_out >> 2;
-      const int per = (MODE == 2) ? ((n_quads + parts - 1) / parts + 63) / 64 * 64 : n_quads;
-      const int q_begin = (MODE == 2) ? part * per : 0;
-      const int q_end = min(n_quads, q_begin + per);
-      if (q_begin >= q_end) continue;     // uniform
-#define LORA_EXPAND_CALL(N, K) \
-  expand_unit<TI, TO, N, K>(ym, a.ld_y, L, nt, pages, ids_a, h, a.magic, a.h_out, e.rank, e.scale, q_begin, q_end)
-      if (keep) {
-        if (nt == 1) LORA_EXPAND_CALL(1, true);
-        else if (nt == 2) LORA_EXPAND_CALL(2, true);
-        else LORA_EXPAND_CALL(4, true);
-      } else {
-        if (nt == 1) LORA_EXPAND_CALL(1, false);
-        else if (nt == 2) LORA_EXPAND_CALL(2, false);
-        else LORA_EXPAND_CALL(4, false);
-      }
-#undef LORA_EXPAND_CALL
-    }
+    gemv_item<MODE, TI, TO>(a, m, rec, part, L, xs);
   }
 }
 

@@ -41,10 +41,6 @@ constexpr int kExpandBlocks = LORA_EXPAND_BLOCKS;   // column blocks per expand 
 
 __device__ __forceinline__ bf16x8 ld_bf16x8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
-typedef __attribute__((address_space(3))) void* lds_addr_t;
-__device__ __forceinline__ lds_addr_t to_lds(void* p) {
-  return reinterpret_cast<lds_addr_t>(reinterpret_cast<uintptr_t>(p));
-}
 
 
 struct ShrinkArgs {
