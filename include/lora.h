@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 4
+#define LORA_ABI_VERSION 5
 
 typedef int32_t lora_status;
 enum {
@@ -222,6 +222,7 @@ size_t lora_shrink_workspace_bytes(const lora_pool *p, int32_t n_tokens, int32_t
  * for splitting the matrix-core contraction over K when there are too few
  * tiles to fill the GPU; with ws_bytes == 0 no split is made.  Calls that
  * share a workspace must be ordered on one stream.
+ * t must be 16-byte aligned, with ld_t and module_stride_t multiples of 4.
  * On bf16 pools the call is one launch (plus one for the K splits) that
  * runs long segments on matrix-core tiles and short ones on the GEMV path.
  * Errors: ARG, SHAPE (also: a batch whose launch would exceed 2^31 - 1

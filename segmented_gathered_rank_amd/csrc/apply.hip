@@ -13,6 +13,7 @@
 
 #include "fused_gemm.hpp"
 #include "gemv_kernels.hpp"
+#include "launch_limits.hpp"
 #include "mfma_kernels.hpp"
 #include "pool.hpp"
 
@@ -151,11 +152,41 @@ size_t split_ws_bytes(const lora_pool* p, int32_t n_tokens, int32_t n_modules, i
   return tiles * n_modules * ks * kTileTokens * ldr_of(p) * sizeof(float);
 }
 
+// The K split of the matrix-core shrink: ks splits of kps elements (a multiple of 32).
+struct ShrinkSplit {
+  int32_t ks, kps;
+};
 
+// Whether a shrink call runs matrix-core tiles (and so may split K).
+bool shrink_has_tiles(const lora_pool* p, int32_t module0, const lora_segments* seg) {
+  return p->dtype == LORA_BF16 && mfma_ok(p, module0) && seg->max_tiles > 0;
+}
+
+// Split of a shrink call with a workspace of ws_bytes: enough workgroups for 256 CUs when
+// the tiles alone are too few, at most kMaxSplits, at least 256 elements of K per split,
+// and no more partial tiles than the workspace holds.
+ShrinkSplit shrink_split(const lora_pool* p, int32_t module0, int32_t n_modules, int64_t msx,
+                         const lora_segments* seg, size_t ws_bytes) {
+  const int32_t h_in = static_cast<int32_t>(p->h_in[module0]);
+  if (!shrink_has_tiles(p, module0, seg)) return ShrinkSplit{1, (h_in + 31) / 32 * 32};
+  const bool shared = (msx == 0 && n_modules > 1 && n_modules <= kShrinkMaxModules);
+  const int32_t groups = shared ? 1 : n_modules;
+  const int32_t est_tiles = (seg->n_tokens + kTileTokens - 1) / kTileTokens;
+  int32_t ks = kShrinkWgTarget / (est_tiles * groups > 0 ? est_tiles * groups : 1);
+  if (ks > kMaxSplits) ks = kMaxSplits;
+  if (ks > h_in / 256) ks = h_in / 256;
+  if (ks < 1) ks = 1;
+  while (ks > 1 && split_ws_bytes(p, seg->n_tokens, n_modules, ks) > ws_bytes) --ks;
+  int32_t kps = (h_in + ks - 1) / ks;
+  kps = (kps + 31) / 32 * 32;
+  return ShrinkSplit{(h_in + kps - 1) / kps, kps};
+}
+
+// sp: the K split (shrink_split); ws holds its partial tiles when sp.ks > 1.
 template <typename TI>
 lora_status launch_shrink(const lora_pool* p, int32_t module0, int32_t n_modules, const void* x, int64_t ld_x,
-                          int64_t msx, const lora_segments* seg, float* t, int64_t ld_t, int64_t mst, void* ws,
-                          size_t ws_bytes, hipStream_t s) {
+                          int64_t msx, const lora_segments* seg, float* t, int64_t ld_t, int64_t mst,
+                          ShrinkSplit sp, void* ws, hipStream_t s) {
   const PoolView pv = p->view();
   const SegView sv = seg_view(seg);
   const int32_t h_in = static_cast<int32_t>(p->h_in[module0]);
@@ -177,16 +208,7 @@ lora_status launch_shrink(const lora_pool* p, int32_t module0, int32_t n_modules
       const bool shared = (msx == 0 && n_modules > 1 && n_modules <= kShrinkMaxModules);
       const int32_t groups = shared ? 1 : n_modules;
       const int32_t per_wg = shared ? n_modules : 1;
-      // enough workgroups for 256 CUs: split K when tiles alone are too few
-      const int32_t est_tiles = (seg->n_tokens + kTileTokens - 1) / kTileTokens;
-      int32_t ks = kShrinkWgTarget / (est_tiles * groups > 0 ? est_tiles * groups : 1);
-      if (ks > kMaxSplits) ks = kMaxSplits;
-      if (ks > h_in / 256) ks = h_in / 256;
-      if (ks < 1) ks = 1;
-      while (ks > 1 && split_ws_bytes(p, seg->n_tokens, n_modules, ks) > ws_bytes) --ks;
-      int32_t kps = (h_in + ks - 1) / ks;
-      kps = (kps + 31) / 32 * 32;
-      ks = (h_in + kps - 1) / kps;
+      const int32_t ks = sp.ks, kps = sp.kps;
       ShrinkArgs a;
       a.pv = pv;
       a.sv = sv;
@@ -217,7 +239,7 @@ lora_status launch_shrink(const lora_pool* p, int32_t module0, int32_t n_modules
       a.part = ks > 1 ? static_cast<float*>(ws) : nullptr;
       const int tnx = static_cast<int>(tile_grid_of(seg->max_tiles));
       const int64_t n_blocks = static_cast<int64_t>(tnx) * ks * groups + static_cast<int64_t>(gx) * n_modules;
-      if (n_blocks > INT32_MAX) return LORA_ERR_SHAPE;   // beyond one launch's grid (nothing launched yet)
+      if (!grid_fits(n_blocks, kMfmaThreads)) return LORA_ERR_SHAPE;   // beyond one launch (nothing launched yet)
       const dim3 grid(static_cast<unsigned>(n_blocks)), block(kMfmaThreads);
       set_module_groups(g, gx, n_modules);
 #define LORA_SHRINK_LAUNCH(M, NT)                                                                        \
@@ -362,7 +384,7 @@ lora_status launch_expand(const lora_pool* p, int32_t module0, int32_t n_modules
       const int tnx = static_cast<int>(tile_grid_of(seg->max_tiles));
       const int col_groups = (n_blocks + ea.blocks - 1) / ea.blocks;
       const int64_t n_wgs = static_cast<int64_t>(tnx) * col_groups * n_modules + static_cast<int64_t>(gx) * n_modules;
-      if (n_wgs > INT32_MAX) return LORA_ERR_SHAPE;   // beyond one launch's grid (nothing launched yet)
+      if (!grid_fits(n_wgs, kMfmaThreads)) return LORA_ERR_SHAPE;   // beyond one launch (nothing launched yet)
       const dim3 grid(static_cast<unsigned>(n_wgs));
       set_module_groups(g, gx, n_modules);
       hipLaunchKernelGGL((k_expand_mixed<TO>), grid, dim3(kMfmaThreads), lds, s, ea, g, tnx, col_groups, n_modules,
@@ -397,6 +419,27 @@ lora_status launch_bgmv(const lora_pool* p, int32_t module0, int32_t n_modules, 
   return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
+// Argument checks of the shrink calls.
+lora_status shrink_checks(const lora_pool* p, int32_t module0, int32_t n_modules, const void* x, int64_t ld_x,
+                          int64_t msx, const lora_segments* seg, const float* t, int64_t ld_t, int64_t mst) {
+  lora_status st = check_call(p, module0, n_modules, seg, false);
+  if (st != LORA_OK) return st;
+  const int32_t n = seg->n_tokens;
+  st = check_operand(x, ld_x, msx, p->h_in[module0], p->elem_bytes(), n, n_modules, false, true);
+  if (st != LORA_OK) return st;
+  // t takes 16-byte stores (the K-split sum writes four rank columns at once)
+  return check_operand(t, ld_t, mst, p->max_rank, 4, n, n_modules, true, true);
+}
+
+// A checked shrink call on the current device.
+lora_status shrink_call(const lora_pool* p, int32_t module0, int32_t n_modules, const void* x, int64_t ld_x,
+                        int64_t msx, const lora_segments* seg, float* t, int64_t ld_t, int64_t mst, ShrinkSplit sp,
+                        void* ws, hipStream_t s) {
+  if (p->dtype == LORA_BF16)
+    return launch_shrink<__bf16>(p, module0, n_modules, x, ld_x, msx, seg, t, ld_t, mst, sp, ws, s);
+  return launch_shrink<float>(p, module0, n_modules, x, ld_x, msx, seg, t, ld_t, mst, sp, ws, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -409,23 +452,16 @@ size_t lora_shrink_workspace_bytes(const lora_pool* p, int32_t n_tokens, int32_t
 lora_status lora_shrink(const lora_pool* p, int32_t module0, int32_t n_modules, const void* x, int64_t ld_x,
                         int64_t module_stride_x, const lora_segments* seg, float* t, int64_t ld_t,
                         int64_t module_stride_t, void* ws, size_t ws_bytes, void* stream) {
-  lora_status st = check_call(p, module0, n_modules, seg, false);
+  const lora_status st = shrink_checks(p, module0, n_modules, x, ld_x, module_stride_x, seg, t, ld_t, module_stride_t);
   if (st != LORA_OK) return st;
   const int32_t n = seg->n_tokens;
-  st = check_operand(x, ld_x, module_stride_x, p->h_in[module0], p->elem_bytes(), n, n_modules, false, true);
-  if (st != LORA_OK) return st;
-  st = check_operand(t, ld_t, module_stride_t, p->max_rank, 4, n, n_modules, true, false);
-  if (st != LORA_OK) return st;
   if (ws_bytes > 0 && (!ws || !aligned16(ws))) return LORA_ERR_ARG;
   if (n == 0) return LORA_OK;
   DeviceGuard g(p->device);
   if (!g.ok) return LORA_ERR_HIP;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (p->dtype == LORA_BF16)
-    return launch_shrink<__bf16>(p, module0, n_modules, x, ld_x, module_stride_x, seg, t, ld_t, module_stride_t,
-                                 ws, ws_bytes, s);
-  return launch_shrink<float>(p, module0, n_modules, x, ld_x, module_stride_x, seg, t, ld_t, module_stride_t, ws,
-                              ws_bytes, s);
+  const ShrinkSplit sp = shrink_split(p, module0, n_modules, module_stride_x, seg, ws_bytes);
+  return shrink_call(p, module0, n_modules, x, ld_x, module_stride_x, seg, t, ld_t, module_stride_t, sp, ws,
+                     static_cast<hipStream_t>(stream));
 }
 
 lora_status lora_expand(const lora_pool* p, int32_t module0, int32_t n_modules, const float* t, int64_t ld_t,

@@ -188,6 +188,24 @@ def test_pool_round_trip_and_page_accounting():
     dw.close()
 
 
+def test_shrink_rejects_t_rows_that_are_not_16_byte_aligned():
+    """The K-split sum stores four rank columns at once: t must be 16-byte aligned
+    with ld_t and module_stride_t multiples of 4 (checked before any launch)."""
+    wl = W.c2_bgmv_decode(draw_w=False, h=256, n_tokens=40)
+    dw = DeviceWorkload(wl, device=0)
+    dw.build_segments()
+    x = dw._xp(dw.x_off[0])
+    t = torch.zeros(wl.n_tokens * 20 + 8, dtype=torch.float32, device=dw.dev)
+    bad = [(t.data_ptr() + 4, 16, 0), (t, 17, 0), (t, 18, 0)]
+    for tp, ld, ms in bad:
+        with pytest.raises(sgr.LoraError) as ei:
+            sgr.lora_shrink(dw.pool, 0, 1, x, 256, 0, dw.seg, tp, ld, ms, dw.ws, dw.ws_bytes)
+        assert ei.value.status == -1
+    sgr.lora_shrink(dw.pool, 0, 1, x, 256, 0, dw.seg, t, 20, 0, dw.ws, dw.ws_bytes)   # aligned: accepted
+    torch.cuda.synchronize()
+    dw.close()
+
+
 # ----------------------------------------------------------------- exact cases
 @pytest.mark.parametrize("mode", ["sgmv", "bgmv"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     import segmented_gathered_rank_amd as sgr
-    assert sgr.lora_abi_version() == 4
+    assert sgr.lora_abi_version() == 5
     for code in sgr.STATUS:
         assert sgr.lora_status_str(code) and sgr.lora_status_str(code) != "unknown status"
 
@@ -125,9 +125,11 @@ def test_segment_builder_schedule():
 
 
 @pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
-def test_page_allocator_under_sanitizers(tmp_path):
-    exe = tmp_path / "test_page_alloc"
-    src = os.path.join(ROOT, "tests", "cpp", "test_page_alloc.cpp")
+@pytest.mark.parametrize("name", ["test_page_alloc", "test_launch_limits"])
+def test_host_code_under_sanitizers(tmp_path, name):
+    """The page allocator and the launch-size guard, built for the host with g++."""
+    exe = tmp_path / name
+    src = os.path.join(ROOT, "tests", "cpp", name + ".cpp")
     inc = os.path.join(ROOT, "segmented_gathered_rank_amd", "csrc")
     subprocess.run(["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
                     "-I", inc, src, "-o", str(exe)], check=True)
