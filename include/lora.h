@@ -233,6 +233,25 @@ lora_status lora_shrink(const lora_pool *p, int32_t module0, int32_t n_modules,
                         float *t, int64_t ld_t, int64_t module_stride_t,
                         void *ws, size_t ws_bytes, void *stream);
 
+/* lora_shrink for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, serving loops that forbid
+ * allocation).  Same arguments and result as lora_shrink with a workspace of
+ * lora_shrink_workspace_bytes (the same K split, so the same t bit for bit),
+ * but the split's partial tiles go to a device array that the library holds,
+ * LORA_NOALLOC_SCRATCH_BYTES per GPU, until the process ends.  Nothing is
+ * allocated by the call.
+ * Every call on one GPU uses that GPU's array: calls that overlap on one GPU
+ * (other streams, other host threads) race and must be ordered by the caller.
+ * The array keeps the last call's contents; the call reads only what it wrote.
+ * Errors: as lora_shrink, and WORKSPACE when that split needs more than
+ * LORA_NOALLOC_SCRATCH_BYTES (nothing is launched; lora_shrink with a
+ * workspace serves such calls); HIP when the array's address cannot be had. */
+#define LORA_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
+lora_status lora_shrink_noalloc(const lora_pool *p, int32_t module0, int32_t n_modules,
+                                const void *x, int64_t ld_x, int64_t module_stride_x,
+                                const lora_segments *seg,
+                                float *t, int64_t ld_t, int64_t module_stride_t, void *stream);
+
 /* Expand: y_i[c] = round(y_i[c] + scale_a * sum_{j<rank_a} t[i][j] B_a[j][c])
  * for tokens with a valid id ("expand" of the study page's demo, fused into
  * the update of y).  Other rows of y are not touched.

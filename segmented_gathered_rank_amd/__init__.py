@@ -19,7 +19,8 @@ __all__ = [
     "lora_abi_version", "lora_status_str", "lora_pool_create", "lora_pool_destroy",
     "lora_pool_load", "lora_pool_evict", "lora_pool_stats", "lora_pool_read",
     "lora_segments_bytes", "lora_segments_bind", "lora_build_segments",
-    "lora_segments_check", "lora_shrink_workspace_bytes", "lora_shrink",
+    "lora_segments_check", "lora_shrink_workspace_bytes", "lora_shrink", "lora_shrink_noalloc",
+    "LORA_NOALLOC_SCRATCH_BYTES",
     "lora_expand", "lora_apply_bgmv", "lora_fused_gemm",
     "LORA_TIER_GPU", "LORA_TIER_HOST", "LORA_TIER_COLD", "lora_tiers_create", "lora_tiers_destroy",
     "lora_tiers_touch", "lora_tiers_stats", "lora_tiers_slot_of", "lora_tiers_acquire",
@@ -31,6 +32,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblora_mi3
 LORA_F32 = 0
 LORA_BF16 = 1
 LORA_MAX_RANK = 64
+LORA_NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024
 LORA_META_WORDS = 16
 META = {
     "n_seg": 0, "n_active": 1, "max_seg_len": 2, "n_bad": 3, "n_units_short": 4,
@@ -92,6 +94,7 @@ _SIGS = {
     "lora_segments_check": (_I32, [_SEGP, _P, ctypes.POINTER(_I32)]),
     "lora_shrink_workspace_bytes": (_SZ, [_P, _I32, _I32]),
     "lora_shrink": (_I32, [_P, _I32, _I32, _P, _I64, _I64, _SEGP, _P, _I64, _I64, _P, _SZ, _P]),
+    "lora_shrink_noalloc": (_I32, [_P, _I32, _I32, _P, _I64, _I64, _SEGP, _P, _I64, _I64, _P]),
     "lora_expand": (_I32, [_P, _I32, _I32, _P, _I64, _I64, _SEGP, _P, _I64, _I64, _I32, _P]),
     "lora_apply_bgmv": (_I32, [_P, _I32, _I32, _P, _I64, _I64, _SEGP, _P, _I64, _I64, _I32, _P]),
     "lora_fused_gemm": (_I32, [_P, _I32, _P, _I64, _P, _I64, _P, _I32, _P, _I64, _P]),
@@ -234,6 +237,12 @@ def lora_shrink(pool: int, module0: int, n_modules: int, x, ld_x: int, module_st
     _check(_lib.lora_shrink(pool, module0, n_modules, _ptr(x), ld_x, module_stride_x, ctypes.byref(seg),
                             _ptr(t), ld_t, module_stride_t, _ptr(ws), ws_bytes, _stream(stream)),
            "lora_shrink")
+
+
+def lora_shrink_noalloc(pool: int, module0: int, n_modules: int, x, ld_x: int, module_stride_x: int,
+                        seg: lora_segments, t, ld_t: int, module_stride_t: int, stream=None) -> None:
+    _check(_lib.lora_shrink_noalloc(pool, module0, n_modules, _ptr(x), ld_x, module_stride_x, ctypes.byref(seg),
+                                    _ptr(t), ld_t, module_stride_t, _stream(stream)), "lora_shrink_noalloc")
 
 
 def lora_expand(pool: int, module0: int, n_modules: int, t, ld_t: int, module_stride_t: int,

@@ -442,6 +442,34 @@ lora_status shrink_call(const lora_pool* p, int32_t module0, int32_t n_modules, 
 
 }  // namespace
 
+// Device memory of lora_shrink_noalloc's K-split partial tiles, in place of a
+// caller workspace: one copy per GPU, held until the process ends, shared by
+// every lora_shrink_noalloc call on that GPU.
+static __device__ __align__(256) unsigned char scratch[LORA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of `scratch` on `device`, which must be current: taken with
+// hipGetSymbolAddress on the first call for that device and kept; nullptr if
+// HIP cannot give it.  Host code uses only this address, never the array's
+// name (a host-side stand-in).
+void* scratch_on_device(int device) {
+  static std::mutex mu;
+  static std::map<int, void*> ptrs;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto it = ptrs.find(device);
+  if (it != ptrs.end()) return it->second;
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  ptrs.emplace(device, ptr);
+  return ptr;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t lora_shrink_workspace_bytes(const lora_pool* p, int32_t n_tokens, int32_t n_modules) {
@@ -460,6 +488,27 @@ lora_status lora_shrink(const lora_pool* p, int32_t module0, int32_t n_modules, 
   DeviceGuard g(p->device);
   if (!g.ok) return LORA_ERR_HIP;
   const ShrinkSplit sp = shrink_split(p, module0, n_modules, module_stride_x, seg, ws_bytes);
+  return shrink_call(p, module0, n_modules, x, ld_x, module_stride_x, seg, t, ld_t, module_stride_t, sp, ws,
+                     static_cast<hipStream_t>(stream));
+}
+
+lora_status lora_shrink_noalloc(const lora_pool* p, int32_t module0, int32_t n_modules, const void* x, int64_t ld_x,
+                                int64_t module_stride_x, const lora_segments* seg, float* t, int64_t ld_t,
+                                int64_t module_stride_t, void* stream) {
+  lora_status st = shrink_checks(p, module0, n_modules, x, ld_x, module_stride_x, seg, t, ld_t, module_stride_t);
+  if (st != LORA_OK) return st;
+  if (seg->n_tokens == 0) return LORA_OK;
+  // the split lora_shrink makes with a workspace of lora_shrink_workspace_bytes, if it fits the scratch
+  const ShrinkSplit sp = shrink_split(p, module0, n_modules, module_stride_x, seg, SIZE_MAX);
+  const size_t need = split_ws_bytes(p, seg->n_tokens, n_modules, sp.ks);
+  if (need > static_cast<size_t>(LORA_NOALLOC_SCRATCH_BYTES)) return LORA_ERR_WORKSPACE;
+  DeviceGuard g(p->device);
+  if (!g.ok) return LORA_ERR_HIP;
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = scratch_on_device(p->device);
+    if (!ws) return LORA_ERR_HIP;
+  }
   return shrink_call(p, module0, n_modules, x, ld_x, module_stride_x, seg, t, ld_t, module_stride_t, sp, ws,
                      static_cast<hipStream_t>(stream));
 }
