@@ -39,7 +39,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="bgmv_decode_x128",
                     choices=["bgmv_decode_x128", "bgmv_decode", "sgmv_prefill", "mixed_rank", "encoder_step",
-                             "encoder_fused", "prefill_fused", "tiers_trace"])
+                             "encoder_fused", "prefill_fused", "encoder_fused_fp8", "prefill_fused_fp8",
+                             "tiers_trace"])
     ap.add_argument("--path", choices=["auto", "bgmv", "sgmv"], default="auto",
                     help="force the fused BGMV or the shrink+expand path (default: the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -89,6 +90,14 @@ def make_workload(name):
             "workload": "encoder_fused", "tokens": 32768, "slots": 1024, "rank": 16,
             "modules": "qkv 768->2304, o 768->768, up 768->3072, down 3072->768",
             "step": "y = x W + adapter term per module, one lora_fused_gemm call each"}
+    if name in ("encoder_fused_fp8", "prefill_fused_fp8"):
+        base = W.c5_encoder_step() if name == "encoder_fused_fp8" else W.c3_sgmv_prefill()
+        return W.with_fp8_base(base), "fused8", {
+            "workload": name, "tokens": base.n_tokens, "rank": 16,
+            "modules": ("qkv 768->2304, o 768->768, up 768->3072, down 3072->768" if name == "encoder_fused_fp8"
+                        else "q,k,v,o 4096->4096 (q,k,v share x)"),
+            "base": "W as OCP FP8 E4M3 with one float32 scale per output column; x, adapters, y bf16",
+            "step": "y = x W + adapter term per module, one lora_fused_gemm_fp8w call each"}
     if name == "prefill_fused":
         return W.c3_sgmv_prefill(), "fused", {
             "workload": "prefill_fused", "tokens": 4096, "segments": 8, "h": 4096, "rank": 16,
@@ -246,17 +255,20 @@ def cpu_baseline(wl, seconds):
                       f"per-token loop, {el:.1f} s on one core (BLAS threads = 1)"}
 
 
-def fused_work(wl):
+def fused_work(wl, w_elem_bytes=2):
     """Algorithmic flops and bytes of one fused step: every module's base
     product (x read, W read, y written once) plus its adapter term (each
-    distinct adapter's A and B pages read once)."""
+    distinct adapter's A and B pages read once).  w_elem_bytes 1: W as FP8
+    codes plus one float32 scale per output column."""
     import numpy as np
     flops = byts = 0
     used = sorted(set(int(i) for i in np.unique(wl.ids) if 0 <= i < wl.n_slots))
     for m, mod in enumerate(wl.modules):
         n = wl.n_tokens
         flops += 2.0 * n * mod.h_in * mod.h_out
-        byts += 2 * (n * mod.h_in + mod.h_in * mod.h_out + n * mod.h_out)
+        byts += 2 * (n * mod.h_in + n * mod.h_out) + w_elem_bytes * mod.h_in * mod.h_out
+        if w_elem_bytes == 1:
+            byts += 4 * mod.h_out
         for i in range(n):
             a = wl.adapters[int(wl.ids[i])][m] if 0 <= wl.ids[i] < wl.n_slots else None
             if a is not None:
@@ -268,9 +280,10 @@ def fused_work(wl):
     return flops, byts
 
 
-def cpu_baseline_fused(wl, seconds):
+def cpu_baseline_fused(wl, seconds, fp8=False):
     """The oracle, untouched, on one core: y = x W + adapter term for whole
-    tokens (all modules) of the workload, 64 tokens at a time, until `seconds`."""
+    tokens (all modules) of the workload, 64 tokens at a time, until `seconds`
+    (fp8: the FP8-base forward)."""
     from threadpoolctl import threadpool_limits
     from oracle import lora_oracle as lo
     done, t0 = 0, time.perf_counter()
@@ -278,14 +291,15 @@ def cpu_baseline_fused(wl, seconds):
         while done < wl.n_tokens:
             toks = range(done, min(wl.n_tokens, done + 64))
             for m in range(wl.n_modules):
-                lo.lora_forward(wl, m, toks)
+                (lo.lora_forward_fp8w if fp8 else lo.lora_forward)(wl, m, toks)
             done += len(toks)
             if time.perf_counter() - t0 >= seconds:
                 break
     el = time.perf_counter() - t0
     return {"value": done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"the first {done} of {wl.n_tokens} tokens x {wl.n_modules} modules, fp64 per-token "
-                      f"x W plus adapter term, {el:.1f} s on one core (BLAS threads = 1)"}
+                      f"x W{' (FP8 base)' if fp8 else ''} plus adapter term, {el:.1f} s on one core "
+                      f"(BLAS threads = 1)"}
 
 
 def time_ms(fn, reps=10):
@@ -420,10 +434,14 @@ def main():
     if mode == "fused":
         for d in dws:
             d.upload_weights()
+    if mode == "fused8":
+        for d in dws:
+            d.upload_weights_fp8()
+            d.upload_weights()   # the bf16 pass of the same layer, timed beside it
 
     def step(ev=None, i=0):
         d = dws[i % rotate]
-        if mode != "fused":
+        if mode not in ("fused", "fused8"):
             d.build_segments()
         if ev is not None:
             ev[0].record(stream)
@@ -431,6 +449,8 @@ def main():
             d.bgmv()
         elif mode == "fused":
             d.fused()
+        elif mode == "fused8":
+            d.fused_fp8()
         else:
             d.shrink()
             d.expand()
@@ -484,10 +504,11 @@ def main():
         extra["single_module_bytes"] = work["per_module"][0]["bytes"]
         extra["single_module_GBps"] = work["per_module"][0]["bytes"] / (np.median(lat) * 1e-3) / 1e9
 
-    if mode == "fused":
-        flops, byts = fused_work(wl)
+    if mode in ("fused", "fused8"):
+        fp8 = mode == "fused8"
+        flops, byts = fused_work(wl, 1 if fp8 else 2)
         tf = flops / (kern_avg * 1e-3) / 1e12
-        base_ours = time_ms(lambda: dw.fused(adapters=False))
+        base_ours = time_ms(lambda: (dw.fused_fp8 if fp8 else dw.fused)(adapters=False))
         gms, _ = base_gemm_ms(wl)
         unfused = time_ms(lambda: dw.sgmv_step())
         extra = {"fused_ms_mean": kern_avg, "fused_ms_min": float(np.min(kern_ms)), "flops_per_step": flops,
@@ -497,11 +518,18 @@ def main():
                  "hipblaslt_plus_unfused_ms": round(gms + unfused, 4),
                  "fused_over_hipblaslt_plus_unfused": round(kern_avg / (gms + unfused), 4),
                  "fused_over_hipblaslt_base": round(kern_avg / gms, 4)}
+        if fp8:   # the bf16 pass of the same layer and its W bytes, beside the FP8 one
+            bf16_ms = time_ms(lambda: dw.fused())
+            _, byts16 = fused_work(wl, 2)
+            extra.update({"bf16_fused_ms": round(bf16_ms, 4), "fp8_over_bf16_fused": round(kern_avg / bf16_ms, 4),
+                          "w_bytes_fp8": int(sum(m.h_in * m.h_out + 4 * m.h_out for m in wl.modules)),
+                          "w_bytes_bf16": int(sum(2 * m.h_in * m.h_out for m in wl.modules)),
+                          "algorithmic_bytes_bf16_pass": byts16})
         # traffic: counter-measured HBM bytes of one step (all its launches), against
         # algorithmic_bytes_per_step
         roofline = {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": load_traffic(args.workload),
-                    "kernel": "k_fused_gemm", "flops_per_launch_set": flops}
+                    "kernel": "k_fused_gemm<W8>" if fp8 else "k_fused_gemm", "flops_per_launch_set": flops}
         out = {
             "metric": METRIC, "value": round(wl.n_tokens / (ms_step * 1e-3), 1), "unit": "tokens/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
@@ -511,7 +539,7 @@ def main():
         for d in dws:
             d.close()
         if not args.no_cpu_baseline:
-            out["cpu_baseline"] = cpu_baseline_fused(wl, args.cpu_seconds)
+            out["cpu_baseline"] = cpu_baseline_fused(wl, args.cpu_seconds, fp8=fp8)
         print(json.dumps(out), flush=True)
         return
 

@@ -307,6 +307,26 @@ lora_status lora_fused_gemm(const lora_pool *p, int32_t module,
                             const int32_t *ids, int32_t n_tokens,
                             void *y, int64_t ld_y, void *stream);
 
+/* lora_fused_gemm with an FP8 base (study page, section "Operating it": a
+ * quantized base serves under the bf16 adapters; its design scenario takes
+ * the base in FP8).  W is given as OCP FP8 E4M3 codes (1 sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits; exponent 0 holds the subnormals m * 2^-9;
+ * 0x7F and 0xFF are NaN; largest finite 448) with one float32 scale per output
+ * column:
+ *   y_i[c] = round(w_scale[c] * sum_k x_i[k] E(w8[c][k]) + scale_a * sum_{j<rank_a} t_i[j] B_a[j][c]),
+ * E the exact value of a code.  x, ids, the adapters and y are as for
+ * lora_fused_gemm (bf16 activations and adapters: W8A16).  Each code is
+ * widened to bf16, which holds every E4M3 value exactly, so the matrix-core
+ * products are exact; the sum is fp32, then multiplied by the column scale.
+ *   w8 [h_out][ld_w] bytes: row c holds the codes of output column c; 16-byte
+ *     aligned, ld_w a multiple of 16.
+ *   w_scale [h_out] float32, 16-byte aligned.
+ * Errors: as lora_fused_gemm. */
+lora_status lora_fused_gemm_fp8w(const lora_pool *p, int32_t module,
+                                 const void *x, int64_t ld_x, const void *w8, int64_t ld_w,
+                                 const float *w_scale, const int32_t *ids, int32_t n_tokens,
+                                 void *y, int64_t ld_y, void *stream);
+
 /* ---- Adapter tiers: GPU slots <- host memory <- cold store ----------------
  * Study page "Multi-LoRA Serving", section "Memory: slots, tiers and paging"
  * and its cache simulation: the engine keeps a fixed number of adapters in

@@ -33,8 +33,9 @@ from typing import Dict, Iterable, Optional, Sequence
 import numpy as np
 
 __all__ = [
-    "decode", "adapter_term", "lora_delta", "base_product", "lora_forward",
+    "decode", "decode_e4m3", "adapter_term", "lora_delta", "base_product", "lora_forward",
     "apply_to_y0", "merged_forward", "build_segments", "shrink_t",
+    "base_product_fp8w", "lora_forward_fp8w",
 ]
 
 
@@ -50,6 +51,22 @@ def decode(a: np.ndarray, dtype: str) -> np.ndarray:
         bits = np.asarray(a, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
         return bits.view(np.float32).astype(np.float64)
     raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def decode_e4m3(codes: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3 codes (uint8) -> float64, exactly, from the format's
+    definition: bit 7 is the sign, bits 6..3 the exponent e (bias 7), bits 2..0
+    the mantissa m.  e >= 1: (1 + m/8) 2^(e-7) = (8 + m) 2^(e-10); e = 0: the
+    subnormals m 2^-9 (and +-0); e = 15 with m = 7 is NaN; there are no
+    infinities, so the largest finite magnitude is 448 (e = 15, m = 6)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = (c >> 7) & 1
+    e = (c >> 3) & 0xF
+    m = c & 7
+    mag = np.where(e == 0, np.ldexp(m.astype(np.float64), -9),
+                   np.ldexp((8 + m).astype(np.float64), (e - 10).astype(np.int64)))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(sign == 1, -mag, mag)
 
 
 def _adapter(wl, slot: int, module: int):
@@ -132,6 +149,26 @@ def base_product(wl, module: int, tokens: Optional[Iterable[int]] = None) -> np.
 def lora_forward(wl, module: int, tokens: Optional[Iterable[int]] = None) -> np.ndarray:
     """y_i = x_i W + scale_a (x_i A_a^T) B_a for each requested token."""
     return base_product(wl, module, tokens) + lora_delta(wl, module, tokens)
+
+
+def base_product_fp8w(wl, module: int, tokens: Optional[Iterable[int]] = None) -> np.ndarray:
+    """The base product with an FP8 base (the study page's "Operating it":
+    a quantized base under bf16 adapters): x_i W with W[k][c] =
+    w_scale[c] * E(W8[k][c]), E the exact value of an E4M3 code and w_scale
+    one float32 scale per output column.  fp64 per token."""
+    mod = wl.modules[module]
+    x = wl.x[mod.x_group]
+    W = decode_e4m3(wl.W8[module]) * np.asarray(wl.W8_scale[module], np.float32).astype(np.float64)[None, :]
+    toks = _tokens(wl, tokens)
+    out = np.empty((len(toks), mod.h_out), dtype=np.float64)
+    for row, i in enumerate(toks):
+        out[row] = decode(x[i], wl.dtype) @ W
+    return out
+
+
+def lora_forward_fp8w(wl, module: int, tokens: Optional[Iterable[int]] = None) -> np.ndarray:
+    """y_i = x_i W (FP8 base, base_product_fp8w) + scale_a (x_i A_a^T) B_a."""
+    return base_product_fp8w(wl, module, tokens) + lora_delta(wl, module, tokens)
 
 
 def apply_to_y0(wl, module: int, tokens: Optional[Iterable[int]] = None) -> np.ndarray:

@@ -21,7 +21,7 @@ __all__ = [
     "lora_segments_bytes", "lora_segments_bind", "lora_build_segments",
     "lora_segments_check", "lora_shrink_workspace_bytes", "lora_shrink", "lora_shrink_noalloc",
     "LORA_NOALLOC_SCRATCH_BYTES",
-    "lora_expand", "lora_apply_bgmv", "lora_fused_gemm",
+    "lora_expand", "lora_apply_bgmv", "lora_fused_gemm", "lora_fused_gemm_fp8w",
     "LORA_TIER_GPU", "LORA_TIER_HOST", "LORA_TIER_COLD", "lora_tiers_create", "lora_tiers_destroy",
     "lora_tiers_touch", "lora_tiers_stats", "lora_tiers_slot_of", "lora_tiers_acquire",
     "lora_tiers_batch_done", "lora_tiers_prefetch",
@@ -98,6 +98,7 @@ _SIGS = {
     "lora_expand": (_I32, [_P, _I32, _I32, _P, _I64, _I64, _SEGP, _P, _I64, _I64, _I32, _P]),
     "lora_apply_bgmv": (_I32, [_P, _I32, _I32, _P, _I64, _I64, _SEGP, _P, _I64, _I64, _I32, _P]),
     "lora_fused_gemm": (_I32, [_P, _I32, _P, _I64, _P, _I64, _P, _I32, _P, _I64, _P]),
+    "lora_fused_gemm_fp8w": (_I32, [_P, _I32, _P, _I64, _P, _I64, _P, _P, _I32, _P, _I64, _P]),
     "lora_tiers_create": (_I32, [ctypes.POINTER(_P), _I32, _I32]),
     "lora_tiers_destroy": (_I32, [_P]),
     "lora_tiers_touch": (_I32, [_P, _P, _I32, _P, _P, _P]),
@@ -262,6 +263,12 @@ def lora_fused_gemm(pool: int, module: int, x, ld_x: int, w, ld_w: int, ids, n_t
                     stream=None) -> None:
     _check(_lib.lora_fused_gemm(pool, module, _ptr(x), ld_x, _ptr(w), ld_w, _ptr(ids), n_tokens, _ptr(y), ld_y,
                                 _stream(stream)), "lora_fused_gemm")
+
+
+def lora_fused_gemm_fp8w(pool: int, module: int, x, ld_x: int, w8, ld_w: int, w_scale, ids, n_tokens: int, y,
+                         ld_y: int, stream=None) -> None:
+    _check(_lib.lora_fused_gemm_fp8w(pool, module, _ptr(x), ld_x, _ptr(w8), ld_w, _ptr(w_scale), _ptr(ids),
+                                     n_tokens, _ptr(y), ld_y, _stream(stream)), "lora_fused_gemm_fp8w")
 
 
 # ------------------------------------------------------------------ adapter tiers

@@ -440,6 +440,61 @@ lora_status shrink_call(const lora_pool* p, int32_t module0, int32_t n_modules, 
   return launch_shrink<float>(p, module0, n_modules, x, ld_x, msx, seg, t, ld_t, mst, sp, ws, s);
 }
 
+// The fused base + adapter pass: checks shared by both weight formats, then the
+// launch.  Exactly one of w (bf16 W^T) and w8 (e4m3 W^T with column scales) is
+// given; their own alignment is checked by the caller.
+lora_status fused_call(const lora_pool* p, int32_t module, const void* x, int64_t ld_x, const void* w,
+                       const uint8_t* w8, int64_t ld_w, const float* w_scale, const int32_t* ids, int32_t n_tokens,
+                       void* y, int64_t ld_y, void* stream) {
+  if (!p || module < 0 || module >= p->n_modules || n_tokens < 0) return LORA_ERR_ARG;
+  if (p->dtype != LORA_BF16) return LORA_ERR_DTYPE;
+  const int64_t h_in = p->h_in[module], h_out = p->h_out[module];
+  if (h_in / p->page_elems > kFgMaxPpr || p->n_slots > kFgMaxSlots) return LORA_ERR_SHAPE;
+  if (!x || !y) return LORA_ERR_ARG;
+  if (ld_x < h_in || ld_w < h_in || ld_y < h_out) return LORA_ERR_ARG;
+  // a tile's 256 rows of x or W^T are addressed with 32-bit byte offsets
+  if (ld_x > (int64_t(1) << 22) || ld_w > (int64_t(1) << 22)) return LORA_ERR_SHAPE;
+  if (!aligned16(x) || (ld_x * 2) % 16 != 0) return LORA_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(y) & 7u) != 0 || (ld_y * 2) % 8 != 0) return LORA_ERR_ARG;
+  if (n_tokens == 0) return LORA_OK;
+  DeviceGuard g(p->device);
+  if (!g.ok) return LORA_ERR_HIP;
+  FusedArgs fa{};
+  fa.pv = p->view();
+  fa.x = static_cast<const __bf16*>(x);
+  fa.w = static_cast<const __bf16*>(w);
+  fa.w8 = w8;
+  fa.w_scale = w_scale;
+  fa.ids = ids;
+  fa.y = static_cast<__bf16*>(y);
+  fa.ld_x = ld_x;
+  fa.ld_w = ld_w;
+  fa.ld_y = ld_y;
+  fa.n = n_tokens;
+  fa.h_in = static_cast<int32_t>(h_in);
+  fa.h_out = static_cast<int32_t>(h_out);
+  fa.module = module;
+  const int64_t n_rt = (static_cast<int64_t>(n_tokens) + kFgBM - 1) / kFgBM;
+  fa.n_ct = static_cast<int32_t>((h_out + kFgBN - 1) / kFgBN);
+  const int64_t tiles = n_rt * fa.n_ct;
+  if (tiles > (int64_t(1) << 30)) return LORA_ERR_SHAPE;
+  fa.n_tiles = static_cast<int32_t>(tiles);
+  const unsigned grid = static_cast<unsigned>((tiles + 7) / 8 * 8);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (w8) {
+    if (ids)
+      hipLaunchKernelGGL((k_fused_gemm<true, true>), dim3(grid), dim3(kFgThreads), 0, s, fa);
+    else
+      hipLaunchKernelGGL((k_fused_gemm<false, true>), dim3(grid), dim3(kFgThreads), 0, s, fa);
+  } else {
+    if (ids)
+      hipLaunchKernelGGL((k_fused_gemm<true, false>), dim3(grid), dim3(kFgThreads), 0, s, fa);
+    else
+      hipLaunchKernelGGL((k_fused_gemm<false, false>), dim3(grid), dim3(kFgThreads), 0, s, fa);
+  }
+  return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
 }  // namespace
 
 // Device memory of lora_shrink_noalloc's K-split partial tiles, in place of a
@@ -576,44 +631,18 @@ lora_status lora_apply_bgmv(const lora_pool* p, int32_t module0, int32_t n_modul
 lora_status lora_fused_gemm(const lora_pool* p, int32_t module, const void* x, int64_t ld_x, const void* w,
                             int64_t ld_w, const int32_t* ids, int32_t n_tokens, void* y, int64_t ld_y,
                             void* stream) {
-  if (!p || module < 0 || module >= p->n_modules || n_tokens < 0) return LORA_ERR_ARG;
-  if (p->dtype != LORA_BF16) return LORA_ERR_DTYPE;
-  const int64_t h_in = p->h_in[module], h_out = p->h_out[module];
-  if (h_in / p->page_elems > kFgMaxPpr || p->n_slots > kFgMaxSlots) return LORA_ERR_SHAPE;
-  if (!x || !w || !y) return LORA_ERR_ARG;
-  if (ld_x < h_in || ld_w < h_in || ld_y < h_out) return LORA_ERR_ARG;
-  // a tile's 256 rows of x or W^T are addressed with 32-bit byte offsets
-  if (ld_x > (int64_t(1) << 22) || ld_w > (int64_t(1) << 22)) return LORA_ERR_SHAPE;
-  if (!aligned16(x) || !aligned16(w) || (ld_x * 2) % 16 != 0 || (ld_w * 2) % 16 != 0) return LORA_ERR_ARG;
-  if ((reinterpret_cast<uintptr_t>(y) & 7u) != 0 || (ld_y * 2) % 8 != 0) return LORA_ERR_ARG;
-  if (n_tokens == 0) return LORA_OK;
-  DeviceGuard g(p->device);
-  if (!g.ok) return LORA_ERR_HIP;
-  FusedArgs fa{};
-  fa.pv = p->view();
-  fa.x = static_cast<const __bf16*>(x);
-  fa.w = static_cast<const __bf16*>(w);
-  fa.ids = ids;
-  fa.y = static_cast<__bf16*>(y);
-  fa.ld_x = ld_x;
-  fa.ld_w = ld_w;
-  fa.ld_y = ld_y;
-  fa.n = n_tokens;
-  fa.h_in = static_cast<int32_t>(h_in);
-  fa.h_out = static_cast<int32_t>(h_out);
-  fa.module = module;
-  const int64_t n_rt = (static_cast<int64_t>(n_tokens) + kFgBM - 1) / kFgBM;
-  fa.n_ct = static_cast<int32_t>((h_out + kFgBN - 1) / kFgBN);
-  const int64_t tiles = n_rt * fa.n_ct;
-  if (tiles > (int64_t(1) << 30)) return LORA_ERR_SHAPE;
-  fa.n_tiles = static_cast<int32_t>(tiles);
-  const unsigned grid = static_cast<unsigned>((tiles + 7) / 8 * 8);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (ids)
-    hipLaunchKernelGGL((k_fused_gemm<true>), dim3(grid), dim3(kFgThreads), 0, s, fa);
-  else
-    hipLaunchKernelGGL((k_fused_gemm<false>), dim3(grid), dim3(kFgThreads), 0, s, fa);
-  return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+  if (!w) return LORA_ERR_ARG;
+  if (!aligned16(w) || (ld_w * 2) % 16 != 0) return LORA_ERR_ARG;
+  return fused_call(p, module, x, ld_x, w, nullptr, ld_w, nullptr, ids, n_tokens, y, ld_y, stream);
+}
+
+lora_status lora_fused_gemm_fp8w(const lora_pool* p, int32_t module, const void* x, int64_t ld_x, const void* w8,
+                                 int64_t ld_w, const float* w_scale, const int32_t* ids, int32_t n_tokens, void* y,
+                                 int64_t ld_y, void* stream) {
+  if (!w8 || !w_scale) return LORA_ERR_ARG;
+  if (!aligned16(w8) || ld_w % 16 != 0 || !aligned16(w_scale)) return LORA_ERR_ARG;
+  return fused_call(p, module, x, ld_x, nullptr, static_cast<const uint8_t*>(w8), ld_w, w_scale, ids, n_tokens, y,
+                    ld_y, stream);
 }
 
 }  // extern "C"

@@ -62,6 +62,8 @@ struct FusedArgs {
   PoolView pv;
   const __bf16* x;        // [n][ld_x]
   const __bf16* w;        // W^T: [h_out][ld_w], row c = weights of output column c
+  const uint8_t* w8;      // W8 kernel: W^T as OCP e4m3 codes, [h_out][ld_w] bytes
+  const float* w_scale;   // W8 kernel: [h_out] scale of each output column
   const int32_t* ids;     // [n]; unused by the base-only kernel
   __bf16* y;              // [n][ld_y], written
   int64_t ld_x, ld_w, ld_y;
@@ -137,8 +139,21 @@ __device__ __forceinline__ bf16x8 fg_lds8(const unsigned char* base, int off) {
 template <int V>
 using fg_int = std::integral_constant<int, V>;
 
-// LORA false: base product only.
-template <bool LORA>
+// Two OCP e4m3 codes (the low or high half of w) widened to two bf16 values.
+// Every e4m3 value has at most 4 significant bits and an exponent inside
+// bf16's range, so the widening is exact (scale 1).
+__device__ __forceinline__ uint32_t fg_e4m3x2_to_bf16x2(uint32_t w, bool high) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = high ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                        : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// LORA false: base product only.  W8: W^T given as e4m3 codes with a scale per
+// output column (W8A16: the codes are widened to bf16 on their way into LDS,
+// exactly, and the column scale multiplies the base product before the
+// adapter term is added).
+template <bool LORA, bool W8>
 __global__ __launch_bounds__(kFgThreads, 1) void k_fused_gemm(FusedArgs a) {
   __shared__ FgShared sh;
   constexpr int CB = 4;   // 16-column blocks per wave
@@ -185,8 +200,44 @@ __global__ __launch_bounds__(kFgThreads, 1) void k_fused_gemm(FusedArgs a) {
     for (int q = 0; q < 4; ++q)
       __builtin_amdgcn_global_load_lds(wb + woff[q], fg_lds_ptr(sh.stage[buf][1] + 1024 * (wave + 8 * q)), 16, 0, 0);
   };
+  // W8: each thread moves two 16-byte pieces of e4m3 codes per K step (rows
+  // i / 4 of the tile, k 16 (i % 4) .. +16, for i = tid, tid + 512) through
+  // registers, widened to four bf16 chunks in the same swizzled layout
+  const uint8_t* w8base = W8 ? a.w8 + static_cast<int64_t>(col0) * a.ld_w : nullptr;
+  uint32_t w8off[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int i = tid + kFgThreads * q;
+    const int r = i >> 2;
+    w8off[q] = static_cast<uint32_t>(min(r, a.h_out - 1 - col0) * a.ld_w + 16 * (i & 3));
+  }
+  u32x4 w8reg[2];
+  auto issue_w8 = [&](int kt) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) w8reg[q] = *reinterpret_cast<const u32x4*>(w8base + kt * kFgBK + w8off[q]);
+  };
+  auto store_w8 = [&](int buf) {
+    unsigned char* Ws = sh.stage[buf][1];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int i = tid + kFgThreads * q;
+      const int r = i >> 2, c = 2 * (i & 3);
+      const u32x4 v = w8reg[q];
+      const u32x4 lo{fg_e4m3x2_to_bf16x2(v.x, false), fg_e4m3x2_to_bf16x2(v.x, true),
+                     fg_e4m3x2_to_bf16x2(v.y, false), fg_e4m3x2_to_bf16x2(v.y, true)};
+      const u32x4 hi{fg_e4m3x2_to_bf16x2(v.z, false), fg_e4m3x2_to_bf16x2(v.z, true),
+                     fg_e4m3x2_to_bf16x2(v.w, false), fg_e4m3x2_to_bf16x2(v.w, true)};
+      *reinterpret_cast<u32x4*>(Ws + fg_swz(r, c)) = lo;
+      *reinterpret_cast<u32x4*>(Ws + fg_swz(r, c + 1)) = hi;
+    }
+  };
   load_x(0, 0);
-  load_w(0, 0);
+  if constexpr (W8) {
+    issue_w8(0);
+    store_w8(0);
+  } else {
+    load_w(0, 0);
+  }
 
   // ---- the tile's adapters and units
   int n_units = 0;
@@ -348,9 +399,11 @@ __global__ __launch_bounds__(kFgThreads, 1) void k_fused_gemm(FusedArgs a) {
     for (int kt = 0; kt < nk - 1; ++kt) {
       const int buf = kt & 1;
       load_x(kt + 1, buf ^ 1);   // that buffer's readers passed the last barrier
-      if constexpr (BASE) load_w(kt + 1, buf ^ 1);
+      if constexpr (BASE && !W8) load_w(kt + 1, buf ^ 1);
+      if constexpr (BASE && W8) issue_w8(kt + 1);
       if constexpr (P > 0) load_a(P_, kt + 1, buf ^ 1);
       step(buf);
+      if constexpr (BASE && W8) store_w8(buf ^ 1);   // widened after this step's reads of buf
       __syncthreads();
     }
     if constexpr (P > 0) load_b(P_, idle + kFgTileBytes + kFgBOff);
@@ -413,6 +466,20 @@ __global__ __launch_bounds__(kFgThreads, 1) void k_fused_gemm(FusedArgs a) {
     }
   };
 
+  // W8: the base accumulators times each output column's scale (before any
+  // adapter term is added).  Lane: columns col0 + 64 wn + 16 cb + 4 lq .. +4.
+  auto scale_base = [&]() {
+    if constexpr (W8) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int col = col0 + 64 * wn + 16 * cb + 4 * lq;
+        const f32x4 sc = col < a.h_out ? *reinterpret_cast<const f32x4*>(a.w_scale + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int tb = 0; tb < 8; ++tb) acc[cb][tb] *= sc;
+      }
+    }
+  };
+
   // ---- pass 0: the base product with up to two units
   if constexpr (LORA) {
     const int np0 = min(n_units, kFgPassUnits);
@@ -424,15 +491,18 @@ __global__ __launch_bounds__(kFgThreads, 1) void k_fused_gemm(FusedArgs a) {
       load_a(fg_int<2>{}, 0, 0);
       __syncthreads();
       kloop(fg_int<2>{}, fg_int<1>{});
+      scale_base();
       expand(fg_int<2>{}, 0);
     } else if (np0 == 1) {
       load_a(fg_int<1>{}, 0, 0);
       __syncthreads();
       kloop(fg_int<1>{}, fg_int<1>{});
+      scale_base();
       expand(fg_int<1>{}, 0);
     } else {
       __syncthreads();
       kloop(fg_int<0>{}, fg_int<1>{});
+      scale_base();
     }
     // ---- further passes, one unit at a time, shrink only
     for (int u0 = np0; u0 < n_units; ++u0) {
@@ -448,6 +518,7 @@ __global__ __launch_bounds__(kFgThreads, 1) void k_fused_gemm(FusedArgs a) {
   } else {
     __syncthreads();   // stage 0 has landed (the barrier waits for the loads)
     kloop(fg_int<0>{}, fg_int<1>{});
+    scale_base();
   }
 
   // ---- y: lane holds output columns 4 lq .. +4 of col block cb for token

@@ -16,6 +16,7 @@ import numpy as np
 import torch
 
 from . import (LORA_BF16, LORA_F32, lora_apply_bgmv, lora_build_segments, lora_expand, lora_fused_gemm,
+               lora_fused_gemm_fp8w,
                lora_pool_create, lora_pool_destroy, lora_pool_load, lora_segments_bind,
                lora_segments_bytes, lora_shrink, lora_shrink_workspace_bytes)
 
@@ -203,6 +204,28 @@ class DeviceWorkload:
             h_in, h_out = mods[m].h_in, mods[m].h_out
             lora_fused_gemm(self.pool, m, self._xp(self.x_off[mods[m].x_group]), h_in, self.wT[m], h_in,
                             self.ids if adapters else None, self.n, self.y_of(m), h_out, stream)
+
+    def upload_weights_fp8(self):
+        """W^T as E4M3 codes ([h_out][h_in] bytes) and the column scales of every module."""
+        self.w8T, self.w8s = [], []
+        for m in range(len(self.wl.modules)):
+            W8 = self.wl.W8[m]
+            if W8 is None:
+                self.w8T.append(None)
+                self.w8s.append(None)
+                continue
+            self.w8T.append(torch.from_numpy(np.ascontiguousarray(W8.T)).to(self.dev))
+            self.w8s.append(torch.from_numpy(np.ascontiguousarray(self.wl.W8_scale[m], np.float32)).to(self.dev))
+
+    def fused_fp8(self, stream=None, adapters: bool = True, modules=None):
+        """y = x W (FP8 base) (+ the adapter term) per module in one lora_fused_gemm_fp8w call each."""
+        mods = self.wl.modules
+        if not hasattr(self, "w8T"):
+            self.upload_weights_fp8()
+        for m in (range(len(mods)) if modules is None else modules):
+            h_in, h_out = mods[m].h_in, mods[m].h_out
+            lora_fused_gemm_fp8w(self.pool, m, self._xp(self.x_off[mods[m].x_group]), h_in, self.w8T[m], h_in,
+                                 self.w8s[m], self.ids if adapters else None, self.n, self.y_of(m), h_out, stream)
 
     def sgmv_step(self, stream=None):
         self.build_segments(stream)

@@ -264,3 +264,82 @@ def test_pins_catch_planted_decode_mistake(monkeypatch):
     monkeypatch.setattr(lo, "decode", real)
     assert np.array_equal(lo.decode(np.array([0x3F80, 0xC000], np.uint16), "bf16"), [1.0, -2.0])
     assert wl.n_tokens == 4
+
+
+# ---------------------------------------------------------------- FP8 base
+def _e4m3_pins(decode):
+    """The OCP E4M3 decode against what fixes it outside the oracle: a library
+    routine over all 256 codes, closed forms and invariants of the format."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    d = decode(codes)
+    lib = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ok = np.array_equal(np.isnan(d), np.isnan(lib))
+    fin = ~np.isnan(lib)
+    ok &= np.array_equal(d[fin], lib[fin]) and np.array_equal(np.signbit(d[fin]), np.signbit(lib[fin]))
+    closed = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0, 0x3C: 1.5,
+              0x78: 256.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0, 0x80: -0.0}
+    for c, v in closed.items():
+        ok &= bool(d[c] == v) and bool(np.signbit(d[c]) == np.signbit(v))
+    ok &= bool(np.isnan(d[0x7F]) and np.isnan(d[0xFF])) and int(np.isnan(d).sum()) == 2
+    pos = d[:0x7F]
+    ok &= bool(np.all(np.diff(pos) > 0))                          # magnitudes increase with the code
+    ok &= np.array_equal(d[0x80:0xFF], -d[:0x7F])                 # the sign bit only flips the sign
+    bf = (np.asarray(pos, np.float32).view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
+    ok &= np.array_equal(bf.astype(np.float64), pos)              # every value is a bf16 value
+    return bool(ok)
+
+
+def test_e4m3_decode_pins():
+    assert _e4m3_pins(lo.decode_e4m3)
+
+
+def test_fp8_base_brute_force_and_identity():
+    """base_product_fp8w: exact rationals on a tiny case; the code sweep's identity x."""
+    rng = np.random.default_rng(31)
+    wl = W.Workload("t8", "bf16", 8, 1, [W.Module("p", 8, 5, 0)], np.array([-1, -1, -1], np.int32),
+                    [W.to_bf16_bits(rng.normal(0, 1, (3, 8)).astype(np.float32))],
+                    [W.to_bf16_bits(np.zeros((3, 5), np.float32))], [None], [[None]])
+    codes = rng.integers(0, 256, (8, 5)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3A
+    wl.W8 = [codes]
+    wl.W8_scale = [rng.uniform(0.5, 2.0, 5).astype(np.float32)]
+    got = lo.base_product_fp8w(wl, 0)
+    x = lo.decode(wl.x[0], "bf16")
+    val = lo.decode_e4m3(codes)
+    for i in range(3):
+        for c in range(5):
+            exact = sum(Fraction(float(x[i][k])) * Fraction(float(val[k][c])) for k in range(8))
+            exact *= Fraction(float(wl.W8_scale[0][c]))
+            assert abs(float(exact) - got[i][c]) <= 1e-13 * max(1.0, abs(float(exact)))
+    sw = W.fp8_code_sweep()
+    y = lo.base_product_fp8w(sw, 0)
+    k = np.arange(256)
+    codes = ((k[:, None] + k[None, :]) % 256).astype(np.uint8)
+    codes[(codes == 0x7F) | (codes == 0xFF)] = 0          # the sweep's stand-in for the NaN codes
+    assert np.array_equal(y, lo.decode_e4m3(codes))
+
+
+def test_e4m3_planted_mistakes_fail_a_pin():
+    """A bias of 8 (the other FP8 E4M3 variant), subnormals read as normals, and
+    the NaN code read as 480 each fail the decode pins."""
+    def bias8(c):
+        c = np.asarray(c, np.uint8).astype(np.int64)
+        s, e, m = (c >> 7) & 1, (c >> 3) & 15, c & 7
+        mag = np.where(e == 0, np.ldexp(m.astype(float), -10), np.ldexp((8 + m).astype(float), e - 11))
+        mag = np.where((e == 15) & (m == 7), np.nan, mag)
+        return np.where(s == 1, -mag, mag)
+
+    def no_subnormals(c):
+        c = np.asarray(c, np.uint8).astype(np.int64)
+        s, e, m = (c >> 7) & 1, (c >> 3) & 15, c & 7
+        mag = np.ldexp((8 + m).astype(float), e - 10)
+        mag = np.where((e == 15) & (m == 7), np.nan, mag)
+        return np.where(s == 1, -mag, mag)
+
+    def nan_as_480(c):
+        d = lo.decode_e4m3(c)
+        return np.where(np.isnan(d), np.where(np.asarray(c) >= 0x80, -480.0, 480.0), d)
+
+    for mutant in (bias8, no_subnormals, nan_as_480):
+        assert not _e4m3_pins(mutant), mutant.__name__

@@ -37,7 +37,7 @@ __all__ = [
     "Module", "Workload", "to_bf16_bits", "zipf_ids", "finite_zipf_cdf",
     "c0_worked_example", "c1_tiny_f32", "c2_bgmv_decode", "c3_sgmv_prefill",
     "c4_mixed_rank", "c5_encoder_step", "fused_tiles", "fingerprint_rank1", "integer_exact",
-    "lcg_uniforms", "request_trace", "tier_batches",
+    "lcg_uniforms", "request_trace", "tier_batches", "with_fp8_base", "fp8_code_sweep",
     "BY_NAME",
 ]
 
@@ -113,6 +113,10 @@ class Workload:
     # adapters[slot][module] = (rank, scale, A [rank, h_in], B [rank, h_out]) or None
     adapters: List[List[Optional[Tuple[int, float, np.ndarray, np.ndarray]]]]
     notes: Dict[str, object] = dataclasses.field(default_factory=dict)
+    # FP8 base (optional): per module, W as OCP E4M3 codes [h_in, h_out] (uint8)
+    # and one float32 scale per output column [h_out]
+    W8: Optional[List[Optional[np.ndarray]]] = None
+    W8_scale: Optional[List[Optional[np.ndarray]]] = None
 
     @property
     def n_tokens(self) -> int:
@@ -399,6 +403,64 @@ def fused_tiles(seed: int = 14, h_in: int = 320, h_out: int = 384, page: int = 6
     xs, Ws, ad, y0 = _draw_values(rng, "bf16", ids.shape[0], mods, 1, [[r] for r in ranks],
                                   [32.0 / r for r in ranks], 1.0, 0.005, 0.02)
     return Workload("fused_tiles", "bf16", page, n_slots, mods, ids, xs, y0, Ws, ad)
+
+
+# --------------------------------------------------------------------------
+# FP8 base
+# --------------------------------------------------------------------------
+E4M3_MAX = 448.0   # largest finite OCP E4M3 magnitude
+
+
+def to_e4m3_codes(a: np.ndarray) -> np.ndarray:
+    """float32 values with |a| <= 448 -> OCP E4M3 codes (uint8), rounded to
+    nearest, ties to even (torch's float8_e4m3fn conversion on the CPU)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy().copy()
+
+
+def with_fp8_base(wl: Workload) -> Workload:
+    """The workload with an FP8 base: each module's drawn W (its bf16 values)
+    quantized per output column, scale_c = max_k |W[k][c]| / 448 (float32; 1
+    for an all-zero column), codes = E4M3(W[k][c] / scale_c).  The bf16 W, x,
+    ids and adapters are kept; y0 is not used by the fused pass."""
+    import copy
+    out = copy.copy(wl)
+    out.W8, out.W8_scale = [], []
+    for m, W in enumerate(wl.W):
+        if W is None:
+            out.W8.append(None)
+            out.W8_scale.append(None)
+            continue
+        w32 = (np.asarray(W, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32) \
+            if wl.dtype == "bf16" else np.asarray(W, np.float32)
+        amax = np.max(np.abs(w32), axis=0)
+        scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+        q = np.clip(w32 / scale[None, :], -E4M3_MAX, E4M3_MAX)
+        out.W8.append(to_e4m3_codes(q))
+        out.W8_scale.append(scale)
+    out.name = wl.name + "_fp8w"
+    return out
+
+
+def fp8_code_sweep(h: int = 256, page: int = 256, nan_codes: bool = False) -> Workload:
+    """Every E4M3 code through the FP8 base: x is the identity (token i is
+    e_i, h tokens), W8[k][c] = (k + c) mod 256 and scale 1, so y[i][c] is the
+    value of code (i + c) mod 256 exactly.  The two NaN codes (0x7F, 0xFF) are
+    replaced by 0x00 unless nan_codes (a NaN in W reaches every token through
+    the zero products).  No adapters (ids -1)."""
+    k = np.arange(h)[:, None]
+    c = np.arange(h)[None, :]
+    codes = ((k + c) % 256).astype(np.uint8)
+    if not nan_codes:
+        codes[(codes == 0x7F) | (codes == 0xFF)] = 0
+    x = to_bf16_bits(np.eye(h, dtype=np.float32))
+    mods = [Module("proj", h, h, 0)]
+    wl = Workload("fp8_code_sweep", "bf16", page, 1, mods, np.full(h, -1, np.int32), [x],
+                  [to_bf16_bits(np.zeros((h, h), np.float32))], [None], [[None]])
+    wl.W8 = [codes]
+    wl.W8_scale = [np.ones(h, np.float32)]
+    return wl
 
 
 # --------------------------------------------------------------------------
