@@ -277,6 +277,24 @@ lora_status lora_apply_bgmv(const lora_pool *p, int32_t module0, int32_t n_modul
                             void *y, int64_t ld_y, int64_t module_stride_y, lora_dtype ydtype,
                             void *stream);
 
+/* lora_apply_bgmv for 2..4 modules that share one x (the q, k, v projections
+ * of a layer: "Thousands of adapters", slide 5), taken together: one work
+ * item per unit stages the unit's x rows once, shrinks the modules' rank rows
+ * as one stacked block, then expands each module's y from its own t columns.
+ * Same result as lora_apply_bgmv with module_stride_x = 0 (bit for bit when
+ * every rank is a multiple of 8, or on exact inputs).  It saves x reads and
+ * per-unit setup but makes each work item as long as all its modules
+ * together: it pays only when a launch's units fill the GPU many times over;
+ * a decode batch of 64 tokens on q, k, v of 4096 x 4096 takes longer than
+ * lora_apply_bgmv's one work item per (unit, module).
+ * Requires n_modules * max_rank <= LORA_MAX_RANK and the modules' page ids of
+ * one adapter, n_modules * max_rank * (h_in + h_out) / page_elems, <= 1024.
+ * Errors: ARG, SHAPE (also: the modules do not fit one work item), DTYPE, HIP. */
+lora_status lora_apply_bgmv_packed(const lora_pool *p, int32_t module0, int32_t n_modules,
+                                   const void *x, int64_t ld_x, const lora_segments *seg,
+                                   void *y, int64_t ld_y, int64_t module_stride_y, lora_dtype ydtype,
+                                   void *stream);
+
 /* Base product and adapter term in one matrix-core pass, for batches whose
  * tokens come in runs of one adapter, such as prefills (study page, "The
  * kernel trick: gather, do not merge": one shared base matmul plus each

@@ -396,9 +396,20 @@ lora_status launch_expand(const lora_pool* p, int32_t module0, int32_t n_modules
   return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
+// Whether n_modules modules from module0 fit one packed work item: at most
+// kBgmvMaxPack modules, their stacked rank rows within a unit's t, and all their
+// page ids within its LDS table.
+bool packable(const lora_pool* p, int32_t module0, int32_t n_modules) {
+  const int64_t ids_per = static_cast<int64_t>(p->max_rank) * ((p->h_in[module0] + p->h_out[module0]) / p->page_elems);
+  return n_modules >= 2 && n_modules <= kBgmvMaxPack && n_modules * p->max_rank <= kMaxRank &&
+         n_modules * ids_per <= kMaxEntryPages;
+}
+
+// packed: the modules share x and one work item takes all of them (k_bgmv_packed).
 template <typename TI, typename TO>
 lora_status launch_bgmv(const lora_pool* p, int32_t module0, int32_t n_modules, const void* x, int64_t ld_x,
-                        int64_t msx, const lora_segments* seg, void* y, int64_t ld_y, int64_t msy, hipStream_t s) {
+                        int64_t msx, const lora_segments* seg, void* y, int64_t ld_y, int64_t msy, hipStream_t s,
+                        bool packed = false) {
   GemvArgs g = gemv_args(p, module0, seg_view(seg), LORA_META_N_UNITS_ALL);
   g.x = x;
   g.ld_x = ld_x;
@@ -407,6 +418,14 @@ lora_status launch_bgmv(const lora_pool* p, int32_t module0, int32_t n_modules, 
   g.ld_y = ld_y;
   g.msy = msy;
   const unsigned gx = gemv_grid_of(seg->max_units);
+  const bool shared_x = msx == 0 && n_modules > 1;
+  g.pack = packed ? n_modules : 1;
+  // x rows read by one work item only are streamed
+  g.x_stream = (!shared_x || packed) ? 1 : 0;
+  if (packed) {
+    hipLaunchKernelGGL((k_bgmv_packed<TI, TO>), dim3(gx, 1), dim3(kGemvThreads), 0, s, g);
+    return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+  }
   if (n_modules >= kBgmvGroupedFrom &&
       static_cast<int64_t>(n_modules) * gx * kGemvThreads <= static_cast<int64_t>(UINT32_MAX)) {
     // several modules: one 1-D grid taken in groups of up to kBgmvModuleGroup modules
@@ -626,6 +645,33 @@ lora_status lora_apply_bgmv(const lora_pool* p, int32_t module0, int32_t n_modul
                                       module_stride_y, s);
   return launch_bgmv<float, float>(p, module0, n_modules, x, ld_x, module_stride_x, seg, y, ld_y, module_stride_y,
                                    s);
+}
+
+lora_status lora_apply_bgmv_packed(const lora_pool* p, int32_t module0, int32_t n_modules, const void* x,
+                                   int64_t ld_x, const lora_segments* seg, void* y, int64_t ld_y,
+                                   int64_t module_stride_y, lora_dtype ydtype, void* stream) {
+  lora_status st = check_call(p, module0, n_modules, seg, true);
+  if (st != LORA_OK) return st;
+  if (ydtype != LORA_F32 && ydtype != LORA_BF16) return LORA_ERR_DTYPE;
+  if (!packable(p, module0, n_modules)) return LORA_ERR_SHAPE;
+  const int32_t n = seg->n_tokens;
+  st = check_operand(x, ld_x, 0, p->h_in[module0], p->elem_bytes(), n, n_modules, false, true);
+  if (st != LORA_OK) return st;
+  st = check_operand(y, ld_y, module_stride_y, p->h_out[module0], ydtype == LORA_BF16 ? 2 : 4, n, n_modules, true,
+                     true);
+  if (st != LORA_OK) return st;
+  if (n == 0) return LORA_OK;
+  DeviceGuard g(p->device);
+  if (!g.ok) return LORA_ERR_HIP;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p->dtype == LORA_BF16) {
+    if (ydtype == LORA_BF16)
+      return launch_bgmv<__bf16, __bf16>(p, module0, n_modules, x, ld_x, 0, seg, y, ld_y, module_stride_y, s, true);
+    return launch_bgmv<__bf16, float>(p, module0, n_modules, x, ld_x, 0, seg, y, ld_y, module_stride_y, s, true);
+  }
+  if (ydtype == LORA_BF16)
+    return launch_bgmv<float, __bf16>(p, module0, n_modules, x, ld_x, 0, seg, y, ld_y, module_stride_y, s, true);
+  return launch_bgmv<float, float>(p, module0, n_modules, x, ld_x, 0, seg, y, ld_y, module_stride_y, s, true);
 }
 
 lora_status lora_fused_gemm(const lora_pool* p, int32_t module, const void* x, int64_t ld_x, const void* w,

@@ -49,6 +49,7 @@ namespace lora {
 #define LORA_UNIT_RUN 8
 #endif
 constexpr int kGemvThreads = LORA_GEMV_THREADS;
+constexpr int kBgmvMaxPack = 4;                     // modules sharing x that one fused BGMV work item takes
 constexpr int kGemvWaves = kGemvThreads / 64;
 constexpr int kXSliceBytes = 32768;                 // LDS for the staged x rows of a unit
 constexpr int kShrinkBatch = LORA_SHRINK_BATCH;     // 16-byte chunks of a row in flight per lane
@@ -133,27 +134,37 @@ struct UnitLds {
 };
 
 // Copies x[tok][k0 .. k0+len) of the unit's tokens into xs[tb][0 .. len);
-// NT: streaming loads (the rows are read by this work item only).
-template <typename TI, bool NT>
+// stream: streaming loads (no other work item of the launch reads these rows).
+template <typename TI>
 __device__ __forceinline__ void stage_x(const TI* __restrict__ x, int64_t ld_x, const int32_t* toks, int nt,
-                                        int k0, int len, TI* xs) {
+                                        int k0, int len, TI* xs, bool stream) {
   constexpr int V = 16 / sizeof(TI);
   constexpr int S = XSlice<TI>::kElems;
   const int per_tok = len / V;
   for (int i = threadIdx.x; i < nt * per_tok; i += kGemvThreads) {
     const int tb = i / per_tok, c = (i - tb * per_tok) * V;
-    *reinterpret_cast<u32x4*>(xs + tb * S + c) =
-        ld16<NT>(reinterpret_cast<const u32x4*>(x + static_cast<int64_t>(toks[tb]) * ld_x + k0 + c));
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + static_cast<int64_t>(toks[tb]) * ld_x + k0 + c);
+    *reinterpret_cast<u32x4*>(xs + tb * S + c) = stream ? ld16<true>(src) : ld16<false>(src);
   }
 }
 
 // KEEP: the unit's segment spans several units, whose workgroups read the
 // same pages, so they are loaded through the caches; a page read by one
 // unit only is streamed with non-temporal loads.
-template <typename TI, int NT, bool KEEP, bool NTX>
+// Where the stacked rank rows of up to kBgmvMaxPack modules that share x
+// start (rstart[0] = 0; a module past the pack starts past every row), and
+// the page ids per module (module mi's at L.pid[mi * ids_per]).
+struct Stack {
+  int rstart[kBgmvMaxPack];
+  int ids_per;
+};
+
+// STACK: rank rows [j_begin, j_end) are the stacked rows of the modules of st.
+template <typename TI, int NT, bool KEEP, bool STACK = false>
 __device__ __forceinline__ void shrink_unit(const TI* __restrict__ x, int64_t ld_x, UnitLds& L, int nt,
                                             const TI* __restrict__ pages, int pid0, int32_t h, uint32_t magic,
-                                            int32_t h_in, int32_t j_begin, int32_t j_end, TI* xs) {
+                                            int32_t h_in, int32_t j_begin, int32_t j_end, TI* xs, bool x_stream,
+                                            const Stack& st = Stack{}) {
   constexpr int S = XSlice<TI>::kElems;
   constexpr int CE = 16 / sizeof(TI);  // elements per 16-byte chunk
   constexpr int SR = kShrinkRows;      // rank rows a wave streams at once
@@ -169,7 +180,18 @@ __device__ __forceinline__ void shrink_unit(const TI* __restrict__ x, int64_t ld
 #pragma unroll
     for (int q = 0; q < SR; ++q) {
       const int j = min(jw + kGemvWaves * q, j_end - 1);  // rows past the range repeat its last
-      const int pid = __builtin_amdgcn_readfirstlane(L.pid[pid0 + j * ppr + p]);
+      int slot_ix = pid0 + j * ppr + p;
+      if constexpr (STACK) {   // the module whose rows hold j, and j's row in it
+        int jm = j, base_ix = 0;
+#pragma unroll
+        for (int k = 1; k < kBgmvMaxPack; ++k)
+          if (j >= st.rstart[k]) {
+            jm = j - st.rstart[k];
+            base_ix = k * st.ids_per;
+          }
+        slot_ix = base_ix + jm * ppr + p;
+      }
+      const int pid = __builtin_amdgcn_readfirstlane(L.pid[slot_ix]);
       base[q] = pages + (static_cast<int64_t>(pid) - p) * h;
     }
   };
@@ -216,7 +238,7 @@ __device__ __forceinline__ void shrink_unit(const TI* __restrict__ x, int64_t ld
   };
 
   if (n_slices == 1) {
-    stage_x<TI, NTX>(x, ld_x, L.toks, nt, 0, h_in, xs);
+    stage_x<TI>(x, ld_x, L.toks, nt, 0, h_in, xs, x_stream);
     __syncthreads();
   }
   // wave w streams rows j0 + w + kGemvWaves*q for q < SR, rank rows [j_begin, j_end)
@@ -227,7 +249,7 @@ __device__ __forceinline__ void shrink_unit(const TI* __restrict__ x, int64_t ld
       const int len = min(S, h_in - k0);
       if (n_slices > 1) {
         __syncthreads();
-        stage_x<TI, NTX>(x, ld_x, L.toks, nt, k0, len, xs);
+        stage_x<TI>(x, ld_x, L.toks, nt, k0, len, xs, x_stream);
         __syncthreads();
       }
       if (jw >= j_end) continue;         // wave-uniform
@@ -257,10 +279,13 @@ __device__ __forceinline__ void shrink_unit(const TI* __restrict__ x, int64_t ld
 
 // NTY: y is read and written with streaming accesses (each element is touched
 // by this work item only).
-template <typename TI, typename TO, int NT, bool KEEP, bool NTY>
+// STACKED: the unit's t columns of this adapter start at toff and the next
+// columns belong to another module, so rows past the rank are masked.
+template <typename TI, typename TO, int NT, bool KEEP, bool NTY, bool STACKED = false>
 __device__ __forceinline__ void expand_unit(TO* __restrict__ y, int64_t ld_y, const UnitLds& L, int nt,
                                             const TI* __restrict__ pages, int pid0, int32_t h, uint32_t magic,
-                                            int32_t h_out, int32_t rank, float scale, int q_begin, int q_end) {
+                                            int32_t h_out, int32_t rank, float scale, int q_begin, int q_end,
+                                            int toff = 0) {
   constexpr int EB = kExpandBatch<TI>; // rank rows of B in flight
   const int n_quads = h_out >> 2;
   const int ppr = h_out / h;
@@ -305,9 +330,11 @@ __device__ __forceinline__ void expand_unit(TO* __restrict__ y, int64_t ld_y, co
         raw[jj].unpack(bv);
 #pragma unroll
         for (int tb = 0; tb < NT; ++tb) {
-          // t is the same for the whole workgroup: keep it in a scalar register
-          const float tv = __builtin_bit_cast(
-              float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, L.t[tb * kMaxRank + j0 + jj])));
+          // t is the same for the whole workgroup: keep it in a scalar register (rows past
+          // the rank read zeros, except in a stacked block, where they are masked)
+          float tv = __builtin_bit_cast(
+              float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, L.t[tb * kMaxRank + toff + j0 + jj])));
+          if constexpr (STACKED) tv = j0 + jj < rank ? tv : 0.f;
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc[tb][e] = fmaf(tv, bv[e], acc[tb][e]);
         }
@@ -362,6 +389,9 @@ struct GemvArgs {
   int64_t ld_y, msy;
   int32_t module_group;   // modules per dispatch group of the GEMV grid (0: one module after another)
   int32_t group_nx;       // ... and each module's unit workgroups
+  int32_t pack;           // fused BGMV: modules sharing x that one work item takes (1: none); the
+                          // grid's module coordinate then counts packs
+  int32_t x_stream;       // fused BGMV: no two work items read the same x rows (stream them)
 };
 
 // LDS of the GEMV body: the unit's tables, then (shrink modes) its staged x rows.
@@ -399,9 +429,9 @@ __device__ __forceinline__ void gemv_item(const GemvArgs& a, int m, int2 rec, in
   const int j_end = (MODE == 1) ? min(e.rank, j_begin + kPartRows) : e.rank;
   if (j_begin >= j_end) return;         // uniform: this part has no rows of this rank
   if constexpr (MODE != 2) {
-    constexpr bool ntx = MODE == 0 && LORA_BGMV_NT_XY != 0;
+    const bool x_stream = MODE == 0 && LORA_BGMV_NT_XY != 0 && a.x_stream != 0;
 #define LORA_SHRINK_CALL(N, K) \
-  shrink_unit<TI, N, K, ntx>(xm, a.ld_x, L, nt, pages, 0, h, a.magic, a.h_in, j_begin, j_end, xs)
+  shrink_unit<TI, N, K>(xm, a.ld_x, L, nt, pages, 0, h, a.magic, a.h_in, j_begin, j_end, xs, x_stream)
     if (keep) {
       if (nt == 1) LORA_SHRINK_CALL(1, true);
       else if (nt == 2) LORA_SHRINK_CALL(2, true);
@@ -448,6 +478,84 @@ __device__ __forceinline__ void gemv_item(const GemvArgs& a, int m, int2 rec, in
       else LORA_EXPAND_CALL(4, false);
     }
 #undef LORA_EXPAND_CALL
+  }
+}
+
+// Fused BGMV work item for a pack of np = a.pack modules that share x (q, k, v
+// of one layer: the slide deck "Thousands of adapters", slide 5, adapts the
+// attention projections): unit `rec` of modules g*np .. g*np + np - 1.  The
+// x rows are staged once; the modules' rank rows are shrunk as one stacked
+// block of sum(rank) rows; then each module's y is expanded from its own t
+// columns.  Per module, the rank rows keep the wave and batch they have in a
+// one-module item when every rank is a multiple of 8.
+template <typename TI, typename TO>
+__device__ __forceinline__ void gemv_item_packed(const GemvArgs& a, int g, int2 rec, UnitLds& L, TI* xs) {
+  const int np = a.pack;
+  const int m0 = g * np;
+  const TI* xm = static_cast<const TI*>(a.x) + m0 * a.msx;
+  const TI* pages = static_cast<const TI*>(a.pv.pages);
+  const int32_t h = static_cast<int32_t>(a.pv.page_elems);
+  const int ppr_a = a.h_in / h, ppr_b = a.h_out / h;
+  const int ids_a = a.pv.max_rank * ppr_a;
+  const int ids_per = ids_a + a.pv.max_rank * ppr_b;   // page ids of one module's entry
+  const int slot = rec.x & 0xffff, nt = (rec.x >> 16) & 0xff, pos = rec.y;
+  const bool keep = (rec.x >> 24) & 1;
+  const int e0 = slot * a.pv.n_modules + a.module0 + m0;
+  int rk[kBgmvMaxPack];   // ranks of the pack's entries (0 past np or for an empty entry)
+#pragma unroll
+  for (int mi = 0; mi < kBgmvMaxPack; ++mi) rk[mi] = mi < np ? max(a.pv.entries[e0 + mi].rank, 0) : 0;
+  int rows = 0;
+#pragma unroll
+  for (int mi = 0; mi < kBgmvMaxPack; ++mi) rows += rk[mi];
+  // prologue: tokens, every module's page ids, stacked row starts; t cleared
+  __syncthreads();   // the previous item is done with LDS
+  const int tid = threadIdx.x;
+  if (tid < kUnitTokens) L.toks[tid] = tid < nt ? a.sv.perm[pos + tid] : 0;
+  for (int i = tid; i < np * ids_per; i += kGemvThreads) {
+    const int mi = i / ids_per;
+    L.pid[i] = a.pv.page_ids[static_cast<int64_t>(e0 + mi) * a.pv.ppe + (i - mi * ids_per)];
+  }
+  for (int i = tid; i < kUnitTokens * kMaxRank; i += kGemvThreads) L.t[i] = 0.f;
+  __syncthreads();
+  if (rows <= 0) return;
+  Stack st;
+  st.ids_per = ids_per;
+  st.rstart[0] = 0;
+#pragma unroll
+  for (int mi = 1; mi < kBgmvMaxPack; ++mi) st.rstart[mi] = mi < np ? st.rstart[mi - 1] + rk[mi - 1] : rows;
+  const bool x_stream = LORA_BGMV_NT_XY != 0 && a.x_stream != 0;
+#define LORA_SHRINK_CALL(N, K) \
+  shrink_unit<TI, N, K, true>(xm, a.ld_x, L, nt, pages, 0, h, a.magic, a.h_in, 0, rows, xs, x_stream, st)
+  if (keep) {
+    if (nt == 1) LORA_SHRINK_CALL(1, true);
+    else if (nt == 2) LORA_SHRINK_CALL(2, true);
+    else LORA_SHRINK_CALL(4, true);
+  } else {
+    if (nt == 1) LORA_SHRINK_CALL(1, false);
+    else if (nt == 2) LORA_SHRINK_CALL(2, false);
+    else LORA_SHRINK_CALL(4, false);
+  }
+#undef LORA_SHRINK_CALL
+  constexpr bool nty = LORA_BGMV_NT_XY != 0;
+  int toff = 0;   // t columns of module mi start after those of the modules before it
+  for (int mi = 0; mi < np; ++mi) {
+    const SlotEntry em = a.pv.entries[e0 + mi];
+    if (em.rank <= 0) continue;   // uniform
+    TO* ym = static_cast<TO*>(a.y) + (m0 + mi) * a.msy;
+#define LORA_EXPAND_CALL(N, K)                                                                                  \
+  expand_unit<TI, TO, N, K, nty, true>(ym, a.ld_y, L, nt, pages, mi * ids_per + ids_a, h, a.magic, a.h_out,    \
+                                       em.rank, em.scale, 0, a.h_out >> 2, toff)
+    if (keep) {
+      if (nt == 1) LORA_EXPAND_CALL(1, true);
+      else if (nt == 2) LORA_EXPAND_CALL(2, true);
+      else LORA_EXPAND_CALL(4, true);
+    } else {
+      if (nt == 1) LORA_EXPAND_CALL(1, false);
+      else if (nt == 2) LORA_EXPAND_CALL(2, false);
+      else LORA_EXPAND_CALL(4, false);
+    }
+#undef LORA_EXPAND_CALL
+    toff += em.rank;
   }
 }
 
@@ -498,6 +606,25 @@ __global__ __launch_bounds__(kGemvThreads, 4) void k_gemv(GemvArgs a) {
                              static_cast<int>(gridDim.x) / a.group_nx, a.module_group, it0);
   gemv_body<MODE, TI, TO>(a, b, *reinterpret_cast<UnitLds*>(lds),
                           reinterpret_cast<TI*>(lds + gemv_xs_offset<MODE, TI>()), it0);
+}
+
+// Fused BGMV over packs of a.pack modules that share x (gemv_item_packed): a
+// grid of units x 1; each workgroup loops over units like k_gemv's.  Three
+// waves per SIMD: the stacked row lookup and the per-module expands do not
+// fit k_gemv's register budget without spilling.
+template <typename TI, typename TO>
+__global__ __launch_bounds__(kGemvThreads, 3) void k_bgmv_packed(GemvArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[gemv_lds_bytes<0, TI>()];
+  UnitLds& L = *reinterpret_cast<UnitLds*>(lds);
+  TI* xs = reinterpret_cast<TI*>(lds + gemv_xs_offset<0, TI>());
+  const int2* units = reinterpret_cast<const int2*>(a.sv.units);
+  const int n_units = a.sv.meta[LORA_META_N_UNITS_ALL];
+  int it = unit_of_block(static_cast<int>(blockIdx.x), 0);
+  int2 rec = units[min(it, a.sv.max_units - 1)];
+  for (; it < n_units; it += static_cast<int>(gridDim.x)) {
+    if (it >= static_cast<int>(gridDim.x)) rec = units[it];
+    gemv_item_packed<TI, TO>(a, static_cast<int>(blockIdx.y), rec, L, xs);
+  }
 }
 
 }  // namespace lora

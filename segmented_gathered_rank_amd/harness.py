@@ -15,8 +15,8 @@ from typing import List, Optional, Tuple
 import numpy as np
 import torch
 
-from . import (LORA_BF16, LORA_F32, lora_apply_bgmv, lora_build_segments, lora_expand, lora_fused_gemm,
-               lora_fused_gemm_fp8w,
+from . import (LORA_BF16, LORA_F32, lora_apply_bgmv, lora_apply_bgmv_packed, lora_build_segments, lora_expand,
+               lora_fused_gemm, lora_fused_gemm_fp8w,
                lora_pool_create, lora_pool_destroy, lora_pool_load, lora_segments_bind,
                lora_segments_bytes, lora_shrink, lora_shrink_workspace_bytes)
 
@@ -187,6 +187,21 @@ class DeviceWorkload:
                 yp = y.data_ptr() + (a - m0) * y.stride(0) * y.element_size()
                 lora_apply_bgmv(self.pool, a, b - a, self._xp(xo), mods[m0].h_in, msx, self.seg, yp,
                                 mods[m0].h_out, y.stride(0), ydt, stream)
+
+    def bgmv_packed(self, stream=None):
+        """As bgmv(), with runs of 2..4 modules that share x through lora_apply_bgmv_packed."""
+        ydt = LORA_BF16 if self.y_dtype == "bf16" else LORA_F32
+        mods = self.wl.modules
+        for gi, (m0, m1) in enumerate(self.groups):
+            y = self.y[gi]
+            for (a, b, xo, msx) in self._x_runs(m0, m1):
+                yp = y.data_ptr() + (a - m0) * y.stride(0) * y.element_size()
+                if msx == 0 and 2 <= b - a <= 4:
+                    lora_apply_bgmv_packed(self.pool, a, b - a, self._xp(xo), mods[m0].h_in, self.seg, yp,
+                                           mods[m0].h_out, y.stride(0), ydt, stream)
+                else:
+                    lora_apply_bgmv(self.pool, a, b - a, self._xp(xo), mods[m0].h_in, msx, self.seg, yp,
+                                    mods[m0].h_out, y.stride(0), ydt, stream)
 
     def upload_weights(self):
         """W^T of every module ([h_out][h_in], the layout lora_fused_gemm reads)."""
