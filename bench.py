@@ -47,8 +47,10 @@ def parse():
     ap.add_argument("--rotate", type=int, default=0,
                     help="input sets the steps cycle through (each with its own pool, x and y); default: enough "
                          "that one cycle moves more than twice the 256 MB Infinity Cache")
-    ap.add_argument("--single-module", action="store_true",
-                    help="also time one-module calls of the decode batch (replayed from a captured graph)")
+    ap.add_argument("--no-single-module", action="store_true",
+                    help="skip the one-module calls of the decode batch (timed by default, replayed from a graph)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the GPU apply times of the prefill, mixed-rank and encoder configs (default workload)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="copy a buffer of this size once before timing (reference for HBM counters)")
@@ -56,6 +58,9 @@ def parse():
                     help="summarize two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) instead of benchmarking")
     ap.add_argument("--pmc-kernel", default="k_gemvILi0E", help="substring of the kernel to summarize")
     ap.add_argument("--pmc-out", default=None, help="write the traffic summary JSON here")
+    ap.add_argument("--pmc-mfma-summary", metavar="DIR",
+                    help="summarize a rocprofv3 --pmc run of the matrix-core counters (MFMA busy and ops, CU busy, "
+                         "LDS bank conflicts) for the kernels named by --pmc-kernel (name substrings separated by semicolons)")
     ap.add_argument("--pmc-per-step", type=int, default=0,
                     help="the step makes this many launches of the kernel (one per module): average over all "
                          "of them and report HBM bytes per step")
@@ -184,6 +189,41 @@ def pmc_summary(args):
     print(json.dumps(out))
 
 
+MFMA_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                 "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE"]
+
+
+def pmc_mfma_summary(args):
+    """Per kernel (name substrings of --pmc-kernel), each counter averaged over its
+    dispatches, and: MFMA utilisation = MFMA busy cycles over (GPU active cycles x
+    SIMDs), the rocprofv3 MfmaUtil expression, with GRBM_GUI_ACTIVE summed over the
+    8 XCDs divided by 8 and 1,024 SIMDs (256 CUs x 4); bf16 MFMA flops = MOPS x 512
+    (per dispatch);
+    LDS bank-conflict cycles per LDS-active cycle (SQ_ACTIVE_INST_LDS is in quad-cycles)."""
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(args.pmc_mfma_summary, "**", "*counter_collection.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    out = {}
+    for pat in args.pmc_kernel.split(";"):
+        disp = {}
+        for r in rows:
+            if pat in r["Kernel_Name"]:
+                disp.setdefault(r["Dispatch_Id"], {})[r["Counter_Name"]] = float(r["Counter_Value"])
+        full = [d for d in disp.values() if all(c in d for c in MFMA_COUNTERS)]
+        if not full:
+            raise SystemExit(f"no dispatch of {pat!r} with all counters in {args.pmc_mfma_summary}")
+        avg = {c: sum(d[c] for d in full) / len(full) for c in MFMA_COUNTERS}
+        active = avg["GRBM_GUI_ACTIVE"] / 8.0
+        out[pat] = {"dispatches": len(full), "counters_mean": avg,
+                    "mfma_util_pct": round(100.0 * avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (active * 1024), 2),
+                    "bf16_mfma_flops": avg["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512,
+                    "lds_bank_conflict_per_lds_cycle": round(avg["SQ_LDS_BANK_CONFLICT"] /
+                                                             max(4 * avg["SQ_ACTIVE_INST_LDS"], 1.0), 4)}
+    print(json.dumps(out, indent=1))
+
+
 def copy_gbps(mib=1024, reps=10):
     """Measured device-to-device copy bandwidth (read + write bytes per second):
     the streaming rate this GPU reaches, a second denominator beside the spec peak."""
@@ -237,22 +277,107 @@ def base_gemm_ms(wl, reps=10):
     return best, flops
 
 
-def cpu_baseline(wl, seconds):
-    """The oracle, untouched, on one core: whole steps (all modules, all tokens) until `seconds`."""
+_CPU_WL = None   # the workload the forked CPU workers read (set before their pool starts)
+
+
+def _cpu_cores():
+    """Host cores for the all-cores leg: the process's CPU set, at most 16 (a GPU machine's share per GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _oracle_tokens(job):
+    """The oracle on tokens [t0, t1) of modules [m0, m1) of _CPU_WL, BLAS threads = 1:
+    the adapter term, or (fused) x W plus the term.  Returns token-modules done."""
+    t0, t1, m0, m1, fused, fp8 = job
     from threadpoolctl import threadpool_limits
     from oracle import lora_oracle as lo
-    steps, t0 = 0, time.perf_counter()
+    wl = _CPU_WL
+    f = (lo.lora_forward_fp8w if fp8 else lo.lora_forward) if fused else lo.lora_delta
     with threadpool_limits(1):
+        for m in range(m0, m1):
+            f(wl, m, range(t0, t1))
+    return (t1 - t0) * (m1 - m0)
+
+
+def cpu_baseline(wl, seconds, fused=False, fp8=False, block=64, base_wl=None):
+    """The oracle as it stands, on the host's cores, over blocks of `block`
+    tokens (every module) of the workload, in order, for about `seconds` per
+    leg: one core, then all cores (forked workers, each a contiguous share of a
+    block).  Runs before anything touches the GPU (the workers are forked).
+    base_wl: a one-module workload with W drawn, whose fp64 base product x W is
+    timed on one core as well (the base is not part of the adapter term)."""
+    global _CPU_WL
+    import multiprocessing
+    _CPU_WL = wl
+    n, nm = wl.n_tokens, wl.n_modules
+    blocks = [(t, min(n, t + block)) for t in range(0, n, block)]
+    # one core
+    done, b, t0 = 0, 0, time.perf_counter()
+    while True:
+        done += _oracle_tokens((*blocks[b % len(blocks)], 0, nm, fused, fp8))
+        b += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or el * (b + 1) / b > 3 * seconds:
+            break
+    one = done / nm / el
+    one_sample = f"{b} block(s) of up to {block} tokens x {nm} modules in {el:.1f} s"
+    # all cores: a block's modules split over the workers when there are enough, else its tokens
+    cores = _cpu_cores()
+    jobs_of = []
+    for (s0, s1) in blocks:
+        if nm >= cores:
+            cuts = [nm * k // cores for k in range(cores + 1)]
+            jobs_of.append([(s0, s1, cuts[k], cuts[k + 1], fused, fp8) for k in range(cores) if cuts[k + 1] > cuts[k]])
+        else:
+            cuts = [s0 + (s1 - s0) * k // cores for k in range(cores + 1)]
+            jobs_of.append([(cuts[k], cuts[k + 1], 0, nm, fused, fp8) for k in range(cores) if cuts[k + 1] > cuts[k]])
+    split = "modules" if nm >= cores else "tokens"
+    ctx = multiprocessing.get_context("fork")
+    with ctx.Pool(cores) as pool:
+        pool.map(_oracle_tokens, jobs_of[0])            # workers up (not timed)
+        done, b, t0 = 0, 0, time.perf_counter()
         while True:
-            for m in range(wl.n_modules):
-                lo.lora_delta(wl, m)
-            steps += 1
+            done += sum(pool.map(_oracle_tokens, jobs_of[b % len(jobs_of)]))
+            b += 1
             el = time.perf_counter() - t0
-            if el >= seconds or (steps >= 1 and el * (steps + 1) / steps > 3 * seconds):
+            if el >= seconds or el * (b + 1) / b > 3 * seconds:
                 break
-    return {"value": wl.n_tokens * steps / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{steps} whole step(s): {wl.n_tokens} tokens x {wl.n_modules} modules, fp64 "
-                      f"per-token loop, {el:.1f} s on one core (BLAS threads = 1)"}
+    allc = done / nm / el
+    out = {"value": round(one, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+           "sample": f"{one_sample}; fp64 per-token {'x W + adapter term' if fused else 'adapter term'} "
+                     f"({'FP8 base, ' if fp8 else ''}the oracle as written), BLAS threads = 1",
+           "all_cores": {"value": round(allc, 2), "unit": "tokens/s", "cores": cores,
+                         "sample": f"{b} block(s) of up to {block} tokens, each block's {split} split over "
+                                   f"{cores} forked workers, {el:.1f} s"},
+           "cpu_model": _cpu_model()}
+    if base_wl is not None:   # the shared base product x W of one module, fp64, one core
+        from threadpoolctl import threadpool_limits
+        from oracle import lora_oracle as lo
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            lo.base_product(base_wl, 0)
+            el = time.perf_counter() - t0
+        mod = base_wl.modules[0]
+        out["base_product_fp64"] = {
+            "seconds_per_module": round(el, 4), "tokens_per_s_per_module": round(base_wl.n_tokens / el, 2),
+            "shape": f"{base_wl.n_tokens} tokens x {mod.h_in} -> {mod.h_out}, one core, row by row"}
+    return out
 
 
 def fused_work(wl, w_elem_bytes=2):
@@ -278,28 +403,6 @@ def fused_work(wl, w_elem_bytes=2):
             if a is not None:
                 byts += 2 * a[0] * (mod.h_in + mod.h_out)
     return flops, byts
-
-
-def cpu_baseline_fused(wl, seconds, fp8=False):
-    """The oracle, untouched, on one core: y = x W + adapter term for whole
-    tokens (all modules) of the workload, 64 tokens at a time, until `seconds`
-    (fp8: the FP8-base forward)."""
-    from threadpoolctl import threadpool_limits
-    from oracle import lora_oracle as lo
-    done, t0 = 0, time.perf_counter()
-    with threadpool_limits(1):
-        while done < wl.n_tokens:
-            toks = range(done, min(wl.n_tokens, done + 64))
-            for m in range(wl.n_modules):
-                (lo.lora_forward_fp8w if fp8 else lo.lora_forward)(wl, m, toks)
-            done += len(toks)
-            if time.perf_counter() - t0 >= seconds:
-                break
-    el = time.perf_counter() - t0
-    return {"value": done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"the first {done} of {wl.n_tokens} tokens x {wl.n_modules} modules, fp64 per-token "
-                      f"x W{' (FP8 base)' if fp8 else ''} plus adapter term, {el:.1f} s on one core "
-                      f"(BLAS threads = 1)"}
 
 
 def time_ms(fn, reps=10):
@@ -399,10 +502,58 @@ def tiers_trace(args):
     print(json.dumps(out), flush=True)
 
 
+def config_runs(DeviceWorkload, accounting, steps=20, warmup=3):
+    """GPU apply time (shrink + expand, HIP events on the launch stream) and
+    step time (segment build + apply) of the prefill, mixed-rank and encoder
+    configs, each cycling through its input sets; HBM fraction of the apply
+    from its algorithmic bytes."""
+    import numpy as np
+    import torch
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name in ("sgmv_prefill", "mixed_rank", "encoder_step"):
+        wl, _, _ = make_workload(name)
+        sets = ROTATE.get(name, 1)
+        dws = [DeviceWorkload(wl, device=0) for _ in range(sets)]
+        work = accounting.step_work(wl, fused=False)
+        for i in range(warmup):
+            d = dws[i % sets]
+            d.build_segments()
+            d.shrink()
+            d.expand()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for i in range(steps):
+            d = dws[i % sets]
+            ev[i][0].record(stream)
+            d.build_segments()
+            ev[i][1].record(stream)
+            d.shrink()
+            d.expand()
+            ev[i][2].record(stream)
+        torch.cuda.synchronize()
+        apply = np.array([e[1].elapsed_time(e[2]) for e in ev])
+        stepm = np.array([e[0].elapsed_time(e[2]) for e in ev])
+        gbps = work["bytes"] / (apply.mean() * 1e-3) / 1e9
+        res[name] = {"apply_ms_mean": round(float(apply.mean()), 5), "apply_ms_min": round(float(apply.min()), 5),
+                     "step_ms_mean": round(float(stepm.mean()), 5), "tokens": wl.n_tokens,
+                     "tokens_per_s": round(wl.n_tokens / (stepm.mean() * 1e-3), 1),
+                     "algorithmic_bytes": work["bytes"], "hbm_GBps": round(gbps, 1),
+                     "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBS, 4), "input_sets": sets}
+        for d in dws:
+            d.close()
+        del dws
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     if args.pmc_summary:
         pmc_summary(args)
+        return
+    if args.pmc_mfma_summary:
+        pmc_mfma_summary(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (tokens shard across data-parallel "
@@ -412,15 +563,20 @@ def main():
     if args.workload == "tiers_trace":
         tiers_trace(args)
         return
-    import numpy as np
-    import torch
-    from segmented_gathered_rank_amd import accounting
-    from segmented_gathered_rank_amd.harness import DeviceWorkload
-
     wl, mode, config = make_workload(args.workload)
     if args.path != "auto":
         mode = args.path
         config["path"] = mode
+    cpu = None
+    if not args.no_cpu_baseline:   # first: the all-cores leg forks workers, before the GPU is touched
+        import workloads as W
+        base_wl = W.c2_bgmv_decode(seed=12, n_modules=1) if mode == "bgmv" else None
+        cpu = cpu_baseline(wl, args.cpu_seconds, fused=mode in ("fused", "fused8"), fp8=mode == "fused8",
+                           base_wl=base_wl)
+    import numpy as np
+    import torch
+    from segmented_gathered_rank_amd import accounting
+    from segmented_gathered_rank_amd.harness import DeviceWorkload
     # input sets the steps cycle through, so that a cycle's distinct bytes exceed twice the
     # 256 MB Infinity Cache and the kernels read from HBM: the decode batch covers that with its
     # 128 modules in one launch, the prefill step (346 MB) takes 2 sets, the mixed batch (43 MB) 16
@@ -479,7 +635,7 @@ def main():
     extra = {"apply_ms_mean": kern_avg, "apply_ms_min": float(np.min(kern_ms)),
              "algorithmic_bytes_per_step": work["bytes"], "flops_per_step": work["flops"],
              "achieved_tflops": work["flops"] / (kern_avg * 1e-3) / 1e12}
-    if mode == "bgmv" and wl.n_modules > 1 and args.single_module:
+    if mode == "bgmv" and wl.n_modules > 1 and not args.no_single_module:
         # one-module calls (the decode batch as the config states it), replayed from a
         # captured graph so that host launch cost is not in the figure
         import segmented_gathered_rank_amd as sgr
@@ -538,8 +694,8 @@ def main():
         }
         for d in dws:
             d.close()
-        if not args.no_cpu_baseline:
-            out["cpu_baseline"] = cpu_baseline_fused(wl, args.cpu_seconds, fp8=fp8)
+        if cpu is not None:
+            out["cpu_baseline"] = cpu
         print(json.dumps(out), flush=True)
         return
 
@@ -563,7 +719,7 @@ def main():
         extra["lora_apply_over_base_gemm"] = round(kern_avg / gms, 4)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(args.workload),
-                "kernel": "k_bgmv" if mode == "bgmv" else "shrink+expand",
+                "kernel": "k_gemv<0> (fused BGMV)" if mode == "bgmv" else "shrink+expand",
                 "bytes_per_launch": bound_bytes}
     out = {
         "metric": METRIC, "value": round(wl.n_tokens / (ms_step * 1e-3), 1), "unit": "tokens/s",
@@ -573,8 +729,12 @@ def main():
     }
     for d in dws:
         d.close()
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    del dws, dw
+    torch.cuda.empty_cache()
+    if args.workload == "bgmv_decode_x128" and not args.no_configs:
+        extra["configs"] = config_runs(DeviceWorkload, accounting)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 
