@@ -326,27 +326,7 @@ def lora_tiers_acquire(tiers: int, pool: int, ids, fetch, stream=None):
     n = ids.shape[0]
     slots = np.empty(n, np.int32)
     errors = []
-
-    def _cb(ctx, adapter, module, rank, scale, a_ptr, b_ptr):
-        try:
-            got = fetch(int(adapter), int(module))
-            if got is None:
-                rank[0] = 0
-                scale[0] = 0.0
-                return 0
-            r, s, A, B = got
-            A = np.ascontiguousarray(A)
-            B = np.ascontiguousarray(B)
-            ctypes.memmove(a_ptr, A.ctypes.data, A.nbytes)
-            ctypes.memmove(b_ptr, B.ctypes.data, B.nbytes)
-            rank[0] = int(r)
-            scale[0] = float(s)
-            return 0
-        except Exception as e:  # reported after the call returns
-            errors.append(e)
-            return 1
-
-    cb = LORA_FETCH_FN(_cb)
+    cb = _fetch_cb(fetch, errors)
     st = _lib.lora_tiers_acquire(tiers, pool, _ptr(ids), n, ctypes.cast(cb, _P), None, _ptr(slots),
                                  _stream(stream))
     if errors:

@@ -53,19 +53,25 @@ def pin_merged(o=lo):
 
 
 def pin_worked_example(o=lo):
-    """P13: the page's demo: 34 distinct ids, gathered == merged within 1e-3."""
+    """P13: the page's demo.  Its batch holds 34 distinct adapters, and the page
+    reports the merged-weight and gathered outputs equal within 1e-3.  Checked:
+    the oracle's gathered form against the same sum written in the page's own
+    operand layout (W x + s B (A x) per token, fp64, so the layout mapping of the
+    workload is checked too), and the oracle's merged form against its gathered
+    form at the page's tolerance."""
     gold = json.load(open(GOLD))["printed"]
     wl = W.c0_worked_example()
     if len(np.unique(wl.ids)) != gold["distinct_adapters_in_batch"]:
         return False
-    Wp, Ap, Bp = wl.notes["W_page"], wl.notes["A_page"], wl.notes["B_page"]
-    X, ids, scale = wl.x[0], wl.ids, 2.0
-    Y1 = np.empty_like(X)          # option 1 of the page, fp32, page layout
-    for a in np.unique(ids):
-        rows = ids == a
-        Y1[rows] = X[rows] @ (Wp + scale * Bp[a] @ Ap[a]).T
-    Y2 = o.lora_forward(wl, 0)
-    return bool(np.allclose(Y1, Y2, atol=1e-3)) == gold["same_outputs_allclose_atol_1e-3"]
+    Wp, Ap, Bp = (wl.notes[k].astype(np.float64) for k in ("W_page", "A_page", "B_page"))
+    X = wl.x[0].astype(np.float64)
+    low = np.einsum("nrd,nd->nr", Ap[wl.ids], X)                 # A_a x_i, page layout
+    page_form = X @ Wp.T + 2.0 * np.einsum("ndr,nr->nd", Bp[wl.ids], low)
+    gathered = o.lora_forward(wl, 0)
+    if _rel(gathered, page_form) > 1e-12:
+        return False
+    same = bool(np.allclose(o.merged_forward(wl, 0), gathered, atol=1e-3))
+    return same == gold["same_outputs_allclose_atol_1e-3"]
 
 
 def pin_fingerprint(o=lo):
@@ -176,8 +182,28 @@ def pin_linearity(o=lo):
     return _rel(d3, d1 + 2 * d2) <= 1e-12
 
 
+def pin_shrink_columns(o=lo):
+    """P15: t's column j is rank row j's dot product with x (ranks 2..5, integer
+    inputs, so the exact sums are Python integers); columns past the rank and
+    tokens without an adapter are NaN."""
+    wl = W.integer_exact(seed=31, n_tokens=40, ranks=[2, 3, 4, 5, 2, 3])
+    t = o.shrink_t(wl, 0)
+    x = wl.x[0].astype(np.int64)
+    for i, a in enumerate(wl.ids):
+        if not 0 <= a < wl.n_slots:
+            if not np.all(np.isnan(t[i])):
+                return False
+            continue
+        rank, _, A, _ = wl.adapters[a][0]
+        want = [sum(int(p) * int(q) for p, q in zip(x[i], A[j].astype(np.int64))) for j in range(rank)]
+        if t[i, :rank].tolist() != want or not np.all(np.isnan(t[i, rank:])):
+            return False
+    return True
+
+
 ALL_PINS = [pin_merged, pin_worked_example, pin_fingerprint, pin_bruteforce,
-            pin_scale_zero, pin_no_adapter, pin_linearity]
+            pin_scale_zero, pin_no_adapter, pin_linearity,
+            pin_shrink_columns]
 
 
 # ---------------------------------------------------------------- the pins
@@ -239,12 +265,31 @@ def _mutant_last_row_dropped(x_row, A, B, scale):
     return scale * (t @ B[:-1]), t
 
 
+def _mutant_t_reversed(x_row, A, B, scale):      # right term, t columns in reverse
+    t = A @ x_row
+    return scale * (t @ B), t[::-1].copy()
+
+
+def _mutant_t_from_columns(x_row, A, B, scale):  # A read with its strides swapped ([h][r] storage)
+    t = A.reshape(A.shape[1], A.shape[0]).T @ x_row
+    return scale * ((A @ x_row) @ B), t
+
+
+def _fails(pin):
+    """A pin fails if it returns False or cannot run (a wrongly shaped t raises)."""
+    try:
+        return not pin()
+    except (ValueError, IndexError):
+        return True
+
+
 @pytest.mark.parametrize("mutant", [_mutant_no_scale, _mutant_sign, _mutant_rank_order,
-                                    _mutant_last_row_dropped],
+                                    _mutant_last_row_dropped, _mutant_t_reversed,
+                                    _mutant_t_from_columns],
                          ids=lambda f: f.__name__)
 def test_pins_catch_planted_term_mistakes(monkeypatch, mutant):
     monkeypatch.setattr(lo, "adapter_term", mutant)
-    failed = [p.__name__ for p in ALL_PINS if not p()]
+    failed = [p.__name__ for p in ALL_PINS if _fails(p)]
     assert failed, "no pin caught the planted mistake"
 
 

@@ -185,25 +185,25 @@ def _draw_values(rng, dtype, n_tokens, modules, x_groups, slot_ranks, scales,
 def c0_worked_example() -> Workload:
     """The numpy demo of the study page ("The kernel trick: gather, do not merge").
 
-    Same seed and draw order as the page: W, A, B, X, then the ids.  Mapped to
-    this library's layout: W_ours = W_page^T, A rows = A_page[a],
-    B rows = B_page[a]^T.  The page prints 34 distinct adapters for this draw.
+    fp32, d = 2048, rank 16, 50 adapters, 64 tokens, scale 2.  The draws keep the
+    demo's seed and order (base weight, adapter down and up factors, activations,
+    then the ids), which is what makes the page's count of 34 distinct adapters
+    in the batch a usable check.  The page keeps W as [out][in], A as [adapter]
+    [rank][in] and B as [adapter][out][rank]; this library's layout is their
+    transpose for W and B (A rows are already rank rows).
     """
-    rng = np.random.default_rng(0)
     d, r, n_ad, batch, scale = 2048, 16, 50, 64, 2.0
-    W = rng.normal(0, 0.02, (d, d)).astype(np.float32)
-    A = rng.normal(0, 0.02, (n_ad, r, d)).astype(np.float32)
-    B = rng.normal(0, 0.02, (n_ad, d, r)).astype(np.float32)
-    X = rng.normal(0, 1, (batch, d)).astype(np.float32)
+    draws = (("W", 0.02, (d, d)), ("A", 0.02, (n_ad, r, d)), ("B", 0.02, (n_ad, d, r)), ("X", 1.0, (batch, d)))
+    rng = np.random.default_rng(0)
+    page = {name: rng.normal(0, sigma, shape).astype(np.float32) for name, sigma, shape in draws}
     ids = rng.integers(0, n_ad, batch).astype(np.int32)
-    mods = [Module("proj", d, d, 0)]
-    adapters = [[(r, scale, np.ascontiguousarray(A[a]), np.ascontiguousarray(B[a].T))]
-                for a in range(n_ad)]
+    A, B = page["A"], page["B"]
+    adapters = [[(r, scale, np.ascontiguousarray(A[a]), np.ascontiguousarray(B[a].T))] for a in range(n_ad)]
     return Workload(
         name="c0_worked_example", dtype="f32", page_elems=d, n_slots=n_ad,
-        modules=mods, ids=ids, x=[X], y0=[np.zeros((batch, d), np.float32)],
-        W=[np.ascontiguousarray(W.T)], adapters=adapters,
-        notes={"W_page": W, "A_page": A, "B_page": B})
+        modules=[Module("proj", d, d, 0)], ids=ids, x=[page["X"]], y0=[np.zeros((batch, d), np.float32)],
+        W=[np.ascontiguousarray(page["W"].T)], adapters=adapters,
+        notes={"W_page": page["W"], "A_page": A, "B_page": B})
 
 
 # --------------------------------------------------------------------------
