@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 5
+#define LORA_ABI_VERSION 6
 
 typedef int32_t lora_status;
 enum {
@@ -264,6 +264,26 @@ lora_status lora_expand(const lora_pool *p, int32_t module0, int32_t n_modules,
                         const lora_segments *seg,
                         void *y, int64_t ld_y, int64_t module_stride_y, lora_dtype ydtype,
                         void *stream);
+
+/* SGMV: lora_shrink then lora_expand on the same t and workspace, with one
+ * difference: when the shrink splits its matrix-core contraction over K, the
+ * expand adds the splits' partial tiles itself, in split order as
+ * lora_shrink's own sum does, and the launch that would sum them is not
+ * made: two launches in place of three ("Thousands of adapters", slide 11:
+ * one SGMV call for a mixed batch).  y is the same bit for bit as with the
+ * two calls.  t is scratch here: rows of tokens in matrix-core tiles are
+ * left unwritten when K is split.  Modules share h_in and h_out; argument
+ * rules are those of both calls; the workspace must not be in use by another
+ * call in flight.  One call per step pays most: where a step's modules need
+ * several calls (q, k, v sharing x beside o), lora_shrink per x and one
+ * lora_expand over all of them make fewer, larger launches.
+ * Errors: ARG, SHAPE, DTYPE, HIP (nothing is launched on an argument error). */
+lora_status lora_apply_sgmv(const lora_pool *p, int32_t module0, int32_t n_modules,
+                            const void *x, int64_t ld_x, int64_t module_stride_x,
+                            const lora_segments *seg,
+                            float *t, int64_t ld_t, int64_t module_stride_t,
+                            void *y, int64_t ld_y, int64_t module_stride_y, lora_dtype ydtype,
+                            void *ws, size_t ws_bytes, void *stream);
 
 /* Fused BGMV for decode (study page, "The kernel trick": a batched gather
  * matrix-vector product in which each decode token may bring its own

@@ -182,11 +182,13 @@ ShrinkSplit shrink_split(const lora_pool* p, int32_t module0, int32_t n_modules,
   return ShrinkSplit{(h_in + kps - 1) / kps, kps};
 }
 
-// sp: the K split (shrink_split); ws holds its partial tiles when sp.ks > 1.
+// sp: the K split (shrink_split); ws holds its partial tiles when sp.ks > 1.  fold: the
+// partial tiles are left in ws for the expand to add (no k_shrink_reduce launch), so
+// the t rows of tokens in matrix-core tiles are not written.
 template <typename TI>
 lora_status launch_shrink(const lora_pool* p, int32_t module0, int32_t n_modules, const void* x, int64_t ld_x,
                           int64_t msx, const lora_segments* seg, float* t, int64_t ld_t, int64_t mst,
-                          ShrinkSplit sp, void* ws, hipStream_t s) {
+                          ShrinkSplit sp, void* ws, hipStream_t s, bool fold = false) {
   const PoolView pv = p->view();
   const SegView sv = seg_view(seg);
   const int32_t h_in = static_cast<int32_t>(p->h_in[module0]);
@@ -260,7 +262,7 @@ lora_status launch_shrink(const lora_pool* p, int32_t module0, int32_t n_modules
 #undef LORA_SHRINK_NT
 #undef LORA_SHRINK_LAUNCH
       if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
-      if (ks > 1) {
+      if (ks > 1 && !fold) {
         hipLaunchKernelGGL(k_shrink_reduce, dim3(tile_grid_of(seg->max_tiles), n_modules), block, 0, s, a);
         if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
       }
@@ -312,10 +314,10 @@ int expand_group_blocks(int n_blocks, int tiles, int n_modules, int resident) {
   return best_g;
 }
 
-// Workgroups of k_expand_mixed<TO> resident on the whole device at `lds` bytes
+// Workgroups of k_expand_mixed<TO, PQ> resident on the whole device at `lds` bytes
 // of dynamic LDS (occupancy per CU times CUs), cached per device and LDS size;
 // 0 on a HIP error.
-template <typename TO>
+template <typename TO, int PQ>
 int expand_resident_groups(int device, size_t lds) {
   static std::mutex mu;
   static std::map<std::pair<int, size_t>, int> cache;
@@ -324,7 +326,7 @@ int expand_resident_groups(int device, size_t lds) {
   const auto it = cache.find(key);
   if (it != cache.end()) return it->second;
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&k_expand_mixed<TO>),
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&k_expand_mixed<TO, PQ>),
                                                    kMfmaThreads, lds) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) {
     (void)hipGetLastError();
@@ -335,10 +337,47 @@ int expand_resident_groups(int device, size_t lds) {
   return resident;
 }
 
+// Dynamic LDS of k_expand_mixed<TO, *> at rank cap ldr: up to 78 KiB at rank 64
+// with fp32 y (gfx950: 160 KiB per workgroup).
+template <typename TO>
+size_t expand_mixed_lds(int ldr) {
+  return std::max(expand_lds_bytes(ldr, static_cast<int>(sizeof(TO))), gemv_lds_bytes<2, __bf16>());
+}
+
+// expand_resident_groups<TO, PQ> once the kernel may take `lds` bytes of
+// dynamic LDS (the occupancy query needs that limit in place); 0 on a HIP error.
+template <typename TO, int PQ>
+int expand_resident_ready(int device, size_t lds) {
+  if (!allow_dynamic_lds(reinterpret_cast<const void*>(&k_expand_mixed<TO, PQ>), device, lds)) return 0;
+  return expand_resident_groups<TO, PQ>(device, lds);
+}
+
+// The matrix-core expand launch: tiles of long segments, then the GEMV items of
+// short units (gx workgroups per module); PQ as for expand_mfma_body.
+template <typename TO, int PQ>
+lora_status expand_mixed_call(const lora_pool* p, ExpandArgs& ea, GemvArgs& g, const lora_segments* seg, unsigned gx,
+                              int32_t n_modules, hipStream_t s) {
+  const size_t lds = expand_mixed_lds<TO>(ea.ldr);
+  const int resident = expand_resident_ready<TO, PQ>(p->device, lds);
+  if (resident <= 0) return LORA_ERR_HIP;
+  const int n_blocks = ea.h_out / kExpandCols;
+  ea.blocks = expand_group_blocks(n_blocks, (seg->n_tokens + kTileTokens - 1) / kTileTokens, n_modules, resident);
+  const int tnx = static_cast<int>(tile_grid_of(seg->max_tiles));
+  const int col_groups = (n_blocks + ea.blocks - 1) / ea.blocks;
+  const int64_t n_wgs = static_cast<int64_t>(tnx) * col_groups * n_modules + static_cast<int64_t>(gx) * n_modules;
+  if (!grid_fits(n_wgs, kMfmaThreads)) return LORA_ERR_SHAPE;   // beyond one launch (nothing launched yet)
+  set_module_groups(g, gx, n_modules);
+  hipLaunchKernelGGL((k_expand_mixed<TO, PQ>), dim3(static_cast<unsigned>(n_wgs)), dim3(kMfmaThreads), lds, s, ea, g,
+                     tnx, col_groups, n_modules, static_cast<int>(gx), n_modules);
+  return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+// part: the shrink's K-split partial tiles of these modules (ks splits), summed
+// into the T tiles in place of t's rows; nullptr: t.
 template <typename TI, typename TO>
 lora_status launch_expand(const lora_pool* p, int32_t module0, int32_t n_modules, const float* t, int64_t ld_t,
                           int64_t mst, const lora_segments* seg, void* y, int64_t ld_y, int64_t msy,
-                          hipStream_t s) {
+                          hipStream_t s, const float* part = nullptr, int32_t ks = 1) {
   const PoolView pv = p->view();
   const SegView sv = seg_view(seg);
   const int32_t h_out = static_cast<int32_t>(p->h_out[module0]);
@@ -372,24 +411,15 @@ lora_status launch_expand(const lora_pool* p, int32_t module0, int32_t n_modules
       ea.h_out = h_out;
       ea.ldr = ldr_of(p);
       ea.b_ids_at = static_cast<int32_t>(p->max_rank * (p->h_in[module0] / p->page_elems));
-      const size_t lds =
-          std::max(expand_lds_bytes(ea.ldr, static_cast<int>(sizeof(TO))), gemv_lds_bytes<2, __bf16>());
-      // up to 78 KiB at rank 64 with fp32 y (gfx950: 160 KiB per workgroup)
-      if (!allow_dynamic_lds(reinterpret_cast<const void*>(&k_expand_mixed<TO>), p->device, lds)) return LORA_ERR_HIP;
-      const int n_blocks = h_out / kExpandCols;
-      const int resident = expand_resident_groups<TO>(p->device, lds);
-      if (resident <= 0) return LORA_ERR_HIP;
-      ea.blocks = expand_group_blocks(n_blocks, (seg->n_tokens + kTileTokens - 1) / kTileTokens, n_modules,
-                                      resident);
-      const int tnx = static_cast<int>(tile_grid_of(seg->max_tiles));
-      const int col_groups = (n_blocks + ea.blocks - 1) / ea.blocks;
-      const int64_t n_wgs = static_cast<int64_t>(tnx) * col_groups * n_modules + static_cast<int64_t>(gx) * n_modules;
-      if (!grid_fits(n_wgs, kMfmaThreads)) return LORA_ERR_SHAPE;   // beyond one launch (nothing launched yet)
-      const dim3 grid(static_cast<unsigned>(n_wgs));
-      set_module_groups(g, gx, n_modules);
-      hipLaunchKernelGGL((k_expand_mixed<TO>), grid, dim3(kMfmaThreads), lds, s, ea, g, tnx, col_groups, n_modules,
-                         static_cast<int>(gx), n_modules);
-      return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+      ea.part = part;
+      ea.ks = part ? ks : 1;
+      switch (part ? ea.ldr / 16 : 0) {   // 16-byte column groups of a partial tile row per thread
+        case 0: return expand_mixed_call<TO, 0>(p, ea, g, seg, gx, n_modules, s);
+        case 1: return expand_mixed_call<TO, 1>(p, ea, g, seg, gx, n_modules, s);
+        case 2: return expand_mixed_call<TO, 2>(p, ea, g, seg, gx, n_modules, s);
+        case 3: return expand_mixed_call<TO, 3>(p, ea, g, seg, gx, n_modules, s);
+        default: return expand_mixed_call<TO, 4>(p, ea, g, seg, gx, n_modules, s);
+      }
     }
   }
   hipLaunchKernelGGL((k_gemv<2, TI, TO>), dim3(gx, n_modules), dim3(kGemvThreads), 0, s, g);
@@ -450,13 +480,40 @@ lora_status shrink_checks(const lora_pool* p, int32_t module0, int32_t n_modules
   return check_operand(t, ld_t, mst, p->max_rank, 4, n, n_modules, true, true);
 }
 
-// A checked shrink call on the current device.
+// A checked shrink call on the current device (fold as for launch_shrink).
 lora_status shrink_call(const lora_pool* p, int32_t module0, int32_t n_modules, const void* x, int64_t ld_x,
                         int64_t msx, const lora_segments* seg, float* t, int64_t ld_t, int64_t mst, ShrinkSplit sp,
-                        void* ws, hipStream_t s) {
+                        void* ws, hipStream_t s, bool fold = false) {
   if (p->dtype == LORA_BF16)
-    return launch_shrink<__bf16>(p, module0, n_modules, x, ld_x, msx, seg, t, ld_t, mst, sp, ws, s);
-  return launch_shrink<float>(p, module0, n_modules, x, ld_x, msx, seg, t, ld_t, mst, sp, ws, s);
+    return launch_shrink<__bf16>(p, module0, n_modules, x, ld_x, msx, seg, t, ld_t, mst, sp, ws, s, fold);
+  return launch_shrink<float>(p, module0, n_modules, x, ld_x, msx, seg, t, ld_t, mst, sp, ws, s, fold);
+}
+
+// Argument checks of the expand calls (modules of one shape).
+lora_status expand_checks(const lora_pool* p, int32_t module0, int32_t n_modules, const float* t, int64_t ld_t,
+                          int64_t mst, const lora_segments* seg, const void* y, int64_t ld_y, int64_t msy,
+                          lora_dtype ydtype) {
+  lora_status st = check_call(p, module0, n_modules, seg, true);
+  if (st != LORA_OK) return st;
+  if (ydtype != LORA_F32 && ydtype != LORA_BF16) return LORA_ERR_DTYPE;
+  const int32_t n = seg->n_tokens;
+  st = check_operand(t, ld_t, mst, p->max_rank, 4, n, n_modules, false, false);
+  if (st != LORA_OK) return st;
+  return check_operand(y, ld_y, msy, p->h_out[module0], ydtype == LORA_BF16 ? 2 : 4, n, n_modules, true, true);
+}
+
+// A checked expand call on the current device; part / ks as for launch_expand.
+lora_status expand_call(const lora_pool* p, int32_t module0, int32_t n_modules, const float* t, int64_t ld_t,
+                        int64_t mst, const lora_segments* seg, void* y, int64_t ld_y, int64_t msy, lora_dtype ydtype,
+                        hipStream_t s, const float* part = nullptr, int32_t ks = 1) {
+  if (p->dtype == LORA_BF16) {
+    if (ydtype == LORA_BF16)
+      return launch_expand<__bf16, __bf16>(p, module0, n_modules, t, ld_t, mst, seg, y, ld_y, msy, s, part, ks);
+    return launch_expand<__bf16, float>(p, module0, n_modules, t, ld_t, mst, seg, y, ld_y, msy, s, part, ks);
+  }
+  if (ydtype == LORA_BF16)
+    return launch_expand<float, __bf16>(p, module0, n_modules, t, ld_t, mst, seg, y, ld_y, msy, s);
+  return launch_expand<float, float>(p, module0, n_modules, t, ld_t, mst, seg, y, ld_y, msy, s);
 }
 
 // The fused base + adapter pass: checks shared by both weight formats, then the
@@ -590,31 +647,36 @@ lora_status lora_shrink_noalloc(const lora_pool* p, int32_t module0, int32_t n_m
 lora_status lora_expand(const lora_pool* p, int32_t module0, int32_t n_modules, const float* t, int64_t ld_t,
                         int64_t module_stride_t, const lora_segments* seg, void* y, int64_t ld_y,
                         int64_t module_stride_y, lora_dtype ydtype, void* stream) {
-  lora_status st = check_call(p, module0, n_modules, seg, true);
+  const lora_status st =
+      expand_checks(p, module0, n_modules, t, ld_t, module_stride_t, seg, y, ld_y, module_stride_y, ydtype);
   if (st != LORA_OK) return st;
-  if (ydtype != LORA_F32 && ydtype != LORA_BF16) return LORA_ERR_DTYPE;
-  const int32_t n = seg->n_tokens;
-  st = check_operand(t, ld_t, module_stride_t, p->max_rank, 4, n, n_modules, false, false);
+  if (seg->n_tokens == 0) return LORA_OK;
+  DeviceGuard g(p->device);
+  if (!g.ok) return LORA_ERR_HIP;
+  return expand_call(p, module0, n_modules, t, ld_t, module_stride_t, seg, y, ld_y, module_stride_y, ydtype,
+                     static_cast<hipStream_t>(stream));
+}
+
+lora_status lora_apply_sgmv(const lora_pool* p, int32_t module0, int32_t n_modules, const void* x, int64_t ld_x,
+                            int64_t module_stride_x, const lora_segments* seg, float* t, int64_t ld_t,
+                            int64_t module_stride_t, void* y, int64_t ld_y, int64_t module_stride_y,
+                            lora_dtype ydtype, void* ws, size_t ws_bytes, void* stream) {
+  lora_status st = shrink_checks(p, module0, n_modules, x, ld_x, module_stride_x, seg, t, ld_t, module_stride_t);
   if (st != LORA_OK) return st;
-  st = check_operand(y, ld_y, module_stride_y, p->h_out[module0], ydtype == LORA_BF16 ? 2 : 4, n, n_modules, true,
-                     true);
+  st = expand_checks(p, module0, n_modules, t, ld_t, module_stride_t, seg, y, ld_y, module_stride_y, ydtype);
   if (st != LORA_OK) return st;
-  if (n == 0) return LORA_OK;
+  if (ws_bytes > 0 && (!ws || !aligned16(ws))) return LORA_ERR_ARG;
+  if (seg->n_tokens == 0) return LORA_OK;
   DeviceGuard g(p->device);
   if (!g.ok) return LORA_ERR_HIP;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (p->dtype == LORA_BF16) {
-    if (ydtype == LORA_BF16)
-      return launch_expand<__bf16, __bf16>(p, module0, n_modules, t, ld_t, module_stride_t, seg, y, ld_y,
-                                           module_stride_y, s);
-    return launch_expand<__bf16, float>(p, module0, n_modules, t, ld_t, module_stride_t, seg, y, ld_y,
-                                        module_stride_y, s);
-  }
-  if (ydtype == LORA_BF16)
-    return launch_expand<float, __bf16>(p, module0, n_modules, t, ld_t, module_stride_t, seg, y, ld_y,
-                                        module_stride_y, s);
-  return launch_expand<float, float>(p, module0, n_modules, t, ld_t, module_stride_t, seg, y, ld_y,
-                                     module_stride_y, s);
+  const ShrinkSplit sp = shrink_split(p, module0, n_modules, module_stride_x, seg, ws_bytes);
+  // partial tiles exist only where the shrink splits K, on its matrix-core tiles
+  const bool fold = sp.ks > 1 && shrink_has_tiles(p, module0, seg);
+  st = shrink_call(p, module0, n_modules, x, ld_x, module_stride_x, seg, t, ld_t, module_stride_t, sp, ws, s, fold);
+  if (st != LORA_OK) return st;
+  return expand_call(p, module0, n_modules, t, ld_t, module_stride_t, seg, y, ld_y, module_stride_y, ydtype, s,
+                     fold ? static_cast<const float*>(ws) : nullptr, sp.ks);
 }
 
 lora_status lora_apply_bgmv(const lora_pool* p, int32_t module0, int32_t n_modules, const void* x, int64_t ld_x,

@@ -362,10 +362,17 @@ struct ExpandArgs {
   int32_t ldr;                // rank cap of the pool rounded up to 16
   int32_t b_ids_at;           // offset of B's page ids in a (slot, module) page table
   int32_t blocks;             // column blocks per workgroup (<= kExpandBlocks)
+  const float* part;          // the shrink's K-split partial tiles [tile][module][split][64][ldr] (PQ > 0)
+  int32_t ks;                 // their split count
 };
 
 // Grid (b): x over tiles, y over groups of ea.blocks column blocks, z over modules.
-template <typename TO>
+// PQ = 0: the T tile comes from t (rows by token id).  PQ = ldr / 16 > 0: it is
+// the sum, in split order, of the shrink's K-split partial tiles (rows by tile
+// row), which the shrink leaves in the workspace in place of t: each thread
+// loads PQ 16-byte column groups of its row per split, the first batch of
+// splits together with the tile's entry, token ids and page ids.
+template <typename TO, int PQ>
 __device__ __forceinline__ void expand_mfma_body(const ExpandArgs& ea, const Blk b, unsigned char* smem) {
   const PoolView& pv = ea.pv;
   const SegView& sv = ea.sv;
@@ -403,8 +410,25 @@ __device__ __forceinline__ void expand_mfma_body(const ExpandArgs& ea, const Blk
   int tile = item_of_block<kTileRun>(b.x, b.y + b.ny * b.z);
   int2 rec = tiles[min(tile, sv.max_tiles - 1)];
   const int n_bids = pv.max_rank * ppr;
+  // partial tiles: splits [s0, s0 + PG) of tile tl into pt (PG * PQ * 4 registers per batch)
+  constexpr int PG = PQ <= 2 ? kMaxSplits : kMaxSplits / 2;
+  constexpr int PQN = PQ > 0 ? PQ : 1;
+  const int64_t tile_block = static_cast<int64_t>(kTileTokens) * ldr;
+  f32x4 pt[PG][PQN];
+  auto load_parts = [&](int tl, int s0) {
+    int lt = tid;
+    __asm__ volatile("" : "+v"(lt));   // per-call thread offsets: nothing hoisted out of the tile loop
+    const float* pp = ea.part + ((static_cast<int64_t>(tl) * b.nz + m) * ea.ks + s0) * tile_block +
+                      (lt >> 2) * ldr + 4 * (lt & 3);
+#pragma unroll
+    for (int u = 0; u < PG; ++u)
+#pragma unroll
+      for (int q = 0; q < PQN; ++q)
+        if (s0 + u < ea.ks) pt[u][q] = *reinterpret_cast<const f32x4*>(pp + u * tile_block + 16 * q);
+  };
   for (; tile < n_tiles; tile += b.nx) {
     if (tile >= b.nx) rec = tiles[tile];
+    if constexpr (PQ > 0) load_parts(tile, 0);   // with the entry, token and page id loads
     const int slot = rec.x & 0xffff, len = rec.x >> 16, pos = rec.y;
     const int ei = slot * pv.n_modules + module0 + m;
     const SlotEntry e = pv.entries[ei];
@@ -452,10 +476,53 @@ __device__ __forceinline__ void expand_mfma_body(const ExpandArgs& ea, const Blk
     };
     const int n_cb = min(ea.blocks, (h_out - b.y * ea.blocks * TN + TN - 1) / TN);
     // T tile: t = hi + mid + lo, three bf16 values whose sum is t exactly (3 x 8 significand
-    // bits cover fp32's 24), so the bf16 matrix cores multiply by t itself.  Thread -> row
-    // tid/4, columns (tid%4) + 4q; its loads go out with block 0's.  Each later block's loads
-    // are issued as soon as the block before it is staged in LDS.
-    {
+    // bits cover fp32's 24), so the bf16 matrix cores multiply by t itself.  From t: thread ->
+    // row tid/4, columns (tid%4) + 4q, its loads going out with block 0's.  Each later block's
+    // loads are issued as soon as the block before it is staged in LDS.
+    // put_t: the three parts of t at T3_s row r, column j (zero past the rank and for rows
+    // without a token)
+    auto put_t = [&](int r, int j, float t_rj, bool live) {
+      const float v = live ? t_rj : 0.f;
+      const __bf16 hi = static_cast<__bf16>(v);
+      const float r1 = v - static_cast<float>(hi);
+      const __bf16 mid = static_cast<__bf16>(r1);
+      const __bf16 lo = static_cast<__bf16>(r1 - static_cast<float>(mid));
+      T3_s[r * LD + j] = hi;
+      T3_s[(kTileTokens + r) * LD + j] = mid;
+      T3_s[(2 * kTileTokens + r) * LD + j] = lo;
+    };
+    if constexpr (PQ > 0) {
+      // thread -> tile row tid/4, columns 16q + 4(tid%4) .. +3; splits added in order.  The
+      // empty asm keeps the LDS addresses from being hoisted out of the tile loop (they would
+      // stay live across the matrix-core blocks and spill)
+      int r = tid >> 2, c = 4 * (tid & 3);
+      __asm__ volatile("" : "+v"(r), "+v"(c));
+      const bool row_live = toks_s[r] >= 0;
+      f32x4 sum[PQN];
+#pragma unroll
+      for (int q = 0; q < PQN; ++q) sum[q] = pt[0][q];
+#pragma unroll
+      for (int u = 1; u < PG; ++u)
+#pragma unroll
+        for (int q = 0; q < PQN; ++q)
+          if (u < ea.ks) sum[q] += pt[u][q];
+      for (int s0 = PG; s0 < ea.ks; s0 += PG) {   // rank caps above 32: the remaining splits
+        load_parts(tile, s0);
+#pragma unroll
+        for (int u = 0; u < PG; ++u)
+#pragma unroll
+          for (int q = 0; q < PQN; ++q)
+            if (s0 + u < ea.ks) sum[q] += pt[u][q];
+      }
+      if (n_cb > 0) issue(0, yv, bv);   // after the partials are summed: their registers are free
+#pragma unroll
+      for (int q = 0; q < PQN; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 16 * q + c + e;
+          if (j < rk) put_t(r, j, sum[q][e], row_live && j < rank);
+        }
+    } else {
       const int r = tid >> 2, jq = tid & 3;
       const int tk = toks_s[r];
       const float* trow = tm + static_cast<int64_t>(tk >= 0 ? tk : first) * ld_t;
@@ -466,16 +533,7 @@ __device__ __forceinline__ void expand_mfma_body(const ExpandArgs& ea, const Blk
 #pragma unroll
       for (int q = 0; q < kMaxRank / 4; ++q) {
         const int j = jq + 4 * q;
-        if (j < rk) {
-          const float v = (tk >= 0 && j < rank) ? tv[q] : 0.f;
-          const __bf16 hi = static_cast<__bf16>(v);
-          const float r1 = v - static_cast<float>(hi);
-          const __bf16 mid = static_cast<__bf16>(r1);
-          const __bf16 lo = static_cast<__bf16>(r1 - static_cast<float>(mid));
-          T3_s[r * LD + j] = hi;
-          T3_s[(kTileTokens + r) * LD + j] = mid;
-          T3_s[(2 * kTileTokens + r) * LD + j] = lo;
-        }
+        if (j < rk) put_t(r, j, tv[q], tk >= 0 && j < rank);
       }
     }
 #pragma unroll 1
@@ -582,15 +640,18 @@ __global__ __launch_bounds__(kMfmaThreads) void k_shrink_mixed(ShrinkArgs a, Gem
   }
 }
 
-template <typename TO>
-__global__ __launch_bounds__(kMfmaThreads, sizeof(TO) == 2 ? 3 : 2) void k_expand_mixed(ExpandArgs ea, GemvArgs g,
+// Partial tiles of rank caps of 32 or more (PQ >= 2) need the registers of a
+// third resident workgroup; at those caps the LDS tile leaves room for at most
+// three (32), or two (48, 64), anyway.
+template <typename TO, int PQ>
+__global__ __launch_bounds__(kMfmaThreads, (sizeof(TO) == 2 && PQ <= 1) ? 3 : 2) void k_expand_mixed(ExpandArgs ea, GemvArgs g,
                                                                                       int tnx, int tny, int tnz,
                                                                                       int gnx, int gny) {
   static_assert(kMfmaThreads == kGemvThreads, "both parts run on one workgroup size");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int lin = static_cast<int>(blockIdx.x), tile_blocks = tnx * tny * tnz;
   if (lin < tile_blocks) {
-    expand_mfma_body<TO>(ea, blk_of_linear(lin, tnx, tny, tnz), smem);
+    expand_mfma_body<TO, PQ>(ea, blk_of_linear(lin, tnx, tny, tnz), smem);
   } else {
     int it0 = -1;
     const Blk b = g.module_group > 0 ? blk_of_module_groups(lin - tile_blocks, gnx, gny, g.module_group, it0)

@@ -12,12 +12,18 @@ def say(*a):
 
 
 def run(wl, mode, y_dtype=None, **kw):
-    """Runs one step ('sgmv' or 'bgmv') from y = y0; returns (dw, y per module as float64)."""
+    """Runs one step from y = y0: 'sgmv' (the harness's choice of lora_apply_sgmv or
+    lora_shrink + lora_expand), 'sgmv_calls' (always lora_shrink + lora_expand) or
+    'bgmv'; returns (dw, y per module as float64)."""
     from segmented_gathered_rank_amd.harness import DeviceWorkload, from_device
     import torch
     dw = DeviceWorkload(wl, y_dtype=y_dtype, **kw)
     if mode == "sgmv":
         dw.sgmv_step()
+    elif mode == "sgmv_calls":
+        dw.build_segments()
+        dw.shrink()
+        dw.expand()
     else:
         dw.bgmv_step()
     torch.cuda.synchronize()
