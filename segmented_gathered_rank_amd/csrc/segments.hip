@@ -55,6 +55,20 @@ int rows_of(int n_slots) {
   return v > kWaves ? kWaves : v;
 }
 
+#ifndef LORA_SEG_WAVE_TOKENS
+#define LORA_SEG_WAVE_TOKENS 512
+#endif
+#ifndef LORA_SEG_QUAD_TOKENS
+#define LORA_SEG_QUAD_TOKENS 2048
+#endif
+// Threads of the one-workgroup schedule: one wave, four, or sixteen, as the
+// batch grows (slots per thread stay at most 4 in the smaller two).
+int one_group_threads(int n, int n_slots) {
+  if (n <= LORA_SEG_WAVE_TOKENS && n_slots <= 4 * 64) return 64;
+  if (n <= LORA_SEG_QUAD_TOKENS && n_slots <= 4 * 256) return 256;
+  return kThreads;
+}
+
 // Chunked schedule: tokens per chunk (a multiple of 64) and number of chunks;
 // 0 chunks means the one-workgroup schedule.
 int chunk_tokens_of(int n, int n_slots) {
@@ -186,9 +200,10 @@ __device__ __forceinline__ int2 unit_record(int slot, int run, int u, int first)
 // together; a batch with more falls back to each owning wave writing its own.
 constexpr int kLongDesc = 512;
 
+template <int W>
 struct LayoutLds {
-  int wsum[kWaves][7];   // per wave: inclusive counter totals, max segment length
-  int woff[kWaves][6];   // per wave: exclusive offsets
+  int wsum[W][7];   // per wave: inclusive counter totals, max segment length
+  int woff[W][6];   // per wave: exclusive offsets
   int tot[6];
   // long segment d: slot, length, first position, first unit (after the short
   // units) and first tile; ld_u0 / ld_t0 end with the totals
@@ -207,13 +222,15 @@ __device__ __forceinline__ int last_at_most(const int* a, int n, int v) {
   return lo;
 }
 
-// Block-wide layout from the per-slot totals `total` (LDS).  Thread tid owns
-// slots [s0, s1) (consecutive, in slot order, the same partition the caller
-// used to fill `total`).  Writes meta, seg_start/seg_slot and both work lists
-// and calls base_of(s, first position in perm) for each slot that has tokens.
-template <class BaseFn>
+// Block-wide layout (a workgroup of TH threads) from the per-slot totals
+// `total` (LDS).  Thread tid owns slots [s0, s1) (consecutive, in slot order,
+// the same partition the caller used to fill `total`).  Writes meta,
+// seg_start/seg_slot and both work lists and calls base_of(s, first position
+// in perm) for each slot that has tokens.
+template <int TH, class BaseFn>
 __device__ void layout_segments(const int32_t* total, int n_tokens, int n_slots, int s0, int s1, int bpt,
-                                int bad_total, const Out& o, LayoutLds& L, BaseFn base_of) {
+                                int bad_total, const Out& o, LayoutLds<TH / 64>& L, BaseFn base_of) {
+  constexpr int W = TH / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int own[6] = {0, 0, 0, 0, 0, 0};   // tokens, segments, short units, long units, tiles, long segments
   int mx = 0;
@@ -247,12 +264,12 @@ __device__ void layout_segments(const int32_t* total, int n_tokens, int n_slots,
     int tq[6];
 #pragma unroll
     for (int q = 0; q < 6; ++q) {
-      const int v = lane < kWaves ? L.wsum[lane][q] : 0;
+      const int v = lane < W ? L.wsum[lane][q] : 0;
       const int c = wave_scan<false>(v);
-      if (lane < kWaves) L.woff[lane][q] = c - v;
+      if (lane < W) L.woff[lane][q] = c - v;
       tq[q] = lane63(c);
     }
-    const int m = lane63(wave_scan<true>(lane < kWaves ? L.wsum[lane][6] : 0));
+    const int m = lane63(wave_scan<true>(lane < W ? L.wsum[lane][6] : 0));
     if (lane == 0) {
 #pragma unroll
       for (int q = 0; q < 6; ++q) L.tot[q] = tq[q];
@@ -336,11 +353,11 @@ __device__ void layout_segments(const int32_t* total, int n_tokens, int n_slots,
   if (spread && n_long > 0) {   // uniform
     __syncthreads();
     const int n_lu = L.tot[3], n_t = L.tot[4];
-    for (int i = threadIdx.x; i < n_lu; i += kThreads) {
+    for (int i = threadIdx.x; i < n_lu; i += TH) {
       const int d = last_at_most(L.ld_u0, n_long, i);
       units[long_at + i] = unit_record(L.ld_slot[d], L.ld_run[d], i - L.ld_u0[d], L.ld_first[d]);
     }
-    for (int i = threadIdx.x; i < n_t; i += kThreads) {
+    for (int i = threadIdx.x; i < n_t; i += TH) {
       const int d = last_at_most(L.ld_t0, n_long, i);
       const int u = i - L.ld_t0[d], r = L.ld_run[d];
       tiles[i] = make_int2(L.ld_slot[d] + (min(kTileTokens, r - u * kTileTokens) << 16),
@@ -349,40 +366,47 @@ __device__ void layout_segments(const int32_t* total, int n_tokens, int n_slots,
   }
 }
 
-// Per-slot exclusive prefix over V rows plus `base`, written back into the rows.
+// Per-slot exclusive prefix over V <= W rows plus `base`, written back into the rows.
+template <int W>
 __device__ __forceinline__ void rows_to_cursors(int32_t* hist, int n_slots, int V, int s, int base) {
-  int c[kWaves];
+  int c[W];
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) c[w] = hist[min(w, V - 1) * n_slots + s];
+  for (int w = 0; w < W; ++w) c[w] = hist[min(w, V - 1) * n_slots + s];
   int run = base;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < W; ++w) {
     if (w < V) {
       hist[w * n_slots + s] = run;
       run += c[w];
     }
   }
 }
+template <int W>
 __device__ __forceinline__ int rows_total(const int32_t* hist, int n_slots, int V, int s) {
-  int c[kWaves];
+  int c[W];
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) c[w] = hist[min(w, V - 1) * n_slots + s];
+  for (int w = 0; w < W; ++w) c[w] = hist[min(w, V - 1) * n_slots + s];
   int run = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) run += (w < V) ? c[w] : 0;
+  for (int w = 0; w < W; ++w) run += (w < V) ? c[w] : 0;
   return run;
 }
 
 // ------------------------------------------------------------ one workgroup
-__global__ __launch_bounds__(kThreads) void k_segments_one(const int32_t* __restrict__ ids, int32_t n_tokens,
-                                                           int32_t n_slots, int32_t V, int32_t nbits, Out o) {
+// TH threads (V <= TH / 64 histogram rows).  Every thread runs the layout's
+// code, so a small batch takes a small workgroup: with 1024 threads the
+// layout alone took about 3 us for 32 slots, all of it instruction issue.
+template <int TH>
+__global__ __launch_bounds__(TH) void k_segments_one(const int32_t* __restrict__ ids, int32_t n_tokens,
+                                                     int32_t n_slots, int32_t V, int32_t nbits, Out o) {
+  constexpr int W = TH / 64;
   extern __shared__ int32_t lds[];
   int32_t* hist = lds;                  // [V][n_slots]: counts, then cursors
   int32_t* total = lds + V * n_slots;   // [n_slots]
-  __shared__ LayoutLds L;
+  __shared__ LayoutLds<W> L;
   __shared__ int bad_cell;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < V * n_slots; i += kThreads) hist[i] = 0;
+  for (int i = tid; i < V * n_slots; i += TH) hist[i] = 0;
   if (tid == 0) bad_cell = 0;
   __syncthreads();
 
@@ -398,14 +422,14 @@ __global__ __launch_bounds__(kThreads) void k_segments_one(const int32_t* __rest
     bad += count_round(idv, base, end, lane, n_slots, row);
   }
   block_add(bad, lane, &bad_cell);
-  const int bpt = (n_slots + kThreads - 1) / kThreads;
+  const int bpt = (n_slots + TH - 1) / TH;
   const int s0 = min(n_slots, tid * bpt);
   const int s1 = min(n_slots, s0 + bpt);
   __syncthreads();
 
-  for (int s = s0; s < s1; ++s) total[s] = rows_total(hist, n_slots, V, s);
-  layout_segments(total, n_tokens, n_slots, s0, s1, bpt, bad_cell, o, L,
-                  [&](int s, int base) { rows_to_cursors(hist, n_slots, V, s, base); });
+  for (int s = s0; s < s1; ++s) total[s] = rows_total<W>(hist, n_slots, V, s);
+  layout_segments<TH>(total, n_tokens, n_slots, s0, s1, bpt, bad_cell, o, L,
+                      [&](int s, int base) { rows_to_cursors<W>(hist, n_slots, V, s, base); });
   __syncthreads();
 
   // scatter: same ranges, same order as the count
@@ -454,7 +478,7 @@ __global__ __launch_bounds__(kThreads) void k_seg_scan(int32_t n_tokens, int32_t
                                                        const int32_t* __restrict__ bad_of,
                                                        int32_t* __restrict__ slot_base, Out o) {
   extern __shared__ int32_t total[];   // [n_slots]
-  __shared__ LayoutLds L;
+  __shared__ LayoutLds<kWaves> L;
   __shared__ int bad_cell;
   const int tid = threadIdx.x, lane = tid & 63;
   if (tid == 0) bad_cell = 0;
@@ -496,7 +520,7 @@ __global__ __launch_bounds__(kThreads) void k_seg_scan(int32_t n_tokens, int32_t
   const int bpt = (n_slots + kThreads - 1) / kThreads;
   const int s0 = min(n_slots, tid * bpt);
   const int s1 = min(n_slots, s0 + bpt);
-  layout_segments(total, n_tokens, n_slots, s0, s1, bpt, bad_cell, o, L,
+  layout_segments<kThreads>(total, n_tokens, n_slots, s0, s1, bpt, bad_cell, o, L,
                   [&](int s, int base) { slot_base[s] = base; });
 }
 
@@ -536,7 +560,7 @@ __global__ __launch_bounds__(kThreads) void k_seg_scatter(const int32_t* __restr
 #pragma unroll
   for (int k = 0; k < kBpt; ++k) {
     const int s = tid + k * kThreads;
-    if (s < n_slots && cg[k] > 0) rows_to_cursors(hist, n_slots, V, s, base_of[k]);
+    if (s < n_slots && cg[k] > 0) rows_to_cursors<kWaves>(hist, n_slots, V, s, base_of[k]);
   }
   __syncthreads();
   const bool one_round = end - beg <= kRound;
@@ -554,7 +578,8 @@ bool lds_limit(K* k) {
                              kLdsWords * 4) == hipSuccess;
 }
 bool set_lds_limit() {   // gfx950 allows 160 KiB of LDS per workgroup; these use up to 64 KiB + static
-  static const bool ok = lds_limit(&k_segments_one) && lds_limit(&k_seg_scatter<1>) &&
+  static const bool ok = lds_limit(&k_segments_one<64>) && lds_limit(&k_segments_one<256>) &&
+                         lds_limit(&k_segments_one<1024>) && lds_limit(&k_seg_scatter<1>) &&
                          lds_limit(&k_seg_scatter<2>) && lds_limit(&k_seg_scatter<4>) &&
                          lds_limit(&k_seg_scatter<8>);
   return ok;
@@ -632,8 +657,15 @@ lora_status lora_build_segments(const int32_t* ids, const lora_segments* seg, vo
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const Out o{seg->perm, seg->seg_start, seg->seg_slot, seg->meta, seg->units, seg->tiles};
   if (G == 0) {
-    const size_t lds = static_cast<size_t>(V + 1) * n_slots * 4;
-    hipLaunchKernelGGL(k_segments_one, dim3(1), dim3(kThreads), lds, st, ids, n, n_slots, V, nbits, o);
+    const int th = one_group_threads(n, n_slots);
+    const int32_t v = std::min<int32_t>(V, th / 64);
+    const size_t lds = static_cast<size_t>(v + 1) * n_slots * 4;
+    if (th == 64)
+      hipLaunchKernelGGL(k_segments_one<64>, dim3(1), dim3(64), lds, st, ids, n, n_slots, v, nbits, o);
+    else if (th == 256)
+      hipLaunchKernelGGL(k_segments_one<256>, dim3(1), dim3(256), lds, st, ids, n, n_slots, v, nbits, o);
+    else
+      hipLaunchKernelGGL(k_segments_one<1024>, dim3(1), dim3(1024), lds, st, ids, n, n_slots, v, nbits, o);
   } else {
     const int32_t chunk = chunk_tokens_of(n, n_slots);
     int32_t* cnt = seg->work;

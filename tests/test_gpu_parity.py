@@ -70,6 +70,15 @@ SEG_CASES = {
     "one_group_many_long": (np.repeat(np.random.default_rng(26).permutation(100), 64 + 5), 100),
     "chunked_many_long": (np.repeat(np.random.default_rng(27).permutation(400), 130), 400),
     "chunked_too_many_long": (np.repeat(np.random.default_rng(28).permutation(1500), 70), 1500),
+    # one-workgroup sizes: one wave up to 512 tokens and 256 slots (4 slots per lane), four
+    # waves up to 2048 tokens and 1024 slots, sixteen above; each edge from both sides
+    "wave_max": (np.random.default_rng(29).integers(-1, 256, 512), 256),
+    "wave_long_segments": (np.repeat(np.random.default_rng(30).permutation(8), 64), 8),
+    "quad_tokens": (np.random.default_rng(31).integers(-1, 40, 513), 40),
+    "quad_slots": (np.random.default_rng(32).integers(-1, 257, 300), 257),
+    "quad_max": (np.random.default_rng(33).integers(-1, 1024, 2048), 1024),
+    "quad_long_and_short": (np.concatenate([np.repeat([5, 9], 700), np.arange(600) % 50]), 64),
+    "sixteen_from": (np.random.default_rng(34).integers(-1, 64, 2049), 64),
 }
 
 
