@@ -254,22 +254,31 @@ __device__ void layout_segments(const int32_t* total, int n_tokens, int n_slots,
 #pragma unroll
   for (int q = 0; q < 6; ++q) incl[q] = wave_scan<false>(own[q]);
   const int wmx = lane63(wave_scan<true>(mx));
-  if (lane == 63) {
+  if (W > 1 && lane == 63) {
 #pragma unroll
     for (int q = 0; q < 6; ++q) L.wsum[wave][q] = incl[q];
     L.wsum[wave][6] = wmx;
   }
-  __syncthreads();
+  if constexpr (W > 1) __syncthreads();
   if (wave == 0) {
-    int tq[6];
+    int tq[6], m;
+    if constexpr (W == 1) {   // one wave: its totals are the workgroup's, its offsets 0
 #pragma unroll
-    for (int q = 0; q < 6; ++q) {
-      const int v = lane < W ? L.wsum[lane][q] : 0;
-      const int c = wave_scan<false>(v);
-      if (lane < W) L.woff[lane][q] = c - v;
-      tq[q] = lane63(c);
+      for (int q = 0; q < 6; ++q) {
+        tq[q] = lane63(incl[q]);
+        if (lane == 0) L.woff[0][q] = 0;
+      }
+      m = wmx;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 6; ++q) {
+        const int v = lane < W ? L.wsum[lane][q] : 0;
+        const int c = wave_scan<false>(v);
+        if (lane < W) L.woff[lane][q] = c - v;
+        tq[q] = lane63(c);
+      }
+      m = lane63(wave_scan<true>(lane < W ? L.wsum[lane][6] : 0));
     }
-    const int m = lane63(wave_scan<true>(lane < W ? L.wsum[lane][6] : 0));
     if (lane == 0) {
 #pragma unroll
       for (int q = 0; q < 6; ++q) L.tot[q] = tq[q];
@@ -288,9 +297,9 @@ __device__ void layout_segments(const int32_t* total, int n_tokens, int n_slots,
       meta[LORA_META_LONG_MIN] = kLongMin;
       meta[LORA_META_N_TOKENS] = n_tokens;
       meta[LORA_META_N_SLOTS] = n_slots;
-      for (int q = 12; q < LORA_META_WORDS; ++q) meta[q] = 0;
       o.seg_start[tq[1]] = tq[0];
     }
+    for (int q = 12 + lane; q < LORA_META_WORDS; q += 64) o.meta[q] = 0;   // reserved words
   }
   __syncthreads();
 
