@@ -115,10 +115,14 @@ lora_status lora_pool_destroy(lora_pool *p);
 
 /* Copies one adapter into freshly allocated pages and publishes the
  * (slot, module) entry (the hot-swap strategy of the study page, section
- * "Strategies compared": an adapter's weights are copied into a GPU slot).  A and B are [rank][h_in] and [rank][h_out] of the
- * pool's dtype, in host or device memory.  The upload runs on `stream` and
- * the call returns once it has completed, so A and B may be reused at once.
- * Kernels enqueued later on `stream` see the entry.
+ * "Strategies compared": an adapter's weights are copied into a GPU slot;
+ * "Thousands of adapters", slide 9: the copy overlaps the GPU's work).  A and
+ * B are [rank][h_in] and [rank][h_out] of the pool's dtype, in host or device
+ * memory.  The call returns before the upload completes: A and B in host
+ * memory are copied into a page-locked staging buffer before it returns (so
+ * they may be reused at once); A and B in device memory are read on `stream`
+ * in stream order.  Kernels enqueued later on `stream` see the entry.  Up to
+ * 4 uploads are in flight per pool; a fifth call waits for the oldest.
  * Errors: ARG (null), SLOT (range / already loaded), RANK, NO_PAGES, HIP. */
 lora_status lora_pool_load(lora_pool *p, int32_t slot, int32_t module, int32_t rank,
                            const void *A, const void *B, float scale, void *stream);

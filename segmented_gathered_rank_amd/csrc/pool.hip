@@ -66,11 +66,29 @@ void free_device(lora_pool* p) {
   if (p->d_pages) (void)hipFree(p->d_pages);
   if (p->d_entries) (void)hipFree(p->d_entries);
   if (p->d_page_ids) (void)hipFree(p->d_page_ids);
-  if (p->d_staging) (void)hipFree(p->d_staging);
+  for (int r = 0; r < lora_pool::kLoadRing; ++r) {
+    if (p->d_staging[r]) (void)hipFree(p->d_staging[r]);
+    if (p->h_staging[r]) (void)hipHostFree(p->h_staging[r]);
+    if (p->ring_done[r]) (void)hipEventDestroy(p->ring_done[r]);
+    p->d_staging[r] = nullptr;
+    p->h_staging[r] = nullptr;
+    p->ring_done[r] = nullptr;
+  }
   p->d_pages = nullptr;
   p->d_entries = nullptr;
   p->d_page_ids = nullptr;
-  p->d_staging = nullptr;
+}
+
+// Whether ptr is device memory (hipPointerGetAttributes fails for pageable
+// host memory the runtime has never seen: that is host memory too, and the
+// error is cleared so that later checks do not report it).
+bool is_device_memory(const void* ptr) {
+  hipPointerAttribute_t attr{};
+  if (hipPointerGetAttributes(&attr, ptr) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return attr.type == hipMemoryTypeDevice;
 }
 
 }  // namespace
@@ -187,8 +205,11 @@ lora_status lora_pool_create(lora_pool** out, int32_t device, lora_dtype wdtype,
   bool ok = hipMalloc(&p->d_pages, static_cast<size_t>(n_pages + 1) * page_bytes) == hipSuccess &&
             hipMalloc(reinterpret_cast<void**>(&p->d_entries), n_entries * sizeof(SlotEntry)) == hipSuccess &&
             hipMalloc(reinterpret_cast<void**>(&p->d_page_ids),
-                      static_cast<size_t>(table > 0 ? table : 1) * 4) == hipSuccess &&
-            hipMalloc(&p->d_staging, p->staging_bytes) == hipSuccess;
+                      static_cast<size_t>(table > 0 ? table : 1) * 4) == hipSuccess;
+  for (int r = 0; ok && r < lora_pool::kLoadRing; ++r)
+    ok = hipMalloc(&p->d_staging[r], p->staging_bytes) == hipSuccess &&
+         hipHostMalloc(&p->h_staging[r], p->staging_bytes, hipHostMallocDefault) == hipSuccess &&
+         hipEventCreateWithFlags(&p->ring_done[r], hipEventDisableTiming) == hipSuccess;
   ok = ok && fill_zero(static_cast<char*>(p->d_pages) + static_cast<size_t>(n_pages) * page_bytes, page_bytes, nullptr) &&
        fill_zero(p->d_entries, n_entries * sizeof(SlotEntry), nullptr) &&
        fill_zero(p->d_page_ids, static_cast<size_t>(table) * 4, nullptr) &&
@@ -232,7 +253,6 @@ lora_status lora_pool_load(lora_pool* p, int32_t slot, int32_t module, int32_t r
   const size_t a_bytes = static_cast<size_t>(rank) * p->h_in[module] * eb;
   const size_t b_bytes = static_cast<size_t>(rank) * p->h_out[module] * eb;
   const size_t ids_at = (a_bytes + b_bytes + 255) / 256 * 256;
-  char* st = static_cast<char*>(p->d_staging);
   const int32_t ids_off = static_cast<int32_t>(ei * p->max_pages_per_entry);
   // A's page ids from ids_off (rank row j, page p at j*ppr_a + p); B's from
   // ids_off + max_rank*ppr_a whatever the rank, so kernels can fetch both
@@ -242,31 +262,50 @@ lora_status lora_pool_load(lora_pool* p, int32_t slot, int32_t module, int32_t r
   SlotEntry value{rank, scale, ids_off, ids_off + n_a + b_gap};
 
   DeviceGuard g(p->device);
-  bool ok = g.ok &&
-            hipMemcpyAsync(st, A, a_bytes, hipMemcpyDefault, s) == hipSuccess &&
-            hipMemcpyAsync(st + a_bytes, B, b_bytes, hipMemcpyDefault, s) == hipSuccess &&
-            hipMemcpyAsync(st + ids_at, pages.data(), pages.size() * 4, hipMemcpyHostToDevice, s) ==
-                hipSuccess;
+  bool ok = g.ok;
+  // the next ring slot, once the upload that used it last has passed its stream
+  const int r = p->ring_next;
+  ok = ok && hipEventSynchronize(p->ring_done[r]) == hipSuccess;
+  char* hs = static_cast<char*>(p->h_staging[r]);
+  char* ds = static_cast<char*>(p->d_staging[r]);
+  if (ok) {
+    // host rows and the page list are copied into the slot's page-locked buffer now (the
+    // caller may reuse A and B at once); rows in device memory are copied on the stream
+    const bool a_dev = is_device_memory(A), b_dev = is_device_memory(B);
+    if (!a_dev) std::memcpy(hs, A, a_bytes);
+    if (!b_dev) std::memcpy(hs + a_bytes, B, b_bytes);
+    std::memcpy(hs + ids_at, pages.data(), pages.size() * 4);
+    if (!a_dev && !b_dev) {
+      ok = hipMemcpyAsync(ds, hs, ids_at + pages.size() * 4, hipMemcpyHostToDevice, s) == hipSuccess;
+    } else {
+      ok = hipMemcpyAsync(ds, a_dev ? A : hs, a_bytes, a_dev ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, s) ==
+               hipSuccess &&
+           hipMemcpyAsync(ds + a_bytes, b_dev ? B : hs + a_bytes, b_bytes,
+                          b_dev ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, s) == hipSuccess &&
+           hipMemcpyAsync(ds + ids_at, hs + ids_at, pages.size() * 4, hipMemcpyHostToDevice, s) == hipSuccess;
+    }
+  }
   if (ok) {
     if (p->dtype == LORA_BF16) {
       hipLaunchKernelGGL(k_upload<__bf16>, dim3(static_cast<unsigned>(n_plist)), dim3(256), 0, s,
-                         static_cast<__bf16*>(p->d_pages), reinterpret_cast<const __bf16*>(st),
-                         reinterpret_cast<const __bf16*>(st + a_bytes),
-                         reinterpret_cast<const int32_t*>(st + ids_at), static_cast<int32_t>(n_plist), h,
+                         static_cast<__bf16*>(p->d_pages), reinterpret_cast<const __bf16*>(ds),
+                         reinterpret_cast<const __bf16*>(ds + a_bytes),
+                         reinterpret_cast<const int32_t*>(ds + ids_at), static_cast<int32_t>(n_plist), h,
                          p->d_page_ids, ids_off, n_a, b_gap, p->d_entries + ei, value);
     } else {
       hipLaunchKernelGGL(k_upload<float>, dim3(static_cast<unsigned>(n_plist)), dim3(256), 0, s,
-                         static_cast<float*>(p->d_pages), reinterpret_cast<const float*>(st),
-                         reinterpret_cast<const float*>(st + a_bytes),
-                         reinterpret_cast<const int32_t*>(st + ids_at), static_cast<int32_t>(n_plist), h,
+                         static_cast<float*>(p->d_pages), reinterpret_cast<const float*>(ds),
+                         reinterpret_cast<const float*>(ds + a_bytes),
+                         reinterpret_cast<const int32_t*>(ds + ids_at), static_cast<int32_t>(n_plist), h,
                          p->d_page_ids, ids_off, n_a, b_gap, p->d_entries + ei, value);
     }
-    ok = hipGetLastError() == hipSuccess && hipStreamSynchronize(s) == hipSuccess;
+    ok = hipGetLastError() == hipSuccess && hipEventRecord(p->ring_done[r], s) == hipSuccess;
   }
   if (!ok) {
     p->alloc.release(pages);
     return LORA_ERR_HIP;
   }
+  p->ring_next = (r + 1) % lora_pool::kLoadRing;
   auto& e = p->entries[ei];
   e.rank = rank;
   e.scale = scale;

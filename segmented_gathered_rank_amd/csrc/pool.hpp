@@ -20,7 +20,16 @@ struct lora_pool {
   void* d_pages = nullptr;
   lora::SlotEntry* d_entries = nullptr;
   int32_t* d_page_ids = nullptr;
-  void* d_staging = nullptr;      // A and B rows of one upload, then its page list
+  // lora_pool_load's staging ring: kLoadRing uploads may be in flight.  Slot r
+  // holds one upload's A and B rows and its page list in page-locked host
+  // memory (h_staging) and device memory (d_staging); ring_done[r] is recorded
+  // on the upload's stream after it, so the slot is reused only once its
+  // copy and kernel are done.
+  static constexpr int kLoadRing = 4;
+  void* h_staging[kLoadRing] = {};
+  void* d_staging[kLoadRing] = {};
+  hipEvent_t ring_done[kLoadRing] = {};
+  int ring_next = 0;
   size_t staging_bytes = 0;
 
   lora::PageAllocator alloc;
