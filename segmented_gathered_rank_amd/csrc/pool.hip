@@ -41,6 +41,33 @@ __global__ __launch_bounds__(256) void k_upload(T* __restrict__ pages, const T* 
   }
 }
 
+// Batched uploads: workgroup b < n_pieces copies piece b's page and records its
+// page id; the workgroups after them publish the entry writes, one per thread.
+// A kernel boundary orders every page before any entry that lists it, as the
+// entries are only read by later kernels.
+template <typename T>
+__global__ __launch_bounds__(256) void k_upload_batch(T* __restrict__ pages, int64_t page_elems,
+                                                      const UploadPiece* __restrict__ pieces, int32_t n_pieces,
+                                                      const EntryWrite* __restrict__ writes, int32_t n_writes,
+                                                      int32_t* __restrict__ page_ids, SlotEntry* __restrict__ entries) {
+  const int32_t b = blockIdx.x;
+  if (b < n_pieces) {
+    const UploadPiece pc = pieces[b];
+    const T* src = static_cast<const T*>(pc.src);
+    T* d = pages + static_cast<int64_t>(pc.page) * page_elems;
+    constexpr int kVec = 16 / sizeof(T);
+    for (int64_t e = static_cast<int64_t>(threadIdx.x) * kVec; e < page_elems; e += 256 * kVec)
+      *reinterpret_cast<u32x4*>(d + e) = *reinterpret_cast<const u32x4*>(src + e);
+    if (threadIdx.x == 0) page_ids[pc.id_at] = pc.page;
+    return;
+  }
+  const int32_t w = (b - n_pieces) * 256 + static_cast<int32_t>(threadIdx.x);
+  if (w < n_writes) {
+    const EntryWrite ew = writes[w];
+    entries[ew.index] = ew.value;
+  }
+}
+
 __global__ void k_clear_entries(SlotEntry* __restrict__ e, int32_t count) {
   const int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < count) e[i] = SlotEntry{0, 0.f, 0, 0};
@@ -130,6 +157,67 @@ lora_status pool_upload_async(lora_pool* p, int32_t slot, int32_t module, int32_
   e.pages = std::move(pages);
   ++p->loads;
   return LORA_OK;
+}
+
+bool pool_evict_host(lora_pool* p, int32_t slot) {
+  bool any = false;
+  for (int32_t m = 0; m < p->n_modules; ++m) {
+    auto& e = p->entries[static_cast<size_t>(slot) * p->n_modules + m];
+    if (e.rank == 0) continue;
+    any = true;
+    p->alloc.release(e.pages);
+    e = lora_pool::Entry();
+  }
+  if (any) ++p->evicts;
+  return any;
+}
+
+lora_status pool_stage_upload(lora_pool* p, int32_t slot, int32_t module, int32_t rank, const void* a,
+                              const void* b, float scale, std::vector<UploadPiece>& pieces,
+                              std::vector<EntryWrite>& entries) {
+  if (slot < 0 || slot >= p->n_slots || module < 0 || module >= p->n_modules) return LORA_ERR_SLOT;
+  if (rank < 1 || rank > p->max_rank) return LORA_ERR_RANK;
+  const size_t ei = static_cast<size_t>(slot) * p->n_modules + module;
+  if (p->entries[ei].rank != 0) return LORA_ERR_SLOT;
+  const int64_t h = p->page_elems;
+  const int64_t ppr_a = p->h_in[module] / h, ppr_b = p->h_out[module] / h;
+  const int64_t n_a = rank * ppr_a, n_plist = rank * (ppr_a + ppr_b);
+  std::vector<int32_t> pages;
+  if (!p->alloc.allocate(n_plist, pages)) return LORA_ERR_NO_PAGES;
+  const int32_t ids_off = static_cast<int32_t>(ei * p->max_pages_per_entry);
+  const int32_t b_gap = static_cast<int32_t>((p->max_rank - rank) * ppr_a);
+  const size_t pb = static_cast<size_t>(h) * p->elem_bytes();
+  for (int64_t i = 0; i < n_plist; ++i) {
+    const bool is_a = i < n_a;
+    const char* src = static_cast<const char*>(is_a ? a : b) + static_cast<size_t>(is_a ? i : i - n_a) * pb;
+    pieces.push_back(UploadPiece{src, pages[static_cast<size_t>(i)],
+                                 static_cast<int32_t>(ids_off + i + (is_a ? 0 : b_gap))});
+  }
+  entries.push_back(EntryWrite{static_cast<int32_t>(ei), 0,
+                               SlotEntry{rank, scale, ids_off, static_cast<int32_t>(ids_off + n_a + b_gap)}});
+  auto& e = p->entries[ei];
+  e.rank = rank;
+  e.scale = scale;
+  e.pages = std::move(pages);
+  ++p->loads;
+  return LORA_OK;
+}
+
+lora_status pool_upload_batch(lora_pool* p, const UploadPiece* pieces, int32_t n_pieces, const EntryWrite* entries,
+                              int32_t n_entries, hipStream_t s) {
+  if (n_pieces < 0 || n_entries < 0) return LORA_ERR_ARG;
+  const int64_t blocks = static_cast<int64_t>(n_pieces) + (n_entries + 255) / 256;
+  if (blocks == 0) return LORA_OK;
+  if (blocks > INT32_MAX) return LORA_ERR_SHAPE;
+  if (p->dtype == LORA_BF16)
+    hipLaunchKernelGGL(k_upload_batch<__bf16>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                       static_cast<__bf16*>(p->d_pages), p->page_elems, pieces, n_pieces, entries, n_entries,
+                       p->d_page_ids, p->d_entries);
+  else
+    hipLaunchKernelGGL(k_upload_batch<float>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                       static_cast<float*>(p->d_pages), p->page_elems, pieces, n_pieces, entries, n_entries,
+                       p->d_page_ids, p->d_entries);
+  return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
 extern "C" {

@@ -82,3 +82,39 @@ struct DeviceGuard {
 // passes the upload.  Same checks and bookkeeping as lora_pool_load.
 lora_status pool_upload_async(lora_pool* p, int32_t slot, int32_t module, int32_t rank, const void* a,
                               const void* b, float scale, int32_t* plist, hipStream_t s);
+
+// Batched uploads (several (slot, module) entries in one launch).  A piece is
+// one page: its source (device memory or page-locked host memory), its page
+// and its position in the page-id table.  An entry write publishes (or, with
+// rank 0, clears) one (slot, module) entry after the pieces.  Descriptors may
+// themselves live in page-locked host memory.
+namespace lora {
+struct UploadPiece {
+  const void* src;
+  int32_t page;
+  int32_t id_at;
+};
+struct EntryWrite {
+  int32_t index;
+  int32_t pad_;
+  SlotEntry value;
+};
+}  // namespace lora
+
+// Host bookkeeping of evicting every module of `slot` (pages back to the free
+// list, entries empty); the caller clears the device entries (an EntryWrite of
+// rank 0 per module).  Returns whether anything was loaded.
+bool pool_evict_host(lora_pool* p, int32_t slot);
+
+// Host bookkeeping of one upload: checks, allocates the pages and appends the
+// pieces (A's rows from a, B's from b, page by page) and the entry write; the
+// entry reads as loaded on the host at once.  No device work.
+lora_status pool_stage_upload(lora_pool* p, int32_t slot, int32_t module, int32_t rank, const void* a,
+                              const void* b, float scale, std::vector<lora::UploadPiece>& pieces,
+                              std::vector<lora::EntryWrite>& entries);
+
+// One launch for n_pieces pieces and n_entries entry writes (descriptors in
+// device or page-locked host memory, unchanged until the stream passes it).
+lora_status pool_upload_batch(lora_pool* p, const lora::UploadPiece* pieces, int32_t n_pieces,
+                              const lora::EntryWrite* entries, int32_t n_entries, hipStream_t s);
+

@@ -12,10 +12,11 @@
 // Both tiers are intrusive doubly linked lists over fixed entry arrays, so a
 // request costs O(1) besides one hash lookup per tier.
 //
-// lora_tiers_acquire drives a slot pool with it: each GPU miss evicts the
-// displaced adapter's entries and uploads the new adapter's A and B rows for
-// every module from page-locked host buffers (the host tier), asynchronously
-// on the caller's stream.  A host-tier miss first asks the caller's fetch
+// lora_tiers_acquire drives a slot pool with it: the GPU misses of a batch
+// evict the displaced adapters' entries and upload the new adapters' A and B
+// rows for every module from page-locked host buffers (the host tier), all in
+// one launch and asynchronously on the caller's stream: the host only does
+// bookkeeping per miss.  A host-tier miss first asks the caller's fetch
 // function to fill a host buffer (the cold store is the caller's).
 //
 // lora_tiers_prefetch is the forecast of "Thousands of adapters" (slide 9: a
@@ -26,6 +27,8 @@
 // them) before it reuses a slot.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <cstring>
 #include <new>
 #include <unordered_map>
 #include <vector>
@@ -101,6 +104,14 @@ struct LruList {
 
 }  // namespace
 
+// Page-locked descriptors of one batched upload, and the event behind it.
+struct UploadRing {
+  void* buf = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  uint64_t serial = 0;   // the batch that used it last
+};
+
 struct lora_tiers {
   LruList gpu, host;
   int64_t gpu_hits = 0, host_hits = 0, cold = 0;
@@ -110,8 +121,18 @@ struct lora_tiers {
   size_t entry_bytes = 0;
   std::vector<int32_t> rank;    // [host entry][module]
   std::vector<float> scale;     // [host entry][module]
-  std::vector<hipEvent_t> done; // [host entry]: last upload that read the entry's buffer
-  std::vector<uint8_t> pending;
+  // batched uploads: two descriptor buffers used in turn; batch `serial` is the
+  // last one launched, and host entry e's buffer was last read by batch
+  // he_serial[e] through ring[he_ring[e]] (0: never)
+  UploadRing ring[2];
+  int ring_next = 0;
+  uint64_t serial = 0;
+  std::vector<uint64_t> he_serial;
+  std::vector<int8_t> he_ring;
+  // the batch being staged: pieces, entry writes and the host entries they read
+  std::vector<lora::UploadPiece> pieces;
+  std::vector<lora::EntryWrite> writes;
+  std::vector<int32_t> staged_he;
   // prefetch: adapters of the batch in flight (never displaced by a prefetch),
   // the end of the two latest batches' kernels, and the end of the latest prefetch
   std::vector<int32_t> inflight;
@@ -170,8 +191,11 @@ lora_status lora_tiers_create(lora_tiers** out, int32_t gpu_slots, int32_t host_
 lora_status lora_tiers_destroy(lora_tiers* t) {
   if (!t) return LORA_OK;
   lora_status st = LORA_OK;
-  for (size_t e = 0; e < t->done.size(); ++e)
-    if (t->done[e] && hipEventDestroy(t->done[e]) != hipSuccess) st = LORA_ERR_HIP;
+  for (UploadRing& r : t->ring) {   // uploads still reading page-locked memory finish first
+    if (r.ev && hipEventSynchronize(r.ev) != hipSuccess) st = LORA_ERR_HIP;
+    if (r.ev && hipEventDestroy(r.ev) != hipSuccess) st = LORA_ERR_HIP;
+    if (r.buf && hipHostFree(r.buf) != hipSuccess) st = LORA_ERR_HIP;
+  }
   for (hipEvent_t ev : {t->batch_ev[0], t->batch_ev[1], t->prefetch_ev})
     if (ev && hipEventDestroy(ev) != hipSuccess) st = LORA_ERR_HIP;
   if (t->pinned && hipHostFree(t->pinned) != hipSuccess) st = LORA_ERR_HIP;
@@ -232,26 +256,80 @@ lora_status bind_pool(lora_tiers* t, lora_pool* p) {
   t->entry_bytes = per;
   t->rank.assign(nh * p->n_modules, 0);
   t->scale.assign(nh * p->n_modules, 0.f);
-  t->done.assign(nh, nullptr);
-  t->pending.assign(nh, 0);
-  for (size_t e = 0; e < nh; ++e)
-    if (hipEventCreateWithFlags(&t->done[e], hipEventDisableTiming) != hipSuccess) return LORA_ERR_HIP;
-  for (hipEvent_t* ev : {&t->batch_ev[0], &t->batch_ev[1], &t->prefetch_ev})
+  t->he_serial.assign(nh, 0);
+  t->he_ring.assign(nh, 0);
+  for (hipEvent_t* ev : {&t->batch_ev[0], &t->batch_ev[1], &t->prefetch_ev, &t->ring[0].ev, &t->ring[1].ev})
     if (hipEventCreateWithFlags(ev, hipEventDisableTiming) != hipSuccess) return LORA_ERR_HIP;
   return LORA_OK;
 }
 
+// Launches the staged batch on stream s: its descriptors go to the next ring
+// buffer (once the batch that used it last has passed), one upload launch,
+// one event.
+lora_status flush_uploads(lora_tiers* t, lora_pool* p, hipStream_t s) {
+  if (t->pieces.empty() && t->writes.empty()) return LORA_OK;
+  UploadRing& r = t->ring[t->ring_next];
+  if (hipEventSynchronize(r.ev) != hipSuccess) return LORA_ERR_HIP;
+  const size_t pb = t->pieces.size() * sizeof(lora::UploadPiece);
+  const size_t wb = t->writes.size() * sizeof(lora::EntryWrite);
+  const size_t need = (pb + 255) / 256 * 256 + wb;
+  if (need > r.cap) {
+    if (r.buf && hipHostFree(r.buf) != hipSuccess) return LORA_ERR_HIP;
+    r.buf = nullptr;
+    r.cap = 0;
+    const size_t cap = std::max(need, 2 * r.cap + (size_t(1) << 16));
+    if (hipHostMalloc(&r.buf, cap, hipHostMallocDefault) != hipSuccess) {
+      r.buf = nullptr;
+      return LORA_ERR_HIP;
+    }
+    r.cap = cap;
+  }
+  char* d = static_cast<char*>(r.buf);
+  std::memcpy(d, t->pieces.data(), pb);
+  std::memcpy(d + (pb + 255) / 256 * 256, t->writes.data(), wb);
+  lora_status st = pool_upload_batch(p, reinterpret_cast<const lora::UploadPiece*>(d),
+                                     static_cast<int32_t>(t->pieces.size()),
+                                     reinterpret_cast<const lora::EntryWrite*>(d + (pb + 255) / 256 * 256),
+                                     static_cast<int32_t>(t->writes.size()), s);
+  if (st == LORA_OK && hipEventRecord(r.ev, s) != hipSuccess) st = LORA_ERR_HIP;
+  r.serial = ++t->serial;
+  for (int32_t he : t->staged_he) {
+    t->he_serial[he] = r.serial;
+    t->he_ring[he] = static_cast<int8_t>(t->ring_next);
+  }
+  t->ring_next ^= 1;
+  t->pieces.clear();
+  t->writes.clear();
+  t->staged_he.clear();
+  return st;
+}
+
+// Before host entry he's buffer is overwritten: the staged batch (if it reads
+// it) is launched, and the last upload that read it has completed.
+lora_status free_host_entry(lora_tiers* t, lora_pool* p, int32_t he, hipStream_t s) {
+  for (int32_t e : t->staged_he)
+    if (e == he) {
+      const lora_status st = flush_uploads(t, p, s);
+      if (st != LORA_OK) return st;
+      break;
+    }
+  const UploadRing& r = t->ring[t->he_ring[he]];
+  if (t->he_serial[he] != 0 && r.serial == t->he_serial[he] && hipEventSynchronize(r.ev) != hipSuccess)
+    return LORA_ERR_HIP;
+  return LORA_OK;
+}
+
 // A GPU miss of adapter id in slot `slot`, host entry he: fill the host
-// buffer from the cold store if needed, evict the slot's previous adapter,
-// upload the new one on stream s (asynchronously, from the host buffer).
-lora_status serve_miss(lora_tiers* t, lora_pool* p, int32_t id, int32_t tier, int32_t slot, int32_t he,
+// buffer from the cold store if needed, then stage the eviction of the slot's
+// previous adapter and the uploads of the new one into the batch (flushed by
+// the caller: device work happens in flush_uploads).
+lora_status stage_miss(lora_tiers* t, lora_pool* p, int32_t id, int32_t tier, int32_t slot, int32_t he,
                        lora_fetch_fn fetch, void* ctx, hipStream_t s) {
   const int32_t nm = p->n_modules;
-  // the entry's buffers (rows, page lists) may still feed an earlier upload
-  if (t->pending[he] && hipEventSynchronize(t->done[he]) != hipSuccess) return LORA_ERR_HIP;
-  t->pending[he] = 0;
   char* buf = static_cast<char*>(t->pinned) + static_cast<size_t>(he) * t->entry_bytes;
   if (tier == LORA_TIER_COLD) {   // the caller's cold store fills the host buffer
+    lora_status st = free_host_entry(t, p, he, s);
+    if (st != LORA_OK) return st;
     char* q = buf;
     for (int32_t m = 0; m < nm; ++m) {
       int32_t r = 0;
@@ -263,26 +341,22 @@ lora_status serve_miss(lora_tiers* t, lora_pool* p, int32_t id, int32_t tier, in
       q += a_bytes_of(p, m) + b_bytes_of(p, m) + ids_bytes_of(p);
     }
   }
-  // the slot's previous adapter leaves (stream-ordered), the new one is copied in
-  bool loaded = false;
-  for (int32_t m = 0; m < nm; ++m) loaded = loaded || p->entries[static_cast<size_t>(slot) * nm + m].rank > 0;
-  if (loaded) {
-    const lora_status st = lora_pool_evict(p, slot, s);
-    if (st != LORA_OK) return st;
-  }
+  // the slot's previous adapter leaves; each module's entry is then written
+  // once in the batch: the new adapter's, or empty where it has none
+  pool_evict_host(p, slot);
   char* q = buf;
   for (int32_t m = 0; m < nm; ++m) {
     const int32_t r = t->rank[static_cast<size_t>(he) * nm + m];
     if (r > 0) {
-      const lora_status st =
-          pool_upload_async(p, slot, m, r, q, q + a_bytes_of(p, m), t->scale[static_cast<size_t>(he) * nm + m],
-                            reinterpret_cast<int32_t*>(q + a_bytes_of(p, m) + b_bytes_of(p, m)), s);
+      const lora_status st = pool_stage_upload(p, slot, m, r, q, q + a_bytes_of(p, m),
+                                               t->scale[static_cast<size_t>(he) * nm + m], t->pieces, t->writes);
       if (st != LORA_OK) return st;
+    } else {
+      t->writes.push_back(lora::EntryWrite{slot * nm + m, 0, lora::SlotEntry{0, 0.f, 0, 0}});
     }
     q += a_bytes_of(p, m) + b_bytes_of(p, m) + ids_bytes_of(p);
   }
-  if (hipEventRecord(t->done[he], s) != hipSuccess) return LORA_ERR_HIP;
-  t->pending[he] = 1;
+  t->staged_he.push_back(he);
   return LORA_OK;
 }
 
@@ -317,9 +391,14 @@ lora_status lora_tiers_acquire(lora_tiers* t, lora_pool* p, const int32_t* ids, 
     touch_one(t, ids[i], &tier, &slot, &ev, &he);
     slots[i] = slot;
     if (tier == LORA_TIER_GPU) continue;
-    st = serve_miss(t, p, ids[i], tier, slot, he, fetch, ctx, s);
-    if (st != LORA_OK) return st;
+    st = stage_miss(t, p, ids[i], tier, slot, he, fetch, ctx, s);
+    if (st != LORA_OK) {
+      (void)flush_uploads(t, p, s);   // what was staged before the error still goes out
+      return st;
+    }
   }
+  st = flush_uploads(t, p, s);
+  if (st != LORA_OK) return st;
   t->inflight = std::move(distinct);
   return LORA_OK;
 }
@@ -363,12 +442,17 @@ lora_status lora_tiers_prefetch(lora_tiers* t, lora_pool* p, const int32_t* ids,
     if (victim >= 0 && pinned.count(victim)) break;
     int32_t tier, slot, ev, he;
     touch_one(t, id, &tier, &slot, &ev, &he, false);
-    st = serve_miss(t, p, id, tier, slot, he, fetch, ctx, s);
-    if (st != LORA_OK) return st;
+    st = stage_miss(t, p, id, tier, slot, he, fetch, ctx, s);
+    if (st != LORA_OK) {
+      (void)flush_uploads(t, p, s);
+      return st;
+    }
     pinned[id] = 1;
     --free_slots;
     ++count;
   }
+  st = flush_uploads(t, p, s);
+  if (st != LORA_OK) return st;
   if (count > 0) {
     if (hipEventRecord(t->prefetch_ev, s) != hipSuccess) return LORA_ERR_HIP;
     t->prefetch_pending = true;
