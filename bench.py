@@ -516,6 +516,13 @@ def tiers_trace(args):
     print(json.dumps(out), flush=True)
 
 
+def sgmv_calls_of(dw):
+    """The library calls the harness's apply() makes for a workload."""
+    if not dw.sgmv_fused_calls():
+        return "lora_shrink + lora_expand"
+    return "lora_apply_sgmv" if len(dw._x_runs(*dw.groups[0])) == 1 else "lora_apply_sgmv_multi"
+
+
 def config_runs(DeviceWorkload, accounting, steps=20, warmup=3):
     """GPU apply time (the adapter term through the harness's calls: lora_apply_sgmv
     where one call covers the step, else lora_shrink + lora_expand; HIP events on the
@@ -554,7 +561,7 @@ def config_runs(DeviceWorkload, accounting, steps=20, warmup=3):
                      "tokens_per_s": round(wl.n_tokens / (stepm.mean() * 1e-3), 1),
                      "algorithmic_bytes": work["bytes"], "hbm_GBps": round(gbps, 1),
                      "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBS, 4), "input_sets": sets,
-                     "calls": "lora_apply_sgmv" if dws[0].sgmv_fused_calls() else "lora_shrink + lora_expand"}
+                     "calls": sgmv_calls_of(dws[0])}
         for d in dws:
             d.close()
         del dws

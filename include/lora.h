@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 6
+#define LORA_ABI_VERSION 7
 
 typedef int32_t lora_status;
 enum {
@@ -288,6 +288,33 @@ lora_status lora_apply_sgmv(const lora_pool *p, int32_t module0, int32_t n_modul
                             float *t, int64_t ld_t, int64_t module_stride_t,
                             void *y, int64_t ld_y, int64_t module_stride_y, lora_dtype ydtype,
                             void *ws, size_t ws_bytes, void *stream);
+
+/* One x run of lora_apply_sgmv_multi: n_modules consecutive modules whose x
+ * is [n_tokens][ld_x] each, module_stride_x elements apart (0: they share it,
+ * as q, k, v do). */
+typedef struct {
+    const void *x;
+    int64_t ld_x;
+    int64_t module_stride_x;
+    int32_t n_modules;
+} lora_x_run;
+
+/* lora_apply_sgmv for modules of one shape whose x comes in several runs (a
+ * layer's q, k, v sharing x beside o with its own): one shrink launch per run,
+ * all with the same K split, their partial tiles in one layout over the
+ * call's modules, then one expand launch over every module that adds them.
+ * runs[0..n_runs) cover module0 .. module0 + n_modules - 1 in order.  Same
+ * result as lora_shrink per run then one lora_expand, bit for bit when the
+ * runs' own splits agree (each run takes the smallest split any run chooses,
+ * so with unequal choices t's summation order can differ).  The workspace is
+ * lora_shrink_workspace_bytes(p, n_tokens, n_modules).  Other rules as
+ * lora_apply_sgmv.  Errors: ARG (also: runs that do not cover the modules),
+ * SHAPE, DTYPE, HIP; nothing is launched on an argument error. */
+lora_status lora_apply_sgmv_multi(const lora_pool *p, int32_t module0, int32_t n_modules,
+                                  const lora_x_run *runs, int32_t n_runs, const lora_segments *seg,
+                                  float *t, int64_t ld_t, int64_t module_stride_t,
+                                  void *y, int64_t ld_y, int64_t module_stride_y, lora_dtype ydtype,
+                                  void *ws, size_t ws_bytes, void *stream);
 
 /* Fused BGMV for decode (study page, "The kernel trick": a batched gather
  * matrix-vector product in which each decode token may bring its own

@@ -21,7 +21,7 @@ __all__ = [
     "lora_segments_bytes", "lora_segments_bind", "lora_build_segments",
     "lora_segments_check", "lora_shrink_workspace_bytes", "lora_shrink", "lora_shrink_noalloc",
     "LORA_NOALLOC_SCRATCH_BYTES",
-    "lora_expand", "lora_apply_sgmv", "lora_apply_bgmv", "lora_apply_bgmv_packed", "lora_fused_gemm", "lora_fused_gemm_fp8w",
+    "lora_expand", "lora_apply_sgmv", "lora_apply_sgmv_multi", "lora_x_run", "lora_apply_bgmv", "lora_apply_bgmv_packed", "lora_fused_gemm", "lora_fused_gemm_fp8w",
     "LORA_TIER_GPU", "LORA_TIER_HOST", "LORA_TIER_COLD", "lora_tiers_create", "lora_tiers_destroy",
     "lora_tiers_touch", "lora_tiers_stats", "lora_tiers_slot_of", "lora_tiers_acquire",
     "lora_tiers_batch_done", "lora_tiers_prefetch",
@@ -98,6 +98,8 @@ _SIGS = {
     "lora_expand": (_I32, [_P, _I32, _I32, _P, _I64, _I64, _SEGP, _P, _I64, _I64, _I32, _P]),
     "lora_apply_sgmv": (_I32, [_P, _I32, _I32, _P, _I64, _I64, _SEGP, _P, _I64, _I64, _P, _I64, _I64, _I32,
                                _P, _SZ, _P]),
+    "lora_apply_sgmv_multi": (_I32, [_P, _I32, _I32, _P, _I32, _SEGP, _P, _I64, _I64, _P, _I64, _I64, _I32,
+                                     _P, _SZ, _P]),
     "lora_apply_bgmv": (_I32, [_P, _I32, _I32, _P, _I64, _I64, _SEGP, _P, _I64, _I64, _I32, _P]),
     "lora_apply_bgmv_packed": (_I32, [_P, _I32, _I32, _P, _I64, _SEGP, _P, _I64, _I64, _I32, _P]),
     "lora_fused_gemm": (_I32, [_P, _I32, _P, _I64, _P, _I64, _P, _I32, _P, _I64, _P]),
@@ -263,6 +265,22 @@ def lora_apply_sgmv(pool: int, module0: int, n_modules: int, x, ld_x: int, modul
     _check(_lib.lora_apply_sgmv(pool, module0, n_modules, _ptr(x), ld_x, module_stride_x, ctypes.byref(seg),
                                 _ptr(t), ld_t, module_stride_t, _ptr(y), ld_y, module_stride_y, ydtype,
                                 _ptr(ws), ws_bytes, _stream(stream)), "lora_apply_sgmv")
+
+
+class lora_x_run(ctypes.Structure):
+    _fields_ = [("x", _P), ("ld_x", _I64), ("module_stride_x", _I64), ("n_modules", _I32)]
+
+
+def lora_apply_sgmv_multi(pool: int, module0: int, n_modules: int, runs, seg: lora_segments, t, ld_t: int,
+                          module_stride_t: int, y, ld_y: int, module_stride_y: int, ydtype: int, ws=None,
+                          ws_bytes: int = 0, stream=None) -> None:
+    """runs: (x, ld_x, module_stride_x, n_modules) per run of consecutive modules."""
+    arr = (lora_x_run * len(runs))(*[lora_x_run(_ptr(x), ld, ms, n) for (x, ld, ms, n) in runs])
+    if ws is not None and ws_bytes == 0 and hasattr(ws, "numel"):
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(_lib.lora_apply_sgmv_multi(pool, module0, n_modules, arr, len(runs), ctypes.byref(seg), _ptr(t), ld_t,
+                                      module_stride_t, _ptr(y), ld_y, module_stride_y, ydtype, _ptr(ws), ws_bytes,
+                                      _stream(stream)), "lora_apply_sgmv_multi")
 
 
 def lora_apply_bgmv(pool: int, module0: int, n_modules: int, x, ld_x: int, module_stride_x: int,

@@ -184,11 +184,14 @@ ShrinkSplit shrink_split(const lora_pool* p, int32_t module0, int32_t n_modules,
 
 // sp: the K split (shrink_split); ws holds its partial tiles when sp.ks > 1.  fold: the
 // partial tiles are left in ws for the expand to add (no k_shrink_reduce launch), so
-// the t rows of tokens in matrix-core tiles are not written.
+// the t rows of tokens in matrix-core tiles are not written; they sit at modules
+// part_m0 .. part_m0 + n_modules - 1 of a layout of part_nm modules (one call's
+// modules may come from several shrink launches).
 template <typename TI>
 lora_status launch_shrink(const lora_pool* p, int32_t module0, int32_t n_modules, const void* x, int64_t ld_x,
                           int64_t msx, const lora_segments* seg, float* t, int64_t ld_t, int64_t mst,
-                          ShrinkSplit sp, void* ws, hipStream_t s, bool fold = false) {
+                          ShrinkSplit sp, void* ws, hipStream_t s, bool fold = false, int32_t part_m0 = 0,
+                          int32_t part_nm = 0) {
   const PoolView pv = p->view();
   const SegView sv = seg_view(seg);
   const int32_t h_in = static_cast<int32_t>(p->h_in[module0]);
@@ -239,6 +242,8 @@ lora_status launch_shrink(const lora_pool* p, int32_t module0, int32_t n_modules
       a.kc = ((kps + n_sub - 1) / n_sub + 31) / 32 * 32;
       const size_t lds = std::max(stream_lds_bytes(per_wg, ntiles, a.kc, a.max_pids), gemv_lds_bytes<1, __bf16>());
       a.part = ks > 1 ? static_cast<float*>(ws) : nullptr;
+      a.part_m0 = fold ? part_m0 : 0;
+      a.part_nm = fold && part_nm > 0 ? part_nm : n_modules;   // k_shrink_reduce reads this launch's layout
       const int tnx = static_cast<int>(tile_grid_of(seg->max_tiles));
       const int64_t n_blocks = static_cast<int64_t>(tnx) * ks * groups + static_cast<int64_t>(gx) * n_modules;
       if (!grid_fits(n_blocks, kMfmaThreads)) return LORA_ERR_SHAPE;   // beyond one launch (nothing launched yet)
@@ -480,13 +485,15 @@ lora_status shrink_checks(const lora_pool* p, int32_t module0, int32_t n_modules
   return check_operand(t, ld_t, mst, p->max_rank, 4, n, n_modules, true, true);
 }
 
-// A checked shrink call on the current device (fold as for launch_shrink).
+// A checked shrink call on the current device (fold, part_m0, part_nm as for launch_shrink).
 lora_status shrink_call(const lora_pool* p, int32_t module0, int32_t n_modules, const void* x, int64_t ld_x,
                         int64_t msx, const lora_segments* seg, float* t, int64_t ld_t, int64_t mst, ShrinkSplit sp,
-                        void* ws, hipStream_t s, bool fold = false) {
+                        void* ws, hipStream_t s, bool fold = false, int32_t part_m0 = 0, int32_t part_nm = 0) {
   if (p->dtype == LORA_BF16)
-    return launch_shrink<__bf16>(p, module0, n_modules, x, ld_x, msx, seg, t, ld_t, mst, sp, ws, s, fold);
-  return launch_shrink<float>(p, module0, n_modules, x, ld_x, msx, seg, t, ld_t, mst, sp, ws, s, fold);
+    return launch_shrink<__bf16>(p, module0, n_modules, x, ld_x, msx, seg, t, ld_t, mst, sp, ws, s, fold, part_m0,
+                                 part_nm);
+  return launch_shrink<float>(p, module0, n_modules, x, ld_x, msx, seg, t, ld_t, mst, sp, ws, s, fold, part_m0,
+                              part_nm);
 }
 
 // Argument checks of the expand calls (modules of one shape).
@@ -661,20 +668,55 @@ lora_status lora_apply_sgmv(const lora_pool* p, int32_t module0, int32_t n_modul
                             int64_t module_stride_x, const lora_segments* seg, float* t, int64_t ld_t,
                             int64_t module_stride_t, void* y, int64_t ld_y, int64_t module_stride_y,
                             lora_dtype ydtype, void* ws, size_t ws_bytes, void* stream) {
-  lora_status st = shrink_checks(p, module0, n_modules, x, ld_x, module_stride_x, seg, t, ld_t, module_stride_t);
+  const lora_x_run run{x, ld_x, module_stride_x, n_modules};
+  return lora_apply_sgmv_multi(p, module0, n_modules, &run, 1, seg, t, ld_t, module_stride_t, y, ld_y,
+                               module_stride_y, ydtype, ws, ws_bytes, stream);
+}
+
+lora_status lora_apply_sgmv_multi(const lora_pool* p, int32_t module0, int32_t n_modules, const lora_x_run* runs,
+                                  int32_t n_runs, const lora_segments* seg, float* t, int64_t ld_t,
+                                  int64_t module_stride_t, void* y, int64_t ld_y, int64_t module_stride_y,
+                                  lora_dtype ydtype, void* ws, size_t ws_bytes, void* stream) {
+  if (!runs || n_runs < 1 || n_runs > n_modules) return LORA_ERR_ARG;
+  lora_status st = expand_checks(p, module0, n_modules, t, ld_t, module_stride_t, seg, y, ld_y, module_stride_y,
+                                 ydtype);
   if (st != LORA_OK) return st;
-  st = expand_checks(p, module0, n_modules, t, ld_t, module_stride_t, seg, y, ld_y, module_stride_y, ydtype);
-  if (st != LORA_OK) return st;
+  int32_t m = module0;
+  for (int32_t r = 0; r < n_runs; ++r) {   // consecutive runs covering the modules, each with its x
+    if (runs[r].n_modules < 1 || m + runs[r].n_modules > module0 + n_modules) return LORA_ERR_ARG;
+    st = shrink_checks(p, m, runs[r].n_modules, runs[r].x, runs[r].ld_x, runs[r].module_stride_x, seg,
+                       t + static_cast<int64_t>(m - module0) * module_stride_t, ld_t, module_stride_t);
+    if (st != LORA_OK) return st;
+    m += runs[r].n_modules;
+  }
+  if (m != module0 + n_modules) return LORA_ERR_ARG;
   if (ws_bytes > 0 && (!ws || !aligned16(ws))) return LORA_ERR_ARG;
   if (seg->n_tokens == 0) return LORA_OK;
   DeviceGuard g(p->device);
   if (!g.ok) return LORA_ERR_HIP;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const ShrinkSplit sp = shrink_split(p, module0, n_modules, module_stride_x, seg, ws_bytes);
+  // one K split for every run (the expand adds one set of splits per module): the
+  // smallest the runs choose, then as small as the workspace needs for all modules
+  int32_t ks = kMaxSplits;
+  m = module0;
+  for (int32_t r = 0; r < n_runs; ++r) {
+    ks = std::min(ks, shrink_split(p, m, runs[r].n_modules, runs[r].module_stride_x, seg, SIZE_MAX).ks);
+    m += runs[r].n_modules;
+  }
+  while (ks > 1 && split_ws_bytes(p, seg->n_tokens, n_modules, ks) > ws_bytes) --ks;
+  const int32_t h_in = static_cast<int32_t>(p->h_in[module0]);
+  const int32_t kps = ((h_in + ks - 1) / ks + 31) / 32 * 32;
+  const ShrinkSplit sp{(h_in + kps - 1) / kps, kps};
   // partial tiles exist only where the shrink splits K, on its matrix-core tiles
   const bool fold = sp.ks > 1 && shrink_has_tiles(p, module0, seg);
-  st = shrink_call(p, module0, n_modules, x, ld_x, module_stride_x, seg, t, ld_t, module_stride_t, sp, ws, s, fold);
-  if (st != LORA_OK) return st;
+  m = module0;
+  for (int32_t r = 0; r < n_runs; ++r) {
+    st = shrink_call(p, m, runs[r].n_modules, runs[r].x, runs[r].ld_x, runs[r].module_stride_x, seg,
+                     t + static_cast<int64_t>(m - module0) * module_stride_t, ld_t, module_stride_t, sp, ws, s, fold,
+                     m - module0, n_modules);
+    if (st != LORA_OK) return st;
+    m += runs[r].n_modules;
+  }
   return expand_call(p, module0, n_modules, t, ld_t, module_stride_t, seg, y, ld_y, module_stride_y, ydtype, s,
                      fold ? static_cast<const float*>(ws) : nullptr, sp.ks);
 }

@@ -59,7 +59,8 @@ struct ShrinkArgs {
   int32_t kc;                 // K of A rows staged in LDS at a time (multiple of 32)
   int32_t ldr;                // rank rows per module in LDS and columns of a partial tile (multiple of 16)
   int32_t max_pids;           // page ids per entry in LDS
-  float* part;                // [tiles][groups][mods_per_wg][ks_count][64][ldr]
+  float* part;                // partial tiles [tile][part_nm][ks_count][64][ldr]; this launch's
+  int32_t part_m0, part_nm;   // module m at part_m0 + m of part_nm (a call's modules may span launches)
 };
 
 #ifndef LORA_STAGE_BATCH
@@ -255,7 +256,7 @@ __device__ __forceinline__ void shrink_stream_body(const ShrinkArgs& a, const Bl
     // split K: this split's partial tile goes to the workspace; k_shrink_reduce
     // (the next launch on the stream) adds the splits in order
     const int64_t tile_block = static_cast<int64_t>(kTileTokens) * a.ldr;
-    const int64_t base_tg = (static_cast<int64_t>(tile) * groups + grp) * MODS;
+    const int64_t base_tg = static_cast<int64_t>(tile) * a.part_nm + a.part_m0 + grp * MODS;
 #pragma unroll
     for (int mi = 0; mi < MODS; ++mi) {
       float* pp = a.part + ((base_tg + mi) * a.ks_count + ks) * tile_block;

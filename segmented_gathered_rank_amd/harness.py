@@ -15,8 +15,8 @@ from typing import List, Optional, Tuple
 import numpy as np
 import torch
 
-from . import (LORA_BF16, LORA_F32, lora_apply_bgmv, lora_apply_bgmv_packed, lora_apply_sgmv, lora_build_segments,
-               lora_expand,
+from . import (LORA_BF16, LORA_F32, lora_apply_bgmv, lora_apply_bgmv_packed, lora_apply_sgmv, lora_apply_sgmv_multi,
+               lora_build_segments, lora_expand,
                lora_fused_gemm, lora_fused_gemm_fp8w,
                lora_pool_create, lora_pool_destroy, lora_pool_load, lora_segments_bind,
                lora_segments_bytes, lora_shrink, lora_shrink_workspace_bytes)
@@ -180,24 +180,31 @@ class DeviceWorkload:
                         y.stride(0), ydt, stream)
 
     def sgmv(self, stream=None):
-        """Shrink and expand through lora_apply_sgmv: one call per run of modules that
-        share a shape and step uniformly through x."""
+        """Shrink and expand through lora_apply_sgmv (one x run) or lora_apply_sgmv_multi
+        (several: q, k, v sharing x beside o): one call per run of modules of one shape."""
         ydt = LORA_BF16 if self.y_dtype == "bf16" else LORA_F32
         mods = self.wl.modules
         t = self.t
         for gi, (m0, m1) in enumerate(self.groups):
             y = self.y[gi]
-            for (a, b, xo, msx) in self._x_runs(m0, m1):
-                yp = y.data_ptr() + (a - m0) * y.stride(0) * y.element_size()
-                lora_apply_sgmv(self.pool, a, b - a, self._xp(xo), mods[m0].h_in, msx, self.seg, t[a], self.ld_t,
-                                t.stride(0), yp, mods[m0].h_out, y.stride(0), ydt, self.ws, self.ws_bytes, stream)
+            h_in, h_out = mods[m0].h_in, mods[m0].h_out
+            runs = self._x_runs(m0, m1)
+            if len(runs) == 1:
+                a, b, xo, msx = runs[0]
+                lora_apply_sgmv(self.pool, a, b - a, self._xp(xo), h_in, msx, self.seg, t[a], self.ld_t,
+                                t.stride(0), y, h_out, y.stride(0), ydt, self.ws, self.ws_bytes, stream)
+            else:
+                lora_apply_sgmv_multi(self.pool, m0, m1 - m0, [(self._xp(xo), h_in, msx, b - a)
+                                                               for (a, b, xo, msx) in runs],
+                                      self.seg, t[m0], self.ld_t, t.stride(0), y, h_out, y.stride(0), ydt,
+                                      self.ws, self.ws_bytes, stream)
 
     def sgmv_fused_calls(self) -> bool:
-        """Whether apply() takes lora_apply_sgmv: when one call covers every module
-        (one shape, x stepping uniformly).  Where modules need several shrink or
-        expand calls, lora_shrink and lora_expand group them better (one shrink for
-        q, k, v and another for o, then one expand for all four)."""
-        return len(self.groups) == 1 and len(self._x_runs(*self.groups[0])) == 1
+        """Whether apply() takes the combined calls: when the modules have one shape (one
+        call covers the step).  Modules of several shapes (an encoder layer's qkv, o,
+        up and down) are better served by lora_shrink over each run of equal h_in and
+        lora_expand over each shape."""
+        return len(self.groups) == 1
 
     def apply(self, stream=None):
         """The adapter term of every module added to y: lora_apply_sgmv calls where

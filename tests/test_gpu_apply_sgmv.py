@@ -64,9 +64,10 @@ def _assert_same_bits(a, b, what):
 
 @pytest.mark.parametrize("name", ["c3", "c4"])
 def test_full_size_same_bits_as_two_calls(name):
-    """The mixed-rank batch (17 tiles, rank cap 64) and a prefill of 4096 tokens on
-    q, k, v (one call) and o (another): both split K 8 ways and sum the splits in the
-    expand."""
+    """The mixed-rank batch (17 tiles, rank cap 64; lora_apply_sgmv) and a prefill of
+    4096 tokens on q, k, v sharing x beside o (lora_apply_sgmv_multi: two shrink launches
+    into one partial layout, one expand over the four modules): both split K 8 ways and
+    sum the splits in the expand."""
     wl = (W.c3_sgmv_prefill if name == "c3" else W.c4_mixed_rank)(draw_w=False)
     say(f"{name}: lora_apply_sgmv vs lora_shrink + lora_expand")
     fused, calls = _both(wl, folded=True)
@@ -156,3 +157,20 @@ def test_argument_errors_launch_nothing():
     torch.cuda.synchronize()
     assert torch.equal(y_before.view(torch.int16), dw.y_of(0).view(torch.int16))
     dw.close()
+
+
+def test_multi_runs_must_cover_the_modules():
+    wl = W.c3_sgmv_prefill(h=4096, rank=16, units=(2, 8), total_units=32)
+    dw = DeviceWorkload(wl)
+    dw.build_segments()
+    torch.cuda.synchronize()
+    y = dw.y[0]
+    qkv = (dw._xp(dw.x_off[0]), 4096, 0, 3)
+    o = (dw._xp(dw.x_off[1]), 4096, 0, 1)
+    for runs in ([qkv], [qkv, o, o], [(qkv[0], 4096, 0, 0), qkv, o], []):
+        with pytest.raises(sgr.LoraError) as ei:
+            sgr.lora_apply_sgmv_multi(dw.pool, 0, 4, runs, dw.seg, dw.t[0], dw.ld_t, dw.t.stride(0), y, 4096,
+                                      y.stride(0), sgr.LORA_BF16, dw.ws, dw.ws_bytes)
+        assert ei.value.status == -1, len(runs)
+    dw.close()
+
