@@ -461,12 +461,16 @@ lora_status launch_bgmv(const lora_pool* p, int32_t module0, int32_t n_modules, 
     hipLaunchKernelGGL((k_bgmv_packed<TI, TO>), dim3(gx, 1), dim3(kGemvThreads), 0, s, g);
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
   }
+  // several modules: one 1-D grid taken in groups of up to kBgmvModuleGroup modules.  There a
+  // workgroup's unit is its place inside the group, so the grid needs no period: one
+  // workgroup per unit the segments can hold (fewer empty workgroups between the groups)
+  const unsigned gxg = static_cast<unsigned>(std::min<int32_t>(std::max<int32_t>(seg->max_units, 1), kGemvMaxGrid));
   if (n_modules >= kBgmvGroupedFrom &&
-      static_cast<int64_t>(n_modules) * gx * kGemvThreads <= static_cast<int64_t>(UINT32_MAX)) {
-    // several modules: one 1-D grid taken in groups of up to kBgmvModuleGroup modules
+      static_cast<int64_t>(n_modules) * gxg * kGemvThreads <= static_cast<int64_t>(UINT32_MAX)) {
     g.module_group = std::min(kBgmvModuleGroup, n_modules);
-    g.group_nx = static_cast<int32_t>(gx);
-    hipLaunchKernelGGL((k_gemv<0, TI, TO>), dim3(gx * static_cast<unsigned>(n_modules)), dim3(kGemvThreads), 0, s, g);
+    g.group_nx = static_cast<int32_t>(gxg);
+    hipLaunchKernelGGL((k_gemv<0, TI, TO>), dim3(gxg * static_cast<unsigned>(n_modules)), dim3(kGemvThreads), 0, s,
+                       g);
   } else {
     hipLaunchKernelGGL((k_gemv<0, TI, TO>), dim3(gx, n_modules), dim3(kGemvThreads), 0, s, g);
   }
