@@ -401,6 +401,87 @@ __device__ __forceinline__ int rows_total(const int32_t* hist, int n_slots, int 
   return run;
 }
 
+// ------------------------------------------------------------ one wave, up to 64 tokens
+// A decode batch: lane i holds token i.  A token's place in perm is the
+// number of valid tokens of smaller slots plus its rank among its slot's
+// tokens (ballot match per id bit); a segment's first token (its slot's
+// lowest lane) writes the segment's entries, which need the count of smaller
+// slots' segments, tokens, units and tiles: summed over the segments' first
+// lanes only, one packed word each.  The same output as the workgroup kernels
+// without their histogram, barriers and layout phases.
+constexpr int kTinyTokens = 64;
+__global__ __launch_bounds__(64) void k_segments_tiny(const int32_t* __restrict__ ids, int32_t n_tokens,
+                                                      int32_t n_slots, int32_t nbits, Out o) {
+  const int lane = threadIdx.x;
+  const bool in = lane < n_tokens;
+  const int id = in ? ids[lane] : -1;
+  const bool valid = in && id >= 0 && id < n_slots;
+  const int n_bad = __popcll(__ballot(in && (id < -1 || id >= n_slots)));
+  const uint64_t peers = peers_of(id, valid, nbits);   // lanes of the same slot (0 if invalid)
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  const int len = __popcll(peers);
+  const bool first = valid && (peers & below) == 0ull;
+  const bool is_long = len >= kLongMin;
+  const int nu = (len + kUnitTokens - 1) / kUnitTokens;
+  const int nt = is_long ? (len + kTileTokens - 1) / kTileTokens : 0;
+  // a first lane's contribution, 7 bits a field (every sum stays below 128 at 64 tokens; the
+  // tile count keeps the top 4 bits: only a segment of all 64 tokens has a tile):
+  // 1 segment | its tokens | its short-segment units | its long-segment units | its tiles
+  const uint32_t mine = first ? 1u | (static_cast<uint32_t>(len) << 7) | (static_cast<uint32_t>(is_long ? 0 : nu) << 14) |
+                                    (static_cast<uint32_t>(is_long ? nu : 0) << 21) |
+                                    (static_cast<uint32_t>(nt) << 28)
+                              : 0u;
+  uint32_t before = 0;   // the same sums over the segments of smaller slots
+  for (uint64_t fm = __ballot(first); fm; fm &= fm - 1) {
+    const int j = lowest_lane(fm);
+    const int idj = __builtin_amdgcn_readlane(id, j);
+    const uint32_t pj = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mine), j));
+    if (valid && idj < id) before += pj;
+  }
+  const int seg = before & 127, start = (before >> 7) & 127, su = (before >> 14) & 127;
+  const int lu = (before >> 21) & 127, tl = static_cast<int>(before >> 28);
+  if (valid) o.perm[start + __popcll(peers & below)] = lane;
+  const int n_seg = __popcll(__ballot(first));
+  const int n_active = __popcll(__ballot(valid));
+  const int n_short = lane63(wave_scan<false>(first && !is_long ? nu : 0));
+  const int n_long_units = lane63(wave_scan<false>(first && is_long ? nu : 0));
+  const int n_tiles = lane63(wave_scan<false>(first ? nt : 0));
+  const int max_len = lane63(wave_scan<true>(len));
+  if (first) {
+    o.seg_slot[seg] = id;
+    o.seg_start[seg] = start;
+    int2* units = reinterpret_cast<int2*>(o.units);
+    if (!is_long) {
+      for (int u = 0; u < nu; ++u) units[su + u] = unit_record(id, len, u, start);
+    } else {
+      for (int u = 0; u < nu; ++u) units[n_short + lu + u] = unit_record(id, len, u, start);
+      int2* tiles = reinterpret_cast<int2*>(o.tiles);
+      for (int u = 0; u < nt; ++u)
+        tiles[tl + u] = make_int2(id + (min(kTileTokens, len - u * kTileTokens) << 16), start + u * kTileTokens);
+    }
+  }
+  if (lane == 0) o.seg_start[n_seg] = n_active;
+  if (lane < LORA_META_WORDS) {   // one store for the whole meta block
+    int v = 0;
+    switch (lane) {
+      case LORA_META_N_SEG: v = n_seg; break;
+      case LORA_META_N_ACTIVE: v = n_active; break;
+      case LORA_META_MAX_SEG_LEN: v = max_len; break;
+      case LORA_META_N_BAD: v = n_bad; break;
+      case LORA_META_N_UNITS_SHORT: v = n_short; break;
+      case LORA_META_N_UNITS_ALL: v = n_short + n_long_units; break;
+      case LORA_META_N_TILES: v = n_tiles; break;
+      case LORA_META_UNIT_TOKENS: v = kUnitTokens; break;
+      case LORA_META_TILE_TOKENS: v = kTileTokens; break;
+      case LORA_META_LONG_MIN: v = kLongMin; break;
+      case LORA_META_N_TOKENS: v = n_tokens; break;
+      case LORA_META_N_SLOTS: v = n_slots; break;
+      default: v = 0; break;
+    }
+    o.meta[lane] = v;
+  }
+}
+
 // ------------------------------------------------------------ one workgroup
 // TH threads (V <= TH / 64 histogram rows).  Every thread runs the layout's
 // code, so a small batch takes a small workgroup: with 1024 threads the
@@ -665,7 +746,9 @@ lora_status lora_build_segments(const int32_t* ids, const lora_segments* seg, vo
   if (!set_lds_limit()) return LORA_ERR_HIP;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const Out o{seg->perm, seg->seg_start, seg->seg_slot, seg->meta, seg->units, seg->tiles};
-  if (G == 0) {
+  if (G == 0 && n <= kTinyTokens) {
+    hipLaunchKernelGGL(k_segments_tiny, dim3(1), dim3(64), 0, st, ids, n, n_slots, nbits, o);
+  } else if (G == 0) {
     const int th = one_group_threads(n, n_slots);
     const int32_t v = std::min<int32_t>(V, th / 64);
     const size_t lds = static_cast<size_t>(v + 1) * n_slots * 4;

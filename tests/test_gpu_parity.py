@@ -79,6 +79,12 @@ SEG_CASES = {
     "quad_max": (np.random.default_rng(33).integers(-1, 1024, 2048), 1024),
     "quad_long_and_short": (np.concatenate([np.repeat([5, 9], 700), np.arange(600) % 50]), 64),
     "sixteen_from": (np.random.default_rng(34).integers(-1, 64, 2049), 64),
+    # batches of up to 64 tokens take one wave with a token per lane (k_segments_tiny): one
+    # long segment (64 tokens of one id: units and a tile), the same with bad ids, 8,192 slots
+    "tiny_long": ([5] * 64, 8),
+    "tiny_long_minus": ([5] * 62 + [-1, 9], 8),
+    "tiny_max_slots": (np.random.default_rng(35).integers(-1, 8192, 63), 8192),
+    "tiny_runs": (np.repeat(np.random.default_rng(36).integers(0, 5, 16), 4), 5),
 }
 
 
