@@ -135,16 +135,29 @@ struct UnitLds {
 
 // Copies x[tok][k0 .. k0+len) of the unit's tokens into xs[tb][0 .. len);
 // stream: streaming loads (no other work item of the launch reads these rows).
+// The x rows of a unit go straight from memory into LDS (global_load_lds: no
+// registers, no wait between loads), so the slice lands in one round trip.
+// Wave w takes the 64-chunk groups w, w + W, ... of the rows; one instruction
+// moves a group (lane i lands at byte 16 i of the group's LDS base; lanes past
+// the row stay idle).  The barrier after it waits for these loads.
+constexpr int kCpolNt = 2;   // cache-policy bit of a non-temporal load
 template <typename TI>
 __device__ __forceinline__ void stage_x(const TI* __restrict__ x, int64_t ld_x, const int32_t* toks, int nt,
                                         int k0, int len, TI* xs, bool stream) {
   constexpr int V = 16 / sizeof(TI);
   constexpr int S = XSlice<TI>::kElems;
-  const int per_tok = len / V;
-  for (int i = threadIdx.x; i < nt * per_tok; i += kGemvThreads) {
-    const int tb = i / per_tok, c = (i - tb * per_tok) * V;
-    const u32x4* src = reinterpret_cast<const u32x4*>(x + static_cast<int64_t>(toks[tb]) * ld_x + k0 + c);
-    *reinterpret_cast<u32x4*>(xs + tb * S + c) = stream ? ld16<true>(src) : ld16<false>(src);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int per_tok = len / V;                 // 16-byte chunks per row
+  const int groups = (per_tok + 63) >> 6;      // 64-chunk groups per row
+  for (int gi = wave; gi < nt * groups; gi += kGemvWaves) {   // wave-uniform
+    const int tb = gi / groups, g = gi - tb * groups;
+    const int c = 64 * g + lane;
+    if (c < per_tok) {
+      const void* src = x + static_cast<int64_t>(toks[tb]) * ld_x + k0 + c * V;
+      const lds_addr_t dst = to_lds(xs + tb * S + 64 * g * V);
+      if (stream) __builtin_amdgcn_global_load_lds(src, dst, 16, 0, kCpolNt);
+      else __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+    }
   }
 }
 
