@@ -556,20 +556,18 @@ __global__ __launch_bounds__(kThreads) void k_seg_count(const int32_t* __restric
   if (tid == 0) bad_of[g] = bad_cell;
 }
 
-// One workgroup: per slot, the exclusive prefix of the chunk counts
-// (coff[g][s] = chunk g's first position within slot s) and the slot total;
-// then the layout; slot_base[s] = first position of slot s in perm.  Thread
-// tid takes slots tid + k * kThreads (k < kBpt) and keeps 32 counter loads in
-// flight: the counters come from other XCDs' L2 slices, so each round trip is
-// long.
-template <int kBpt>
-__global__ __launch_bounds__(kThreads) void k_seg_scan(int32_t n_tokens, int32_t n_slots, int32_t n_chunks,
-                                                       const int32_t* __restrict__ cnt, int32_t* __restrict__ coff,
-                                                       const int32_t* __restrict__ bad_of,
-                                                       int32_t* __restrict__ slot_base, Out o) {
-  extern __shared__ int32_t total[];   // [n_slots]
-  __shared__ LayoutLds<kWaves> L;
-  __shared__ int bad_cell;
+// One workgroup: per slot, the sum of the chunk counts (OFFSETS: also their
+// exclusive prefix, coff[g][s] = chunk g's first position within slot s);
+// then the layout (OFFSETS: with slot_base[s] = first position of slot s in
+// perm).  Thread tid takes slots tid + k * kThreads (k < kBpt) and keeps 32
+// counter loads in flight: the counters come from other XCDs' L2 slices, so
+// each round trip is long.
+template <int kBpt, bool OFFSETS>
+__device__ __forceinline__ void totals_and_layout(int32_t n_tokens, int32_t n_slots, int32_t n_chunks,
+                                                  const int32_t* __restrict__ cnt, int32_t* __restrict__ coff,
+                                                  const int32_t* __restrict__ bad_of,
+                                                  int32_t* __restrict__ slot_base, Out o, int32_t* total,
+                                                  LayoutLds<kWaves>& L, int& bad_cell) {
   const int tid = threadIdx.x, lane = tid & 63;
   if (tid == 0) bad_cell = 0;
   __syncthreads();
@@ -594,10 +592,10 @@ __global__ __launch_bounds__(kThreads) void k_seg_scan(int32_t n_tokens, int32_t
 #pragma unroll
     for (int j = 0; j < kG; ++j) {
       if (g0 + j < n_chunks) {
-        int32_t* row = coff + static_cast<size_t>(g0 + j) * n_slots;
+        int32_t* row = OFFSETS ? coff + static_cast<size_t>(g0 + j) * n_slots : nullptr;
 #pragma unroll
         for (int k = 0; k < kBpt; ++k) {
-          if (tid + k * kThreads < n_slots) row[tid + k * kThreads] = run[k];
+          if (OFFSETS && tid + k * kThreads < n_slots) row[tid + k * kThreads] = run[k];
           run[k] += c[j][k];
         }
       }
@@ -610,8 +608,20 @@ __global__ __launch_bounds__(kThreads) void k_seg_scan(int32_t n_tokens, int32_t
   const int bpt = (n_slots + kThreads - 1) / kThreads;
   const int s0 = min(n_slots, tid * bpt);
   const int s1 = min(n_slots, s0 + bpt);
-  layout_segments<kThreads>(total, n_tokens, n_slots, s0, s1, bpt, bad_cell, o, L,
-                  [&](int s, int base) { slot_base[s] = base; });
+  layout_segments<kThreads>(total, n_tokens, n_slots, s0, s1, bpt, bad_cell, o, L, [&](int s, int base) {
+    if constexpr (OFFSETS) slot_base[s] = base;
+  });
+}
+
+template <int kBpt>
+__global__ __launch_bounds__(kThreads) void k_seg_scan(int32_t n_tokens, int32_t n_slots, int32_t n_chunks,
+                                                       const int32_t* __restrict__ cnt, int32_t* __restrict__ coff,
+                                                       const int32_t* __restrict__ bad_of,
+                                                       int32_t* __restrict__ slot_base, Out o) {
+  extern __shared__ int32_t total[];   // [n_slots]
+  __shared__ LayoutLds<kWaves> L;
+  __shared__ int bad_cell;
+  totals_and_layout<kBpt, true>(n_tokens, n_slots, n_chunks, cnt, coff, bad_of, slot_base, o, total, L, bad_cell);
 }
 
 // Rows, cursors and scatter inside chunk g, starting from the chunk's offsets.
@@ -660,6 +670,107 @@ __global__ __launch_bounds__(kThreads) void k_seg_scatter(const int32_t* __restr
   }
 }
 
+// The chunked schedule in two launches, for at most kPlaceWords chunk
+// counters: after k_seg_count, workgroup 0 sums each slot's counts and lays out
+// the segments, units and tiles (as k_seg_scan, without the offsets), while
+// workgroup 1 + g counts chunk g's rows, derives from the counters each slot's
+// first position in perm (the exclusive prefix of the slot totals) and the
+// chunk's offset within it (the counts of chunks before g), and scatters the
+// chunk.  The layout is then off the scatter's critical path, and no launch
+// waits for it.
+constexpr int kPlaceWords = 1 << 16;
+template <int kBpt>
+__global__ __launch_bounds__(kThreads) void k_seg_place(const int32_t* __restrict__ ids, int32_t n_tokens,
+                                                        int32_t n_slots, int32_t V, int32_t nbits, int32_t chunk,
+                                                        int32_t n_chunks, const int32_t* __restrict__ cnt,
+                                                        const int32_t* __restrict__ bad_of, Out o) {
+  extern __shared__ int32_t lds[];   // chunk: rows [V][n_slots], slot bases [n_slots]; layout: totals
+  __shared__ LayoutLds<kWaves> L;
+  __shared__ int bad_cell;
+  if (blockIdx.x == 0) {   // uniform
+    totals_and_layout<kBpt, false>(n_tokens, n_slots, n_chunks, cnt, nullptr, bad_of, nullptr, o, lds, L, bad_cell);
+    return;
+  }
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = static_cast<int>(blockIdx.x) - 1;
+  int32_t* hist = lds;
+  int32_t* sbase = lds + V * n_slots;
+  const int cb = g * chunk, ce = min(n_tokens, cb + chunk);
+  for (int i = tid; i < V * n_slots; i += kThreads) hist[i] = 0;
+  __syncthreads();
+  const int span = ((ce - cb + V - 1) / V + 63) / 64 * 64;
+  const int beg = min(ce, cb + wave * span);
+  const int end = min(ce, beg + span);
+  int32_t* row = hist + min(wave, V - 1) * n_slots;
+  int idv[kIdBatch];
+  for (int base = beg; base < end; base += kRound) {
+    load_ids(ids, base, end, lane, idv);
+    count_round(idv, base, end, lane, n_slots, row);
+  }
+  // per slot: the total over all chunks, the counts of the chunks before g, and
+  // chunk g's own count (32 counter loads in flight per thread)
+  constexpr int kG = 32 / kBpt;
+  int sl[kBpt], tot[kBpt], pre[kBpt], cg[kBpt];
+#pragma unroll
+  for (int k = 0; k < kBpt; ++k) {
+    sl[k] = min(tid + k * kThreads, n_slots - 1);
+    tot[k] = pre[k] = cg[k] = 0;
+  }
+  for (int g0 = 0; g0 < n_chunks; g0 += kG) {
+    int c[kG][kBpt];
+#pragma unroll
+    for (int j = 0; j < kG; ++j) {
+      const int32_t* crow = cnt + static_cast<size_t>(min(g0 + j, n_chunks - 1)) * n_slots;
+#pragma unroll
+      for (int k = 0; k < kBpt; ++k) c[j][k] = crow[sl[k]];
+    }
+#pragma unroll
+    for (int j = 0; j < kG; ++j) {
+      const int gj = g0 + j;
+#pragma unroll
+      for (int k = 0; k < kBpt; ++k) {
+        const int v = gj < n_chunks ? c[j][k] : 0;
+        tot[k] += v;
+        pre[k] += gj < g ? v : 0;
+        cg[k] = gj == g ? v : cg[k];
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kBpt; ++k)
+    if (tid + k * kThreads < n_slots) sbase[tid + k * kThreads] = tot[k];
+  __syncthreads();
+  // exclusive prefix of the slot totals, in place: thread tid takes slots s0 .. s1 - 1
+  {
+    const int bpt = (n_slots + kThreads - 1) / kThreads;
+    const int s0 = min(n_slots, tid * bpt), s1 = min(n_slots, s0 + bpt);
+    int sum = 0;
+    for (int s = s0; s < s1; ++s) sum += sbase[s];
+    const int incl = wave_scan<false>(sum);
+    if (lane == 63) L.wsum[wave][0] = incl;
+    __syncthreads();
+    int run = incl - sum;
+    for (int w = 0; w < wave; ++w) run += L.wsum[w][0];
+    for (int s = s0; s < s1; ++s) {
+      const int v = sbase[s];
+      sbase[s] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kBpt; ++k) {
+    const int s = tid + k * kThreads;
+    if (s < n_slots && cg[k] > 0) rows_to_cursors<kWaves>(hist, n_slots, V, s, sbase[s] + pre[k]);
+  }
+  __syncthreads();
+  const bool one_round = end - beg <= kRound;
+  for (int base = beg; base < end; base += kRound) {
+    if (!one_round) load_ids(ids, base, end, lane, idv);
+    scatter_round(idv, base, end, lane, n_slots, nbits, row, o.perm);
+  }
+}
+
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
 template <class K>
@@ -671,7 +782,8 @@ bool set_lds_limit() {   // gfx950 allows 160 KiB of LDS per workgroup; these us
   static const bool ok = lds_limit(&k_segments_one<64>) && lds_limit(&k_segments_one<256>) &&
                          lds_limit(&k_segments_one<1024>) && lds_limit(&k_seg_scatter<1>) &&
                          lds_limit(&k_seg_scatter<2>) && lds_limit(&k_seg_scatter<4>) &&
-                         lds_limit(&k_seg_scatter<8>);
+                         lds_limit(&k_seg_scatter<8>) && lds_limit(&k_seg_place<1>) &&
+                         lds_limit(&k_seg_place<2>) && lds_limit(&k_seg_place<4>) && lds_limit(&k_seg_place<8>);
   return ok;
 }
 
@@ -767,11 +879,19 @@ lora_status lora_build_segments(const int32_t* ids, const lora_segments* seg, vo
     const size_t row_bytes = static_cast<size_t>(n_slots) * 4;
     const size_t rows_bytes = static_cast<size_t>(V) * row_bytes;
     hipLaunchKernelGGL(k_seg_count, dim3(G), dim3(kThreads), row_bytes, st, ids, n, n_slots, chunk, cnt, bad_of);
-#define LORA_SEG_CHUNKED(KB)                                                                                  \
-  hipLaunchKernelGGL(k_seg_scan<KB>, dim3(1), dim3(kThreads), row_bytes, st, n, n_slots, G, cnt, coff, bad_of,   \
-                     slot_base, o);                                                                           \
-  hipLaunchKernelGGL(k_seg_scatter<KB>, dim3(G), dim3(kThreads), rows_bytes, st, ids, n, n_slots, V, nbits,     \
-                     chunk, cnt, coff, slot_base, seg->perm)
+    const bool place = static_cast<int64_t>(G) * n_slots <= kPlaceWords;
+#define LORA_SEG_CHUNKED(KB)                                                                                    \
+  do {                                                                                                          \
+    if (place) {                                                                                                \
+      hipLaunchKernelGGL(k_seg_place<KB>, dim3(G + 1), dim3(kThreads), rows_bytes + row_bytes, st, ids, n,      \
+                         n_slots, V, nbits, chunk, G, cnt, bad_of, o);                                          \
+    } else {                                                                                                    \
+      hipLaunchKernelGGL(k_seg_scan<KB>, dim3(1), dim3(kThreads), row_bytes, st, n, n_slots, G, cnt, coff,      \
+                         bad_of, slot_base, o);                                                                 \
+      hipLaunchKernelGGL(k_seg_scatter<KB>, dim3(G), dim3(kThreads), rows_bytes, st, ids, n, n_slots, V, nbits, \
+                         chunk, cnt, coff, slot_base, seg->perm);                                               \
+    }                                                                                                           \
+  } while (0)
     switch (bpt_class(n_slots)) {
       case 1: LORA_SEG_CHUNKED(1); break;
       case 2: LORA_SEG_CHUNKED(2); break;

@@ -85,6 +85,10 @@ SEG_CASES = {
     "tiny_long_minus": ([5] * 62 + [-1, 9], 8),
     "tiny_max_slots": (np.random.default_rng(35).integers(-1, 8192, 63), 8192),
     "tiny_runs": (np.repeat(np.random.default_rng(36).integers(0, 5, 16), 4), 5),
+    # chunked batches in two launches (layout beside the scatter) up to 65,536 chunk counters,
+    # in three (k_seg_scan between them) above: 64 chunks x 1,024 slots, then 65
+    "place_max": (np.random.default_rng(37).integers(-1, 1024, 65536), 1024),
+    "scan_from": (np.random.default_rng(38).integers(-1, 1024, 65537), 1024),
 }
 
 
