@@ -182,22 +182,42 @@ ShrinkSplit shrink_split(const lora_pool* p, int32_t module0, int32_t n_modules,
   return ShrinkSplit{(h_in + kps - 1) / kps, kps};
 }
 
+bool allow_dynamic_lds(const void* fn, int device, size_t lds);
+
+// The shrink launch of one run of modules (modules that share x, or one module
+// after another with x stride msx): its GEMV arguments and grid, and, for bf16
+// pools with matrix-core tiles, its tile arguments, grid and LDS.
+struct ShrinkPlan {
+  GemvArgs g;
+  unsigned gx;          // GEMV workgroups per module
+  bool tiles;           // matrix-core tiles (else the GEMV kernel alone)
+  ShrinkArgs a;
+  int32_t per_wg;       // modules one tile workgroup computes from one x slice
+  int32_t groups;       // module groups (grid z of the tile part)
+  int ntiles;           // 16-column tiles per module (rank cap / 16, rounded to 1, 2 or 4)
+  int tnx;              // tile workgroups per split and group
+  size_t lds;
+  int64_t tile_blocks() const { return static_cast<int64_t>(tnx) * a.ks_count * groups; }
+  int64_t gemv_blocks(int32_t n_modules) const { return static_cast<int64_t>(gx) * n_modules; }
+};
+
 // sp: the K split (shrink_split); ws holds its partial tiles when sp.ks > 1.  fold: the
 // partial tiles are left in ws for the expand to add (no k_shrink_reduce launch), so
 // the t rows of tokens in matrix-core tiles are not written; they sit at modules
 // part_m0 .. part_m0 + n_modules - 1 of a layout of part_nm modules (one call's
 // modules may come from several shrink launches).
 template <typename TI>
-lora_status launch_shrink(const lora_pool* p, int32_t module0, int32_t n_modules, const void* x, int64_t ld_x,
-                          int64_t msx, const lora_segments* seg, float* t, int64_t ld_t, int64_t mst,
-                          ShrinkSplit sp, void* ws, hipStream_t s, bool fold = false, int32_t part_m0 = 0,
-                          int32_t part_nm = 0) {
+ShrinkPlan plan_shrink(const lora_pool* p, int32_t module0, int32_t n_modules, const void* x, int64_t ld_x,
+                       int64_t msx, const lora_segments* seg, float* t, int64_t ld_t, int64_t mst, ShrinkSplit sp,
+                       void* ws, bool fold, int32_t part_m0, int32_t part_nm) {
+  ShrinkPlan pl{};
   const PoolView pv = p->view();
   const SegView sv = seg_view(seg);
   const int32_t h_in = static_cast<int32_t>(p->h_in[module0]);
   const bool use_mfma = mfma_ok(p, module0);
   const int32_t units_word = use_mfma ? LORA_META_N_UNITS_SHORT : LORA_META_N_UNITS_ALL;
-  GemvArgs g = gemv_args(p, module0, sv, units_word);
+  GemvArgs& g = pl.g;
+  g = gemv_args(p, module0, sv, units_word);
   g.x = x;
   g.ld_x = ld_x;
   g.msx = msx;
@@ -206,76 +226,121 @@ lora_status launch_shrink(const lora_pool* p, int32_t module0, int32_t n_modules
   g.mst = mst;
   const int32_t gemv_units = use_mfma ? max_short_units_of(seg) : seg->max_units;   // what units_word can count
   g.parts = (p->max_rank + kPartRows - 1) / kPartRows;   // a work item per kPartRows rank rows of a unit
-  const unsigned gx = gemv_grid_of(gemv_units * g.parts);
-  if constexpr (sizeof(TI) == 2) {
-    // long segments on matrix-core tiles and short units on the GEMV path, in one launch
-    if (use_mfma && seg->max_tiles > 0) {
-      const bool shared = (msx == 0 && n_modules > 1 && n_modules <= kShrinkMaxModules);
-      const int32_t groups = shared ? 1 : n_modules;
-      const int32_t per_wg = shared ? n_modules : 1;
-      const int32_t ks = sp.ks, kps = sp.kps;
-      ShrinkArgs a;
-      a.pv = pv;
-      a.sv = sv;
-      a.x = static_cast<const __bf16*>(x);
-      a.ld_x = ld_x;
-      a.msx = shared ? 0 : msx;
-      a.t = t;
-      a.ld_t = ld_t;
-      a.mst = mst;
-      a.module0 = module0;
-      a.mods_per_wg = per_wg;
-      a.h_in = h_in;
-      a.ks_count = ks;
-      a.k_per_split = kps;
-      a.ldr = ldr_of(p);
-      a.magic = static_cast<uint32_t>(((uint64_t(1) << 32) + p->page_elems - 1) / p->page_elems);
-      a.max_pids = p->max_pages_per_entry;
-      const int ntiles = a.ldr <= 16 ? 1 : a.ldr <= 32 ? 2 : 4;
-      // A rows staged in LDS at once: the whole split when they fit the LDS budget,
-      // else equal sub-ranges (multiples of 32) that do
-      const size_t ids_bytes = static_cast<size_t>(per_wg) * a.max_pids * 4;
-      const size_t row_bytes = static_cast<size_t>(per_wg) * 16 * ntiles * 2;   // per k of A rows
-      int32_t kc_max = static_cast<int32_t>((kStreamLdsBudget - ids_bytes) / row_bytes) - 8;
-      kc_max = std::max(32, kc_max / 32 * 32);
-      const int32_t n_sub = (kps + kc_max - 1) / kc_max;
-      a.kc = ((kps + n_sub - 1) / n_sub + 31) / 32 * 32;
-      const size_t lds = std::max(stream_lds_bytes(per_wg, ntiles, a.kc, a.max_pids), gemv_lds_bytes<1, __bf16>());
-      a.part = ks > 1 ? static_cast<float*>(ws) : nullptr;
-      a.part_m0 = fold ? part_m0 : 0;
-      a.part_nm = fold && part_nm > 0 ? part_nm : n_modules;   // k_shrink_reduce reads this launch's layout
-      const int tnx = static_cast<int>(tile_grid_of(seg->max_tiles));
-      const int64_t n_blocks = static_cast<int64_t>(tnx) * ks * groups + static_cast<int64_t>(gx) * n_modules;
-      if (!grid_fits(n_blocks, kMfmaThreads)) return LORA_ERR_SHAPE;   // beyond one launch (nothing launched yet)
-      const dim3 grid(static_cast<unsigned>(n_blocks)), block(kMfmaThreads);
-      set_module_groups(g, gx, n_modules);
-#define LORA_SHRINK_LAUNCH(M, NT)                                                                        \
-  hipLaunchKernelGGL((k_shrink_mixed<M, NT, kStreamDepth>), grid, block, lds, s, a, g, tnx, ks, groups, \
-                     static_cast<int>(gx), n_modules)
+  pl.gx = gemv_grid_of(gemv_units * g.parts);
+  // long segments on matrix-core tiles and short units on the GEMV path, in one launch
+  pl.tiles = sizeof(TI) == 2 && use_mfma && seg->max_tiles > 0;
+  if (!pl.tiles) return pl;
+  const bool shared = (msx == 0 && n_modules > 1 && n_modules <= kShrinkMaxModules);
+  pl.groups = shared ? 1 : n_modules;
+  pl.per_wg = shared ? n_modules : 1;
+  const int32_t ks = sp.ks, kps = sp.kps;
+  ShrinkArgs& a = pl.a;
+  a.pv = pv;
+  a.sv = sv;
+  a.x = static_cast<const __bf16*>(x);
+  a.ld_x = ld_x;
+  a.msx = shared ? 0 : msx;
+  a.t = t;
+  a.ld_t = ld_t;
+  a.mst = mst;
+  a.module0 = module0;
+  a.mods_per_wg = pl.per_wg;
+  a.h_in = h_in;
+  a.ks_count = ks;
+  a.k_per_split = kps;
+  a.ldr = ldr_of(p);
+  a.magic = static_cast<uint32_t>(((uint64_t(1) << 32) + p->page_elems - 1) / p->page_elems);
+  a.max_pids = p->max_pages_per_entry;
+  pl.ntiles = a.ldr <= 16 ? 1 : a.ldr <= 32 ? 2 : 4;
+  // A rows staged in LDS at once: the whole split when they fit the LDS budget,
+  // else equal sub-ranges (multiples of 32) that do
+  const size_t ids_bytes = static_cast<size_t>(pl.per_wg) * a.max_pids * 4;
+  const size_t row_bytes = static_cast<size_t>(pl.per_wg) * 16 * pl.ntiles * 2;   // per k of A rows
+  int32_t kc_max = static_cast<int32_t>((kStreamLdsBudget - ids_bytes) / row_bytes) - 8;
+  kc_max = std::max(32, kc_max / 32 * 32);
+  const int32_t n_sub = (kps + kc_max - 1) / kc_max;
+  a.kc = ((kps + n_sub - 1) / n_sub + 31) / 32 * 32;
+  pl.lds = std::max(stream_lds_bytes(pl.per_wg, pl.ntiles, a.kc, a.max_pids), gemv_lds_bytes<1, __bf16>());
+  a.part = ks > 1 ? static_cast<float*>(ws) : nullptr;
+  a.part_m0 = fold ? part_m0 : 0;
+  a.part_nm = fold && part_nm > 0 ? part_nm : n_modules;   // k_shrink_reduce reads this launch's layout
+  pl.tnx = static_cast<int>(tile_grid_of(seg->max_tiles));
+  set_module_groups(g, pl.gx, n_modules);
+  return pl;
+}
+
+template <typename TI>
+lora_status launch_shrink(const lora_pool* p, int32_t module0, int32_t n_modules, const void* x, int64_t ld_x,
+                          int64_t msx, const lora_segments* seg, float* t, int64_t ld_t, int64_t mst,
+                          ShrinkSplit sp, void* ws, hipStream_t s, bool fold = false, int32_t part_m0 = 0,
+                          int32_t part_nm = 0) {
+  ShrinkPlan pl =
+      plan_shrink<TI>(p, module0, n_modules, x, ld_x, msx, seg, t, ld_t, mst, sp, ws, fold, part_m0, part_nm);
+  if (pl.tiles) {
+    const int32_t ks = pl.a.ks_count;
+    const int64_t n_blocks = pl.tile_blocks() + pl.gemv_blocks(n_modules);
+    if (!grid_fits(n_blocks, kMfmaThreads)) return LORA_ERR_SHAPE;   // beyond one launch (nothing launched yet)
+    const dim3 grid(static_cast<unsigned>(n_blocks)), block(kMfmaThreads);
+#define LORA_SHRINK_LAUNCH(M, NT)                                                                              \
+  hipLaunchKernelGGL((k_shrink_mixed<M, NT, kStreamDepth>), grid, block, pl.lds, s, pl.a, pl.g, pl.tnx, ks, \
+                     pl.groups, static_cast<int>(pl.gx), n_modules)
 #define LORA_SHRINK_NT(M)                                 \
   do {                                                    \
-    if (ntiles == 1) LORA_SHRINK_LAUNCH(M, 1);            \
-    else if (ntiles == 2) LORA_SHRINK_LAUNCH(M, 2);       \
+    if (pl.ntiles == 1) LORA_SHRINK_LAUNCH(M, 1);         \
+    else if (pl.ntiles == 2) LORA_SHRINK_LAUNCH(M, 2);    \
     else LORA_SHRINK_LAUNCH(M, 4);                        \
   } while (0)
-      switch (per_wg) {
-        case 1: LORA_SHRINK_NT(1); break;
-        case 2: LORA_SHRINK_NT(2); break;
-        case 3: LORA_SHRINK_NT(3); break;
-        default: LORA_SHRINK_NT(4); break;
-      }
+    switch (pl.per_wg) {
+      case 1: LORA_SHRINK_NT(1); break;
+      case 2: LORA_SHRINK_NT(2); break;
+      case 3: LORA_SHRINK_NT(3); break;
+      default: LORA_SHRINK_NT(4); break;
+    }
 #undef LORA_SHRINK_NT
 #undef LORA_SHRINK_LAUNCH
+    if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
+    if (ks > 1 && !fold) {
+      hipLaunchKernelGGL(k_shrink_reduce, dim3(tile_grid_of(seg->max_tiles), n_modules), block, 0, s, pl.a);
       if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
-      if (ks > 1 && !fold) {
-        hipLaunchKernelGGL(k_shrink_reduce, dim3(tile_grid_of(seg->max_tiles), n_modules), block, 0, s, a);
-        if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
-      }
-      return LORA_OK;
     }
+    return LORA_OK;
   }
-  hipLaunchKernelGGL((k_gemv<1, TI, TI>), dim3(gx, n_modules), dim3(kGemvThreads), 0, s, g);
+  hipLaunchKernelGGL((k_gemv<1, TI, TI>), dim3(pl.gx, n_modules), dim3(kGemvThreads), 0, s, pl.g);
   return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+// The two shrink launches of an attention layer's runs, q,k,v sharing x (3 modules
+// per tile workgroup) and o with its own x, as one launch: its grid holds both
+// runs' tiles, then both runs' GEMV items, so the two x streams overlap instead of
+// each ramping up and draining alone.  Both plans have matrix-core tiles, one
+// module group each, the same K split and tile width; returns false when the runs
+// are not of that shape (nothing launched).
+bool launch_shrink_pair(const ShrinkPlan& p1, int32_t n1, const ShrinkPlan& p2, int32_t n2, hipStream_t s,
+                        int device, lora_status* st) {
+  if (!p1.tiles || !p2.tiles || p1.per_wg != 3 || n1 != 3 || p2.per_wg != 1 || n2 != 1 || p1.groups != 1 ||
+      p2.groups != 1 || p1.ntiles != p2.ntiles || p1.a.ks_count != p2.a.ks_count || p1.tnx != p2.tnx ||
+      p1.gx != p2.gx)
+    return false;
+  const int64_t n_blocks = p1.tile_blocks() + p2.tile_blocks() + p1.gemv_blocks(n1) + p2.gemv_blocks(n2);
+  if (!grid_fits(n_blocks, kMfmaThreads)) return false;
+  const size_t lds = std::max(p1.lds, p2.lds);
+  const dim3 grid(static_cast<unsigned>(n_blocks)), block(kMfmaThreads);
+  const int ks = p1.a.ks_count, gx = static_cast<int>(p1.gx);
+#define LORA_PAIR_LAUNCH(NT)                                                                                     \
+  do {                                                                                                           \
+    if (!allow_dynamic_lds(reinterpret_cast<const void*>(&k_shrink_pair<3, 1, NT, kStreamDepth>), device, lds)) { \
+      *st = LORA_ERR_HIP;                                                                                        \
+      return true;                                                                                               \
+    }                                                                                                            \
+    hipLaunchKernelGGL((k_shrink_pair<3, 1, NT, kStreamDepth>), grid, block, lds, s, p1.a, p1.g, p2.a, p2.g,     \
+                       p1.tnx, ks, gx, n1, n2);                                                                  \
+  } while (0)
+  if (p1.ntiles == 1) LORA_PAIR_LAUNCH(1);
+  else if (p1.ntiles == 2) LORA_PAIR_LAUNCH(2);
+  else LORA_PAIR_LAUNCH(4);
+#undef LORA_PAIR_LAUNCH
+  *st = hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+  return true;
 }
 
 // Raises kernel `fn`'s dynamic LDS limit on `device` to at least `lds` bytes
@@ -713,6 +778,19 @@ lora_status lora_apply_sgmv_multi(const lora_pool* p, int32_t module0, int32_t n
   const ShrinkSplit sp{(h_in + kps - 1) / kps, kps};
   // partial tiles exist only where the shrink splits K, on its matrix-core tiles
   const bool fold = sp.ks > 1 && shrink_has_tiles(p, module0, seg);
+  if (n_runs == 2 && p->dtype == LORA_BF16) {   // q,k,v beside o: one launch for both runs when it fits
+    const int32_t n0 = runs[0].n_modules;
+    const ShrinkPlan p0 = plan_shrink<__bf16>(p, module0, n0, runs[0].x, runs[0].ld_x, runs[0].module_stride_x, seg,
+                                              t, ld_t, module_stride_t, sp, ws, fold, 0, n_modules);
+    const ShrinkPlan p1 = plan_shrink<__bf16>(p, module0 + n0, runs[1].n_modules, runs[1].x, runs[1].ld_x,
+                                              runs[1].module_stride_x, seg, t + static_cast<int64_t>(n0) * module_stride_t,
+                                              ld_t, module_stride_t, sp, ws, fold, n0, n_modules);
+    if (launch_shrink_pair(p0, n0, p1, runs[1].n_modules, s, p->device, &st)) {
+      if (st != LORA_OK) return st;
+      return expand_call(p, module0, n_modules, t, ld_t, module_stride_t, seg, y, ld_y, module_stride_y, ydtype, s,
+                         fold ? static_cast<const float*>(ws) : nullptr, sp.ks);
+    }
+  }
   m = module0;
   for (int32_t r = 0; r < n_runs; ++r) {
     st = shrink_call(p, m, runs[r].n_modules, runs[r].x, runs[r].ld_x, runs[r].module_stride_x, seg,

@@ -641,6 +641,36 @@ __global__ __launch_bounds__(kMfmaThreads) void k_shrink_mixed(ShrinkArgs a, Gem
   }
 }
 
+// Two shrink launches in one (see launch_shrink_pair): the tiles of run 1 (M1
+// modules sharing x), the tiles of run 2 (M2), then the GEMV items of run 1 (n1
+// modules) and of run 2 (n2).  Each part starts at a multiple of 8 workgroups.
+template <int M1, int M2, int NTILES, int D>
+__global__ __launch_bounds__(kMfmaThreads) void k_shrink_pair(ShrinkArgs a1, GemvArgs g1, ShrinkArgs a2, GemvArgs g2,
+                                                              int tnx, int tny, int gnx, int n1, int n2) {
+  static_assert(kMfmaThreads == kGemvThreads, "both parts run on one workgroup size");
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  int lin = static_cast<int>(blockIdx.x);
+  const int tile_blocks = tnx * tny;
+  if (lin < tile_blocks) {
+    shrink_stream_body<M1, NTILES, D>(a1, blk_of_linear(lin, tnx, tny, 1), smem);
+    return;
+  }
+  lin -= tile_blocks;
+  if (lin < tile_blocks) {
+    shrink_stream_body<M2, NTILES, D>(a2, blk_of_linear(lin, tnx, tny, 1), smem);
+    return;
+  }
+  lin -= tile_blocks;
+  UnitLds& L = *reinterpret_cast<UnitLds*>(smem);
+  __bf16* xs = reinterpret_cast<__bf16*>(smem + gemv_xs_offset<1, __bf16>());
+  if (lin < gnx * n1) {
+    gemv_body<1, __bf16, __bf16>(g1, blk_of_linear(lin, gnx, n1, 1), L, xs);
+    return;
+  }
+  lin -= gnx * n1;
+  gemv_body<1, __bf16, __bf16>(g2, blk_of_linear(lin, gnx, n2, 1), L, xs);
+}
+
 // Partial tiles of rank caps of 32 or more (PQ >= 2) need the registers of a
 // third resident workgroup; at those caps the LDS tile leaves room for at most
 // three (32), or two (48, 64), anyway.
