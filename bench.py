@@ -116,12 +116,12 @@ def make_workload(name):
 # HIP sources that build the kernel whose HBM traffic a workload's counters measured, and
 # its launch (apply.hip sizes the grids): a change to any of them voids the stored counters.
 KERNEL_SOURCES = {
-    "bgmv_decode_x128": ["common.hpp", "gemv_kernels.hpp", "apply.hip"],
+    "bgmv_decode_x128": ["common.hpp", "segments_wave.hpp", "gemv_kernels.hpp", "apply.hip"],
     "encoder_fused": ["common.hpp", "fused_gemm.hpp", "apply.hip"],
     "prefill_fused": ["common.hpp", "fused_gemm.hpp", "apply.hip"],
 }
-ALL_KERNEL_SOURCES = ["common.hpp", "gemv_kernels.hpp", "mfma_kernels.hpp", "fused_gemm.hpp", "apply.hip",
-                      "segments.hip"]
+ALL_KERNEL_SOURCES = ["common.hpp", "segments_wave.hpp", "gemv_kernels.hpp", "mfma_kernels.hpp", "fused_gemm.hpp",
+                      "apply.hip", "segments.hip"]
 
 
 def kernel_source_sha(workload):
@@ -617,14 +617,22 @@ def main():
             d.upload_weights_fp8()
             d.upload_weights()   # the bf16 pass of the same layer, timed beside it
 
+    # a decode batch of at most 64 tokens runs straight from its ids (lora_apply_bgmv_ids): each
+    # workgroup of the one launch builds the batch's unit list itself, so the step has no
+    # separate segment build
+    ids_path = mode == "bgmv" and wl.n_tokens <= 64
+
     def step(ev=None, i=0):
         d = dws[i % rotate]
-        if mode not in ("fused", "fused8"):
+        if mode not in ("fused", "fused8") and not ids_path:
             d.build_segments()
         if ev is not None:
             ev[0].record(stream)
         if mode == "bgmv":
-            d.bgmv()
+            if ids_path:
+                d.bgmv_ids()
+            else:
+                d.bgmv()
         elif mode == "fused":
             d.fused()
         elif mode == "fused8":
@@ -640,6 +648,16 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    # the GPU's clocks settle only after some milliseconds of steady work (the first few dozen
+    # steps of a cold box ran about 6% slower): untimed steps for about 100 ms, then the
+    # warm-up steps proper
+    t_warm = time.perf_counter()
+    for i in range(2000):
+        step(None, i)
+        if i % 8 == 7:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t_warm > 0.1:
+                break
     for i in range(args.warmup):
         step(None, i)
     torch.cuda.synchronize()
@@ -660,6 +678,8 @@ def main():
         # one-module calls (the decode batch as the config states it), replayed from a
         # captured graph so that host launch cost is not in the figure
         import segmented_gathered_rank_amd as sgr
+        dw.build_segments()   # the ids path of the step does not build them
+        torch.cuda.synchronize()
         y = dw.y[0]
         calls = 16
         g = torch.cuda.CUDAGraph()
@@ -680,6 +700,16 @@ def main():
         extra["single_module_call_us"] = float(np.median(lat) * 1e3)
         extra["single_module_bytes"] = work["per_module"][0]["bytes"]
         extra["single_module_GBps"] = work["per_module"][0]["bytes"] / (np.median(lat) * 1e-3) / 1e9
+    if ids_path:
+        # the same step through the segment builder: lora_build_segments + lora_apply_bgmv, two launches
+        k = [0]
+
+        def segments_step():
+            d = dws[k[0] % rotate]
+            k[0] += 1
+            d.build_segments()
+            d.bgmv()
+        extra["segments_path_step_ms"] = round(time_ms(segments_step, reps=20), 5)
 
     if mode in ("fused", "fused8"):
         fp8 = mode == "fused8"
@@ -740,7 +770,8 @@ def main():
         extra["lora_apply_over_base_gemm"] = round(kern_avg / gms, 4)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(args.workload),
-                "kernel": "k_gemv<0> (fused BGMV)" if mode == "bgmv" else "shrink+expand",
+                "kernel": ("k_bgmv_ids (fused BGMV from the ids)" if ids_path else "k_gemv<0> (fused BGMV)")
+                if mode == "bgmv" else "shrink+expand",
                 "bytes_per_launch": bound_bytes}
     out = {
         "metric": METRIC, "value": round(wl.n_tokens / (ms_step * 1e-3), 1), "unit": "tokens/s",

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 7
+#define LORA_ABI_VERSION 8
 
 typedef int32_t lora_status;
 enum {
@@ -327,6 +327,25 @@ lora_status lora_apply_bgmv(const lora_pool *p, int32_t module0, int32_t n_modul
                             const lora_segments *seg,
                             void *y, int64_t ld_y, int64_t module_stride_y, lora_dtype ydtype,
                             void *stream);
+
+/* lora_apply_bgmv straight from the batch's adapter ids, for decode batches
+ * of at most LORA_IDS_MAX_TOKENS tokens (study page, "The kernel trick": each
+ * decode token brings its own adapter index, and the kernel gathers by it).
+ * ids: device int32 [n_tokens], the pool slot of each token; -1 (and any id
+ * outside [0, n_slots of the pool)) leaves the token's y rows untouched and is
+ * not reported (lora_build_segments + lora_segments_check report bad ids).
+ * Every workgroup of the launch builds the batch's unit list in its own LDS,
+ * with the same lists lora_build_segments writes, so the step needs no segment
+ * build launch and no lora_segments buffer.  Same y as lora_build_segments over
+ * the pool's slots followed by lora_apply_bgmv, bit for bit.  x, y and their
+ * strides as lora_apply_bgmv.  Errors: ARG, SHAPE (also: n_tokens >
+ * LORA_IDS_MAX_TOKENS), DTYPE, HIP; nothing is launched on an error. */
+#define LORA_IDS_MAX_TOKENS 64
+lora_status lora_apply_bgmv_ids(const lora_pool *p, int32_t module0, int32_t n_modules,
+                                const void *x, int64_t ld_x, int64_t module_stride_x,
+                                const int32_t *ids, int32_t n_tokens,
+                                void *y, int64_t ld_y, int64_t module_stride_y, lora_dtype ydtype,
+                                void *stream);
 
 /* lora_apply_bgmv for 2..4 modules that share one x (the q, k, v projections
  * of a layer: "Thousands of adapters", slide 5), taken together: one work

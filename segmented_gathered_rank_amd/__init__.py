@@ -21,7 +21,7 @@ __all__ = [
     "lora_segments_bytes", "lora_segments_bind", "lora_build_segments",
     "lora_segments_check", "lora_shrink_workspace_bytes", "lora_shrink", "lora_shrink_noalloc",
     "LORA_NOALLOC_SCRATCH_BYTES",
-    "lora_expand", "lora_apply_sgmv", "lora_apply_sgmv_multi", "lora_x_run", "lora_apply_bgmv", "lora_apply_bgmv_packed", "lora_fused_gemm", "lora_fused_gemm_fp8w",
+    "lora_expand", "lora_apply_sgmv", "lora_apply_sgmv_multi", "lora_x_run", "lora_apply_bgmv", "lora_apply_bgmv_ids", "lora_apply_bgmv_packed", "lora_fused_gemm", "lora_fused_gemm_fp8w",
     "LORA_TIER_GPU", "LORA_TIER_HOST", "LORA_TIER_COLD", "lora_tiers_create", "lora_tiers_destroy",
     "lora_tiers_touch", "lora_tiers_stats", "lora_tiers_slot_of", "lora_tiers_acquire",
     "lora_tiers_batch_done", "lora_tiers_prefetch",
@@ -101,6 +101,7 @@ _SIGS = {
     "lora_apply_sgmv_multi": (_I32, [_P, _I32, _I32, _P, _I32, _SEGP, _P, _I64, _I64, _P, _I64, _I64, _I32,
                                      _P, _SZ, _P]),
     "lora_apply_bgmv": (_I32, [_P, _I32, _I32, _P, _I64, _I64, _SEGP, _P, _I64, _I64, _I32, _P]),
+    "lora_apply_bgmv_ids": (_I32, [_P, _I32, _I32, _P, _I64, _I64, _P, _I32, _P, _I64, _I64, _I32, _P]),
     "lora_apply_bgmv_packed": (_I32, [_P, _I32, _I32, _P, _I64, _SEGP, _P, _I64, _I64, _I32, _P]),
     "lora_fused_gemm": (_I32, [_P, _I32, _P, _I64, _P, _I64, _P, _I32, _P, _I64, _P]),
     "lora_fused_gemm_fp8w": (_I32, [_P, _I32, _P, _I64, _P, _I64, _P, _P, _I32, _P, _I64, _P]),
@@ -288,6 +289,12 @@ def lora_apply_bgmv(pool: int, module0: int, n_modules: int, x, ld_x: int, modul
                     stream=None) -> None:
     _check(_lib.lora_apply_bgmv(pool, module0, n_modules, _ptr(x), ld_x, module_stride_x, ctypes.byref(seg),
                                 _ptr(y), ld_y, module_stride_y, ydtype, _stream(stream)), "lora_apply_bgmv")
+
+
+def lora_apply_bgmv_ids(pool: int, module0: int, n_modules: int, x, ld_x: int, module_stride_x: int, ids,
+                        n_tokens: int, y, ld_y: int, module_stride_y: int, ydtype: int, stream=None) -> None:
+    _check(_lib.lora_apply_bgmv_ids(pool, module0, n_modules, _ptr(x), ld_x, module_stride_x, _ptr(ids), n_tokens,
+                                    _ptr(y), ld_y, module_stride_y, ydtype, _stream(stream)), "lora_apply_bgmv_ids")
 
 
 def lora_apply_bgmv_packed(pool: int, module0: int, n_modules: int, x, ld_x: int, seg: lora_segments, y,

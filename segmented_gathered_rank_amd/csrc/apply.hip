@@ -47,6 +47,15 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Checks shared by the apply calls.  `need_out` also checks equal h_out.
 // same_out: the call also needs equal h_out (expand and BGMV; the shrink only reads h_in).
+// Modules module0 .. module0 + n_modules - 1 exist and share h_in (and h_out when same_out).
+lora_status check_modules(const lora_pool* p, int32_t module0, int32_t n_modules, bool same_out) {
+  if (!p || n_modules < 1 || module0 < 0 || module0 + n_modules > p->n_modules) return LORA_ERR_ARG;
+  for (int32_t m = module0 + 1; m < module0 + n_modules; ++m) {
+    if (p->h_in[m] != p->h_in[module0] || (same_out && p->h_out[m] != p->h_out[module0])) return LORA_ERR_SHAPE;
+  }
+  return LORA_OK;
+}
+
 lora_status check_call(const lora_pool* p, int32_t module0, int32_t n_modules, const lora_segments* seg,
                        bool same_out) {
   if (!p || !seg) return LORA_ERR_ARG;
@@ -57,10 +66,7 @@ lora_status check_call(const lora_pool* p, int32_t module0, int32_t n_modules, c
     return LORA_ERR_ARG;
   if (seg->max_units != max_units_of(seg->n_tokens, seg->n_slots) || seg->max_tiles != max_tiles_of(seg->n_tokens))
     return LORA_ERR_ARG;
-  for (int32_t m = module0 + 1; m < module0 + n_modules; ++m) {
-    if (p->h_in[m] != p->h_in[module0] || (same_out && p->h_out[m] != p->h_out[module0])) return LORA_ERR_SHAPE;
-  }
-  return LORA_OK;
+  return check_modules(p, module0, n_modules, same_out);
 }
 
 // Element rows of a [n_tokens][ld] operand repeated per module.
@@ -341,6 +347,40 @@ bool launch_shrink_pair(const ShrinkPlan& p1, int32_t n1, const ShrinkPlan& p2, 
 #undef LORA_PAIR_LAUNCH
   *st = hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
   return true;
+}
+
+static_assert(LORA_IDS_MAX_TOKENS == kWaveSegTokens, "the ids path builds the unit list on one wave");
+
+// The fused BGMV from the ids (k_bgmv_ids): grid as launch_bgmv's, one workgroup
+// per unit 64 tokens can hold over the pool's slots.
+template <typename TI, typename TO>
+lora_status launch_bgmv_ids(const lora_pool* p, int32_t module0, int32_t n_modules, const void* x, int64_t ld_x,
+                            int64_t msx, const int32_t* ids, int32_t n, void* y, int64_t ld_y, int64_t msy,
+                            hipStream_t s) {
+  GemvArgs g = gemv_args(p, module0, SegView{}, LORA_META_N_UNITS_ALL);   // the kernel fills g.sv in LDS
+  g.x = x;
+  g.ld_x = ld_x;
+  g.msx = msx;
+  g.y = y;
+  g.ld_y = ld_y;
+  g.msy = msy;
+  g.pack = 1;
+  g.x_stream = (msx == 0 && n_modules > 1) ? 0 : 1;   // x rows read by one work item only are streamed
+  int32_t nbits = 0;
+  while ((1 << nbits) < p->n_slots) ++nbits;
+  const int32_t units = max_units_of(n, p->n_slots);
+  if (n_modules >= kBgmvGroupedFrom) {
+    const unsigned gxg = static_cast<unsigned>(units);
+    if (static_cast<int64_t>(n_modules) * gxg * kGemvThreads > static_cast<int64_t>(UINT32_MAX)) return LORA_ERR_SHAPE;
+    g.module_group = std::min(kBgmvModuleGroup, n_modules);
+    g.group_nx = static_cast<int32_t>(gxg);
+    hipLaunchKernelGGL((k_bgmv_ids<TI, TO>), dim3(gxg * static_cast<unsigned>(n_modules)), dim3(kGemvThreads), 0, s,
+                       g, ids, n, nbits);
+  } else {
+    hipLaunchKernelGGL((k_bgmv_ids<TI, TO>), dim3(gemv_grid_of(units), n_modules), dim3(kGemvThreads), 0, s, g, ids,
+                       n, nbits);
+  }
+  return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
 // Raises kernel `fn`'s dynamic LDS limit on `device` to at least `lds` bytes
@@ -831,6 +871,38 @@ lora_status lora_apply_bgmv(const lora_pool* p, int32_t module0, int32_t n_modul
                                       module_stride_y, s);
   return launch_bgmv<float, float>(p, module0, n_modules, x, ld_x, module_stride_x, seg, y, ld_y, module_stride_y,
                                    s);
+}
+
+lora_status lora_apply_bgmv_ids(const lora_pool* p, int32_t module0, int32_t n_modules, const void* x, int64_t ld_x,
+                                int64_t module_stride_x, const int32_t* ids, int32_t n_tokens, void* y, int64_t ld_y,
+                                int64_t module_stride_y, lora_dtype ydtype, void* stream) {
+  lora_status st = check_modules(p, module0, n_modules, true);
+  if (st != LORA_OK) return st;
+  if (n_tokens < 0) return LORA_ERR_ARG;
+  if (n_tokens > LORA_IDS_MAX_TOKENS) return LORA_ERR_SHAPE;
+  if (ydtype != LORA_F32 && ydtype != LORA_BF16) return LORA_ERR_DTYPE;
+  st = check_operand(x, ld_x, module_stride_x, p->h_in[module0], p->elem_bytes(), n_tokens, n_modules, false, true);
+  if (st != LORA_OK) return st;
+  st = check_operand(y, ld_y, module_stride_y, p->h_out[module0], ydtype == LORA_BF16 ? 2 : 4, n_tokens, n_modules,
+                     true, true);
+  if (st != LORA_OK) return st;
+  if (n_tokens == 0) return LORA_OK;
+  if (!ids) return LORA_ERR_ARG;
+  DeviceGuard g(p->device);
+  if (!g.ok) return LORA_ERR_HIP;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p->dtype == LORA_BF16) {
+    if (ydtype == LORA_BF16)
+      return launch_bgmv_ids<__bf16, __bf16>(p, module0, n_modules, x, ld_x, module_stride_x, ids, n_tokens, y, ld_y,
+                                             module_stride_y, s);
+    return launch_bgmv_ids<__bf16, float>(p, module0, n_modules, x, ld_x, module_stride_x, ids, n_tokens, y, ld_y,
+                                          module_stride_y, s);
+  }
+  if (ydtype == LORA_BF16)
+    return launch_bgmv_ids<float, __bf16>(p, module0, n_modules, x, ld_x, module_stride_x, ids, n_tokens, y, ld_y,
+                                          module_stride_y, s);
+  return launch_bgmv_ids<float, float>(p, module0, n_modules, x, ld_x, module_stride_x, ids, n_tokens, y, ld_y,
+                                       module_stride_y, s);
 }
 
 lora_status lora_apply_bgmv_packed(const lora_pool* p, int32_t module0, int32_t n_modules, const void* x,

@@ -30,6 +30,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "segments_wave.hpp"
 
 namespace lora {
 
@@ -619,6 +620,43 @@ __global__ __launch_bounds__(kGemvThreads, 4) void k_gemv(GemvArgs a) {
                              static_cast<int>(gridDim.x) / a.group_nx, a.module_group, it0);
   gemv_body<MODE, TI, TO>(a, b, *reinterpret_cast<UnitLds*>(lds),
                           reinterpret_cast<TI*>(lds + gemv_xs_offset<MODE, TI>()), it0);
+}
+
+// Fused BGMV straight from the batch's adapter ids, for batches of at most
+// kWaveSegTokens tokens: each decode token brings its own adapter index, as in
+// the study page's BGMV.  Wave 0 of every workgroup builds the batch's unit
+// list in LDS (segments_of_wave: the lists the segment builder writes), and the
+// workgroup then runs its unit as k_gemv<0> does.  The 64 ids take the place
+// of the work-list record in the first round trip, and the step needs no
+// separate segment build launch.  Grid as k_gemv<0>.
+constexpr int kIdsMaxUnits = kWaveSegTokens / kUnitTokens + kWaveSegTokens;   // units of 64 tokens, any slots
+template <typename TI, typename TO>
+__global__ __launch_bounds__(kGemvThreads, 4) void k_bgmv_ids(GemvArgs a, const int32_t* __restrict__ ids,
+                                                              int32_t n_tokens, int32_t nbits) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[gemv_lds_bytes<0, TI>()];
+  __shared__ int32_t perm_s[kWaveSegTokens], seg_start_s[kWaveSegTokens + 1], seg_slot_s[kWaveSegTokens];
+  __shared__ int32_t meta_s[LORA_META_WORDS];
+  __shared__ int2 units_s[kIdsMaxUnits], tiles_s[2];
+  if (threadIdx.x < 64)   // wave 0
+    segments_of_wave(ids, n_tokens, a.pv.n_slots, nbits,
+                     SegOut{perm_s, seg_start_s, seg_slot_s, meta_s, reinterpret_cast<int32_t*>(units_s),
+                            reinterpret_cast<int32_t*>(tiles_s)});
+  __syncthreads();
+  a.sv.perm = perm_s;
+  a.sv.seg_start = seg_start_s;
+  a.sv.seg_slot = seg_slot_s;
+  a.sv.meta = meta_s;
+  a.sv.units = reinterpret_cast<const int32_t*>(units_s);
+  a.sv.tiles = reinterpret_cast<const int32_t*>(tiles_s);
+  a.sv.max_units = kIdsMaxUnits;
+  a.sv.max_tiles = 1;
+  Blk b = blk_of_launch();
+  int it0 = -1;
+  if (a.module_group > 0)
+    b = blk_of_module_groups(static_cast<int>(blockIdx.x), a.group_nx, static_cast<int>(gridDim.x) / a.group_nx,
+                             a.module_group, it0);
+  gemv_body<0, TI, TO>(a, b, *reinterpret_cast<UnitLds*>(lds), reinterpret_cast<TI*>(lds + gemv_xs_offset<0, TI>()),
+                       it0);
 }
 
 // Fused BGMV over packs of a.pack modules that share x (gemv_item_packed): a

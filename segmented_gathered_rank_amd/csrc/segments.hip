@@ -30,6 +30,7 @@
 //                   batches over the whole chip.
 // All counts stay on the device: no host synchronization.
 #include "common.hpp"
+#include "segments_wave.hpp"
 
 using namespace lora;
 
@@ -89,46 +90,6 @@ size_t work_words_of(int n, int n_slots) {
   return g ? 2 * g * n_slots + n_slots + g : 0;   // chunk counts, chunk offsets, slot bases, bad ids
 }
 
-// ------------------------------------------------------------ wave helpers
-template <int kCtrl, int kRowMask>
-__device__ __forceinline__ int dpp0(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, kCtrl, kRowMask, 0xf, false);
-}
-// Inclusive scan over the 64 lanes with DPP: row shifts by 1, 2, 4, 8 inside
-// each row of 16 lanes, then the row broadcasts of lane 15 and lane 31.
-// Lanes outside a shift's row read 0, the identity of both operations
-// (values are non-negative).
-template <bool kMax>
-__device__ __forceinline__ int wave_scan(int v) {
-  auto op = [](int a, int b) { return kMax ? (a > b ? a : b) : a + b; };
-  v = op(v, dpp0<0x111, 0xf>(v));
-  v = op(v, dpp0<0x112, 0xf>(v));
-  v = op(v, dpp0<0x114, 0xf>(v));
-  v = op(v, dpp0<0x118, 0xf>(v));
-  v = op(v, dpp0<0x142, 0xa>(v));
-  v = op(v, dpp0<0x143, 0xc>(v));
-  return v;
-}
-__device__ __forceinline__ int lane63(int v) { return __builtin_amdgcn_readlane(v, 63); }
-
-__device__ __forceinline__ int lowest_lane(uint64_t m) {
-  return __ffsll(static_cast<unsigned long long>(m)) - 1;
-}
-
-// Mask of the lanes whose (valid) id equals this lane's id; 0 for an invalid lane.
-__device__ __forceinline__ uint64_t peers_of(int id, bool valid, int nbits) {
-  const uint64_t vm = __ballot(valid);
-  const int first = __builtin_amdgcn_readfirstlane(id);
-  if (__ballot(valid && id == first) == vm) return valid ? vm : 0ull;   // one id in the batch
-  uint64_t peers = vm;
-  for (int b = 0; b < nbits; ++b) {
-    const bool bit = valid && ((id >> b) & 1);
-    const uint64_t m = __ballot(bit);
-    peers &= bit ? m : ~m;
-  }
-  return valid ? peers : 0ull;
-}
-
 // Ids of tokens [base, base + kRound) clamped to end - 1 (base < end): every
 // load is unconditional so all are in flight at once; callers mask t >= end.
 __device__ __forceinline__ void load_ids(const int32_t* __restrict__ ids, int base, int end, int lane,
@@ -184,16 +145,10 @@ __device__ __forceinline__ void block_add(int v, int lane, int* cell) {
   if (lane == 0 && w) atomicAdd(cell, w);
 }
 
-struct Out {
-  int32_t *perm, *seg_start, *seg_slot, *meta, *units, *tiles;
-};
-
-// GEMV work unit u of a segment of `run` tokens of `slot` that starts at
-// position `first` of perm: (slot + 65536 * tokens in the unit + 2^24 if the
-// segment has more than one unit, position).
-__device__ __forceinline__ int2 unit_record(int slot, int run, int u, int first) {
-  return make_int2(slot + (min(kUnitTokens, run - u * kUnitTokens) << 16) + ((run > kUnitTokens) ? (1 << 24) : 0),
-                   first + u * kUnitTokens);
+// Batches of up to 64 tokens: one wave, one token per lane (segments_of_wave).
+__global__ __launch_bounds__(64) void k_segments_tiny(const int32_t* __restrict__ ids, int32_t n_tokens,
+                                                      int32_t n_slots, int32_t nbits, SegOut o) {
+  segments_of_wave(ids, n_tokens, n_slots, nbits, o);
 }
 
 // Long segments whose unit and tile records the whole workgroup writes
@@ -229,7 +184,7 @@ __device__ __forceinline__ int last_at_most(const int* a, int n, int v) {
 // in perm) for each slot that has tokens.
 template <int TH, class BaseFn>
 __device__ void layout_segments(const int32_t* total, int n_tokens, int n_slots, int s0, int s1, int bpt,
-                                int bad_total, const Out& o, LayoutLds<TH / 64>& L, BaseFn base_of) {
+                                int bad_total, const SegOut& o, LayoutLds<TH / 64>& L, BaseFn base_of) {
   constexpr int W = TH / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int own[6] = {0, 0, 0, 0, 0, 0};   // tokens, segments, short units, long units, tiles, long segments
@@ -401,94 +356,13 @@ __device__ __forceinline__ int rows_total(const int32_t* hist, int n_slots, int 
   return run;
 }
 
-// ------------------------------------------------------------ one wave, up to 64 tokens
-// A decode batch: lane i holds token i.  A token's place in perm is the
-// number of valid tokens of smaller slots plus its rank among its slot's
-// tokens (ballot match per id bit); a segment's first token (its slot's
-// lowest lane) writes the segment's entries, which need the count of smaller
-// slots' segments, tokens, units and tiles: summed over the segments' first
-// lanes only, one packed word each.  The same output as the workgroup kernels
-// without their histogram, barriers and layout phases.
-constexpr int kTinyTokens = 64;
-__global__ __launch_bounds__(64) void k_segments_tiny(const int32_t* __restrict__ ids, int32_t n_tokens,
-                                                      int32_t n_slots, int32_t nbits, Out o) {
-  const int lane = threadIdx.x;
-  const bool in = lane < n_tokens;
-  const int id = in ? ids[lane] : -1;
-  const bool valid = in && id >= 0 && id < n_slots;
-  const int n_bad = __popcll(__ballot(in && (id < -1 || id >= n_slots)));
-  const uint64_t peers = peers_of(id, valid, nbits);   // lanes of the same slot (0 if invalid)
-  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  const int len = __popcll(peers);
-  const bool first = valid && (peers & below) == 0ull;
-  const bool is_long = len >= kLongMin;
-  const int nu = (len + kUnitTokens - 1) / kUnitTokens;
-  const int nt = is_long ? (len + kTileTokens - 1) / kTileTokens : 0;
-  // a first lane's contribution, 7 bits a field (every sum stays below 128 at 64 tokens; the
-  // tile count keeps the top 4 bits: only a segment of all 64 tokens has a tile):
-  // 1 segment | its tokens | its short-segment units | its long-segment units | its tiles
-  const uint32_t mine = first ? 1u | (static_cast<uint32_t>(len) << 7) | (static_cast<uint32_t>(is_long ? 0 : nu) << 14) |
-                                    (static_cast<uint32_t>(is_long ? nu : 0) << 21) |
-                                    (static_cast<uint32_t>(nt) << 28)
-                              : 0u;
-  uint32_t before = 0;   // the same sums over the segments of smaller slots
-  for (uint64_t fm = __ballot(first); fm; fm &= fm - 1) {
-    const int j = lowest_lane(fm);
-    const int idj = __builtin_amdgcn_readlane(id, j);
-    const uint32_t pj = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mine), j));
-    if (valid && idj < id) before += pj;
-  }
-  const int seg = before & 127, start = (before >> 7) & 127, su = (before >> 14) & 127;
-  const int lu = (before >> 21) & 127, tl = static_cast<int>(before >> 28);
-  if (valid) o.perm[start + __popcll(peers & below)] = lane;
-  const int n_seg = __popcll(__ballot(first));
-  const int n_active = __popcll(__ballot(valid));
-  const int n_short = lane63(wave_scan<false>(first && !is_long ? nu : 0));
-  const int n_long_units = lane63(wave_scan<false>(first && is_long ? nu : 0));
-  const int n_tiles = lane63(wave_scan<false>(first ? nt : 0));
-  const int max_len = lane63(wave_scan<true>(len));
-  if (first) {
-    o.seg_slot[seg] = id;
-    o.seg_start[seg] = start;
-    int2* units = reinterpret_cast<int2*>(o.units);
-    if (!is_long) {
-      for (int u = 0; u < nu; ++u) units[su + u] = unit_record(id, len, u, start);
-    } else {
-      for (int u = 0; u < nu; ++u) units[n_short + lu + u] = unit_record(id, len, u, start);
-      int2* tiles = reinterpret_cast<int2*>(o.tiles);
-      for (int u = 0; u < nt; ++u)
-        tiles[tl + u] = make_int2(id + (min(kTileTokens, len - u * kTileTokens) << 16), start + u * kTileTokens);
-    }
-  }
-  if (lane == 0) o.seg_start[n_seg] = n_active;
-  if (lane < LORA_META_WORDS) {   // one store for the whole meta block
-    int v = 0;
-    switch (lane) {
-      case LORA_META_N_SEG: v = n_seg; break;
-      case LORA_META_N_ACTIVE: v = n_active; break;
-      case LORA_META_MAX_SEG_LEN: v = max_len; break;
-      case LORA_META_N_BAD: v = n_bad; break;
-      case LORA_META_N_UNITS_SHORT: v = n_short; break;
-      case LORA_META_N_UNITS_ALL: v = n_short + n_long_units; break;
-      case LORA_META_N_TILES: v = n_tiles; break;
-      case LORA_META_UNIT_TOKENS: v = kUnitTokens; break;
-      case LORA_META_TILE_TOKENS: v = kTileTokens; break;
-      case LORA_META_LONG_MIN: v = kLongMin; break;
-      case LORA_META_N_TOKENS: v = n_tokens; break;
-      case LORA_META_N_SLOTS: v = n_slots; break;
-      default: v = 0; break;
-    }
-    o.meta[lane] = v;
-  }
-}
-
 // ------------------------------------------------------------ one workgroup
 // TH threads (V <= TH / 64 histogram rows).  Every thread runs the layout's
 // code, so a small batch takes a small workgroup: with 1024 threads the
 // layout alone took about 3 us for 32 slots, all of it instruction issue.
 template <int TH>
 __global__ __launch_bounds__(TH) void k_segments_one(const int32_t* __restrict__ ids, int32_t n_tokens,
-                                                     int32_t n_slots, int32_t V, int32_t nbits, Out o) {
+                                                     int32_t n_slots, int32_t V, int32_t nbits, SegOut o) {
   constexpr int W = TH / 64;
   extern __shared__ int32_t lds[];
   int32_t* hist = lds;                  // [V][n_slots]: counts, then cursors
@@ -566,7 +440,7 @@ template <int kBpt, bool OFFSETS>
 __device__ __forceinline__ void totals_and_layout(int32_t n_tokens, int32_t n_slots, int32_t n_chunks,
                                                   const int32_t* __restrict__ cnt, int32_t* __restrict__ coff,
                                                   const int32_t* __restrict__ bad_of,
-                                                  int32_t* __restrict__ slot_base, Out o, int32_t* total,
+                                                  int32_t* __restrict__ slot_base, SegOut o, int32_t* total,
                                                   LayoutLds<kWaves>& L, int& bad_cell) {
   const int tid = threadIdx.x, lane = tid & 63;
   if (tid == 0) bad_cell = 0;
@@ -617,7 +491,7 @@ template <int kBpt>
 __global__ __launch_bounds__(kThreads) void k_seg_scan(int32_t n_tokens, int32_t n_slots, int32_t n_chunks,
                                                        const int32_t* __restrict__ cnt, int32_t* __restrict__ coff,
                                                        const int32_t* __restrict__ bad_of,
-                                                       int32_t* __restrict__ slot_base, Out o) {
+                                                       int32_t* __restrict__ slot_base, SegOut o) {
   extern __shared__ int32_t total[];   // [n_slots]
   __shared__ LayoutLds<kWaves> L;
   __shared__ int bad_cell;
@@ -683,7 +557,7 @@ template <int kBpt>
 __global__ __launch_bounds__(kThreads) void k_seg_place(const int32_t* __restrict__ ids, int32_t n_tokens,
                                                         int32_t n_slots, int32_t V, int32_t nbits, int32_t chunk,
                                                         int32_t n_chunks, const int32_t* __restrict__ cnt,
-                                                        const int32_t* __restrict__ bad_of, Out o) {
+                                                        const int32_t* __restrict__ bad_of, SegOut o) {
   extern __shared__ int32_t lds[];   // chunk: rows [V][n_slots], slot bases [n_slots]; layout: totals
   __shared__ LayoutLds<kWaves> L;
   __shared__ int bad_cell;
@@ -857,8 +731,8 @@ lora_status lora_build_segments(const int32_t* ids, const lora_segments* seg, vo
   while ((1 << nbits) < n_slots) ++nbits;
   if (!set_lds_limit()) return LORA_ERR_HIP;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  const Out o{seg->perm, seg->seg_start, seg->seg_slot, seg->meta, seg->units, seg->tiles};
-  if (G == 0 && n <= kTinyTokens) {
+  const SegOut o{seg->perm, seg->seg_start, seg->seg_slot, seg->meta, seg->units, seg->tiles};
+  if (G == 0 && n <= kWaveSegTokens) {
     hipLaunchKernelGGL(k_segments_tiny, dim3(1), dim3(64), 0, st, ids, n, n_slots, nbits, o);
   } else if (G == 0) {
     const int th = one_group_threads(n, n_slots);

@@ -15,7 +15,7 @@ from typing import List, Optional, Tuple
 import numpy as np
 import torch
 
-from . import (LORA_BF16, LORA_F32, lora_apply_bgmv, lora_apply_bgmv_packed, lora_apply_sgmv, lora_apply_sgmv_multi,
+from . import (LORA_BF16, LORA_F32, lora_apply_bgmv, lora_apply_bgmv_ids, lora_apply_bgmv_packed, lora_apply_sgmv, lora_apply_sgmv_multi,
                lora_build_segments, lora_expand,
                lora_fused_gemm, lora_fused_gemm_fp8w,
                lora_pool_create, lora_pool_destroy, lora_pool_load, lora_segments_bind,
@@ -224,6 +224,17 @@ class DeviceWorkload:
                 yp = y.data_ptr() + (a - m0) * y.stride(0) * y.element_size()
                 lora_apply_bgmv(self.pool, a, b - a, self._xp(xo), mods[m0].h_in, msx, self.seg, yp,
                                 mods[m0].h_out, y.stride(0), ydt, stream)
+
+    def bgmv_ids(self, stream=None):
+        """As bgmv(), straight from the ids (lora_apply_bgmv_ids: no segment build; <= 64 tokens)."""
+        ydt = LORA_BF16 if self.y_dtype == "bf16" else LORA_F32
+        mods = self.wl.modules
+        for gi, (m0, m1) in enumerate(self.groups):
+            y = self.y[gi]
+            for (a, b, xo, msx) in self._x_runs(m0, m1):
+                yp = y.data_ptr() + (a - m0) * y.stride(0) * y.element_size()
+                lora_apply_bgmv_ids(self.pool, a, b - a, self._xp(xo), mods[m0].h_in, msx, self.ids, self.n, yp,
+                                    mods[m0].h_out, y.stride(0), ydt, stream)
 
     def bgmv_packed(self, stream=None):
         """As bgmv(), with runs of 2..4 modules that share x through lora_apply_bgmv_packed."""

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     import segmented_gathered_rank_amd as sgr
-    assert sgr.lora_abi_version() == 7
+    assert sgr.lora_abi_version() == 8
     for code in sgr.STATUS:
         assert sgr.lora_status_str(code) and sgr.lora_status_str(code) != "unknown status"
 
