@@ -637,10 +637,11 @@ __global__ __launch_bounds__(kGemvThreads, 4) void k_bgmv_ids(GemvArgs a, const 
   __shared__ int32_t perm_s[kWaveSegTokens], seg_start_s[kWaveSegTokens + 1], seg_slot_s[kWaveSegTokens];
   __shared__ int32_t meta_s[LORA_META_WORDS];
   __shared__ int2 units_s[kIdsMaxUnits], tiles_s[2];
-  if (threadIdx.x < 64)   // wave 0
+  if (threadIdx.x < 64)   // wave 0; its slot table lives where the x rows go later
     segments_of_wave(ids, n_tokens, a.pv.n_slots, nbits,
                      SegOut{perm_s, seg_start_s, seg_slot_s, meta_s, reinterpret_cast<int32_t*>(units_s),
-                            reinterpret_cast<int32_t*>(tiles_s)});
+                            reinterpret_cast<int32_t*>(tiles_s)},
+                     reinterpret_cast<uint32_t*>(lds + gemv_xs_offset<0, TI>()));
   __syncthreads();
   a.sv.perm = perm_s;
   a.sv.seg_start = seg_start_s;

@@ -148,7 +148,8 @@ __device__ __forceinline__ void block_add(int v, int lane, int* cell) {
 // Batches of up to 64 tokens: one wave, one token per lane (segments_of_wave).
 __global__ __launch_bounds__(64) void k_segments_tiny(const int32_t* __restrict__ ids, int32_t n_tokens,
                                                       int32_t n_slots, int32_t nbits, SegOut o) {
-  segments_of_wave(ids, n_tokens, n_slots, nbits, o);
+  __shared__ uint32_t table[64];
+  segments_of_wave(ids, n_tokens, n_slots, nbits, o, table);
 }
 
 // Long segments whose unit and tile records the whole workgroup writes

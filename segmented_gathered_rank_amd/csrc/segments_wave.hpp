@@ -70,8 +70,11 @@ __device__ __forceinline__ int2 unit_record(int slot, int run, int u, int first)
 // builders, without their histogram, barriers and layout phases.  Called by
 // all 64 lanes of one wave; n_tokens <= kWaveSegTokens.
 constexpr int kWaveSegTokens = 64;
+// table: 64 words of LDS the wave may use (or null): with at most 64 slots the
+// sums over smaller slots come from one scan over a slot table instead of a
+// loop over the segments.
 __device__ __forceinline__ void segments_of_wave(const int32_t* __restrict__ ids, int32_t n_tokens, int32_t n_slots,
-                                                 int32_t nbits, SegOut o) {
+                                                 int32_t nbits, SegOut o, uint32_t* table = nullptr) {
   const int lane = static_cast<int>(threadIdx.x) & 63;
   const bool in = lane < n_tokens;
   const int id = in ? ids[lane] : -1;
@@ -92,11 +95,30 @@ __device__ __forceinline__ void segments_of_wave(const int32_t* __restrict__ ids
                                     (static_cast<uint32_t>(nt) << 28)
                               : 0u;
   uint32_t before = 0;   // the same sums over the segments of smaller slots
-  for (uint64_t fm = __ballot(first); fm; fm &= fm - 1) {
-    const int j = lowest_lane(fm);
-    const int idj = __builtin_amdgcn_readlane(id, j);
-    const uint32_t pj = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mine), j));
-    if (valid && idj < id) before += pj;
+  if (table != nullptr && n_slots <= 64) {   // uniform
+    // slot s's record at table[s], then its exclusive prefix over the slots (each field's sum
+    // stays inside its bits, so the packed words add field by field)
+    table[lane] = 0u;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (first) table[id] = mine;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    const uint32_t v = table[lane];
+    const uint32_t incl = static_cast<uint32_t>(wave_scan<false>(static_cast<int>(v)));
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    table[lane] = incl - v;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (valid) before = table[id];
+  } else {
+    for (uint64_t fm = __ballot(first); fm; fm &= fm - 1) {
+      const int j = lowest_lane(fm);
+      const int idj = __builtin_amdgcn_readlane(id, j);
+      const uint32_t pj = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mine), j));
+      if (valid && idj < id) before += pj;
+    }
   }
   const int seg = before & 127, start = (before >> 7) & 127, su = (before >> 14) & 127;
   const int lu = (before >> 21) & 127, tl = static_cast<int>(before >> 28);
