@@ -349,6 +349,38 @@ bool launch_shrink_pair(const ShrinkPlan& p1, int32_t n1, const ShrinkPlan& p2, 
   return true;
 }
 
+// Work items per unit of a fused BGMV launch: with few modules the units leave
+// most of the GPU idle and each unit's chain of round trips sets the latency,
+// so a unit is split into column ranges, each item running the whole shrink
+// (from the same XCD's L2 after the first) and its range of the expand: as many
+// ranges as the resident workgroups (four per CU) hold beside the launch's
+// units, at most one 4-column chunk per thread.  A single module of 64 decode
+// tokens over 32 slots (48 units at most) takes 4 ranges of 4096 columns:
+// 28.2 -> 20.4 us per call; the 128-module launch keeps 1.
+int32_t bgmv_parts(int device, int32_t n_modules, int32_t max_units, int32_t h_out) {
+  static std::mutex mu;
+  static std::map<int, int> cus_of;
+  int cus = 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cus_of.find(device);
+    if (it == cus_of.end()) {
+      if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) {
+        (void)hipGetLastError();
+        cus = 0;
+      }
+      cus_of.emplace(device, cus);
+    } else {
+      cus = it->second;
+    }
+  }
+  const int64_t resident = 4 * static_cast<int64_t>(cus);
+  const int64_t items = static_cast<int64_t>(n_modules) * std::max(max_units, 1);
+  const int32_t by_cols = std::max(1, h_out / (4 * kGemvThreads));
+  const int64_t by_room = resident / items;
+  return static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(by_cols, by_room)));
+}
+
 static_assert(LORA_IDS_MAX_TOKENS == kWaveSegTokens, "the ids path builds the unit list on one wave");
 
 // The fused BGMV from the ids (k_bgmv_ids): grid as launch_bgmv's, one workgroup
@@ -365,20 +397,21 @@ lora_status launch_bgmv_ids(const lora_pool* p, int32_t module0, int32_t n_modul
   g.ld_y = ld_y;
   g.msy = msy;
   g.pack = 1;
-  g.x_stream = (msx == 0 && n_modules > 1) ? 0 : 1;   // x rows read by one work item only are streamed
   int32_t nbits = 0;
   while ((1 << nbits) < p->n_slots) ++nbits;
   const int32_t units = max_units_of(n, p->n_slots);
+  g.parts = bgmv_parts(p->device, n_modules, units, static_cast<int32_t>(p->h_out[module0]));
+  g.x_stream = (msx == 0 && n_modules > 1) || g.parts > 1 ? 0 : 1;   // x rows read by one work item only are streamed
   if (n_modules >= kBgmvGroupedFrom) {
-    const unsigned gxg = static_cast<unsigned>(units);
+    const unsigned gxg = static_cast<unsigned>(units * g.parts);
     if (static_cast<int64_t>(n_modules) * gxg * kGemvThreads > static_cast<int64_t>(UINT32_MAX)) return LORA_ERR_SHAPE;
     g.module_group = std::min(kBgmvModuleGroup, n_modules);
     g.group_nx = static_cast<int32_t>(gxg);
     hipLaunchKernelGGL((k_bgmv_ids<TI, TO>), dim3(gxg * static_cast<unsigned>(n_modules)), dim3(kGemvThreads), 0, s,
                        g, ids, n, nbits);
   } else {
-    hipLaunchKernelGGL((k_bgmv_ids<TI, TO>), dim3(gemv_grid_of(units), n_modules), dim3(kGemvThreads), 0, s, g, ids,
-                       n, nbits);
+    hipLaunchKernelGGL((k_bgmv_ids<TI, TO>), dim3(gemv_grid_of(units * g.parts), n_modules), dim3(kGemvThreads), 0, s,
+                       g, ids, n, nbits);
   }
   return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
@@ -557,11 +590,12 @@ lora_status launch_bgmv(const lora_pool* p, int32_t module0, int32_t n_modules, 
   g.y = y;
   g.ld_y = ld_y;
   g.msy = msy;
-  const unsigned gx = gemv_grid_of(seg->max_units);
   const bool shared_x = msx == 0 && n_modules > 1;
   g.pack = packed ? n_modules : 1;
+  g.parts = packed ? 1 : bgmv_parts(p->device, n_modules, seg->max_units, static_cast<int32_t>(p->h_out[module0]));
+  const unsigned gx = gemv_grid_of(seg->max_units * g.parts);
   // x rows read by one work item only are streamed
-  g.x_stream = (!shared_x || packed) ? 1 : 0;
+  g.x_stream = ((!shared_x || packed) && g.parts == 1) ? 1 : 0;
   if (packed) {
     hipLaunchKernelGGL((k_bgmv_packed<TI, TO>), dim3(gx, 1), dim3(kGemvThreads), 0, s, g);
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
@@ -569,7 +603,8 @@ lora_status launch_bgmv(const lora_pool* p, int32_t module0, int32_t n_modules, 
   // several modules: one 1-D grid taken in groups of up to kBgmvModuleGroup modules.  There a
   // workgroup's unit is its place inside the group, so the grid needs no period: one
   // workgroup per unit the segments can hold (fewer empty workgroups between the groups)
-  const unsigned gxg = static_cast<unsigned>(std::min<int32_t>(std::max<int32_t>(seg->max_units, 1), kGemvMaxGrid));
+  const unsigned gxg =
+      static_cast<unsigned>(std::min<int32_t>(std::max<int32_t>(seg->max_units * g.parts, 1), kGemvMaxGrid));
   if (n_modules >= kBgmvGroupedFrom &&
       static_cast<int64_t>(n_modules) * gxg * kGemvThreads <= static_cast<int64_t>(UINT32_MAX)) {
     g.module_group = std::min(kBgmvModuleGroup, n_modules);

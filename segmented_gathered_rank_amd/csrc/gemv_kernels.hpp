@@ -392,7 +392,8 @@ struct GemvArgs {
   SegView sv;
   int32_t module0;
   int32_t units_word;   // meta word holding the unit count to process
-  int32_t parts;        // work items per unit (1 for MODE 0): rank-row blocks (MODE 1) or column ranges (MODE 2)
+  int32_t parts;        // work items per unit: rank-row blocks (MODE 1) or column ranges (MODE 0, 2; in
+                        // MODE 0 each range's item runs the whole shrink)
   int32_t h_in, h_out;
   uint32_t magic;       // reciprocal of the page size
   const void* x;
@@ -432,7 +433,9 @@ __device__ __forceinline__ void gemv_item(const GemvArgs& a, int m, int2 rec, in
   const int ids_a = (MODE == 2) ? 0 : a.pv.max_rank * ppr_a;   // page ids loaded for A
   const int ids_b = (MODE == 1) ? 0 : a.pv.max_rank * ppr_b;   // ... and for B, after A's
   const int slot = rec.x & 0xffff, nt = (rec.x >> 16) & 0xff, pos = rec.y;
-  const bool keep = (rec.x >> 24) & 1;
+  // pages several work items read (a segment of several units, or a unit split into
+  // column ranges) go through the caches; the others are streamed
+  const bool keep = ((rec.x >> 24) & 1) || (MODE == 0 && a.parts > 1);
   const int ei = slot * a.pv.n_modules + a.module0 + m;
   const SlotEntry e = a.pv.entries[ei];
   const int32_t* ids = a.pv.page_ids + static_cast<int64_t>(ei) * a.pv.ppe;
@@ -474,8 +477,8 @@ __device__ __forceinline__ void gemv_item(const GemvArgs& a, int m, int2 rec, in
   if constexpr (MODE != 1) {
     // column quads of this part: ranges of whole waves (64 quads), the last one ragged
     const int n_quads = a.h_out >> 2;
-    const int per = (MODE == 2) ? ((n_quads + a.parts - 1) / a.parts + 63) / 64 * 64 : n_quads;
-    const int q_begin = (MODE == 2) ? part * per : 0;
+    const int per = ((n_quads + a.parts - 1) / a.parts + 63) / 64 * 64;
+    const int q_begin = part * per;
     const int q_end = min(n_quads, q_begin + per);
     if (q_begin >= q_end) return;       // uniform
     constexpr bool nty = MODE == 0 && LORA_BGMV_NT_XY != 0;
