@@ -47,3 +47,12 @@ def test_graph_replay_shrink_expand():
     on a batch with short and long segments, captured and replayed."""
     _replays_match_eager(W.c3_sgmv_prefill(h=512, units=(2, 8), total_units=32, draw_w=False),
                          lambda dw: dw.sgmv_step())
+
+
+def test_graph_replay_bgmv_ids():
+    """The fused BGMV straight from the ids (one launch, its segment build in LDS) over four
+    modules, units split into column ranges, captured and replayed; and a one-module call."""
+    _replays_match_eager(W.c2_bgmv_decode(n_modules=4, h=4096, n_tokens=48, draw_w=False),
+                         lambda dw: dw.bgmv_ids())
+    _replays_match_eager(W.c2_bgmv_decode(n_modules=1, h=4096, n_tokens=64, draw_w=False),
+                         lambda dw: dw.bgmv_ids())
