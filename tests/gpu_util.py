@@ -13,8 +13,9 @@ def say(*a):
 
 def run(wl, mode, y_dtype=None, **kw):
     """Runs one step from y = y0: 'sgmv' (the harness's choice of lora_apply_sgmv or
-    lora_shrink + lora_expand), 'sgmv_calls' (always lora_shrink + lora_expand) or
-    'bgmv'; returns (dw, y per module as float64)."""
+    lora_shrink + lora_expand), 'sgmv_calls' (always lora_shrink + lora_expand),
+    'bgmv' (segment build + lora_apply_bgmv) or 'bgmv_ids' (lora_apply_bgmv_ids);
+    returns (dw, y per module as float64)."""
     from segmented_gathered_rank_amd.harness import DeviceWorkload, from_device
     import torch
     dw = DeviceWorkload(wl, y_dtype=y_dtype, **kw)
@@ -24,6 +25,8 @@ def run(wl, mode, y_dtype=None, **kw):
         dw.build_segments()
         dw.shrink()
         dw.expand()
+    elif mode == "bgmv_ids":
+        dw.bgmv_ids()
     else:
         dw.bgmv_step()
     torch.cuda.synchronize()

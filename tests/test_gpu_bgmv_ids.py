@@ -9,7 +9,8 @@ adapter index).
 * edges: 0 tokens (nothing written), 1 token, 64 tokens of one id (a segment
   long enough for a matrix-core tile), ids -1 and out of range (rows left as
   they were), 65 tokens (SHAPE, nothing launched);
-* the decode batch of 64 tokens over q, k, v, o of 4096 x 4096 against the oracle.
+* the decode batch of 64 tokens over q, k, v, o of 4096 x 4096 against the oracle;
+* one module of 4096 columns, whose units run as column ranges: exact sums, both paths.
 """
 import dataclasses
 
@@ -142,4 +143,20 @@ def test_qkvo_decode_full_size():
     for m in range(wl.n_modules):
         got = lo.decode(from_device(dw.y_of(m)), "bf16")
         assert_close(got, lo.apply_to_y0(wl, m), "bf16", f"module {m}")
+    dw.close()
+
+
+@pytest.mark.parametrize("path", ["bgmv", "bgmv_ids"])
+def test_split_units_exact(path):
+    """One module of 4096 columns: the launch splits each unit into 4 column ranges, each
+    running the whole shrink; integer inputs make every sum exact, so y equals the oracle."""
+    wl = W.integer_exact(n_tokens=64, h=4096)
+    dw = DeviceWorkload(wl)
+    if path == "bgmv":
+        dw.bgmv_step()
+    else:
+        dw.bgmv_ids()
+    torch.cuda.synchronize()
+    got = lo.decode(from_device(dw.y_of(0)), dw.y_dtype)
+    assert np.array_equal(got, lo.apply_to_y0(wl, 0))
     dw.close()

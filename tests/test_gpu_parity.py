@@ -515,10 +515,11 @@ def test_module_groups_with_short_tail(n_modules, mode):
 
 def test_c2_decode_128_modules_full_size_sampled():
     """The default decode batch: 64 tokens over 128 modules of 4096 x 4096 in one
-    bgmv, and through shrink and expand (four groups of 32 modules); modules at
-    every group edge against the oracle."""
+    launch straight from the ids (the launch the decode bench times), in one bgmv
+    after the segment build, and through shrink and expand (four groups of 32
+    modules); modules at every group edge against the oracle."""
     wl = W.c2_bgmv_decode(n_modules=128, draw_w=False)
-    for mode in ("bgmv", "sgmv"):
+    for mode in ("bgmv_ids", "bgmv", "sgmv"):
         say(f"C2 x128 full {mode}")
         dw, ys = run(wl, mode)
         for m in (0, 1, 31, 32, 63, 64, 95, 96, 126, 127):
