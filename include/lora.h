@@ -303,10 +303,13 @@ typedef struct {
  * layer's q, k, v sharing x beside o with its own): one shrink launch per run,
  * all with the same K split, their partial tiles in one layout over the
  * call's modules, then one expand launch over every module that adds them.
- * runs[0..n_runs) cover module0 .. module0 + n_modules - 1 in order.  Same
- * result as lora_shrink per run then one lora_expand, bit for bit when the
- * runs' own splits agree (each run takes the smallest split any run chooses,
- * so with unequal choices t's summation order can differ).  The workspace is
+ * On bf16 pools two runs (q,k,v beside o) share one shrink launch, and each
+ * then aims at half the workgroups lora_shrink aims at, so it may split K
+ * fewer ways.  runs[0..n_runs) cover module0 .. module0 + n_modules - 1 in
+ * order.  Same result as lora_shrink per run then one lora_expand, bit for
+ * bit when those calls take the same split (each run takes the smallest
+ * split any run chooses; a smaller workspace limits lora_shrink's split, so
+ * with unequal splits t's summation order differs).  The workspace is
  * lora_shrink_workspace_bytes(p, n_tokens, n_modules).  Other rules as
  * lora_apply_sgmv.  Errors: ARG (also: runs that do not cover the modules),
  * SHAPE, DTYPE, HIP; nothing is launched on an argument error. */

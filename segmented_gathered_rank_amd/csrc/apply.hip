@@ -26,6 +26,10 @@ constexpr int kMaxGrid = 4096;   // persistent grids loop over work beyond this
 #define LORA_SHRINK_WG_TARGET 512
 #endif
 constexpr int kShrinkWgTarget = LORA_SHRINK_WG_TARGET;   // matrix-core shrink: split K below this many workgroups
+#ifndef LORA_PAIR_WG_TARGET
+#define LORA_PAIR_WG_TARGET (LORA_SHRINK_WG_TARGET / 2)
+#endif
+constexpr int kPairWgTarget = LORA_PAIR_WG_TARGET;   // the same per run when two runs share one launch
 // LDS for the matrix-core shrink's staged A rows and page ids: three
 // workgroups fit in a CU's 160 KiB
 constexpr size_t kStreamLdsBudget = 52 * 1024;
@@ -172,13 +176,13 @@ bool shrink_has_tiles(const lora_pool* p, int32_t module0, const lora_segments* 
 // the tiles alone are too few, at most kMaxSplits, at least 256 elements of K per split,
 // and no more partial tiles than the workspace holds.
 ShrinkSplit shrink_split(const lora_pool* p, int32_t module0, int32_t n_modules, int64_t msx,
-                         const lora_segments* seg, size_t ws_bytes) {
+                         const lora_segments* seg, size_t ws_bytes, int32_t wg_target = kShrinkWgTarget) {
   const int32_t h_in = static_cast<int32_t>(p->h_in[module0]);
   if (!shrink_has_tiles(p, module0, seg)) return ShrinkSplit{1, (h_in + 31) / 32 * 32};
   const bool shared = (msx == 0 && n_modules > 1 && n_modules <= kShrinkMaxModules);
   const int32_t groups = shared ? 1 : n_modules;
   const int32_t est_tiles = (seg->n_tokens + kTileTokens - 1) / kTileTokens;
-  int32_t ks = kShrinkWgTarget / (est_tiles * groups > 0 ? est_tiles * groups : 1);
+  int32_t ks = wg_target / (est_tiles * groups > 0 ? est_tiles * groups : 1);
   if (ks > kMaxSplits) ks = kMaxSplits;
   if (ks > h_in / 256) ks = h_in / 256;
   if (ks < 1) ks = 1;
@@ -840,11 +844,14 @@ lora_status lora_apply_sgmv_multi(const lora_pool* p, int32_t module0, int32_t n
   if (!g.ok) return LORA_ERR_HIP;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // one K split for every run (the expand adds one set of splits per module): the
-  // smallest the runs choose, then as small as the workspace needs for all modules
+  // smallest the runs choose, then as small as the workspace needs for all modules.  Two
+  // bf16 runs share one shrink launch, so each aims at half the workgroups.
+  const bool paired = n_runs == 2 && p->dtype == LORA_BF16;
   int32_t ks = kMaxSplits;
   m = module0;
   for (int32_t r = 0; r < n_runs; ++r) {
-    ks = std::min(ks, shrink_split(p, m, runs[r].n_modules, runs[r].module_stride_x, seg, SIZE_MAX).ks);
+    ks = std::min(ks, shrink_split(p, m, runs[r].n_modules, runs[r].module_stride_x, seg, SIZE_MAX,
+                                   paired ? kPairWgTarget : kShrinkWgTarget).ks);
     m += runs[r].n_modules;
   }
   while (ks > 1 && split_ws_bytes(p, seg->n_tokens, n_modules, ks) > ws_bytes) --ks;
@@ -853,7 +860,7 @@ lora_status lora_apply_sgmv_multi(const lora_pool* p, int32_t module0, int32_t n
   const ShrinkSplit sp{(h_in + kps - 1) / kps, kps};
   // partial tiles exist only where the shrink splits K, on its matrix-core tiles
   const bool fold = sp.ks > 1 && shrink_has_tiles(p, module0, seg);
-  if (n_runs == 2 && p->dtype == LORA_BF16) {   // q,k,v beside o: one launch for both runs when it fits
+  if (paired) {   // q,k,v beside o: one launch for both runs when it fits
     const int32_t n0 = runs[0].n_modules;
     const ShrinkPlan p0 = plan_shrink<__bf16>(p, module0, n0, runs[0].x, runs[0].ld_x, runs[0].module_stride_x, seg,
                                               t, ld_t, module_stride_t, sp, ws, fold, 0, n_modules);

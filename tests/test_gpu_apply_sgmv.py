@@ -6,7 +6,7 @@ The expand adds the splits in the order lora_shrink's own sum does, so y must
 equal the two-call path bit for bit on every workload; the oracle comparisons
 of the same workloads run through the harness's step (which takes
 lora_apply_sgmv for them) in test_gpu_parity.py.  Covered: the prefill and
-mixed-rank batches at full size (K split 8 ways, rank caps 16 and 64), fp32
+mixed-rank batches at full size (K split 4 and 8 ways, rank caps 16 and 64), fp32
 output, shared-x modules with rank caps 32/48/64 (every partial-tile width),
 many modules per launch, fp32 pools (no matrix cores), no workspace (no split),
 and argument errors.
@@ -56,6 +56,25 @@ def _both(wl, y_dtype=None, folded=None, **kw):
     return out
 
 
+def _calls_with_split(wl, ks):
+    """y after lora_shrink per x run, each given a workspace that holds exactly ks K splits of
+    its modules (lora_shrink_workspace_bytes covers 8), then lora_expand."""
+    dw = DeviceWorkload(wl)
+    dw.build_segments()
+    n = len(wl.ids)
+    per_split = sgr.lora_shrink_workspace_bytes(dw.pool, n, 1) // 8   # one split of one module
+    for (m0, m1) in dw.in_groups:
+        h_in = wl.modules[m0].h_in
+        for (a, b, xo, msx) in dw._x_runs(m0, m1):
+            sgr.lora_shrink(dw.pool, a, b - a, dw._xp(xo), h_in, msx, dw.seg, dw.t[a], dw.ld_t, dw.t.stride(0),
+                            dw.ws, per_split * ks * (b - a))
+    dw.expand()
+    torch.cuda.synchronize()
+    out = [from_device(dw.y_of(m)).copy() for m in range(wl.n_modules)]
+    dw.close()
+    return out
+
+
 def _assert_same_bits(a, b, what):
     for m, (ya, yb) in enumerate(zip(a, b)):
         assert ya.dtype == yb.dtype
@@ -64,13 +83,18 @@ def _assert_same_bits(a, b, what):
 
 @pytest.mark.parametrize("name", ["c3", "c4"])
 def test_full_size_same_bits_as_two_calls(name):
-    """The mixed-rank batch (17 tiles, rank cap 64; lora_apply_sgmv) and a prefill of
-    4096 tokens on q, k, v sharing x beside o (lora_apply_sgmv_multi: two shrink launches
-    into one partial layout, one expand over the four modules): both split K 8 ways and
-    sum the splits in the expand."""
+    """The mixed-rank batch (17 tiles, rank cap 64; lora_apply_sgmv: K split 8 ways, as
+    lora_shrink splits it) and a prefill of 4096 tokens on q, k, v sharing x beside o
+    (lora_apply_sgmv_multi: both runs' tiles in one shrink launch, each run aiming at half
+    of lora_shrink's workgroups, so 64 tiles split K 4 ways; one partial layout, one expand
+    over the four modules), against lora_shrink + lora_expand with the same split."""
     wl = (W.c3_sgmv_prefill if name == "c3" else W.c4_mixed_rank)(draw_w=False)
     say(f"{name}: lora_apply_sgmv vs lora_shrink + lora_expand")
-    fused, calls = _both(wl, folded=True)
+    if name == "c4":
+        fused, calls = _both(wl, folded=True)
+    else:
+        fused, _ = _both(wl, folded=True)
+        calls = _calls_with_split(wl, 4)
     _assert_same_bits(fused, calls, name)
 
 
