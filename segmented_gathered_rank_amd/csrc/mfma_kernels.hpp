@@ -445,6 +445,13 @@ __device__ __forceinline__ void expand_mfma_body(const ExpandArgs& ea, const Blk
     // y block cb [64][TN]: coalesced 16-byte chunks, rows without a token read the first token's;
     // B block [rk <= 32 rows][TN] (bf16): rank row j, columns c0..c0+TN of that row
     u32x4 yv[YCH], bv[2];
+    // B chunk idx of a block (16-byte chunks, TN / 8 = 16 per rank row): each 256 chunks
+    // are 16 rank rows x 16 chunk columns with the rank row fastest, so the 16 lanes of a
+    // chunk column write 32 contiguous bytes of each transposed row in put_b (with the
+    // chunk column fastest, every lane of a wave wrote rows 8 apart: an 8-way bank conflict)
+    static_assert(TN / 8 == 16, "16 chunks per rank row of a block");
+    auto b_row = [](int idx) { return 16 * (idx >> 8) + (idx & 15); };
+    auto b_col = [](int idx) { return ((idx >> 4) & 15) * 8; };
     auto issue = [&](int cb, u32x4 (&yq)[YCH], u32x4 (&bq)[2]) {
       const int c0 = (b.y * ea.blocks + cb) * TN;
       const int p = c0 / h;                    // the column block lies inside page p of each row
@@ -460,7 +467,7 @@ __device__ __forceinline__ void expand_mfma_body(const ExpandArgs& ea, const Blk
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int idx = min(tid + kMfmaThreads * q, rk * (TN / 8) - 1);
-        const int j = idx / (TN / 8), c = (idx % (TN / 8)) * 8;
+        const int j = b_row(idx), c = b_col(idx);
         bq[q] = *reinterpret_cast<const u32x4*>(pages + static_cast<int64_t>(bids_s[min(j, rank - 1) * ppr + p]) * h +
                                                 off + c);
       }
@@ -553,12 +560,12 @@ __device__ __forceinline__ void expand_mfma_body(const ExpandArgs& ea, const Blk
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int idx = tid + kMfmaThreads * q;
-        if (idx < rk * (TN / 8)) put_b(idx / (TN / 8), (idx % (TN / 8)) * 8, bv[q]);
+        if (idx < rk * (TN / 8)) put_b(b_row(idx), b_col(idx), bv[q]);
       }
       for (int base = 2 * kMfmaThreads; base < rk * (TN / 8); base += kMfmaThreads) {   // ranks above 32
         const int idx = base + tid;
         if (idx < rk * (TN / 8)) {
-          const int j = idx / (TN / 8), c = (idx % (TN / 8)) * 8;
+          const int j = b_row(idx), c = b_col(idx);
           put_b(j, c, *reinterpret_cast<const u32x4*>(
                           pages + static_cast<int64_t>(bids_s[min(j, rank - 1) * ppr + p]) * h + off + c));
         }
