@@ -342,13 +342,24 @@ __global__ __launch_bounds__(kMfmaThreads) void k_shrink_reduce(ShrinkArgs a) {
 // rows), and between LDS and the MFMA layout with 8- or 16-byte accesses.
 // T (fp32) is staged once per tile, the B block (bf16) once per column block.
 // LDS of expand_mfma_body for pool rank cap ldr and y element size ysz: the
-// three bf16 parts of the T tile [3][64][r16+8], the transposed B block
-// [128][r16+8] (bf16) and the y block [64][128 + 16/ysz].
+// three bf16 parts of the T tile [3][64][r16+8], the B block [r16][kExpandBRow]
+// (bf16, rank rows as stored) and the y block [64][128 + 16/ysz].
+constexpr int kExpandBRow = kExpandCols + 32;   // B block row stride (bf16): 80 words, 16 mod 64 banks
 __host__ __device__ inline int expand_r16(int ldr) { return (ldr + 15) & ~15; }
 __host__ __device__ inline size_t expand_lds_bytes(int ldr, int ysz) {
   const size_t ld = static_cast<size_t>(expand_r16(ldr) + 8);
-  return 3 * kTileTokens * ld * 2 + static_cast<size_t>(kExpandCols) * ld * 2 +
+  return 3 * kTileTokens * ld * 2 + static_cast<size_t>(expand_r16(ldr)) * kExpandBRow * 2 +
          static_cast<size_t>(kTileTokens) * (kExpandCols + 16 / ysz) * ysz;
+}
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
+// LDS transpose read (ds_read_b64_tr_b16): in each group of 16 lanes, lane 4r + q gives the
+// address of 4 consecutive bf16 values; lane i receives, in slot r, value i % 4 of lane
+// 4r + i / 4's four.  So with lane 4r + q pointing at column c + 4q of row j + r, lane i
+// gets rows j .. j + 3 of column c + i.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(reinterpret_cast<lds_bf16x4_t*>(reinterpret_cast<uintptr_t>(p)));
 }
 
 struct ExpandArgs {
@@ -387,10 +398,10 @@ __device__ __forceinline__ void expand_mfma_body(const ExpandArgs& ea, const Blk
   constexpr int YCH = kTileTokens * YCPR / kMfmaThreads;   // y chunks per thread
   constexpr int YV = 16 / sizeof(TO);                 // elements per 16-byte chunk
   const int r16 = expand_r16(ldr);
-  const int LD = r16 + 8;                             // row stride of T3_s and BT_s (bf16)
+  const int LD = r16 + 8;                             // row stride of T3_s (bf16)
   __bf16* T3_s = reinterpret_cast<__bf16*>(smem);                                  // [3][64][LD]
-  __bf16* BT_s = T3_s + 3 * kTileTokens * LD;                                      // [TN][LD]
-  TO* Y_s = reinterpret_cast<TO*>(BT_s + TN * LD);                                 // [64][YLD]
+  __bf16* B_s = T3_s + 3 * kTileTokens * LD;                                       // [r16][kExpandBRow]
+  TO* Y_s = reinterpret_cast<TO*>(B_s + r16 * kExpandBRow);                         // [64][YLD]
   __shared__ int32_t toks_s[kTileTokens];
   __shared__ int32_t bids_s[kMaxEntryPages];   // B page ids of the tile's (slot, module): row j, page p at j*ppr + p
 
@@ -445,13 +456,11 @@ __device__ __forceinline__ void expand_mfma_body(const ExpandArgs& ea, const Blk
     // y block cb [64][TN]: coalesced 16-byte chunks, rows without a token read the first token's;
     // B block [rk <= 32 rows][TN] (bf16): rank row j, columns c0..c0+TN of that row
     u32x4 yv[YCH], bv[2];
-    // B chunk idx of a block (16-byte chunks, TN / 8 = 16 per rank row): each 256 chunks
-    // are 16 rank rows x 16 chunk columns with the rank row fastest, so the 16 lanes of a
-    // chunk column write 32 contiguous bytes of each transposed row in put_b (with the
-    // chunk column fastest, every lane of a wave wrote rows 8 apart: an 8-way bank conflict)
+    // B chunk idx of a block (16-byte chunks, TN / 8 = 16 per rank row, chunk column fastest):
+    // a row's 16 chunks are loaded and stored by 16 consecutive lanes
     static_assert(TN / 8 == 16, "16 chunks per rank row of a block");
-    auto b_row = [](int idx) { return 16 * (idx >> 8) + (idx & 15); };
-    auto b_col = [](int idx) { return ((idx >> 4) & 15) * 8; };
+    auto b_row = [](int idx) { return idx >> 4; };
+    auto b_col = [](int idx) { return (idx & 15) * 8; };
     auto issue = [&](int cb, u32x4 (&yq)[YCH], u32x4 (&bq)[2]) {
       const int c0 = (b.y * ea.blocks + cb) * TN;
       const int p = c0 / h;                    // the column block lies inside page p of each row
@@ -472,15 +481,11 @@ __device__ __forceinline__ void expand_mfma_body(const ExpandArgs& ea, const Blk
                                                 off + c);
       }
     };
-    // B chunk (row j, columns c..c+7) into the transposed block, zero for rows past the rank
+    // B chunk (row j, columns c..c+7) into the block as stored, zero for rows past the rank;
+    // the matrix-core loop reads it transposed (lds_read_tr16)
     auto put_b = [&](int j, int c, u32x4 v) {
       if (j >= rank) v = u32x4{0u, 0u, 0u, 0u};
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        BT_s[(c + 2 * i) * LD + j] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(w[i] & 0xffffu));
-        BT_s[(c + 2 * i + 1) * LD + j] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(w[i] >> 16));
-      }
+      *reinterpret_cast<u32x4*>(&B_s[j * kExpandBRow + c]) = v;
     };
     const int n_cb = min(ea.blocks, (h_out - b.y * ea.blocks * TN + TN - 1) / TN);
     // T tile: t = hi + mid + lo, three bf16 values whose sum is t exactly (3 x 8 significand
@@ -550,7 +555,7 @@ __device__ __forceinline__ void expand_mfma_body(const ExpandArgs& ea, const Blk
       const int c0 = (b.y * ea.blocks + cb) * TN;
       const int p = c0 / h;
       const int off = c0 - p * h;
-      __syncthreads();                         // the previous block's BT_s / Y_s reads are done
+      __syncthreads();                         // the previous block's B_s / Y_s reads are done
 #pragma unroll
       for (int q = 0; q < YCH; ++q) {
         const int idx = tid + kMfmaThreads * q;
@@ -578,11 +583,18 @@ __device__ __forceinline__ void expand_mfma_body(const ExpandArgs& ea, const Blk
       // Y^T[col][token] += B^T[col][j] T^T[j][token] on v_mfma_f32_32x32x16_bf16: A = B^T
       // (lane -> column l%32 of the wave's 32, j = 8(l/32)..+8), B = one part of T^T (lane ->
       // token l%32 or 32 + l%32, same j), K = 16 per step
+      // A from the stored B block by two transpose reads of 4 rank rows: in lane group
+      // g = l / 16, lane 4r + q points at row 8(g / 2) + r (+ 4) and column
+      // 32 w + 16(g % 2) + 4q, so lane l gets rows j0 .. j0 + 7 of column 32 w + l % 32
+      const int tg = lane >> 4, tl = lane & 15;
+      const __bf16* bt = B_s + (8 * (tg >> 1) + (tl >> 2)) * kExpandBRow + wave * 32 + 16 * (tg & 1) + 4 * (tl & 3);
       f32x16 acc0 = {}, acc1 = {};
 #pragma unroll 1
       for (int kk = 0; kk < rk; kk += 16) {
         const int j0 = kk + 8 * kh;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&BT_s[(wave * 32 + l32) * LD + j0]);
+        const bf16x4 a_lo = lds_read_tr16(bt + kk * kExpandBRow);
+        const bf16x4 a_hi = lds_read_tr16(bt + (kk + 4) * kExpandBRow);
+        const bf16x8 a = __builtin_shufflevector(a_lo, a_hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
         for (int part = 0; part < 3; ++part) {
           const __bf16* tp = T3_s + part * kTileTokens * LD;
