@@ -266,7 +266,7 @@ ShrinkPlan plan_shrink(const lora_pool* p, int32_t module0, int32_t n_modules, c
   // else equal sub-ranges (multiples of 32) that do
   const size_t ids_bytes = static_cast<size_t>(pl.per_wg) * a.max_pids * 4;
   const size_t row_bytes = static_cast<size_t>(pl.per_wg) * 16 * pl.ntiles * 2;   // per k of A rows
-  int32_t kc_max = static_cast<int32_t>((kStreamLdsBudget - ids_bytes) / row_bytes) - 8;
+  int32_t kc_max = static_cast<int32_t>((kStreamLdsBudget - ids_bytes) / row_bytes) - 16;
   kc_max = std::max(32, kc_max / 32 * 32);
   const int32_t n_sub = (kps + kc_max - 1) / kc_max;
   a.kc = ((kps + n_sub - 1) / n_sub + 31) / 32 * 32;

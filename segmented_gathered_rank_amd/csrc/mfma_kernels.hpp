@@ -91,7 +91,12 @@ __device__ __forceinline__ void shrink_stream_body(const ShrinkArgs& a, const Bl
   const __bf16* pages = static_cast<const __bf16*>(a.pv.pages);
   const int k_split = ks * a.k_per_split;
   const int k_split_end = min(a.h_in, k_split + a.k_per_split);
-  const int ALD = a.kc + 8;                                   // A_s row stride (bf16)
+  // A_s row stride (bf16): kc / 2 + 8 words, 8 mod 16.  A 16-byte fragment read serves
+  // its lanes in four rounds of 16, each round two runs of 8 lanes (0-7 with 24-31,
+  // 8-15 with 16-23, and the same in the upper half); lane l reads row l % 16 at
+  // column group l / 16, so a round's 16 reads cover 16 distinct 4-bank groups with
+  // this stride.  With kc + 8 (4 mod 16 words) lanes 0 and 31 met in one group.
+  const int ALD = a.kc + 16;
   __bf16* A_s = reinterpret_cast<__bf16*>(smem);              // [MODS][16*NTILES][ALD]
   int32_t* pid_s = reinterpret_cast<int32_t*>(smem + static_cast<size_t>(MODS) * 16 * NTILES * ALD * 2);
   __shared__ int32_t toks_s[kTileTokens];
@@ -271,10 +276,10 @@ __device__ __forceinline__ void shrink_stream_body(const ShrinkArgs& a, const Bl
   }
 }
 
-// LDS of shrink_stream_body: a sub-range's A rows [mods][16*ntiles][kc + 8] bf16 and
+// LDS of shrink_stream_body: a sub-range's A rows [mods][16*ntiles][kc + 16] bf16 and
 // the tile's A page ids [mods][max_pids].
 __host__ __device__ inline size_t stream_lds_bytes(int mods, int ntiles, int kc, int max_pids) {
-  return static_cast<size_t>(mods) * 16 * ntiles * (kc + 8) * 2 + static_cast<size_t>(mods) * max_pids * 4;
+  return static_cast<size_t>(mods) * 16 * ntiles * (kc + 16) * 2 + static_cast<size_t>(mods) * max_pids * 4;
 }
 
 // Prefetch depth of shrink_stream_body: 32-wide steps of x in flight per wave
